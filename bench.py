@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Benchmark of ragged paged attention with KV append on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the hot path over one batch: KV append of the batch's
+new tokens, then batched attention (all kernels, split-piece merge included),
+with the step's plan built and uploaded beforehand (the plan is host work done
+once per step and reused by every layer; its host time is reported as
+plan_ms).  Inputs are synthetic and seeded (workloads.py) and resident in HBM
+before timing starts.
+
+Default workload: the mixed chunked-prefill step (32 decodes with kv_len
+U{512..4096} plus one 512-token chunk at kv_len 1536; 32/32 heads, d 128,
+bf16, page 16).  `value` is its KV-read bandwidth: algorithmic KV bytes (every
+valid K and V row of every KV head read once) per second of step time.
+`parts` times the decode requests and the prefill chunk as batches of their
+own: decode KV-read GB/s and chunk TFLOP/s, each against the MI355X roofline.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode KV-read HBM GB/s + prefill-chunk attention TFLOP/s (1 GPU, % roofline)"
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+KERNELS = ("append", "generic", "decode", "prefill", "mla", "merge")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# Algorithmic work (valid tokens only; page padding, split partials and the
+# merge are overhead, not work)
+# ----------------------------------------------------------------------------
+
+
+def work(spec, qo_lens, kv_lens):
+    elem = spec.elem_bytes
+    row_stored = spec.head_dim_qk + (0 if spec.shared_latent else spec.head_dim_v)
+    pairs = 0
+    kv_bytes = 0
+    total_q = 0
+    for n, L in zip(qo_lens, kv_lens):
+        n, L = int(n), int(L)
+        c = L - n
+        pairs += (n * c + n * (n + 1) // 2) if spec.causal else n * L
+        kv_bytes += L * spec.num_kv_heads * row_stored * elem
+        total_q += n
+    qo_bytes = total_q * spec.num_qo_heads * (spec.head_dim_qk + spec.head_dim_v) * elem \
+        + total_q * spec.num_qo_heads * 4
+    return {
+        "pairs": pairs,
+        "flops": spec.num_qo_heads * pairs * 2 * (spec.head_dim_qk + spec.head_dim_v),
+        "kv_bytes": kv_bytes,
+        "qo_bytes": qo_bytes,
+        "append_bytes": 2 * total_q * spec.num_kv_heads * row_stored * elem,
+    }
+
+
+# ----------------------------------------------------------------------------
+# Setup
+# ----------------------------------------------------------------------------
+
+
+def sub_batch(meta, requests, tensors):
+    """A batch of some requests of `meta` over the same pools (rows re-packed)."""
+    import numpy as np
+    import torch
+    import workloads
+    qo = [int(meta.qo_indptr[r + 1] - meta.qo_indptr[r]) for r in requests]
+    pages = [meta.kv_page_indices[meta.kv_page_indptr[r]:meta.kv_page_indptr[r + 1]]
+             for r in requests]
+    sub = workloads.Meta(
+        qo_indptr=np.concatenate([[0], np.cumsum(qo)]).astype(np.int32),
+        kv_len=np.array([meta.kv_len[r] for r in requests], dtype=np.int32),
+        kv_page_indptr=np.concatenate([[0], np.cumsum([len(p) for p in pages])]).astype(np.int32),
+        kv_page_indices=np.concatenate(pages).astype(np.int32),
+        num_pages=meta.num_pages, page_size=meta.page_size)
+    rows = np.concatenate([np.arange(meta.qo_indptr[r], meta.qo_indptr[r + 1]) for r in requests])
+    idx = torch.from_numpy(rows).to(tensors["q"].device)
+    t = dict(tensors)
+    for k in ("q", "k_new", "v_new"):
+        if t[k] is not None:
+            t[k] = t[k].index_select(0, idx).contiguous()
+    return sub, t
+
+
+def make_plan(spec, meta):
+    import ragged_paged_kv_append_amd as rpa
+    cfg = rpa.make_config(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim_qk, spec.head_dim_v,
+                          spec.page_size, spec.dtype, spec.causal, spec.sm_scale)
+    return rpa.Plan(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices,
+                    meta.num_pages)
+
+
+def plan_host_ms(spec, meta, reps=20):
+    import ragged_paged_kv_append_amd as rpa
+    cfg = rpa.make_config(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim_qk, spec.head_dim_v,
+                          spec.page_size, spec.dtype, spec.causal, spec.sm_scale)
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        h = rpa.rpa_plan_create(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr,
+                                meta.kv_page_indices, meta.num_pages)
+        ts.append(time.perf_counter() - t0)
+        rpa.rpa_plan_destroy(h)
+    ts.sort()
+    return 1e3 * ts[len(ts) // 2]
+
+
+def request_classes(plan):
+    items = plan.debug("items").reshape(-1, 8)
+    return {int(r): int(k) for r, k in zip(items[:, 0], items[:, 7])}
+
+
+# ----------------------------------------------------------------------------
+# Timing
+# ----------------------------------------------------------------------------
+
+
+def timed_steps(step, steps, warmup):
+    """Runs warmup steps, then times exactly `steps` steps; returns (ms/step,
+    {kernel: (avg ms, launches per step)}) with per-kernel HIP-event timings."""
+    import torch
+    import ragged_paged_kv_append_amd as rpa
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    rpa.rpa_profile_reset()
+    rpa.rpa_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rpa.rpa_profile_enable(False)
+    kernels = {}
+    for name in KERNELS:
+        tot, n = rpa.rpa_profile_read(name)
+        if n:
+            kernels[name] = (tot / n, n / steps)
+    return 1e3 * (t1 - t0) / steps, kernels
+
+
+def run_batch(spec, meta, tensors, steps, warmup):
+    plan = make_plan(spec, meta)
+
+    def step():
+        plan.append(tensors["k_new"], tensors["v_new"], tensors["k_pool"], tensors["v_pool"])
+        plan.attention(tensors["q"], tensors["k_pool"], tensors["v_pool"], o=out["o"],
+                       lse=out["lse"])
+
+    import torch
+    out = {"o": torch.empty((meta.total_q, spec.num_qo_heads, spec.head_dim_v),
+                            dtype=tensors["q"].dtype, device=tensors["q"].device),
+           "lse": torch.empty((meta.total_q, spec.num_qo_heads), dtype=torch.float32,
+                              device=tensors["q"].device)}
+    ms, kernels = timed_steps(step, steps, warmup)
+    if not torch.isfinite(out["o"].float()).all():
+        raise RuntimeError("non-finite attention output")
+    return plan, ms, kernels
+
+
+def roofline_for(spec, meta, plan, kernels):
+    """Roofline entry of the attention kernel that takes the most time per step."""
+    attn = {k: v for k, v in kernels.items() if k in ("generic", "decode", "prefill", "mla")}
+    if not attn:
+        return None
+    name = max(attn, key=lambda k: attn[k][0] * attn[k][1])
+    avg_ms, per_step = attn[name]
+    cls_id = {"generic": 0, "decode": 1, "prefill": 2, "mla": 3}[name]
+    rc = request_classes(plan)
+    reqs = [r for r in range(meta.batch_size) if rc.get(r) == cls_id]
+    qo = [int(meta.qo_indptr[r + 1] - meta.qo_indptr[r]) for r in reqs]
+    kv = [int(meta.kv_len[r]) for r in reqs]
+    w = work(spec, qo, kv)
+    launch_s = avg_ms * 1e-3
+    if name in ("prefill", "mla"):
+        achieved = w["flops"] / per_step / launch_s / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                "avg_launch_us": avg_ms * 1e3,
+                "algorithmic_per_launch": {"flops": w["flops"] / per_step}}
+    nbytes = (w["kv_bytes"] + w["qo_bytes"]) / per_step
+    achieved = nbytes / launch_s / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "avg_launch_us": avg_ms * 1e3, "algorithmic_per_launch": {"bytes": nbytes}}
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample, on this host's cores
+# ----------------------------------------------------------------------------
+
+
+def cpu_baseline(spec, meta, tensors, requests, unit):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+
+    def raw(t):
+        import torch
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    def f64(a):
+        return oracle.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+    sub, t = sub_batch(meta, requests, tensors)
+    # the sample's pages, renumbered (input preparation, not timed)
+    pages = sub.kv_page_indices
+    import torch
+    pidx = torch.from_numpy(pages.astype(np.int64)).to(tensors["k_pool"].device)
+    kp = f64(raw(tensors["k_pool"].index_select(0, pidx)))
+    vp = None if tensors["v_pool"] is None else f64(raw(tensors["v_pool"].index_select(0, pidx)))
+    q = f64(raw(t["q"]))
+    b = oracle.Batch(sub.qo_indptr, sub.kv_len, sub.kv_page_indptr,
+                     np.arange(len(pages)), sub.page_size)
+    t0 = time.perf_counter()
+    oracle.attend(q, kp, vp, b, spec.num_qo_heads, spec.num_kv_heads, spec.sm_scale,
+                  head_dim_v=spec.head_dim_v, causal=spec.causal)
+    secs = time.perf_counter() - t0
+    qo = [int(sub.qo_indptr[r + 1] - sub.qo_indptr[r]) for r in range(sub.batch_size)]
+    w = work(spec, qo, sub.kv_len)
+    value = (w["kv_bytes"] / secs / 1e9) if unit == "GB/s" else (w["flops"] / secs / 1e12)
+    return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "seconds": secs,
+            "sample": f"fp64 numpy oracle attention over {len(requests)} of {meta.batch_size} "
+                      f"requests of the same workload ({w['kv_bytes'] / 1e9:.3f} GB of KV, "
+                      f"{w['flops'] / 1e9:.2f} GFLOP)"}
+
+
+# ----------------------------------------------------------------------------
+# Main
+# ----------------------------------------------------------------------------
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixed_7b",
+                    choices=["mixed_7b", "decode_verify_gqa", "mla_absorbed"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads
+    import ragged_paged_kv_append_amd as rpa
+
+    rpa.lib()
+    torch.cuda.set_device(0)
+    name = args.workload
+    log(f"workload {name}: generating inputs")
+    spec, meta, tensors = workloads.workload(name, device="cuda")
+    torch.cuda.synchronize()
+    qo = [int(meta.qo_indptr[r + 1] - meta.qo_indptr[r]) for r in range(meta.batch_size)]
+    w = work(spec, qo, meta.kv_len)
+
+    log(f"workload {name}: timing {args.steps} steps after {args.warmup} warmup")
+    plan, ms, kernels = run_batch(spec, meta, tensors, args.steps, args.warmup)
+    roof = roofline_for(spec, meta, plan, kernels)
+    plan_ms = plan_host_ms(spec, meta)
+
+    unit = "TFLOP/s" if name == "mla_absorbed" else "GB/s"
+    if unit == "GB/s":
+        value = w["kv_bytes"] / (ms * 1e-3) / 1e9
+    else:
+        value = w["flops"] / (ms * 1e-3) / 1e12
+
+    parts = {}
+    if name == "mixed_7b":
+        dec = [r for r in range(meta.batch_size) if qo[r] == 1]
+        pre = [r for r in range(meta.batch_size) if qo[r] > 1]
+        for label, reqs in (("decode", dec), ("prefill_chunk", pre)):
+            sm, st = sub_batch(meta, reqs, tensors)
+            log(f"part {label}: {len(reqs)} requests")
+            sqo = [int(sm.qo_indptr[r + 1] - sm.qo_indptr[r]) for r in range(sm.batch_size)]
+            sw = work(spec, sqo, sm.kv_len)
+            _, pms, pk = run_batch(spec, sm, st, args.steps, args.warmup)
+            attn_ms = sum(v[0] * v[1] for k, v in pk.items() if k != "append")
+            entry = {"requests": len(reqs), "ms_per_step": pms, "attention_ms": attn_ms,
+                     "kernels_us": {k: v[0] * 1e3 for k, v in pk.items()}}
+            if label == "decode":
+                gbps = (sw["kv_bytes"] + sw["qo_bytes"]) / (attn_ms * 1e-3) / 1e9
+                entry.update({"kv_read_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS})
+            else:
+                tf = sw["flops"] / (attn_ms * 1e-3) / 1e12
+                entry.update({"tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS})
+            parts[label] = entry
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle on a bounded sample")
+        if name == "mixed_7b":
+            sample = list(range(meta.batch_size))
+        elif name == "decode_verify_gqa":
+            sample = list(range(0, meta.batch_size, 16))
+        else:
+            sample = list(range(0, meta.batch_size, 8))
+        cpu = cpu_baseline(spec, meta, tensors, sample, unit)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "requests": meta.batch_size, "total_q": meta.total_q,
+                   "num_qo_heads": spec.num_qo_heads, "num_kv_heads": spec.num_kv_heads,
+                   "head_dim_qk": spec.head_dim_qk, "head_dim_v": spec.head_dim_v,
+                   "page_size": spec.page_size, "kv_tokens": int(np.sum(meta.kv_len)),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "work": {"kv_bytes": w["kv_bytes"], "flops": w["flops"], "qo_bytes": w["qo_bytes"]},
+        "kernels_us": {k: v[0] * 1e3 for k, v in kernels.items()},
+        "launches_per_step": {k: v[1] for k, v in kernels.items()},
+        "plan_ms": plan_ms,
+        "parts": parts,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

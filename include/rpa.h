@@ -1,0 +1,234 @@
+/*
+ * rpa.h -- ragged paged attention with KV append for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of librpa.so.  Plain pointers and sizes only.  Device pointers are
+ * HIP device addresses; a `stream` argument is a hipStream_t passed as void*.
+ *
+ * The problem, as the source pages state it
+ * -----------------------------------------
+ * "Disaggregated prefill and decode" (Perplexity), prefill/decode performance
+ * section: each request of a batch step brings qo_len new query tokens and
+ * attends over kv_len entries of its KV cache; decode has qo_len = 1, a
+ * prefill chunk a large qo_len.  "Accelerating Sonar through speculation"
+ * (Perplexity), runtime section: for every step the host allocates KV pages
+ * for the new tokens, packs tokens and page information, copies the metadata
+ * to the GPU and builds the attention metadata and intermediate buffers once,
+ * for prefill, decode and verification alike.  The disaggregation post, KV
+ * Messenger section: every layer appends its new KV entries to the cache, and
+ * they are valid after the append and before the attention that reads them.
+ * Same post, sharded-transfer section: pages use the HND layout (heads before
+ * tokens).  "Chunked prefill" (k4i.top), section "correctness": attention
+ * over the cache and over the current chunk combine by an online-softmax
+ * merge, so chunked prefill equals one-shot prefill.
+ *
+ * Shape of a step: rpa_plan_create (host) -> rpa_plan_upload (async H2D) ->
+ * per layer { rpa_kv_append ; rpa_batch_attention }.  The plan is reused by
+ * every layer of the step.
+ *
+ * Notation: request r has n_r = qo_len new tokens, L_r = kv_len keys counting
+ * the new ones, c_r = L_r - n_r cached keys, and page size P.  New token t of
+ * request r has global row i = qo_indptr[r] + t and absolute position
+ * p = c_r + t; with causal = 1 it sees keys 0 .. p (bottom-right alignment).
+ * G = num_qo_heads / num_kv_heads; query head h reads KV head h / G.
+ *
+ * Tensor layouts (elements; last dimension contiguous):
+ *   q      [total_q, num_qo_heads, head_dim_qk]      contiguous
+ *   k_new  [total_q, num_kv_heads, head_dim_qk]      contiguous
+ *   v_new  [total_q, num_kv_heads, head_dim_v]       contiguous
+ *   o      [total_q, num_qo_heads, head_dim_v]       contiguous, dtype of q
+ *   lse    [total_q, num_qo_heads]                   float32, natural log
+ *   pools  element (page, head, slot, d) at
+ *          page*page_stride + head*head_stride + slot*token_stride + d
+ *          (HND packed: token_stride = d, head_stride = P*d,
+ *           page_stride = H*P*d; interleaved K/V pages are expressed by strides)
+ *
+ * Ownership: the caller owns every device buffer (q, k_new, v_new, pools, o,
+ * lse, workspace) and every stream.  The library owns only rpa_plan objects
+ * (host memory plus a pinned staging buffer).  No call allocates device
+ * memory or synchronises a stream.
+ *
+ * A plan with no new tokens (total_q == 0) makes rpa_kv_append and
+ * rpa_batch_attention return RPA_OK at once; their tensor pointers may then
+ * be NULL.
+ *
+ * Errors: every call returns rpa_status; RPA_OK is 0, failures are negative.
+ * Arguments are validated on the host before anything is launched: on an
+ * error nothing is launched and no output is touched.  A thread-local message
+ * (rpa_last_error_message) describes the last failure.  No C++ exception
+ * crosses this interface.
+ */
+#ifndef RPA_H_
+#define RPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RPA_ABI_VERSION 1
+
+typedef enum rpa_status {
+  RPA_OK = 0,
+  RPA_ERR_INVALID_ARG = -1,         /* null pointer, bad size, misaligned buffer, bad metadata */
+  RPA_ERR_UNSUPPORTED = -2,         /* valid but not implemented: head dims, page size, dtype */
+  RPA_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace smaller than rpa_plan_workspace_size */
+  RPA_ERR_PAGE_OOB = -4,            /* a page id outside [0, num_pages), or too few pages */
+  RPA_ERR_DUPLICATE_WRITE_PAGE = -5,/* a page written by the append is referenced twice */
+  RPA_ERR_HIP = -6,                 /* a HIP runtime call failed */
+  RPA_ERR_NOT_UPLOADED = -7         /* the plan has not been uploaded to a workspace */
+} rpa_status;
+
+typedef enum rpa_dtype {
+  RPA_DTYPE_F32 = 0,  /* IEEE binary32 */
+  RPA_DTYPE_BF16 = 1  /* bfloat16; arithmetic accumulates in float32 */
+} rpa_dtype;
+
+/* Attention configuration, fixed for a plan.
+ *   num_qo_heads % num_kv_heads == 0.
+ *   (head_dim_qk, head_dim_v) in {(64,64), (128,128), (576,512)}; (576,512) is
+ *   the absorbed latent form: one latent KV head whose first 512 dims are the
+ *   value (v_cache == k_cache with the same strides).
+ *   page_size: a power of two in [1, 256].
+ *   causal: 1 = bottom-right causal (query t sees keys 0 .. c_r + t);
+ *           0 = every query sees all kv_len keys.
+ *   sm_scale: multiplier of q.k (e.g. 1/sqrt(head_dim_qk)). */
+typedef struct rpa_attn_config {
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim_qk;
+  int32_t head_dim_v;
+  int32_t page_size;
+  int32_t dtype;   /* rpa_dtype */
+  int32_t causal;
+  float sm_scale;
+} rpa_attn_config;
+
+/* Ragged batch of one step.  Host int32 arrays, owned by the caller, read only
+ * during rpa_plan_create.
+ *   qo_indptr[batch_size+1]: starts at 0, non-decreasing; n_r = qo_indptr[r+1]-qo_indptr[r].
+ *   kv_len[batch_size]: L_r >= n_r (the new tokens are the last n_r keys).
+ *   kv_page_indptr[batch_size+1], kv_page_indices[kv_page_indptr[batch_size]]:
+ *     CSR page table; request r needs at least ceil(L_r / P) entries, extra
+ *     entries are ignored.
+ *   num_pages: pool size; every used page id lies in [0, num_pages).
+ * A page that the append writes (one holding a position in c_r .. L_r-1) must
+ * not be referenced by any other (request, logical page) of the batch. */
+typedef struct rpa_batch_desc {
+  int32_t batch_size;
+  const int32_t* qo_indptr;
+  const int32_t* kv_len;
+  const int32_t* kv_page_indptr;
+  const int32_t* kv_page_indices;
+  int32_t num_pages;
+} rpa_batch_desc;
+
+/* Strides of a paged pool, in elements; the head dimension is contiguous.
+ * All strides must be multiples of 8 elements (16 bytes) for bf16 and of
+ * 4 elements for f32; token_stride >= the stored row length. */
+typedef struct rpa_cache_strides {
+  int64_t page_stride;
+  int64_t head_stride;
+  int64_t token_stride;
+} rpa_cache_strides;
+
+typedef struct rpa_plan rpa_plan;
+
+/* Validate a batch and build its plan on the host: the per-token append map,
+ * the attention work items (long kv_len split into pieces so that the GPU's
+ * num_cus compute units get balanced work; 0 means 256), and the merge map of
+ * the split pieces.  No device work; may be called without a GPU.  On success
+ * *out receives a plan owned by the library (free with rpa_plan_destroy).
+ * Errors: INVALID_ARG, UNSUPPORTED, PAGE_OOB, DUPLICATE_WRITE_PAGE. */
+rpa_status rpa_plan_create(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                           int32_t num_cus, rpa_plan** out);
+
+/* Device bytes the plan needs in its workspace: metadata plus float32 partial
+ * outputs of split pieces.  Host only. */
+rpa_status rpa_plan_workspace_size(const rpa_plan* plan, size_t* bytes);
+
+/* Copy the plan's metadata into a caller-owned device workspace (256-byte
+ * aligned, at least rpa_plan_workspace_size bytes) with one asynchronous
+ * host-to-device copy on `stream`, from a pinned staging buffer the plan
+ * owns.  Later calls with this plan use that workspace; it must stay alive
+ * and unmodified while they run.  Errors: INVALID_ARG, WORKSPACE_TOO_SMALL, HIP. */
+rpa_status rpa_plan_upload(rpa_plan* plan, void* d_workspace, size_t bytes, void* stream);
+
+/* KV append (the per-layer cache update).  For every new token (r, t) and KV
+ * head h, copies k_new[i, h, :] into k_cache at page pages_r[(c_r+t)/P],
+ * head h, slot (c_r+t)%P, and v_new likewise into v_cache.  A raw copy of the
+ * stored elements: no rounding, no other byte of the pools changes.
+ * Shared latent (head dims 576/512): pass v_new = NULL and v_cache = NULL or
+ * v_cache == k_cache; only k is written.  Pools are in the plan's dtype.
+ * Errors: INVALID_ARG, NOT_UPLOADED, HIP. */
+rpa_status rpa_kv_append(const rpa_plan* plan, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const rpa_cache_strides* ks,
+                         const rpa_cache_strides* vs, void* stream);
+
+/* Batched ragged attention over the paged cache (run after rpa_kv_append of
+ * the same step).  For every new token i of request r and query head h:
+ *   s_j = sm_scale * <q[i,h,:], K(r, h/G, j)> for visible keys j,
+ *   lse[i,h] = ln sum_j exp(s_j),  o[i,h,:] = sum_j exp(s_j - lse) V(r, h/G, j).
+ * Split pieces are combined by the log-sum-exp merge inside this call.
+ * For the shared latent form pass v_cache == k_cache (or NULL) and vs == ks
+ * (or NULL): values are the first head_dim_v elements of each key row.
+ * `lse` may be NULL.  Errors: INVALID_ARG, UNSUPPORTED, NOT_UPLOADED, HIP. */
+rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q, const void* k_cache,
+                               const void* v_cache, const rpa_cache_strides* ks,
+                               const rpa_cache_strides* vs, void* o, float* lse,
+                               void* stream);
+
+/* Standalone softmax merge of two attention states over disjoint key sets
+ * ("Chunked prefill", section "correctness"):
+ *   lse = ln(e^lse_a + e^lse_b),  o = e^(lse_a-lse) o_a + e^(lse_b-lse) o_b.
+ * o_a, o_b, o: [rows, heads, dim] in `dtype`; lse_a, lse_b, lse: [rows, heads]
+ * float32 (lse may be NULL); dim is a multiple of 8 and the o buffers are
+ * 16-byte aligned.  A state with lse = -inf contributes nothing;
+ * two -inf states give (-inf, 0).  o may alias o_a or o_b.
+ * Errors: INVALID_ARG, HIP. */
+rpa_status rpa_merge_state(const void* o_a, const float* lse_a, const void* o_b,
+                           const float* lse_b, void* o, float* lse, int64_t rows,
+                           int32_t heads, int32_t dim, int32_t dtype, void* stream);
+
+/* Free a plan.  Waits for the plan's last upload copy to finish reading the
+ * staging buffer.  NULL is ignored. */
+void rpa_plan_destroy(rpa_plan* plan);
+
+/* Static description of a status code. */
+const char* rpa_status_string(rpa_status status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* rpa_last_error_message(void);
+
+/* RPA_ABI_VERSION of the loaded library. */
+int32_t rpa_abi_version(void);
+
+/* Per-kernel timing for profiling.  While enabled (on = 1), the library
+ * records a pair of HIP events (timing enabled) on the launch stream around
+ * every kernel it launches.  rpa_profile_read waits for the recorded events,
+ * folds them into per-kernel totals and returns the total milliseconds and
+ * launch count of one kernel: "append", "generic", "decode", "prefill",
+ * "mla", "merge" or "merge_state".  rpa_profile_reset clears the totals.
+ * Process-wide and thread-safe; off by default.  Errors: INVALID_ARG, HIP. */
+rpa_status rpa_profile_enable(int32_t on);
+rpa_status rpa_profile_read(const char* kernel, double* total_ms, int64_t* launches);
+rpa_status rpa_profile_reset(void);
+
+/* Host-only introspection of a plan (for tests and tooling).  Copies up to
+ * `cap` int32 values of the named table into `dst` and stores the table's
+ * full length in *len.  Names: "items" (8 int32 per work item: request,
+ * kv head, first row, end row, first key, end key, split index, kernel
+ * class), "splits" (3 int32 per request: number of pieces, keys per piece,
+ * first partial row), "append" (2 int32 per new token: page id, slot),
+ * "merge_rows" (rows whose pieces are merged), "summary" (batch_size,
+ * total_q, num items, partial rows, number of items per kernel class 0..3).
+ * Errors: INVALID_ARG for an unknown name. */
+rpa_status rpa_plan_debug_dump(const rpa_plan* plan, const char* name, int32_t* dst,
+                               int64_t cap, int64_t* len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPA_H_ */

@@ -1,0 +1,330 @@
+"""Ragged paged attention with KV append for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``librpa.so`` (the C ABI declared in ``include/rpa.h``).
+It only marshals arguments: every step of the path runs in the library's HIP
+kernels.  PyTorch supplies device memory and streams.  If the library is not
+built, every call raises ``RpaError``; there is no fallback.
+
+Functions carry the C names (``rpa_plan_create``, ``rpa_plan_upload``,
+``rpa_kv_append``, ``rpa_batch_attention``, ``rpa_merge_state``, ...).  The
+``Plan`` class bundles a plan with its device workspace for convenience.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librpa.so")
+
+RPA_OK = 0
+RPA_ERR_INVALID_ARG = -1
+RPA_ERR_UNSUPPORTED = -2
+RPA_ERR_WORKSPACE_TOO_SMALL = -3
+RPA_ERR_PAGE_OOB = -4
+RPA_ERR_DUPLICATE_WRITE_PAGE = -5
+RPA_ERR_HIP = -6
+RPA_ERR_NOT_UPLOADED = -7
+
+RPA_DTYPE_F32 = 0
+RPA_DTYPE_BF16 = 1
+
+# Kernel classes reported by the plan's "items" table.
+KC_GENERIC, KC_DECODE, KC_PREFILL, KC_MLA = 0, 1, 2, 3
+
+EXPORTED_SYMBOLS = (
+    "rpa_plan_create", "rpa_plan_workspace_size", "rpa_plan_upload", "rpa_kv_append",
+    "rpa_batch_attention", "rpa_merge_state", "rpa_plan_destroy", "rpa_status_string",
+    "rpa_last_error_message", "rpa_abi_version", "rpa_plan_debug_dump", "rpa_profile_enable",
+    "rpa_profile_read", "rpa_profile_reset",
+)
+
+
+class RpaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class rpa_attn_config(ctypes.Structure):
+    _fields_ = [("num_qo_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+
+class rpa_batch_desc(ctypes.Structure):
+    _fields_ = [("batch_size", ctypes.c_int32), ("qo_indptr", ctypes.POINTER(ctypes.c_int32)),
+                ("kv_len", ctypes.POINTER(ctypes.c_int32)),
+                ("kv_page_indptr", ctypes.POINTER(ctypes.c_int32)),
+                ("kv_page_indices", ctypes.POINTER(ctypes.c_int32)),
+                ("num_pages", ctypes.c_int32)]
+
+
+class rpa_cache_strides(ctypes.Structure):
+    _fields_ = [("page_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("token_stride", ctypes.c_int64)]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librpa.so (raises RpaError if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise RpaError(RPA_ERR_UNSUPPORTED,
+                       f"HIP library not built: {LIB_PATH} is missing "
+                       "(run python -m ragged_paged_kv_append_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER
+    L.rpa_plan_create.argtypes = [P(rpa_attn_config), P(rpa_batch_desc), i32, P(vp)]
+    L.rpa_plan_workspace_size.argtypes = [vp, P(sz)]
+    L.rpa_plan_upload.argtypes = [vp, vp, sz, vp]
+    L.rpa_kv_append.argtypes = [vp, vp, vp, vp, vp, P(rpa_cache_strides), P(rpa_cache_strides), vp]
+    L.rpa_batch_attention.argtypes = [vp, vp, vp, vp, P(rpa_cache_strides),
+                                      P(rpa_cache_strides), vp, vp, vp]
+    L.rpa_merge_state.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
+    L.rpa_plan_destroy.argtypes = [vp]
+    L.rpa_plan_destroy.restype = None
+    L.rpa_status_string.argtypes = [i32]
+    L.rpa_status_string.restype = ctypes.c_char_p
+    L.rpa_last_error_message.argtypes = []
+    L.rpa_last_error_message.restype = ctypes.c_char_p
+    L.rpa_abi_version.argtypes = []
+    L.rpa_abi_version.restype = i32
+    L.rpa_plan_debug_dump.argtypes = [vp, ctypes.c_char_p, P(i32), i64, P(i64)]
+    L.rpa_profile_enable.argtypes = [i32]
+    L.rpa_profile_read.argtypes = [ctypes.c_char_p, P(ctypes.c_double), P(i64)]
+    L.rpa_profile_reset.argtypes = []
+    for name in ("rpa_plan_create", "rpa_plan_workspace_size", "rpa_plan_upload", "rpa_kv_append",
+                 "rpa_batch_attention", "rpa_merge_state", "rpa_plan_debug_dump",
+                 "rpa_profile_enable", "rpa_profile_read", "rpa_profile_reset"):
+        getattr(L, name).restype = i32
+    _lib_handle = L
+    return L
+
+
+def _check(status: int):
+    if status != RPA_OK:
+        L = lib()
+        msg = L.rpa_last_error_message().decode()
+        name = L.rpa_status_string(status).decode()
+        raise RpaError(status, f"{name}: {msg}")
+
+
+def _ptr(x) -> Optional[int]:
+    """Device/host address of a tensor, an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def make_config(num_qo_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size, dtype, causal=True,
+                sm_scale=None) -> rpa_attn_config:
+    if isinstance(dtype, str):
+        dtype = {"bf16": RPA_DTYPE_BF16, "f32": RPA_DTYPE_F32}[dtype]
+    if sm_scale is None:
+        sm_scale = head_dim_qk ** -0.5
+    return rpa_attn_config(num_qo_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size, dtype,
+                           1 if causal else 0, float(sm_scale))
+
+
+def strides_of(pool) -> rpa_cache_strides:
+    """Strides (elements) of a 4-D pool tensor [pages, heads, page_size, dim]."""
+    st = pool.stride()
+    if st[3] != 1:
+        raise RpaError(RPA_ERR_INVALID_ARG, "pool's last dimension must be contiguous")
+    return rpa_cache_strides(st[0], st[1], st[2])
+
+
+# ----------------------------------------------------------------------------
+# C-named entry points
+# ----------------------------------------------------------------------------
+
+
+class _PlanHandle:
+    def __init__(self, handle: int, arrays):
+        self.handle = handle
+        self._arrays = arrays
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            try:
+                lib().rpa_plan_destroy(h)
+            except Exception:
+                pass
+            self.handle = None
+
+
+def rpa_plan_create(cfg: rpa_attn_config, qo_indptr, kv_len, kv_page_indptr, kv_page_indices,
+                    num_pages: int, num_cus: int = 0) -> _PlanHandle:
+    """Host-only planning (no device work).  Returns a plan handle."""
+    L = lib()
+    arrays = [_i32(qo_indptr), _i32(kv_len), _i32(kv_page_indptr), _i32(kv_page_indices)]
+    batch = rpa_batch_desc(len(arrays[1]), _i32p(arrays[0]), _i32p(arrays[1]), _i32p(arrays[2]),
+                           _i32p(arrays[3]), int(num_pages))
+    out = ctypes.c_void_p()
+    _check(L.rpa_plan_create(ctypes.byref(cfg), ctypes.byref(batch), int(num_cus),
+                             ctypes.byref(out)))
+    return _PlanHandle(out.value, arrays)
+
+
+def rpa_plan_workspace_size(plan: _PlanHandle) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().rpa_plan_workspace_size(plan.handle, ctypes.byref(n)))
+    return n.value
+
+
+def rpa_plan_upload(plan: _PlanHandle, workspace, nbytes: int, stream=None):
+    _check(lib().rpa_plan_upload(plan.handle, _ptr(workspace), int(nbytes), _stream(stream)))
+
+
+def rpa_kv_append(plan: _PlanHandle, k_new, v_new, k_cache, v_cache, ks: rpa_cache_strides,
+                  vs: Optional[rpa_cache_strides], stream=None):
+    _check(lib().rpa_kv_append(plan.handle, _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                               _ptr(v_cache), ctypes.byref(ks),
+                               None if vs is None else ctypes.byref(vs), _stream(stream)))
+
+
+def rpa_batch_attention(plan: _PlanHandle, q, k_cache, v_cache, ks: rpa_cache_strides,
+                        vs: Optional[rpa_cache_strides], o, lse=None, stream=None):
+    _check(lib().rpa_batch_attention(plan.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     ctypes.byref(ks), None if vs is None else ctypes.byref(vs),
+                                     _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def rpa_merge_state(o_a, lse_a, o_b, lse_b, o, lse, rows: int, heads: int, dim: int, dtype: int,
+                    stream=None):
+    _check(lib().rpa_merge_state(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o),
+                                 _ptr(lse), int(rows), int(heads), int(dim), int(dtype),
+                                 _stream(stream)))
+
+
+def rpa_plan_destroy(plan: _PlanHandle):
+    if plan.handle:
+        lib().rpa_plan_destroy(plan.handle)
+        plan.handle = None
+
+
+def rpa_status_string(status: int) -> str:
+    return lib().rpa_status_string(int(status)).decode()
+
+
+def rpa_last_error_message() -> str:
+    return lib().rpa_last_error_message().decode()
+
+
+def rpa_abi_version() -> int:
+    return int(lib().rpa_abi_version())
+
+
+def rpa_plan_debug_dump(plan: _PlanHandle, name: str) -> np.ndarray:
+    L = lib()
+    n = ctypes.c_int64()
+    _check(L.rpa_plan_debug_dump(plan.handle, name.encode(), None, 0, ctypes.byref(n)))
+    out = np.zeros(max(n.value, 1), dtype=np.int32)
+    _check(L.rpa_plan_debug_dump(plan.handle, name.encode(), _i32p(out), n.value,
+                                 ctypes.byref(n)))
+    return out[:n.value]
+
+
+def rpa_profile_enable(on: bool = True):
+    _check(lib().rpa_profile_enable(1 if on else 0))
+
+
+def rpa_profile_read(kernel: str) -> tuple[float, int]:
+    """(total milliseconds, launches) of one kernel since the last reset."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().rpa_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def rpa_profile_reset():
+    _check(lib().rpa_profile_reset())
+
+
+# ----------------------------------------------------------------------------
+# Convenience wrapper
+# ----------------------------------------------------------------------------
+
+
+class Plan:
+    """A plan plus its device workspace (a torch uint8 tensor on ``device``)."""
+
+    def __init__(self, cfg: rpa_attn_config, qo_indptr, kv_len, kv_page_indptr, kv_page_indices,
+                 num_pages: int, device="cuda", num_cus: int = 0, stream=None):
+        import torch
+        self.cfg = cfg
+        self.handle = rpa_plan_create(cfg, qo_indptr, kv_len, kv_page_indptr, kv_page_indices,
+                                      num_pages, num_cus)
+        self.total_q = int(np.asarray(qo_indptr)[-1]) if len(qo_indptr) else 0
+        self.ws_bytes = rpa_plan_workspace_size(self.handle)
+        self.workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)
+        base = self.workspace.data_ptr()
+        self.ws_ptr = (base + 255) // 256 * 256
+        rpa_plan_upload(self.handle, self.ws_ptr, self.ws_bytes, stream)
+
+    @property
+    def shared_latent(self) -> bool:
+        return self.cfg.head_dim_qk == 576
+
+    def append(self, k_new, v_new, k_cache, v_cache=None, stream=None):
+        ks = strides_of(k_cache)
+        vs = None if v_cache is None else strides_of(v_cache)
+        rpa_kv_append(self.handle, k_new, v_new, k_cache, v_cache, ks, vs, stream)
+
+    def attention(self, q, k_cache, v_cache=None, o=None, lse=None, with_lse=True, stream=None):
+        import torch
+        if o is None:
+            o = torch.empty((self.total_q, self.cfg.num_qo_heads, self.cfg.head_dim_v),
+                            dtype=q.dtype, device=q.device)
+        if lse is None and with_lse:
+            lse = torch.empty((self.total_q, self.cfg.num_qo_heads), dtype=torch.float32,
+                              device=q.device)
+        ks = strides_of(k_cache)
+        vs = None if v_cache is None else strides_of(v_cache)
+        rpa_batch_attention(self.handle, q, k_cache, v_cache, ks, vs, o, lse, stream)
+        return o, lse
+
+    def debug(self, name: str) -> np.ndarray:
+        return rpa_plan_debug_dump(self.handle, name)
+
+
+def merge_state(o_a, lse_a, o_b, lse_b, stream=None):
+    """Merge two attention states [rows, heads, dim] (torch tensors on the GPU)."""
+    import torch
+    rows, heads, dim = o_a.shape
+    o = torch.empty_like(o_a)
+    lse = torch.empty_like(lse_a)
+    dtype = RPA_DTYPE_BF16 if o_a.dtype == torch.bfloat16 else RPA_DTYPE_F32
+    rpa_merge_state(o_a, lse_a, o_b, lse_b, o, lse, rows, heads, dim, dtype, stream)
+    return o, lse

@@ -1,0 +1,431 @@
+// C ABI of librpa.so: argument validation, plan upload and kernel dispatch.
+// Every step of the path runs in the HIP kernels launched from here.
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+#include "plan.h"
+
+#define RPA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rpa_status fail(rpa_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+rpa_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return RPA_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+rpa::DevPlan dev_plan(const rpa_plan* plan) {
+  rpa::DevPlan p{};
+  const int32_t* base = static_cast<const int32_t*>(plan->d_ws);
+  p.qo_indptr = base + plan->off_qo_indptr;
+  p.kv_len = base + plan->off_kv_len;
+  p.page_indptr = base + plan->off_page_indptr;
+  p.page_indices = base + plan->off_page_indices;
+  p.split = base + plan->off_split;
+  p.append = base + plan->off_append;
+  for (int k = 0; k < rpa::KC_COUNT; ++k) {
+    p.items[k] = base + plan->off_items[k];
+    p.n_items[k] = plan->n_items[k];
+  }
+  p.merge_rows = base + plan->off_merge;
+  p.n_merge_rows = plan->n_merge_rows;
+  char* ws = static_cast<char*>(plan->d_ws);
+  p.part_o = reinterpret_cast<float*>(ws + plan->part_o_off);
+  p.part_lse = reinterpret_cast<float*>(ws + plan->part_lse_off);
+  p.batch_size = plan->batch_size;
+  p.total_q = plan->total_q;
+  p.num_qo_heads = plan->cfg.num_qo_heads;
+  p.num_kv_heads = plan->cfg.num_kv_heads;
+  p.group = plan->group;
+  p.head_dim_qk = plan->cfg.head_dim_qk;
+  p.head_dim_v = plan->cfg.head_dim_v;
+  p.page_size = plan->cfg.page_size;
+  int32_t s = 0;
+  while ((1 << s) < plan->cfg.page_size) ++s;
+  p.page_shift = s;
+  p.causal = plan->cfg.causal;
+  p.dtype = plan->cfg.dtype;
+  p.sm_scale = plan->cfg.sm_scale;
+  return p;
+}
+
+// Checks a pool's strides for a row of `row_len` elements.
+bool strides_ok(const rpa_cache_strides* st, int32_t row_len, int32_t dtype, std::string* why) {
+  if (!st) {
+    *why = "null strides";
+    return false;
+  }
+  const int64_t vec = dtype == RPA_DTYPE_BF16 ? 8 : 4;
+  if (st->token_stride < row_len || st->head_stride <= 0 || st->page_stride <= 0) {
+    *why = "strides must be positive and token_stride >= the stored row length";
+    return false;
+  }
+  if (st->token_stride % vec || st->head_stride % vec || st->page_stride % vec) {
+    *why = "strides must be multiples of 16 bytes";
+    return false;
+  }
+  return true;
+}
+
+rpa_status check_uploaded(const rpa_plan* plan) {
+  if (!plan) return fail(RPA_ERR_INVALID_ARG, "null plan");
+  if (!plan->uploaded || !plan->d_ws)
+    return fail(RPA_ERR_NOT_UPLOADED, "plan has not been uploaded (call rpa_plan_upload)");
+  return RPA_OK;
+}
+
+bool shared_latent(const rpa_attn_config& c) { return c.head_dim_qk == 576; }
+
+// ---- optional per-kernel event timing -------------------------------------------
+
+struct ProfRecord {
+  std::string name;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_pending;
+std::vector<hipEvent_t> g_prof_free;
+std::map<std::string, std::pair<double, int64_t>> g_prof_totals;
+
+hipError_t prof_event(hipEvent_t* ev) {
+  if (!g_prof_free.empty()) {
+    *ev = g_prof_free.back();
+    g_prof_free.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(ev);
+}
+
+// Runs `launch`, bracketed by timing events when profiling is on.
+template <class F>
+hipError_t timed(const char* name, hipStream_t st, F&& launch) {
+  std::unique_lock<std::mutex> lock(g_prof_mu);
+  if (!g_prof_on) {
+    lock.unlock();
+    return launch();
+  }
+  hipEvent_t a, b;
+  hipError_t e = prof_event(&a);
+  if (e != hipSuccess) return e;
+  e = prof_event(&b);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(a, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, st);
+  if (e != hipSuccess) return e;
+  g_prof_pending.push_back({name, a, b});
+  return hipSuccess;
+}
+
+hipError_t prof_drain() {
+  for (ProfRecord& rec : g_prof_pending) {
+    hipError_t e = hipEventSynchronize(rec.stop);
+    if (e != hipSuccess) return e;
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, rec.start, rec.stop);
+    if (e != hipSuccess) return e;
+    auto& tot = g_prof_totals[rec.name];
+    tot.first += ms;
+    tot.second += 1;
+    g_prof_free.push_back(rec.start);
+    g_prof_free.push_back(rec.stop);
+  }
+  g_prof_pending.clear();
+  return hipSuccess;
+}
+
+}  // namespace
+
+RPA_EXPORT int32_t rpa_abi_version(void) { return RPA_ABI_VERSION; }
+
+RPA_EXPORT const char* rpa_status_string(rpa_status s) {
+  switch (s) {
+    case RPA_OK: return "RPA_OK";
+    case RPA_ERR_INVALID_ARG: return "RPA_ERR_INVALID_ARG";
+    case RPA_ERR_UNSUPPORTED: return "RPA_ERR_UNSUPPORTED";
+    case RPA_ERR_WORKSPACE_TOO_SMALL: return "RPA_ERR_WORKSPACE_TOO_SMALL";
+    case RPA_ERR_PAGE_OOB: return "RPA_ERR_PAGE_OOB";
+    case RPA_ERR_DUPLICATE_WRITE_PAGE: return "RPA_ERR_DUPLICATE_WRITE_PAGE";
+    case RPA_ERR_HIP: return "RPA_ERR_HIP";
+    case RPA_ERR_NOT_UPLOADED: return "RPA_ERR_NOT_UPLOADED";
+  }
+  return "RPA_ERR_UNKNOWN";
+}
+
+RPA_EXPORT const char* rpa_last_error_message(void) { return g_last_error.c_str(); }
+
+RPA_EXPORT rpa_status rpa_plan_create(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                                      int32_t num_cus, rpa_plan** out) {
+  if (!out) return fail(RPA_ERR_INVALID_ARG, "null output pointer");
+  *out = nullptr;
+  rpa_plan* plan = new (std::nothrow) rpa_plan();
+  if (!plan) return fail(RPA_ERR_INVALID_ARG, "out of host memory");
+  std::string err;
+  rpa_status s;
+  try {
+    s = rpa::build_plan(cfg, batch, num_cus, plan, &err);
+  } catch (const std::bad_alloc&) {
+    s = RPA_ERR_INVALID_ARG;
+    err = "out of host memory while planning";
+  }
+  if (s != RPA_OK) {
+    delete plan;
+    return fail(s, err);
+  }
+  *out = plan;
+  g_last_error.clear();
+  return RPA_OK;
+}
+
+RPA_EXPORT rpa_status rpa_plan_workspace_size(const rpa_plan* plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(RPA_ERR_INVALID_ARG, "null plan or bytes pointer");
+  *bytes = plan->ws_bytes;
+  return RPA_OK;
+}
+
+RPA_EXPORT rpa_status rpa_plan_upload(rpa_plan* plan, void* d_workspace, size_t bytes,
+                                      void* stream) {
+  if (!plan || !d_workspace) return fail(RPA_ERR_INVALID_ARG, "null plan or workspace");
+  if (!aligned(d_workspace, 256)) return fail(RPA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if (bytes < plan->ws_bytes)
+    return fail(RPA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace has " + std::to_string(bytes) + " bytes, plan needs " +
+                    std::to_string(plan->ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (!plan->event) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    plan->event = ev;
+  } else {
+    // The previous upload may still be reading the staging buffer.
+    e = hipEventSynchronize(static_cast<hipEvent_t>(plan->event));
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  }
+  if (!plan->staging) {
+    e = hipHostMalloc(&plan->staging, plan->meta_bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      plan->staging = nullptr;
+      return hip_fail(e, "hipHostMalloc");
+    }
+  }
+  std::memset(plan->staging, 0, plan->meta_bytes);
+  std::memcpy(plan->staging, plan->blob.data(), plan->blob.size() * sizeof(int32_t));
+  e = hipMemcpyAsync(d_workspace, plan->staging, plan->meta_bytes, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipEventRecord(static_cast<hipEvent_t>(plan->event), st);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  plan->d_ws = d_workspace;
+  plan->uploaded = true;
+  g_last_error.clear();
+  return RPA_OK;
+}
+
+RPA_EXPORT rpa_status rpa_kv_append(const rpa_plan* plan, const void* k_new, const void* v_new,
+                                    void* k_cache, void* v_cache, const rpa_cache_strides* ks,
+                                    const rpa_cache_strides* vs, void* stream) {
+  rpa_status s = check_uploaded(plan);
+  if (s != RPA_OK) return s;
+  const rpa_attn_config& c = plan->cfg;
+  const bool latent = shared_latent(c);
+  std::string why;
+  if (plan->total_q == 0) return RPA_OK;  // no new tokens: nothing to read or write
+  if (!k_new || !k_cache) return fail(RPA_ERR_INVALID_ARG, "null k_new or k_cache");
+  if (!aligned(k_new, 16) || !aligned(k_cache, 16))
+    return fail(RPA_ERR_INVALID_ARG, "k_new and k_cache must be 16-byte aligned");
+  if (!strides_ok(ks, c.head_dim_qk, c.dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "k: " + why);
+  if (latent) {
+    if (v_new) return fail(RPA_ERR_INVALID_ARG, "shared latent cache: v_new must be NULL");
+    if (v_cache && v_cache != k_cache)
+      return fail(RPA_ERR_INVALID_ARG, "shared latent cache: v_cache must be NULL or k_cache");
+  } else {
+    if (!v_new || !v_cache) return fail(RPA_ERR_INVALID_ARG, "null v_new or v_cache");
+    if (!aligned(v_new, 16) || !aligned(v_cache, 16))
+      return fail(RPA_ERR_INVALID_ARG, "v_new and v_cache must be 16-byte aligned");
+    if (!strides_ok(vs, c.head_dim_v, c.dtype, &why))
+      return fail(RPA_ERR_INVALID_ARG, "v: " + why);
+  }
+  rpa::DevPlan p = dev_plan(plan);
+  rpa::Strides k_st{ks->page_stride, ks->head_stride, ks->token_stride};
+  rpa::Strides v_st = latent ? k_st : rpa::Strides{vs->page_stride, vs->head_stride, vs->token_stride};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("append", st, [&] {
+    return rpa::launch_append(p, k_new, latent ? nullptr : v_new, k_cache,
+                              latent ? nullptr : v_cache, k_st, v_st, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+  return RPA_OK;
+}
+
+RPA_EXPORT rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q,
+                                          const void* k_cache, const void* v_cache,
+                                          const rpa_cache_strides* ks,
+                                          const rpa_cache_strides* vs, void* o, float* lse,
+                                          void* stream) {
+  rpa_status s = check_uploaded(plan);
+  if (s != RPA_OK) return s;
+  const rpa_attn_config& c = plan->cfg;
+  const bool latent = shared_latent(c);
+  std::string why;
+  if (plan->total_q == 0) return RPA_OK;  // no query rows: nothing to compute
+  if (!q || !k_cache || !o) return fail(RPA_ERR_INVALID_ARG, "null q, k_cache or o");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(o, 16))
+    return fail(RPA_ERR_INVALID_ARG, "q, k_cache and o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(RPA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (!strides_ok(ks, c.head_dim_qk, c.dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "k: " + why);
+  rpa::Strides k_st{ks->page_stride, ks->head_stride, ks->token_stride};
+  rpa::Strides v_st = k_st;
+  const void* vc = v_cache;
+  if (latent) {
+    if (v_cache && v_cache != k_cache)
+      return fail(RPA_ERR_UNSUPPORTED, "576/512 needs the shared latent cache (v_cache == k_cache)");
+    if (vs && (vs->page_stride != ks->page_stride || vs->head_stride != ks->head_stride ||
+               vs->token_stride != ks->token_stride))
+      return fail(RPA_ERR_UNSUPPORTED, "576/512 needs vs == ks (shared latent cache)");
+    vc = k_cache;
+  } else {
+    if (!v_cache) return fail(RPA_ERR_INVALID_ARG, "null v_cache");
+    if (!aligned(v_cache, 16)) return fail(RPA_ERR_INVALID_ARG, "v_cache must be 16-byte aligned");
+    if (!strides_ok(vs, c.head_dim_v, c.dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "v: " + why);
+    v_st = rpa::Strides{vs->page_stride, vs->head_stride, vs->token_stride};
+  }
+  rpa::DevPlan p = dev_plan(plan);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p.n_items[rpa::KC_GENERIC] > 0) {
+    e = timed("generic", st, [&] { return rpa::launch_generic(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
+    if (e != hipSuccess) return hip_fail(e, "generic attention launch");
+  }
+  if (p.n_items[rpa::KC_DECODE] > 0) {
+    e = timed("decode", st, [&] { return rpa::launch_decode(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
+    if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+  }
+  if (p.n_items[rpa::KC_PREFILL] > 0) {
+    e = timed("prefill", st, [&] { return rpa::launch_prefill(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  }
+  if (p.n_items[rpa::KC_MLA] > 0) {
+    e = timed("mla", st, [&] { return rpa::launch_mla(p, q, k_cache, k_st, o, lse, st); });
+    if (e != hipSuccess) return hip_fail(e, "latent attention launch");
+  }
+  if (p.n_merge_rows > 0) {
+    e = timed("merge", st, [&] { return rpa::launch_merge_rows(p, o, lse, st); });
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return RPA_OK;
+}
+
+RPA_EXPORT rpa_status rpa_merge_state(const void* o_a, const float* lse_a, const void* o_b,
+                                      const float* lse_b, void* o, float* lse, int64_t rows,
+                                      int32_t heads, int32_t dim, int32_t dtype, void* stream) {
+  if (dtype != RPA_DTYPE_F32 && dtype != RPA_DTYPE_BF16)
+    return fail(RPA_ERR_INVALID_ARG, "dtype must be RPA_DTYPE_F32 or RPA_DTYPE_BF16");
+  if (rows < 0 || heads <= 0 || dim <= 0) return fail(RPA_ERR_INVALID_ARG, "bad rows/heads/dim");
+  if (dim % 8 != 0) return fail(RPA_ERR_INVALID_ARG, "dim must be a multiple of 8");
+  if (rows == 0) return RPA_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o)
+    return fail(RPA_ERR_INVALID_ARG, "null o_a, lse_a, o_b, lse_b or o");
+  if (!aligned(o_a, 16) || !aligned(o_b, 16) || !aligned(o, 16))
+    return fail(RPA_ERR_INVALID_ARG, "o_a, o_b and o must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("merge_state", st, [&] {
+    return rpa::launch_merge_state(o_a, lse_a, o_b, lse_b, o, lse, rows, heads, dim, dtype, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "merge_state launch");
+  return RPA_OK;
+}
+
+RPA_EXPORT rpa_status rpa_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof_on = on != 0;
+  return RPA_OK;
+}
+
+RPA_EXPORT rpa_status rpa_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return fail(RPA_ERR_INVALID_ARG, "null argument");
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  hipError_t e = prof_drain();
+  if (e != hipSuccess) return hip_fail(e, "profile events");
+  auto it = g_prof_totals.find(kernel);
+  *total_ms = it == g_prof_totals.end() ? 0.0 : it->second.first;
+  *launches = it == g_prof_totals.end() ? 0 : it->second.second;
+  return RPA_OK;
+}
+
+RPA_EXPORT rpa_status rpa_profile_reset(void) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  hipError_t e = prof_drain();
+  g_prof_totals.clear();
+  if (e != hipSuccess) return hip_fail(e, "profile events");
+  return RPA_OK;
+}
+
+RPA_EXPORT void rpa_plan_destroy(rpa_plan* plan) {
+  if (!plan) return;
+  if (plan->event) {
+    (void)hipEventSynchronize(static_cast<hipEvent_t>(plan->event));
+    (void)hipEventDestroy(static_cast<hipEvent_t>(plan->event));
+  }
+  if (plan->staging) (void)hipHostFree(plan->staging);
+  delete plan;
+}
+
+RPA_EXPORT rpa_status rpa_plan_debug_dump(const rpa_plan* plan, const char* name, int32_t* dst,
+                                          int64_t cap, int64_t* len) {
+  if (!plan || !name || !len) return fail(RPA_ERR_INVALID_ARG, "null plan, name or len");
+  const int32_t* src = nullptr;
+  int64_t n = 0;
+  std::vector<int32_t> tmp;
+  const std::string nm(name);
+  const int32_t* blob = plan->blob.data();
+  if (nm == "items") {
+    for (int k = 0; k < rpa::KC_COUNT; ++k)
+      tmp.insert(tmp.end(), blob + plan->off_items[k],
+                 blob + plan->off_items[k] + (int64_t)plan->n_items[k] * rpa::IT_WORDS);
+    src = tmp.data();
+    n = (int64_t)tmp.size();
+  } else if (nm == "splits") {
+    src = blob + plan->off_split;
+    n = (int64_t)plan->batch_size * rpa::SP_WORDS;
+  } else if (nm == "append") {
+    src = blob + plan->off_append;
+    n = (int64_t)plan->total_q * 2;
+  } else if (nm == "merge_rows") {
+    src = blob + plan->off_merge;
+    n = plan->n_merge_rows;
+  } else if (nm == "summary") {
+    int32_t total = 0;
+    for (int k = 0; k < rpa::KC_COUNT; ++k) total += plan->n_items[k];
+    tmp = {plan->batch_size, plan->total_q, total, (int32_t)plan->partial_rows,
+           plan->n_items[0], plan->n_items[1], plan->n_items[2], plan->n_items[3]};
+    src = tmp.data();
+    n = (int64_t)tmp.size();
+  } else {
+    return fail(RPA_ERR_INVALID_ARG, "unknown table name: " + nm);
+  }
+  *len = n;
+  if (dst && cap > 0) std::memcpy(dst, src, (size_t)std::min<int64_t>(cap, n) * sizeof(int32_t));
+  return RPA_OK;
+}

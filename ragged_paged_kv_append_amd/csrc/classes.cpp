@@ -1,0 +1,15 @@
+// Which specialised kernel classes this build provides.  Pure C++ so the
+// planner links without HIP.
+#include "plan.h"
+
+namespace rpa {
+
+bool class_available(int32_t kernel_class, const rpa_attn_config& cfg) {
+  (void)cfg;
+  switch (kernel_class) {
+    case KC_GENERIC: return true;
+    default: return false;
+  }
+}
+
+}  // namespace rpa

@@ -1,0 +1,36 @@
+// Host launchers of the HIP kernels (internal).  Each returns the HIP status
+// of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "rpa_internal.h"
+
+namespace rpa {
+
+hipError_t launch_append(const DevPlan& p, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, Strides ks, Strides vs, hipStream_t stream);
+
+hipError_t launch_generic(const DevPlan& p, const void* q, const void* k_cache,
+                          const void* v_cache, Strides ks, Strides vs, void* o, float* lse,
+                          hipStream_t stream);
+
+hipError_t launch_decode(const DevPlan& p, const void* q, const void* k_cache, const void* v_cache,
+                         Strides ks, Strides vs, void* o, float* lse, hipStream_t stream);
+
+hipError_t launch_prefill(const DevPlan& p, const void* q, const void* k_cache,
+                          const void* v_cache, Strides ks, Strides vs, void* o, float* lse,
+                          hipStream_t stream);
+
+hipError_t launch_mla(const DevPlan& p, const void* q, const void* kv_cache, Strides ks, void* o,
+                      float* lse, hipStream_t stream);
+
+// Folds the split pieces of every row in p.merge_rows into o / lse.
+hipError_t launch_merge_rows(const DevPlan& p, void* o, float* lse, hipStream_t stream);
+
+// Standalone two-state merge.
+hipError_t launch_merge_state(const void* o_a, const float* lse_a, const void* o_b,
+                              const float* lse_b, void* o, float* lse, int64_t rows, int32_t heads,
+                              int32_t dim, int32_t dtype, hipStream_t stream);
+
+}  // namespace rpa

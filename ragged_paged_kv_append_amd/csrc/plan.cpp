@@ -1,0 +1,325 @@
+// Host planner: validation, append map, split of long kv ranges into work
+// items, merge map, workspace layout.  Pure C++ (no HIP), so it also builds
+// and runs on a machine without a GPU.
+//
+// Follows "Accelerating Sonar through speculation" (Perplexity), runtime
+// section: per step, the host packs the new tokens and page information and
+// builds the attention metadata and intermediate buffers once for prefill,
+// decode and verification; and "Disaggregated prefill and decode",
+// performance section: attention parallelises over requests and over kv_len
+// in proportion to the sequence lengths.
+
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+
+namespace rpa {
+
+namespace {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int32_t log2i(int32_t x) {
+  int32_t s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+int32_t rows_per_item(int32_t cls, int32_t rows_total) {
+  switch (cls) {
+    case KC_DECODE: return DEC_MAX_ROWS;
+    case KC_PREFILL: return PRE_ROWS;
+    case KC_MLA: return MLA_ROWS;
+    default: return GEN_ROWS;
+  }
+  (void)rows_total;
+}
+
+}  // namespace
+
+rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, int32_t num_cus,
+                      rpa_plan* plan, std::string* err) {
+  if (!cfg || !batch || !plan) {
+    *err = "null cfg, batch or plan pointer";
+    return RPA_ERR_INVALID_ARG;
+  }
+  const rpa_attn_config c = *cfg;
+  if (c.num_qo_heads <= 0 || c.num_kv_heads <= 0 || c.num_qo_heads % c.num_kv_heads != 0) {
+    *err = "num_qo_heads must be a positive multiple of num_kv_heads";
+    return RPA_ERR_INVALID_ARG;
+  }
+  if (c.dtype != RPA_DTYPE_F32 && c.dtype != RPA_DTYPE_BF16) {
+    *err = "dtype must be RPA_DTYPE_F32 or RPA_DTYPE_BF16";
+    return RPA_ERR_INVALID_ARG;
+  }
+  if (c.causal != 0 && c.causal != 1) {
+    *err = "causal must be 0 or 1";
+    return RPA_ERR_INVALID_ARG;
+  }
+  if (!std::isfinite(c.sm_scale)) {
+    *err = "sm_scale must be finite";
+    return RPA_ERR_INVALID_ARG;
+  }
+  const bool dims_ok = (c.head_dim_qk == 64 && c.head_dim_v == 64) ||
+                       (c.head_dim_qk == 128 && c.head_dim_v == 128) ||
+                       (c.head_dim_qk == 576 && c.head_dim_v == 512);
+  if (!dims_ok) {
+    *err = "unsupported head dims (supported: 64/64, 128/128, 576/512)";
+    return RPA_ERR_UNSUPPORTED;
+  }
+  if (c.head_dim_qk == 576 && c.num_kv_heads != 1) {
+    *err = "the 576/512 latent form has exactly one KV head";
+    return RPA_ERR_UNSUPPORTED;
+  }
+  if (!is_pow2(c.page_size) || c.page_size > 256) {
+    *err = "page_size must be a power of two in [1, 256]";
+    return RPA_ERR_UNSUPPORTED;
+  }
+  const int32_t B = batch->batch_size;
+  if (B < 0) {
+    *err = "batch_size must be >= 0";
+    return RPA_ERR_INVALID_ARG;
+  }
+  if (B > 0 && (!batch->qo_indptr || !batch->kv_len || !batch->kv_page_indptr ||
+                !batch->kv_page_indices)) {
+    *err = "null batch array";
+    return RPA_ERR_INVALID_ARG;
+  }
+  if (batch->num_pages < 0) {
+    *err = "num_pages must be >= 0";
+    return RPA_ERR_INVALID_ARG;
+  }
+  const int32_t P = c.page_size;
+  const int32_t G = c.num_qo_heads / c.num_kv_heads;
+  const int32_t* qo = batch->qo_indptr;
+  const int32_t* kvl = batch->kv_len;
+  const int32_t* pip = batch->kv_page_indptr;
+  const int32_t* pix = batch->kv_page_indices;
+
+  if (B > 0 && (qo[0] != 0 || pip[0] != 0)) {
+    *err = "qo_indptr[0] and kv_page_indptr[0] must be 0";
+    return RPA_ERR_INVALID_ARG;
+  }
+  for (int32_t r = 0; r < B; ++r) {
+    const int64_t n = (int64_t)qo[r + 1] - qo[r];
+    if (n < 0) {
+      *err = "qo_indptr must be non-decreasing (request " + std::to_string(r) + ")";
+      return RPA_ERR_INVALID_ARG;
+    }
+    if (kvl[r] < n) {
+      *err = "kv_len < qo_len for request " + std::to_string(r);
+      return RPA_ERR_INVALID_ARG;
+    }
+    if (pip[r + 1] < pip[r]) {
+      *err = "kv_page_indptr must be non-decreasing (request " + std::to_string(r) + ")";
+      return RPA_ERR_INVALID_ARG;
+    }
+    const int64_t need = ceil_div(kvl[r], P);
+    if ((int64_t)pip[r + 1] - pip[r] < need) {
+      *err = "request " + std::to_string(r) + " has fewer than ceil(kv_len/page_size) pages";
+      return RPA_ERR_PAGE_OOB;
+    }
+    for (int64_t j = 0; j < need; ++j) {
+      const int32_t pg = pix[pip[r] + j];
+      if (pg < 0 || pg >= batch->num_pages) {
+        *err = "page id " + std::to_string(pg) + " of request " + std::to_string(r) +
+               " outside [0, num_pages)";
+        return RPA_ERR_PAGE_OOB;
+      }
+    }
+  }
+  // A page the append writes must be referenced exactly once in the batch.
+  if (B > 0) {
+    std::vector<uint8_t> refs((size_t)batch->num_pages, 0);
+    for (int32_t r = 0; r < B; ++r) {
+      const int64_t need = ceil_div(kvl[r], P);
+      for (int64_t j = 0; j < need; ++j) {
+        uint8_t& x = refs[(size_t)pix[pip[r] + j]];
+        if (x < 255) ++x;
+      }
+    }
+    for (int32_t r = 0; r < B; ++r) {
+      const int64_t n = (int64_t)qo[r + 1] - qo[r];
+      if (n == 0) continue;
+      const int64_t cached = kvl[r] - n;
+      for (int64_t j = cached / P; j <= (kvl[r] - 1) / P; ++j) {
+        const int32_t pg = pix[pip[r] + j];
+        if (refs[(size_t)pg] > 1) {
+          *err = "page " + std::to_string(pg) + " written by request " + std::to_string(r) +
+                 " is referenced more than once";
+          return RPA_ERR_DUPLICATE_WRITE_PAGE;
+        }
+      }
+    }
+  }
+
+  const int64_t total_q = B > 0 ? qo[B] : 0;
+  const int64_t nnz = B > 0 ? pip[B] : 0;
+
+  // ---- kernel class per request --------------------------------------------
+  std::vector<int32_t> cls(B, KC_GENERIC);
+  for (int32_t r = 0; r < B; ++r) {
+    const int64_t n = (int64_t)qo[r + 1] - qo[r];
+    int32_t k = KC_GENERIC;
+    if (c.dtype == RPA_DTYPE_BF16 && P % 16 == 0) {
+      if (c.head_dim_qk == 128 && c.head_dim_v == 128) {
+        k = (n * G <= DEC_MAX_ROWS) ? KC_DECODE : KC_PREFILL;
+      } else if (c.head_dim_qk == 576) {
+        k = KC_MLA;
+      }
+    }
+    if (!class_available(k, c)) k = KC_GENERIC;
+    cls[r] = k;
+  }
+
+  // ---- split of kv ranges into pieces ----------------------------------------
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  // Streaming classes (generic, decode): pieces sized so the whole batch makes
+  // about 8 items per compute unit.  Tile classes (prefill, latent): split only
+  // when the row tiles alone make fewer than 2 items per compute unit.
+  int64_t stream_work = 0, tiles = 0;
+  for (int32_t r = 0; r < B; ++r) {
+    const int64_t n = (int64_t)qo[r + 1] - qo[r];
+    if (n == 0) continue;
+    if (cls[r] == KC_GENERIC || cls[r] == KC_DECODE) {
+      stream_work += (int64_t)kvl[r] * c.num_kv_heads *
+                     ceil_div(n * G, rows_per_item(cls[r], (int32_t)(n * G)));
+    } else {
+      tiles += (int64_t)c.num_kv_heads * ceil_div(n * G, rows_per_item(cls[r], 0));
+    }
+  }
+  const int64_t stream_piece =
+      std::max<int64_t>(KEY_ALIGN, round_up(ceil_div(std::max<int64_t>(stream_work, 1), 8 * cus),
+                                            KEY_ALIGN));
+  const int64_t tile_split = tiles >= 2 * cus ? 1 : ceil_div(2 * cus, std::max<int64_t>(tiles, 1));
+
+  std::vector<int32_t> split((size_t)B * SP_WORDS, 0);
+  int64_t partial_rows = 0;
+  for (int32_t r = 0; r < B; ++r) {
+    const int64_t n = (int64_t)qo[r + 1] - qo[r];
+    const int64_t L = kvl[r];
+    int64_t S = 1, kc = std::max<int64_t>(L, 1);
+    if (n > 0 && L > 0) {
+      if (cls[r] == KC_GENERIC || cls[r] == KC_DECODE) {
+        S = ceil_div(L, stream_piece);
+      } else {
+        S = std::min<int64_t>(tile_split, ceil_div(L, 256));
+      }
+      S = std::max<int64_t>(S, 1);
+      kc = round_up(ceil_div(L, S), KEY_ALIGN);
+      S = ceil_div(L, kc);
+    }
+    split[(size_t)r * SP_WORDS + SP_COUNT] = (int32_t)S;
+    split[(size_t)r * SP_WORDS + SP_CHUNK] = (int32_t)kc;
+    split[(size_t)r * SP_WORDS + SP_BASE] = (int32_t)(S > 1 ? partial_rows : -1);
+    if (S > 1) partial_rows += S * n;
+  }
+  if (partial_rows > INT32_MAX / 2) {
+    *err = "batch too large: partial rows overflow";
+    return RPA_ERR_INVALID_ARG;
+  }
+
+  // ---- work items ----------------------------------------------------------------
+  std::vector<std::vector<int32_t>> items(KC_COUNT);
+  std::vector<std::vector<int64_t>> cost(KC_COUNT);
+  for (int32_t r = 0; r < B; ++r) {
+    const int64_t n = (int64_t)qo[r + 1] - qo[r];
+    if (n == 0) continue;
+    const int64_t L = kvl[r];
+    const int64_t cached = L - n;
+    const int32_t k = cls[r];
+    const int64_t rows_total = n * G;
+    const int64_t R = rows_per_item(k, (int32_t)rows_total);
+    const int64_t S = split[(size_t)r * SP_WORDS + SP_COUNT];
+    const int64_t kc = split[(size_t)r * SP_WORDS + SP_CHUNK];
+    for (int32_t g = 0; g < c.num_kv_heads; ++g) {
+      for (int64_t row0 = 0; row0 < rows_total; row0 += R) {
+        const int64_t row1 = std::min(rows_total, row0 + R);
+        const int64_t t_last = (row1 - 1) / G;
+        const int64_t p_last = c.causal ? cached + t_last : L - 1;
+        for (int64_t s = 0; s < S; ++s) {
+          const int64_t k0 = s * kc;
+          if (k0 > p_last) break;
+          const int64_t k1 = std::min(L, k0 + kc);
+          const int32_t it[IT_WORDS] = {r, g, (int32_t)row0, (int32_t)row1, (int32_t)k0,
+                                        (int32_t)k1, (int32_t)s, k};
+          items[k].insert(items[k].end(), it, it + IT_WORDS);
+          cost[k].push_back((std::min(k1, p_last + 1) - k0) * (row1 - row0));
+        }
+      }
+    }
+  }
+  // Heaviest items first, so the tail of the launch holds the short ones.
+  for (int k = 0; k < KC_COUNT; ++k) {
+    const size_t m = cost[k].size();
+    std::vector<size_t> order(m);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](size_t a, size_t b) { return cost[k][a] > cost[k][b]; });
+    std::vector<int32_t> sorted(items[k].size());
+    for (size_t j = 0; j < m; ++j)
+      std::memcpy(&sorted[j * IT_WORDS], &items[k][order[j] * IT_WORDS], IT_WORDS * sizeof(int32_t));
+    items[k].swap(sorted);
+  }
+
+  // ---- append map and merge rows --------------------------------------------------
+  std::vector<int32_t> append((size_t)total_q * 2);
+  std::vector<int32_t> merge_rows;
+  for (int32_t r = 0; r < B; ++r) {
+    const int64_t n = (int64_t)qo[r + 1] - qo[r];
+    const int64_t cached = (int64_t)kvl[r] - n;
+    for (int64_t t = 0; t < n; ++t) {
+      const int64_t p = cached + t;
+      const int64_t i = qo[r] + t;
+      append[(size_t)i * 2 + 0] = pix[pip[r] + p / P];
+      append[(size_t)i * 2 + 1] = (int32_t)(p % P);
+      if (split[(size_t)r * SP_WORDS + SP_COUNT] > 1) merge_rows.push_back((int32_t)i);
+    }
+  }
+
+  // ---- blob -------------------------------------------------------------------------
+  plan->cfg = c;
+  plan->batch_size = B;
+  plan->total_q = (int32_t)total_q;
+  plan->num_pages = batch->num_pages;
+  plan->group = G;
+  std::vector<int32_t>& blob = plan->blob;
+  blob.clear();
+  auto push = [&](const int32_t* p, int64_t count) {
+    const int64_t off = (int64_t)blob.size();
+    if (count > 0) blob.insert(blob.end(), p, p + count);
+    // keep every table 16-byte aligned
+    while (blob.size() % 4) blob.push_back(0);
+    return off;
+  };
+  const int32_t zero = 0;
+  plan->off_qo_indptr = B > 0 ? push(qo, B + 1) : push(&zero, 1);
+  plan->off_kv_len = push(kvl, B);
+  plan->off_page_indptr = B > 0 ? push(pip, B + 1) : push(&zero, 1);
+  plan->off_page_indices = push(pix, nnz);
+  plan->off_split = push(split.data(), (int64_t)split.size());
+  plan->off_append = push(append.data(), (int64_t)append.size());
+  for (int k = 0; k < KC_COUNT; ++k) {
+    plan->off_items[k] = push(items[k].data(), (int64_t)items[k].size());
+    plan->n_items[k] = (int32_t)(items[k].size() / IT_WORDS);
+  }
+  plan->off_merge = push(merge_rows.data(), (int64_t)merge_rows.size());
+  plan->n_merge_rows = (int32_t)merge_rows.size();
+  plan->partial_rows = partial_rows;
+
+  plan->meta_bytes = (size_t)round_up((int64_t)blob.size() * 4, 256);
+  plan->part_o_off = plan->meta_bytes;
+  plan->part_lse_off =
+      plan->part_o_off + (size_t)round_up(partial_rows * c.num_qo_heads * c.head_dim_v * 4, 256);
+  plan->ws_bytes = plan->part_lse_off + (size_t)round_up(partial_rows * c.num_qo_heads * 4, 256);
+  (void)log2i;
+  return RPA_OK;
+}
+
+}  // namespace rpa

@@ -1,0 +1,49 @@
+// Host-side plan object and planner entry point (pure C++, no HIP calls).
+#pragma once
+
+#include <string>
+#include <vector>
+
+#include "rpa_internal.h"
+
+struct rpa_plan {
+  rpa_attn_config cfg{};
+  int32_t batch_size = 0;
+  int32_t total_q = 0;
+  int32_t num_pages = 0;
+  int32_t group = 1;
+
+  // Metadata in the order it is laid out in the device workspace (int32 words).
+  std::vector<int32_t> blob;
+  int64_t off_qo_indptr = 0, off_kv_len = 0, off_page_indptr = 0, off_page_indices = 0;
+  int64_t off_split = 0, off_append = 0, off_merge = 0;
+  int64_t off_items[rpa::KC_COUNT] = {0, 0, 0, 0};
+  int32_t n_items[rpa::KC_COUNT] = {0, 0, 0, 0};
+  int32_t n_merge_rows = 0;
+  int64_t partial_rows = 0;
+
+  // Workspace layout (bytes from the workspace base).
+  size_t meta_bytes = 0;
+  size_t part_o_off = 0;
+  size_t part_lse_off = 0;
+  size_t ws_bytes = 0;
+
+  // Upload state (set by rpa_plan_upload).
+  void* d_ws = nullptr;
+  void* staging = nullptr;   // pinned host buffer, meta_bytes long
+  void* event = nullptr;     // hipEvent_t recorded after the upload copy
+  bool uploaded = false;
+};
+
+namespace rpa {
+
+// Validates cfg and batch and fills `plan` (metadata, offsets, sizes).
+// On failure returns the status and sets *err.
+rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, int32_t num_cus,
+                      rpa_plan* plan, std::string* err);
+
+// Whether a specialised kernel class is available in this build; the planner
+// routes items of unavailable classes to the generic kernel.
+bool class_available(int32_t kernel_class, const rpa_attn_config& cfg);
+
+}  // namespace rpa

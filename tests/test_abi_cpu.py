@@ -1,0 +1,278 @@
+"""C-ABI library checks that need no GPU: exports, planner properties, error paths.
+
+The planner is pure host code, so plans are built and inspected here through
+rpa_plan_debug_dump; calls that would touch the device are only exercised on
+their argument-validation paths, which return before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+import ragged_paged_kv_append_amd as rpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rpa.LIB_PATH):
+        from ragged_paged_kv_append_amd import build
+        build.build()
+    return rpa.lib()
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "rpa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rpa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_symbols()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(rpa.EXPORTED_SYMBOLS)
+
+
+def test_abi_version_and_status_strings(L):
+    assert rpa.rpa_abi_version() == 1
+    for code, name in [(0, "RPA_OK"), (-1, "RPA_ERR_INVALID_ARG"), (-2, "RPA_ERR_UNSUPPORTED"),
+                       (-3, "RPA_ERR_WORKSPACE_TOO_SMALL"), (-4, "RPA_ERR_PAGE_OOB"),
+                       (-5, "RPA_ERR_DUPLICATE_WRITE_PAGE"), (-6, "RPA_ERR_HIP"),
+                       (-7, "RPA_ERR_NOT_UPLOADED")]:
+        assert rpa.rpa_status_string(code) == name
+
+
+# ----------------------------------------------------------------------------
+# Planner properties
+# ----------------------------------------------------------------------------
+
+
+def plan_for(meta, cfg, num_cus=0):
+    return rpa.rpa_plan_create(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr,
+                               meta.kv_page_indices, meta.num_pages, num_cus)
+
+
+def check_plan(plan, meta, cfg):
+    """Every (row, visible key) pair is in exactly one item; items stay inside
+    their request; splits, merge rows and the append map are consistent."""
+    G = cfg.num_qo_heads // cfg.num_kv_heads
+    items = rpa.rpa_plan_debug_dump(plan, "items").reshape(-1, 8)
+    splits = rpa.rpa_plan_debug_dump(plan, "splits").reshape(-1, 3)
+    merge_rows = set(rpa.rpa_plan_debug_dump(plan, "merge_rows").tolist())
+    app = rpa.rpa_plan_debug_dump(plan, "append").reshape(-1, 2)
+    summary = rpa.rpa_plan_debug_dump(plan, "summary")
+    assert summary[2] == len(items)
+    B = meta.batch_size
+    batch = oracle.Batch(meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices,
+                         meta.page_size)
+    cover = {}
+    for r_, g, row0, row1, k0, k1, s, kc in items.tolist():
+        n = batch.qo_len(r_)
+        Lr = int(meta.kv_len[r_])
+        assert 0 <= r_ < B and 0 <= g < cfg.num_kv_heads
+        assert 0 <= row0 < row1 <= n * G
+        assert 0 <= k0 < k1 <= Lr
+        S, chunk, base = splits[r_]
+        assert 0 <= s < S and k0 == s * chunk and k1 == min(Lr, k0 + chunk)
+        for row in range(row0, row1):
+            key = (r_, g, row)
+            cover.setdefault(key, []).append((k0, k1))
+    for r_ in range(B):
+        n = batch.qo_len(r_)
+        Lr = int(meta.kv_len[r_])
+        c = Lr - n
+        S, chunk, base = splits[r_]
+        for g in range(cfg.num_kv_heads):
+            for row in range(n * G):
+                t = row // G
+                pmax = c + t if cfg.causal else Lr - 1
+                everything = sorted(cover.get((r_, g, row), []))
+                assert len(set(everything)) == len(everything), "a piece covers a row twice"
+                # the merge reads the pieces that hold a key the row sees: they
+                # start at 0, are contiguous and end past the last visible key
+                ranges = [x for x in everything if x[0] <= pmax]
+                assert ranges, (r_, g, row)
+                assert ranges[0][0] == 0
+                for (a0, a1), (b0, b1) in zip(ranges, ranges[1:]):
+                    assert a1 == b0
+                assert ranges[-1][1] > pmax
+                assert len(ranges) == min(S, pmax // chunk + 1)
+        for t in range(n):
+            i = int(meta.qo_indptr[r_]) + t
+            assert (i in merge_rows) == (S > 1)
+            assert tuple(app[i]) == oracle.slot_of(batch, r_, c + t)
+    return items, splits
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "mixed_7b", "decode_verify_gqa", "mla_absorbed"])
+def test_planner_covers_workloads(L, name):
+    spec = workloads.SPECS[name]
+    qo, kv = workloads.lengths(name)
+    meta = workloads.make_meta(qo, kv, spec.page_size, spec.seed)
+    cfg = rpa.make_config(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim_qk, spec.head_dim_v,
+                          spec.page_size, spec.dtype, spec.causal, spec.sm_scale)
+    if name in ("mixed_7b", "decode_verify_gqa", "mla_absorbed"):
+        # full coverage check is quadratic in rows; check a sub-batch plus the summary
+        sub = workloads.make_meta(qo[:6], kv[:6], spec.page_size, spec.seed)
+        check_plan(plan_for(sub, cfg), sub, cfg)
+        plan = plan_for(meta, cfg)
+        summary = rpa.rpa_plan_debug_dump(plan, "summary")
+        assert summary[0] == len(kv) and summary[1] == int(np.sum(qo))
+    else:
+        check_plan(plan_for(meta, cfg), meta, cfg)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_planner_random_batches(L, seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 7))
+    qo = rng.integers(0, 18, size=B)
+    kv = qo + rng.integers(0, 300, size=B)
+    P = int(rng.choice([1, 4, 16, 64]))
+    hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    dims = [(64, 64), (128, 128)][seed % 2]
+    dtype = ["bf16", "f32"][(seed // 2) % 2]
+    causal = seed % 3 != 0
+    meta = workloads.make_meta(qo, kv, P, seed, extra_pages_per_req=seed % 2)
+    cfg = rpa.make_config(hkv * G, hkv, dims[0], dims[1], P, dtype, causal)
+    for cus in (0, 1, 100000):
+        check_plan(plan_for(meta, cfg, cus), meta, cfg)
+
+
+def test_planner_splits_long_requests(L):
+    meta = workloads.make_meta([1, 1], [40000, 100], 16, 1)
+    cfg = rpa.make_config(8, 8, 128, 128, 16, "bf16")
+    plan = plan_for(meta, cfg)
+    splits = rpa.rpa_plan_debug_dump(plan, "splits").reshape(-1, 3)
+    assert splits[0][0] > 1 and splits[1][0] == 1
+    items = rpa.rpa_plan_debug_dump(plan, "items").reshape(-1, 8)
+    costs = (items[:, 5] - items[:, 4]) * (items[:, 3] - items[:, 2])
+    # heaviest items are listed first within each kernel class
+    for k in set(items[:, 7].tolist()):
+        ck = costs[items[:, 7] == k]
+        assert np.all(np.diff(ck) <= 0)
+
+
+def test_planner_empty_batch_and_empty_requests(L):
+    cfg = rpa.make_config(4, 2, 64, 64, 16, "f32")
+    plan = rpa.rpa_plan_create(cfg, [0], [], [0], [], 0)
+    assert rpa.rpa_plan_debug_dump(plan, "summary")[2] == 0
+    meta = workloads.make_meta([0, 3, 0], [5, 3, 0], 16, 2)
+    plan = plan_for(meta, cfg)
+    check_plan(plan, meta, cfg)
+
+
+def test_planner_is_deterministic(L):
+    spec = workloads.SPECS["mixed_7b"]
+    qo, kv = workloads.lengths("mixed_7b")
+    meta = workloads.make_meta(qo, kv, 16, 3)
+    cfg = rpa.make_config(32, 32, 128, 128, 16, "bf16")
+    a = rpa.rpa_plan_debug_dump(plan_for(meta, cfg), "items")
+    b = rpa.rpa_plan_debug_dump(plan_for(meta, cfg), "items")
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------
+# Error paths: each invalid input returns its code and builds nothing
+# ----------------------------------------------------------------------------
+
+
+def expect(status, fn, *args):
+    with pytest.raises(rpa.RpaError) as ei:
+        fn(*args)
+    assert ei.value.status == status, str(ei.value)
+    assert rpa.rpa_last_error_message() != ""
+
+
+def test_plan_create_error_paths(L):
+    cfg = rpa.make_config(4, 2, 64, 64, 16, "f32")
+    ok = dict(qo=[0, 1, 3], kv=[5, 20], pip=[0, 1, 3], pix=[0, 1, 2], num_pages=4)
+
+    def call(cfg=cfg, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return rpa.rpa_plan_create(cfg, a["qo"], a["kv"], a["pip"], a["pix"], a["num_pages"])
+
+    call()  # the baseline is valid
+    expect(rpa.RPA_ERR_INVALID_ARG, lambda: call(qo=[1, 2, 3]))            # indptr not from 0
+    expect(rpa.RPA_ERR_INVALID_ARG, lambda: call(qo=[0, 3, 1]))            # decreasing
+    expect(rpa.RPA_ERR_INVALID_ARG, lambda: call(kv=[0, 20]))              # kv_len < qo_len
+    expect(rpa.RPA_ERR_INVALID_ARG, lambda: call(pip=[0, 2, 1]))           # page indptr decreasing
+    expect(rpa.RPA_ERR_PAGE_OOB, lambda: call(kv=[17, 20]))                # missing page
+    expect(rpa.RPA_ERR_PAGE_OOB, lambda: call(pix=[0, 1, 4]))              # page id >= num_pages
+    expect(rpa.RPA_ERR_PAGE_OOB, lambda: call(pix=[0, -1, 2]))             # negative page id
+    expect(rpa.RPA_ERR_DUPLICATE_WRITE_PAGE, lambda: call(pix=[0, 1, 0]))  # written page twice
+    expect(rpa.RPA_ERR_DUPLICATE_WRITE_PAGE, lambda: call(pix=[2, 1, 2]))
+    # a shared page that nobody writes is fine (prefix sharing)
+    rpa.rpa_plan_create(cfg, [0, 1, 2], [20, 20], [0, 2, 4], [0, 1, 0, 2], 3)
+    bad = [
+        (rpa.RPA_ERR_UNSUPPORTED, rpa.make_config(4, 2, 96, 96, 16, "f32")),
+        (rpa.RPA_ERR_UNSUPPORTED, rpa.make_config(4, 2, 64, 64, 12, "f32")),
+        (rpa.RPA_ERR_UNSUPPORTED, rpa.make_config(4, 2, 64, 64, 512, "f32")),
+        (rpa.RPA_ERR_UNSUPPORTED, rpa.make_config(4, 2, 576, 512, 64, "bf16")),
+        (rpa.RPA_ERR_INVALID_ARG, rpa.make_config(3, 2, 64, 64, 16, "f32")),
+        (rpa.RPA_ERR_INVALID_ARG, rpa.make_config(0, 2, 64, 64, 16, "f32")),
+        (rpa.RPA_ERR_INVALID_ARG, rpa.rpa_attn_config(4, 2, 64, 64, 16, 7, 1, 0.1)),
+        (rpa.RPA_ERR_INVALID_ARG, rpa.rpa_attn_config(4, 2, 64, 64, 16, 0, 2, 0.1)),
+        (rpa.RPA_ERR_INVALID_ARG, rpa.rpa_attn_config(4, 2, 64, 64, 16, 0, 1, float("nan"))),
+    ]
+    for status, c in bad:
+        expect(status, lambda c=c: call(cfg=c))
+    # null pointers through the raw C entry point
+    out = ctypes.c_void_p()
+    assert L.rpa_plan_create(None, None, 0, ctypes.byref(out)) == rpa.RPA_ERR_INVALID_ARG
+    batch = rpa.rpa_batch_desc(2, None, None, None, None, 4)
+    assert L.rpa_plan_create(ctypes.byref(cfg), ctypes.byref(batch), 0,
+                             ctypes.byref(out)) == rpa.RPA_ERR_INVALID_ARG
+    assert out.value is None
+
+
+def test_device_calls_validate_before_touching_the_device(L):
+    cfg = rpa.make_config(4, 2, 64, 64, 16, "f32")
+    plan = rpa.rpa_plan_create(cfg, [0, 1], [5], [0, 1], [0], 1)
+    st = rpa.rpa_cache_strides(2 * 16 * 64, 16 * 64, 64)
+    fake = 1 << 40  # never dereferenced: validation fails first
+    expect(rpa.RPA_ERR_NOT_UPLOADED, rpa.rpa_batch_attention, plan, fake, fake, fake, st, st, fake,
+           None, 0)
+    expect(rpa.RPA_ERR_NOT_UPLOADED, rpa.rpa_kv_append, plan, fake, fake, fake, fake, st, st, 0)
+    size = rpa.rpa_plan_workspace_size(plan)
+    assert size > 0 and size % 256 == 0
+    expect(rpa.RPA_ERR_WORKSPACE_TOO_SMALL, rpa.rpa_plan_upload, plan, fake, size - 1, 0)
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_plan_upload, plan, fake + 16, size, 0)
+    assert L.rpa_plan_upload(None, fake, size, None) == rpa.RPA_ERR_INVALID_ARG
+    # standalone merge argument checks
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_merge_state, fake, fake, fake, fake, fake, fake, 4, 2,
+           12, rpa.RPA_DTYPE_F32, 0)
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_merge_state, fake, fake, fake, fake, fake, fake, -1, 2,
+           8, rpa.RPA_DTYPE_F32, 0)
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_merge_state, None, fake, fake, fake, fake, fake, 4, 2,
+           8, rpa.RPA_DTYPE_F32, 0)
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_merge_state, fake + 4, fake, fake, fake, fake, fake,
+           4, 2, 8, rpa.RPA_DTYPE_F32, 0)
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_merge_state, fake, fake, fake, fake, fake, fake, 4, 2,
+           8, 9, 0)
+    with pytest.raises(rpa.RpaError):
+        rpa.rpa_plan_debug_dump(plan, "no_such_table")
+
+
+def test_plan_debug_dump_append_matches_oracle(L):
+    meta = workloads.make_meta([3, 1, 4], [10, 17, 4], 4, 9)
+    cfg = rpa.make_config(2, 1, 64, 64, 4, "f32")
+    plan = plan_for(meta, cfg)
+    app = rpa.rpa_plan_debug_dump(plan, "append").reshape(-1, 2)
+    batch = oracle.Batch(meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices, 4)
+    i = 0
+    for r in range(3):
+        for t in range(batch.qo_len(r)):
+            assert tuple(app[i]) == oracle.slot_of(batch, r, batch.cached_len(r) + t)
+            i += 1

@@ -1,0 +1,329 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded inputs.
+
+KV pools must match the oracle's append bit for bit (the whole pool, NaN
+sentinels in unreferenced pages included); attention outputs and LSE must be
+within max-abs 2e-2 (bf16) or 1e-4 (fp32) of the oracle.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import ragged_paged_kv_append_amd as rpa
+from tests.gpu_support import (TOL, batch_of, compact, config_of, expected, f64, max_err,
+                               poison_tail_slots, raw, run_library)
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rpa.lib()  # fail loudly if the library is missing
+    yield
+
+
+def check_full(spec, meta, tensors, num_cus=0, label=""):
+    """Whole-batch parity: pools bit-exact, O and LSE within tolerance."""
+    poison_tail_slots(meta, tensors)
+    host = {k: (None if v is None else raw(v)) for k, v in tensors.items()}
+    kp2, vp2, o_ref, lse_ref = expected(spec, meta, host["q"], host["k_new"], host["v_new"],
+                                        host["k_pool"], host["v_pool"])
+    o, lse, plan = run_library(spec, meta, tensors, num_cus=num_cus)
+    assert raw(tensors["k_pool"]).tobytes() == kp2.tobytes(), "K pool differs from the oracle"
+    if vp2 is not None:
+        assert raw(tensors["v_pool"]).tobytes() == vp2.tobytes(), "V pool differs from the oracle"
+    eo = max_err(o, o_ref)
+    el = max_err(lse, lse_ref)
+    log(f"[{label}] max|dO|={eo:.3g} max|dLSE|={el:.3g} summary={plan.debug('summary').tolist()}")
+    tol = TOL[spec.dtype]
+    assert eo <= tol and el <= tol, (eo, el)
+    return o, lse, plan
+
+
+def small_spec(dtype, hq, hkv, dqk, dv, P, causal=True, seed=0):
+    scale = 1.0 / math.sqrt(192 if dqk == 576 else dqk)
+    return workloads.Spec(f"small{seed}", hq, hkv, dqk, dv, P, dtype, scale, seed,
+                          shared_latent=(dqk == 576), causal=causal)
+
+
+# ----------------------------------------------------------------------------
+# Small cases: several tiles and a ragged tail, every supported layout
+# ----------------------------------------------------------------------------
+
+
+def test_tiny_fp32_workload():
+    spec, meta, tensors = workloads.workload("tiny_fp32", device="cuda")
+    check_full(spec, meta, tensors, label="tiny_fp32")
+
+
+SMALL = []
+for seed in range(24):
+    rng = np.random.default_rng(100 + seed)
+    dtype = ["bf16", "f32"][seed % 2]
+    dims = [(128, 128), (64, 64), (128, 128), (576, 512)][(seed // 2) % 4]
+    if dims == (576, 512):
+        dtype = "bf16"
+    P = int([16, 64, 4, 1, 16, 32][seed % 6])
+    hkv = 1 if dims[0] == 576 else int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([16, 32])) if dims[0] == 576 else int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 6))
+    qo = rng.integers(0, 18, size=B)
+    if seed % 5 == 0:
+        qo[0] = 0
+    kv = qo + rng.integers(0, 400, size=B)
+    causal = seed % 4 != 3
+    num_cus = [0, 100000, 4][seed % 3]
+    SMALL.append((seed, dtype, dims, P, hkv, G, qo.tolist(), kv.tolist(), causal, num_cus))
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}" for c in SMALL])
+def test_small_random_batches(case):
+    seed, dtype, dims, P, hkv, G, qo, kv, causal, num_cus = case
+    spec = small_spec(dtype, hkv * G, hkv, dims[0], dims[1], P, causal, seed)
+    meta = workloads.make_meta(qo, kv, P, seed, extra_pages_per_req=seed % 2)
+    tensors = workloads.make_tensors(spec, meta, seed, device="cuda")
+    log(f"case {case}")
+    check_full(spec, meta, tensors, num_cus=num_cus, label=f"small{seed}")
+
+
+def test_prefill_tiles_and_splits_bf16():
+    # several 128-row tiles, a ragged tail, GQA folding and forced kv splits
+    spec = small_spec("bf16", 8, 2, 128, 128, 16, True, 7)
+    meta = workloads.make_meta([300, 1, 4, 129], [900, 700, 50, 129], 16, 7)
+    tensors = workloads.make_tensors(spec, meta, 7, device="cuda")
+    check_full(spec, meta, tensors, num_cus=100000, label="prefill-splits")
+    tensors = workloads.make_tensors(spec, meta, 8, device="cuda")
+    check_full(spec, meta, tensors, num_cus=0, label="prefill-default")
+
+
+def test_interleaved_kv_pages():
+    # K and V of a page interleaved in one allocation: [pages][2][H][P][d]
+    spec = small_spec("bf16", 8, 2, 128, 128, 16, True, 11)
+    meta = workloads.make_meta([1, 5, 33], [70, 40, 90], 16, 11)
+    t = workloads.make_tensors(spec, meta, 11, device="cuda")
+    both = torch.empty((meta.num_pages, 2, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    both[:, 0] = t["k_pool"]
+    both[:, 1] = t["v_pool"]
+    tensors = dict(t, k_pool=both[:, 0], v_pool=both[:, 1])
+    o, lse, _ = check_full(spec, meta, tensors, label="interleaved")
+
+
+def test_deterministic_outputs():
+    spec = small_spec("bf16", 16, 4, 128, 128, 16, True, 3)
+    meta = workloads.make_meta([1, 4, 40], [3000, 2000, 800], 16, 3)
+    outs = []
+    for _ in range(2):
+        tensors = workloads.make_tensors(spec, meta, 3, device="cuda")
+        o, lse, _ = run_library(spec, meta, tensors)
+        outs.append((o.clone(), lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_plan_reuse_across_layers():
+    # one plan, two "layers" with different pools and queries
+    spec = small_spec("bf16", 8, 2, 128, 128, 16, True, 5)
+    meta = workloads.make_meta([1, 4, 20], [500, 300, 64], 16, 5)
+    cfg = config_of(spec)
+    plan = rpa.Plan(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices,
+                    meta.num_pages, num_cus=100000)
+    for layer in range(2):
+        tensors = workloads.make_tensors(spec, meta, 50 + layer, device="cuda")
+        host = {k: (None if v is None else raw(v)) for k, v in tensors.items()}
+        kp2, vp2, o_ref, lse_ref = expected(spec, meta, host["q"], host["k_new"], host["v_new"],
+                                            host["k_pool"], host["v_pool"])
+        plan.append(tensors["k_new"], tensors["v_new"], tensors["k_pool"], tensors["v_pool"])
+        o, lse = plan.attention(tensors["q"], tensors["k_pool"], tensors["v_pool"])
+        torch.cuda.synchronize()
+        assert raw(tensors["k_pool"]).tobytes() == kp2.tobytes()
+        assert max_err(o, o_ref) <= 2e-2 and max_err(lse, lse_ref) <= 2e-2
+
+
+def test_merge_state_matches_oracle():
+    rng = np.random.default_rng(9)
+    for dtype, tol in (("f32", 1e-5), ("bf16", 2e-2)):
+        rows, heads, dim = 37, 5, 64
+        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        o_a = torch.randn(rows, heads, dim, device="cuda").to(tdt)
+        o_b = torch.randn(rows, heads, dim, device="cuda").to(tdt)
+        la = torch.from_numpy(rng.standard_normal((rows, heads)).astype(np.float32) * 3).cuda()
+        lb = torch.from_numpy(rng.standard_normal((rows, heads)).astype(np.float32) * 3).cuda()
+        la[0, :] = float("-inf")           # empty partition A
+        lb[1, :] = float("-inf")           # empty partition B
+        la[2, :] = float("-inf")
+        lb[2, :] = float("-inf")           # both empty
+        o, lse = rpa.merge_state(o_a, la, o_b, lb)
+        torch.cuda.synchronize()
+        want_o, want_l = oracle.merge(f64(raw(o_a)), la.double().cpu().numpy(), f64(raw(o_b)),
+                                      lb.double().cpu().numpy())
+        got_l = lse.double().cpu().numpy()
+        assert np.all(got_l[2] == -np.inf)
+        fin = np.isfinite(want_l)
+        assert np.max(np.abs(got_l[fin] - want_l[fin])) <= 1e-5
+        assert max_err(o, want_o) <= tol
+        # in place: o aliases o_a
+        o_alias = o_a.clone()
+        rpa.rpa_merge_state(o_alias, la, o_b, lb, o_alias, None, rows, heads, dim,
+                            rpa.RPA_DTYPE_F32 if dtype == "f32" else rpa.RPA_DTYPE_BF16)
+        torch.cuda.synchronize()
+        assert torch.equal(o_alias, o)
+
+
+def test_invalid_calls_launch_nothing():
+    spec = small_spec("bf16", 4, 2, 128, 128, 16, True, 1)
+    meta = workloads.make_meta([2], [10], 16, 1)
+    tensors = workloads.make_tensors(spec, meta, 1, device="cuda")
+    before = tensors["k_pool"].clone()
+    cfg = config_of(spec)
+    plan = rpa.Plan(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices,
+                    meta.num_pages)
+    bad = rpa.rpa_cache_strides(1, 1, 1)
+    with pytest.raises(rpa.RpaError) as ei:
+        rpa.rpa_kv_append(plan.handle, tensors["k_new"], tensors["v_new"], tensors["k_pool"],
+                          tensors["v_pool"], bad, bad)
+    assert ei.value.status == rpa.RPA_ERR_INVALID_ARG
+    o = torch.full((2, 4, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(rpa.RpaError):
+        rpa.rpa_batch_attention(plan.handle, tensors["q"], tensors["k_pool"], None,
+                                rpa.strides_of(tensors["k_pool"]), None, o, None)
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int16), tensors["k_pool"].view(torch.int16))
+    assert torch.all(o == 7.0)
+
+
+# ----------------------------------------------------------------------------
+# Full-size workloads (the launch configuration the benchmark times)
+# ----------------------------------------------------------------------------
+
+
+def sampled_parity(spec, meta, tensors, requests, label):
+    """Pools bit-exact over the whole pool; O/LSE checked on sampled requests."""
+    q_raw, kn_raw = raw(tensors["q"]), raw(tensors["k_new"])
+    vn_raw = None if tensors["v_new"] is None else raw(tensors["v_new"])
+    kp_raw = raw(tensors["k_pool"])
+    vp_raw = None if tensors["v_pool"] is None else raw(tensors["v_pool"])
+    b = batch_of(meta)
+    kp2, vp2 = oracle.append(kp_raw, vp_raw, kn_raw, vn_raw, b)
+    o, lse, plan = run_library(spec, meta, tensors)
+    log(f"[{label}] summary={plan.debug('summary').tolist()}")
+    assert raw(tensors["k_pool"]).tobytes() == kp2.tobytes(), "K pool differs from the oracle"
+    if vp2 is not None:
+        assert raw(tensors["v_pool"]).tobytes() == vp2.tobytes(), "V pool differs from the oracle"
+    sub_meta, sub_pools, sub_rows, sel = compact(meta, requests, {"k": kp2, "v": vp2},
+                                                 {"q": q_raw})
+    sb = batch_of(sub_meta)
+    o_ref, lse_ref = oracle.attend(f64(sub_rows["q"]), f64(sub_pools["k"]),
+                                   None if sub_pools["v"] is None else f64(sub_pools["v"]), sb,
+                                   spec.num_qo_heads, spec.num_kv_heads, spec.sm_scale,
+                                   head_dim_v=spec.head_dim_v, causal=spec.causal)
+    sel_t = torch.from_numpy(sel).cuda()
+    eo = max_err(o.index_select(0, sel_t), o_ref)
+    el = max_err(lse.index_select(0, sel_t), lse_ref)
+    log(f"[{label}] sampled {len(requests)} requests: max|dO|={eo:.3g} max|dLSE|={el:.3g}")
+    assert eo <= TOL[spec.dtype] and el <= TOL[spec.dtype]
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_workload_mixed_7b_full():
+    spec, meta, tensors = workloads.workload("mixed_7b", device="cuda")
+    sampled_parity(spec, meta, tensors, range(meta.batch_size), "mixed_7b")
+
+
+def test_workload_decode_verify_gqa_sampled():
+    spec, meta, tensors = workloads.workload("decode_verify_gqa", device="cuda")
+    kv = meta.kv_len
+    picks = sorted(set([int(np.argmax(kv)), int(np.argmin(kv))] +
+                       list(np.random.default_rng(4).choice(meta.batch_size, 22, replace=False))))
+    sampled_parity(spec, meta, tensors, picks, "decode_verify_gqa")
+
+
+def test_workload_mla_absorbed_sampled():
+    spec, meta, tensors = workloads.workload("mla_absorbed", device="cuda")
+    kv = meta.kv_len
+    picks = sorted(set([int(np.argmax(kv)), int(np.argmin(kv)), 1, 17, 33, 50]))
+    sampled_parity(spec, meta, tensors, picks, "mla_absorbed")
+
+
+def _chunked_run(spec, pages, num_pages, q, k, v, C, stop_after=None, pools=None):
+    """GPU chunked prefill of one prompt; returns (o, lse, k_pool, v_pool)."""
+    L = q.shape[0]
+    dev = q.device
+    if pools is None:
+        k_pool = torch.full((num_pages, 1, 16, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+        v_pool = k_pool.clone()
+    else:
+        k_pool, v_pool = pools
+    o = torch.empty((L, spec.num_qo_heads, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((L, spec.num_qo_heads), dtype=torch.float32, device=dev)
+    cfg = config_of(spec)
+    n_chunks = -(-L // C)
+    start_chunk = 0 if stop_after is None else 0
+    for s in range(start_chunk, n_chunks):
+        if stop_after is not None and s > stop_after:
+            break
+        a = s * C
+        n = min(C, L - a)
+        plan = rpa.Plan(cfg, [0, n], [a + n], [0, len(pages)], pages, num_pages)
+        plan.append(k[a:a + n], v[a:a + n], k_pool, v_pool)
+        plan.attention(q[a:a + n], k_pool, v_pool, o=o[a:a + n], lse=lse[a:a + n])
+    torch.cuda.synchronize()
+    return o, lse, k_pool, v_pool
+
+
+def test_workload_chunked_equals_one_shot():
+    spec = workloads.SPECS["chunked_gqa"]
+    L, C = spec.extra["prompt_len"], spec.extra["chunk"]
+    q, k, v = workloads.make_prompt(spec, spec.seed, device="cuda")
+    meta = workloads.make_meta([L], [L], 16, spec.seed)
+    pages = meta.kv_page_indices
+    o_c, l_c, kp_c, vp_c = _chunked_run(spec, pages, meta.num_pages, q, k, v, C)
+    o_1, l_1, kp_1, vp_1 = _chunked_run(spec, pages, meta.num_pages, q, k, v, L)
+    # identical caches, both equal to the oracle's append
+    assert torch.equal(kp_c.view(torch.int16), kp_1.view(torch.int16))
+    assert torch.equal(vp_c.view(torch.int16), vp_1.view(torch.int16))
+    kp0 = np.full((meta.num_pages, 1, 16, 128), 0x7FC0, dtype=np.uint16)
+    b = oracle.Batch([0, L], [L], [0, len(pages)], pages, 16)
+    kp2, vp2 = oracle.append(kp0, kp0.copy(), raw(k), raw(v), b)
+    assert raw(kp_c).tobytes() == kp2.tobytes() and raw(vp_c).tobytes() == vp2.tobytes()
+    # outputs of both GPU runs within tolerance of the oracle's one-shot prefill
+    o_ref, lse_ref = oracle.attend(f64(raw(q)), f64(kp2), f64(vp2), b, 8, 1, spec.sm_scale)
+    for name, o, lse in (("chunked", o_c, l_c), ("one-shot", o_1, l_1)):
+        eo, el = max_err(o, o_ref), max_err(lse, lse_ref)
+        log(f"[chunked_gqa {name}] max|dO|={eo:.3g} max|dLSE|={el:.3g}")
+        assert eo <= 2e-2 and el <= 2e-2
+
+
+def test_chunked_prefill_resumes_from_the_cache_alone():
+    # stop after chunk 5, move the cache through host memory into a fresh pool,
+    # continue: bit-identical to the uninterrupted run
+    spec = workloads.SPECS["chunked_gqa"]
+    L, C = 2048, 256
+    q, k, v = workloads.make_prompt(spec, 77, device="cuda")
+    q, k, v = q[:L].contiguous(), k[:L].contiguous(), v[:L].contiguous()
+    meta = workloads.make_meta([L], [L], 16, 77)
+    pages = meta.kv_page_indices
+    o_full, l_full, kp_full, vp_full = _chunked_run(spec, pages, meta.num_pages, q, k, v, C)
+    o_a, l_a, kp_a, vp_a = _chunked_run(spec, pages, meta.num_pages, q, k, v, C, stop_after=5)
+    kp_host, vp_host = kp_a.cpu(), vp_a.cpu()
+    kp_b, vp_b = kp_host.cuda(), vp_host.cuda()
+    cfg = config_of(spec)
+    for s in range(6, L // C):
+        a = s * C
+        plan = rpa.Plan(cfg, [0, C], [a + C], [0, len(pages)], pages, meta.num_pages)
+        plan.append(k[a:a + C], v[a:a + C], kp_b, vp_b)
+        plan.attention(q[a:a + C], kp_b, vp_b, o=o_a[a:a + C], lse=l_a[a:a + C])
+    torch.cuda.synchronize()
+    assert torch.equal(kp_b.view(torch.int16), kp_full.view(torch.int16))
+    assert torch.equal(o_a.view(torch.int16), o_full.view(torch.int16))
+    assert torch.equal(l_a, l_full)
