@@ -9,6 +9,7 @@ bool class_available(int32_t kernel_class, const rpa_attn_config& cfg) {
   switch (kernel_class) {
     case KC_GENERIC: return true;
     case KC_DECODE: return true;
+    case KC_PREFILL: return true;
     default: return false;
   }
 }

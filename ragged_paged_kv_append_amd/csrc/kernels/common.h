@@ -13,6 +13,33 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits
 
+// Vector types of MFMA operands and accumulators.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane 4c + d receives element d of the four 16-bit elements addressed
+// by lanes c, c + 4, c + 8 and c + 12 of its group (in that order).
+__device__ __forceinline__ s16x4_t lds_read_tr16(const bf16_t* lds_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_addr));
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) {
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// Two floats -> packed bf16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Round to nearest even (the hardware conversion on gfx950).

@@ -27,14 +27,11 @@ namespace rpa {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
 constexpr int kD = 128;
 constexpr int kTile = 16;
-constexpr int kVRow = 132;  // LDS row stride of a V tile (bf16): rows 4 apart fall in distinct banks
+// LDS row stride of a V tile (bf16): 288 bytes keeps rows 16-byte aligned and
+// puts rows 4g .. 4g+3 (read together by one transposing read) in distinct banks.
+constexpr int kVRow = 144;
 constexpr float kMinusBig = -1.0e30f;
 
 struct Frag64 {  // 64 contiguous bytes of one row: 32 bf16
@@ -45,10 +42,6 @@ __device__ __forceinline__ void load_frag(const bf16_t* p, Frag64& f) {
   const u32x4_t* s = reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
   for (int k = 0; k < 4; ++k) f.v[k] = __builtin_nontemporal_load(s + k);
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) {
-  return __builtin_bit_cast(bf16x8_t, u);
 }
 
 }  // namespace
@@ -125,11 +118,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
       bf16_t* dst = &vlds[tile & 1][col * kVRow + 32 * grp];
       const bool key_ok = kb + col < k1;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x4_t w = key_ok ? vf.v[k] : u32x4_t{0u, 0u, 0u, 0u};
-        *reinterpret_cast<uint2*>(dst + 8 * k) = make_uint2(w[0], w[1]);
-        *reinterpret_cast<uint2*>(dst + 8 * k + 4) = make_uint2(w[2], w[3]);
-      }
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<u32x4_t*>(dst + 8 * k) = key_ok ? vf.v[k] : u32x4_t{0u, 0u, 0u, 0u};
     }
     // S^T = K . Q^T
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
@@ -166,12 +156,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
     for (int nb = 0; nb < 8; ++nb) acc[nb] *= alpha;
 
     __syncthreads();  // V tile visible to every lane of the wave
-    const bf16_t* vt = &vlds[tile & 1][0];
+    // V^T operand of block nb: lane (d = 16 nb + col, group grp) needs
+    // V[4 grp + e][d], e = 0..3.  With the transposing read, lane i of the
+    // group supplies row 4 grp + i / 4, columns 16 nb + 4 (i % 4) .. + 3.
+    const bf16_t* vt = &vlds[tile & 1][(4 * grp + (col >> 2)) * kVRow + 4 * (col & 3)];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      s16x4_t va;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) va[e] = (short)vt[(4 * grp + e) * kVRow + 16 * nb + col];
+      const s16x4_t va = lds_read_tr16(vt + 16 * nb);
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[nb], 0, 0, 0);
     }
     if (tile + 1 < ntiles) {

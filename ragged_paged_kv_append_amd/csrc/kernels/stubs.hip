@@ -4,10 +4,6 @@
 
 namespace rpa {
 
-hipError_t launch_prefill(const DevPlan&, const void*, const void*, const void*, Strides, Strides,
-                          void*, float*, hipStream_t) {
-  return hipErrorNotSupported;
-}
 hipError_t launch_mla(const DevPlan&, const void*, const void*, Strides, void*, float*,
                       hipStream_t) {
   return hipErrorNotSupported;
