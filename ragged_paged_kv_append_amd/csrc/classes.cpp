@@ -10,6 +10,7 @@ bool class_available(int32_t kernel_class, const rpa_attn_config& cfg) {
     case KC_GENERIC: return true;
     case KC_DECODE: return true;
     case KC_PREFILL: return true;
+    case KC_MLA: return true;
     default: return false;
   }
 }
