@@ -2,6 +2,7 @@
 """Benchmark of ragged paged attention with KV append on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-calibration      # 1 GiB device copy, for HBM counter scaling
 
 A step is one pass of the hot path over one batch: KV append of the batch's
 new tokens, then batched attention (all kernels, split-piece merge included),
@@ -177,6 +178,38 @@ def run_batch(spec, meta, tensors, steps, warmup):
     return plan, ms, kernels
 
 
+KERNEL_SOURCES = {"generic": "basic.hip", "decode": "decode.hip", "prefill": "prefill.hip",
+                  "mla": "mla.hip"}
+SHARED_SOURCES = ("kernels/common.h", "launch.h", "rpa_internal.h", "plan.cpp")
+
+
+def kernel_source_hash(kernel):
+    """Hash of the sources a kernel's launches depend on (its file, the shared
+    device header, the launch declarations, the plan layout and the planner)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "ragged_paged_kv_append_amd", "csrc")
+    h = hashlib.sha256()
+    for rel in ("kernels/" + KERNEL_SOURCES[kernel],) + SHARED_SOURCES:
+        with open(os.path.join(csrc, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when no run exists for
+    this kernel and workload or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            entry = json.load(f).get(workload, {}).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("src_hash") != kernel_source_hash(kernel):
+        return None
+    return entry["traffic_bytes"]
+
+
 def roofline_for(spec, meta, plan, kernels):
     """Roofline entry of the attention kernel that takes the most time per step."""
     attn = {k: v for k, v in kernels.items() if k in ("generic", "decode", "prefill", "mla")}
@@ -194,13 +227,15 @@ def roofline_for(spec, meta, plan, kernels):
     if name in ("prefill", "mla"):
         achieved = w["flops"] / per_step / launch_s / 1e12
         return {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                "traffic": measured_traffic(spec.name, name),
                 "avg_launch_us": avg_ms * 1e3,
                 "algorithmic_per_launch": {"flops": w["flops"] / per_step}}
     nbytes = (w["kv_bytes"] + w["qo_bytes"]) / per_step
     achieved = nbytes / launch_s / 1e9
     return {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(spec.name, name),
             "avg_launch_us": avg_ms * 1e3, "algorithmic_per_launch": {"bytes": nbytes}}
 
 
@@ -257,6 +292,22 @@ def cpu_baseline(spec, meta, tensors, requests, unit):
 # ----------------------------------------------------------------------------
 
 
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain copy of known size: each launch reads and writes `nbytes`."""
+    import torch
+    torch.cuda.set_device(0)
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps, "ms_per_copy": dt * 1e3,
+                      "gbps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,7 +316,13 @@ def main():
     ap.add_argument("--workload", default="mixed_7b",
                     choices=["mixed_7b", "decode_verify_gqa", "mla_absorbed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
+                         "kernel that FETCH_SIZE / WRITE_SIZE counter readings are scaled by)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

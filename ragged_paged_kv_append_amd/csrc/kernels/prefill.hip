@@ -82,26 +82,28 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(DevPlan p, const bf16_t
   const int lkey = tid >> 2, lq = tid & 3;
   const int32_t* pages = p.page_indices + p.page_indptr[r];
   // Keys past k1 are loaded from the item's last key (always a valid slot) and
-  // replaced by zeros, so that 0 * value can never be NaN.
+  // stored as zeros, so that 0 * value can never be NaN.  The zeroing happens
+  // when the registers are written to LDS, a whole tile after the load was
+  // issued, and page ids are fetched one tile ahead of the K/V loads, so that
+  // nothing waits for a load in flight.
   u32x4_t kr0, kr1, kr2, kr3, vr0, vr1, vr2, vr3;
-#define RPA_LOAD_TILE(kb)                                                                    \
-  do {                                                                                       \
-    const int32_t key_ = (kb) + lkey;                                                        \
-    const bool ok_ = key_ < k1;                                                              \
-    const int32_t kk_ = ok_ ? key_ : k1 - 1;                                                 \
-    const int64_t page_ = pages[kk_ >> p.page_shift];                                        \
-    const int64_t slot_ = kk_ & (p.page_size - 1);                                           \
-    const u32x4_t* kp_ = reinterpret_cast<const u32x4_t*>(kc + page_ * ks.page + k_off +     \
-                                                          slot_ * ks.token);                 \
-    const u32x4_t* vp_ = reinterpret_cast<const u32x4_t*>(vc + page_ * vs.page + v_off +     \
-                                                          slot_ * vs.token);                 \
-    const u32x4_t z_ = {0u, 0u, 0u, 0u};                                                     \
-    kr0 = kp_[0]; kr1 = kp_[1]; kr2 = kp_[2]; kr3 = kp_[3];                                  \
-    vr0 = vp_[0]; vr1 = vp_[1]; vr2 = vp_[2]; vr3 = vp_[3];                                  \
-    if (!ok_) { kr0 = kr1 = kr2 = kr3 = z_; vr0 = vr1 = vr2 = vr3 = z_; }                    \
-  } while (0)
   const int64_t k_off = (int64_t)g * ks.head + 32 * lq;
   const int64_t v_off = (int64_t)g * vs.head + 32 * lq;
+  auto page_of = [&](int32_t kb) {
+    const int32_t key = min(kb + lkey, k1 - 1);
+    return pages[key >> p.page_shift];
+  };
+#define RPA_LOAD_TILE(kb, pg_id)                                                              \
+  do {                                                                                       \
+    const int32_t kk_ = min((kb) + lkey, k1 - 1);                                            \
+    const int64_t slot_ = kk_ & (p.page_size - 1);                                           \
+    const u32x4_t* kp_ = reinterpret_cast<const u32x4_t*>(kc + (int64_t)(pg_id) * ks.page +   \
+                                                          k_off + slot_ * ks.token);         \
+    const u32x4_t* vp_ = reinterpret_cast<const u32x4_t*>(vc + (int64_t)(pg_id) * vs.page +   \
+                                                          v_off + slot_ * vs.token);         \
+    kr0 = kp_[0]; kr1 = kp_[1]; kr2 = kp_[2]; kr3 = kp_[3];                                  \
+    vr0 = vp_[0]; vr1 = vp_[1]; vr2 = vp_[2]; vr3 = vp_[3];                                  \
+  } while (0)
 
   const float sc = p.sm_scale * kLog2e;
   float m = kMinusBig;  // running row max, log2 units
@@ -118,17 +120,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(DevPlan p, const bf16_t
   const int tr_col = 16 * (col >> 4) + 4 * (lane & 3);
 
   const int32_t ntiles = (kend - k0 + kKT - 1) / kKT;
-  if (ntiles > 0) RPA_LOAD_TILE(k0);
+  int32_t page_next = 0;
+  if (ntiles > 0) {
+    RPA_LOAD_TILE(k0, page_of(k0));
+    if (ntiles > 1) page_next = page_of(k0 + kKT);
+  }
   for (int32_t tile = 0; tile < ntiles; ++tile) {
     const int32_t kb = k0 + tile * kKT;
     __syncthreads();  // every wave is done reading the previous tile
     {
+      const bool ok = kb + lkey < k1;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
       u32x4_t* kd = reinterpret_cast<u32x4_t*>(&klds[lkey * kKRow + 32 * lq]);
       u32x4_t* vd = reinterpret_cast<u32x4_t*>(&vlds[lkey * kVRow + 32 * lq]);
-      kd[0] = kr0; kd[1] = kr1; kd[2] = kr2; kd[3] = kr3;
-      vd[0] = vr0; vd[1] = vr1; vd[2] = vr2; vd[3] = vr3;
+      kd[0] = ok ? kr0 : z; kd[1] = ok ? kr1 : z; kd[2] = ok ? kr2 : z; kd[3] = ok ? kr3 : z;
+      vd[0] = ok ? vr0 : z; vd[1] = ok ? vr1 : z; vd[2] = ok ? vr2 : z; vd[3] = ok ? vr3 : z;
     }
-    if (tile + 1 < ntiles) RPA_LOAD_TILE(kb + kKT);
+    if (tile + 1 < ntiles) {
+      RPA_LOAD_TILE(kb + kKT, page_next);
+      if (tile + 2 < ntiles) page_next = page_of(kb + 2 * kKT);
+    }
     __syncthreads();  // tile visible
     if (!wave_has_rows || kb >= kend_wmax) continue;
 
