@@ -10,15 +10,27 @@
 // quarter page for P = 64), so every tile is one contiguous 4 KiB run of K and
 // one of V in the HND layout.
 //
+// Streaming: tiles move from HBM into a ring of kStages LDS slots with the
+// gfx950 global-to-LDS DMA (global_load_lds_dwordx4, 1 KiB per instruction),
+// issued kStages - 1 tiles ahead of the tile being computed.  The waits on
+// the DMA are explicit vmcnt counts, so kStages - 1 tiles (24 KiB per wave)
+// stay in flight through the whole loop without holding any registers.
+// Within a slot, the 16-byte chunk c of row j sits at position c ^ j of the
+// row, so the K-operand reads and the transposing V reads are free of bank
+// conflicts.
+//
 // Per tile, with 16x16 MFMA tiles and query rows padded to 16:
-//   S^T[key][row] = K[key][:] . Q[row][:]      4 x mfma 16x16x32 bf16; the K
-//       tile goes from HBM straight into the A operand (each lane loads 64
-//       contiguous bytes of one key row);
+//   S^T[key][row] = K[key][:] . Q[row][:]      4 x mfma 16x16x32 bf16, K read
+//       from the slot (each lane: 64 bytes of one key row), Q in registers;
 //   online softmax on S^T: each lane holds 4 keys of one query row;
 //   O^T[d][row] += V^T[d][keys] . P^T[keys][row]   8 x mfma 16x16x16 bf16; the
 //       S^T accumulator layout is exactly the B operand layout of P^T, so P
-//       never moves between lanes; V goes through LDS to be read per column.
-// The next tile's K and V are loaded while the current one is computed.
+//       never moves between lanes; V^T comes from the slot through the
+//       transposing LDS read.
+// Keys past the item's end are fetched from its last key (a written slot of
+// the same page), so the masked tail multiplies finite values by zero.
+
+#include <stdlib.h>
 
 #include "common.h"
 #include "../launch.h"
@@ -28,33 +40,72 @@ namespace rpa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kTile = 16;
-// LDS row stride of a V tile (bf16): 288 bytes keeps rows 16-byte aligned and
-// puts rows 4g .. 4g+3 (read together by one transposing read) in distinct banks.
-constexpr int kVRow = 144;
+constexpr int kTile = 16;    // keys per tile
+constexpr int kTileElems = kTile * kD;
 constexpr float kMinusBig = -1.0e30f;
+constexpr int kNonTemporal = 2;  // cache-policy bit of the DMA loads: streaming data
 
-struct Frag64 {  // 64 contiguous bytes of one row: 32 bf16
-  u32x4_t v[4];
-};
+// Waits until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Waits for every LDS operation of this wave.
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ void load_frag(const bf16_t* p, Frag64& f) {
-  const u32x4_t* s = reinterpret_cast<const u32x4_t*>(p);
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Blocking scalar load of one page id.  The page table is read through the
+// scalar cache and the wait covers only LDS/scalar operations, never the DMA
+// stream in flight.
+__device__ __forceinline__ int32_t load_scalar(const int32_t* ptr) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+
+// The eight transposing reads of a V tile (blocks nb = 0..7 of 16 value dims)
+// for the lane whose row is `vrow`: block nb sits in chunk (2 nb + vhalf) ^ vrow.
+// Written as one asm block with its own LDS wait: the compiler cannot tell
+// these reads from the in-flight DMA and would otherwise drain the whole DMA
+// stream before them.
+__device__ __forceinline__ void read_vt(const bf16_t* row_base, int vrow, int vhalf,
+                                        s16x4_t (&va)[8]) {
+  typedef __attribute__((address_space(3))) const bf16_t* lds_ptr_t;
+  uint32_t a[8];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) f.v[k] = __builtin_nontemporal_load(s + k);
+  for (int nb = 0; nb < 8; ++nb)
+    a[nb] = (uint32_t)(uintptr_t)(lds_ptr_t)(row_base + 8 * ((2 * nb + vhalf) ^ vrow));
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]), "=&v"(va[4]), "=&v"(va[5]),
+        "=&v"(va[6]), "=&v"(va[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
 }
 
 }  // namespace
 
+// kStages: LDS ring depth in tiles (8 KiB each); kStages - 1 tiles are in flight.
+template <int kStages>
 __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __restrict__ q,
                                                     const bf16_t* __restrict__ kc,
                                                     const bf16_t* __restrict__ vc, Strides ks,
                                                     Strides vs, bf16_t* __restrict__ o,
                                                     float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) bf16_t vlds[2][kTile * kVRow];
+  // ring[slot][0] = K tile, ring[slot][1] = V tile, rows of 128 bf16.
+  __shared__ __attribute__((aligned(1024))) bf16_t ring[kStages][2][kTileElems];
   const int lane = threadIdx.x;
   const int col = lane & 15;  // query row of S^T / P^T / O^T columns; key row of the K operand
-  const int grp = lane >> 4;  // which 32-element quarter of a row this lane loads
+  const int grp = lane >> 4;  // which 32-element quarter of a row this lane reads
 
   const int32_t* it = p.items[KC_DECODE] + (int64_t)blockIdx.x * IT_WORDS;
   const int32_t r = it[IT_REQ], g = it[IT_KVHEAD], rows = it[IT_ROW1];
@@ -73,24 +124,41 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
   const int32_t t_last = (rows - 1) / G;
   const int32_t kend = min(k1, (p.causal ? cached + t_last : L - 1) + 1);
 
-  Frag64 qf;
-  if (row_ok) {
-    load_frag(q + ((int64_t)(q0 + t) * p.num_qo_heads + h) * kD + 32 * grp, qf);
-  } else {
+  // Q operand: qf[j] = Q[row][32 grp + 8 j .. + 8), the dims of chunk 4 grp + j.
+  u32x4_t qf[4];
+  {
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
+        q + ((int64_t)(q0 + t) * p.num_qo_heads + h) * kD + 32 * grp);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) qf.v[k] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 4; ++j) qf[j] = row_ok ? qp[j] : u32x4_t{0u, 0u, 0u, 0u};
+    // Use Q here so that its load completes before the DMA stream starts: the
+    // loop below then owns the vector-memory counter.
+    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]));
   }
 
   const int32_t* pages = p.page_indices + p.page_indptr[r];
-  const int64_t k_head = (int64_t)g * ks.head + (int64_t)col * ks.token + 32 * grp;
-  const int64_t v_head = (int64_t)g * vs.head + (int64_t)col * vs.token + 32 * grp;
-  auto k_ptr = [&](int32_t kb) {
-    const int64_t page = pages[kb >> p.page_shift];
-    return kc + page * ks.page + (int64_t)(kb & (p.page_size - 1)) * ks.token + k_head;
-  };
-  auto v_ptr = [&](int32_t kb) {
-    const int64_t page = pages[kb >> p.page_shift];
-    return vc + page * vs.page + (int64_t)(kb & (p.page_size - 1)) * vs.token + v_head;
+  // DMA role: instruction i of a tile moves rows 4 (i % 4) + lane / 16, chunk
+  // (lane % 16) ^ row into LDS position lane % 16 of that row.
+  const int drow = lane >> 4;
+  const int64_t k_head = (int64_t)g * ks.head;
+  const int64_t v_head = (int64_t)g * vs.head;
+  auto issue = [&](int32_t kb, int slot) {
+    const int64_t page = load_scalar(pages + (kb >> p.page_shift));
+    const bf16_t* kpage = kc + page * ks.page + k_head;
+    const bf16_t* vpage = vc + page * vs.page + v_head;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * i + drow;
+      const int32_t key = min(kb + row, k1 - 1);
+      const int64_t slot_in_page = key & (p.page_size - 1);
+      const int chunk = (lane & 15) ^ row;
+      __builtin_amdgcn_global_load_lds(kpage + slot_in_page * ks.token + 8 * chunk,
+                                       (lds_void_t*)&ring[slot][0][512 * i], 16, 0,
+                                       kNonTemporal);
+      __builtin_amdgcn_global_load_lds(vpage + slot_in_page * vs.token + 8 * chunk,
+                                       (lds_void_t*)&ring[slot][1][512 * i], 16, 0,
+                                       kNonTemporal);
+    }
   };
 
   const float sc = p.sm_scale * kLog2e;
@@ -100,33 +168,39 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Transposing-read address of this lane inside a V tile: row 4 grp + col / 4,
+  // element column 16 nb + 4 (col % 4), i.e. chunk 2 nb + (col % 4) / 2.
+  const int vrow = 4 * grp + (col >> 2);
+  const int vhalf = (col >> 1) & 1;
+  const int voff = 4 * (col & 1);
+
   const int32_t ntiles = (kend - k0 + kTile - 1) / kTile;
-  Frag64 kf, vf, kf_next, vf_next;
-  if (ntiles > 0) {
-    load_frag(k_ptr(k0), kf);
-    load_frag(v_ptr(k0), vf);
-  }
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j)
+    if (j < ntiles) issue(k0 + j * kTile, j);
+
   for (int32_t tile = 0; tile < ntiles; ++tile) {
     const int32_t kb = k0 + tile * kTile;
-    if (tile + 1 < ntiles) {
-      load_frag(k_ptr(kb + kTile), kf_next);
-      load_frag(v_ptr(kb + kTile), vf_next);
+    const int slot = tile % kStages;
+    if (tile + kStages - 1 < ntiles) {
+      wait_lds();  // the slot about to be refilled was read by the previous tile
+      issue(kb + (kStages - 1) * kTile, (tile + kStages - 1) % kStages);
+      wait_vmem<8 * (kStages - 1)>();  // this tile's 8 DMA instructions are done
+    } else {
+      wait_vmem<0>();
     }
-    // Stage V in LDS; keys past k1 (outside the item, possibly unwritten
-    // slots) become zeros so that 0 * value can never be NaN.
-    {
-      bf16_t* dst = &vlds[tile & 1][col * kVRow + 32 * grp];
-      const bool key_ok = kb + col < k1;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<u32x4_t*>(dst + 8 * k) = key_ok ? vf.v[k] : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    const bf16_t* kt = ring[slot][0];
+    const bf16_t* vt = ring[slot][1];
+
     // S^T = K . Q^T
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf.v[k]), as_bf16x8(qf.v[k]), sacc,
-                                                     0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t a =
+          *reinterpret_cast<const u32x4_t*>(kt + col * kD + 8 * ((4 * grp + j) ^ col));
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qf[j]), sacc, 0, 0,
+                                                     0);
+    }
     // Online softmax for query row `col`; this lane holds keys kb + 4*grp + e.
     float sv[4];
     float mx = kMinusBig;
@@ -149,26 +223,17 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
     }
     lsum = lsum * alpha + psum;
     m = m_new;
-    s16x4_t pb;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pb[e] = (short)f32_to_bf16(pv[e]);
+    const u32x2_t pw = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+    const s16x4_t pb = __builtin_bit_cast(s16x4_t, pw);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) acc[nb] *= alpha;
 
-    __syncthreads();  // V tile visible to every lane of the wave
-    // V^T operand of block nb: lane (d = 16 nb + col, group grp) needs
-    // V[4 grp + e][d], e = 0..3.  With the transposing read, lane i of the
-    // group supplies row 4 grp + i / 4, columns 16 nb + 4 (i % 4) .. + 3.
-    const bf16_t* vt = &vlds[tile & 1][(4 * grp + (col >> 2)) * kVRow + 4 * (col & 3)];
+    // O^T += V^T P^T, V^T of block nb through the transposing read.
+    s16x4_t va[8];
+    read_vt(vt + vrow * kD + voff, vrow, vhalf, va);
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const s16x4_t va = lds_read_tr16(vt + 16 * nb);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[nb], 0, 0, 0);
-    }
-    if (tile + 1 < ntiles) {
-      kf = kf_next;
-      vf = vf_next;
-    }
+    for (int nb = 0; nb < 8; ++nb)
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[nb], pb, acc[nb], 0, 0, 0);
   }
 
   // Row sum over the four lane groups, then normalise and store.
@@ -203,9 +268,25 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
 
 hipError_t launch_decode(const DevPlan& p, const void* q, const void* k_cache, const void* v_cache,
                          Strides ks, Strides vs, void* o, float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_kernel, dim3(p.n_items[KC_DECODE]), dim3(64), 0, stream, p,
-                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_cache),
-                     static_cast<const bf16_t*>(v_cache), ks, vs, static_cast<bf16_t*>(o), lse);
+  // Ring depth: 3 tiles by default (24 KiB of LDS per wave, so six waves fit a
+  // compute unit with two tiles each in flight); RPA_DECODE_STAGES in
+  // {3, 4, 6} overrides it (a tuning knob, read once).
+  static const int stages = [] {
+    const char* e = getenv("RPA_DECODE_STAGES");
+    const int v = e ? atoi(e) : 3;
+    return (v == 4 || v == 6) ? v : 3;
+  }();
+  const dim3 grid(p.n_items[KC_DECODE]), block(64);
+  const bf16_t* qq = static_cast<const bf16_t*>(q);
+  const bf16_t* kk = static_cast<const bf16_t*>(k_cache);
+  const bf16_t* vv = static_cast<const bf16_t*>(v_cache);
+  bf16_t* oo = static_cast<bf16_t*>(o);
+  if (stages == 3)
+    hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
+  else if (stages == 6)
+    hipLaunchKernelGGL(decode_kernel<6>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
+  else
+    hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
   return hipGetLastError();
 }
 
