@@ -239,6 +239,60 @@ def roofline_for(spec, meta, plan, kernels):
             "avg_launch_us": avg_ms * 1e3, "algorithmic_per_launch": {"bytes": nbytes}}
 
 
+def run_chunked(spec, steps, warmup):
+    """The 8192-token GQA prompt run as 16 chunks of 512 (append, then
+    attention over the pages, per chunk) and one-shot.  Every chunk step is
+    timed on its own after the whole prompt has been appended once (the append
+    is idempotent, and a chunk's attention reads only keys below its end)."""
+    import numpy as np
+    import torch
+    import workloads
+    import ragged_paged_kv_append_amd as rpa
+    L, C = spec.extra["prompt_len"], spec.extra["chunk"]
+    q, k, v = workloads.make_prompt(spec, spec.seed, device="cuda")
+    meta = workloads.make_meta([L], [L], spec.page_size, spec.seed)
+    pages = meta.kv_page_indices
+    shape = (meta.num_pages, spec.num_kv_heads, spec.page_size, spec.head_dim_qk)
+    k_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    v_pool = k_pool.clone()
+    o = torch.empty((L, spec.num_qo_heads, spec.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((L, spec.num_qo_heads), dtype=torch.float32, device="cuda")
+    cfg = rpa.make_config(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim_qk, spec.head_dim_v,
+                          spec.page_size, spec.dtype, spec.causal, spec.sm_scale)
+
+    def step_of(a, n):
+        plan = rpa.Plan(cfg, [0, n], [a + n], [0, len(pages)], pages, meta.num_pages)
+
+        def step():
+            plan.append(k[a:a + n], v[a:a + n], k_pool, v_pool)
+            plan.attention(q[a:a + n], k_pool, v_pool, o=o[a:a + n], lse=lse[a:a + n])
+        return step
+
+    chunks = [step_of(a, min(C, L - a)) for a in range(0, L, C)]
+    for st in chunks:
+        st()
+    torch.cuda.synchronize()
+    per_chunk = []
+    for i, st in enumerate(chunks):
+        a = i * C
+        n = min(C, L - a)
+        ms, kernels = timed_steps(st, steps, warmup)
+        w = work(spec, [n], [a + n])
+        attn_ms = sum(t * c for name, (t, c) in kernels.items() if name != "append")
+        per_chunk.append({"chunk": i, "kv_len": a + n, "ms_per_step": ms, "attention_ms": attn_ms,
+                          "flops": w["flops"], "tflops": w["flops"] / (attn_ms * 1e-3) / 1e12,
+                          "kernels_us": {kk: t * 1e3 for kk, (t, c) in kernels.items()},
+                          "launches": {kk: c for kk, (t, c) in kernels.items()}})
+    one = step_of(0, L)
+    ms1, k1 = timed_steps(one, max(3, steps // 4), 1)
+    w1 = work(spec, [L], [L])
+    attn1 = sum(t * c for name, (t, c) in k1.items() if name != "append")
+    one_shot = {"ms_per_step": ms1, "attention_ms": attn1, "flops": w1["flops"],
+                "tflops": w1["flops"] / (attn1 * 1e-3) / 1e12,
+                "kernels_us": {kk: t * 1e3 for kk, (t, c) in k1.items()}}
+    return per_chunk, one_shot
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on a bounded sample, on this host's cores
 # ----------------------------------------------------------------------------
@@ -314,7 +368,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixed_7b",
-                    choices=["mixed_7b", "decode_verify_gqa", "mla_absorbed"])
+                    choices=["mixed_7b", "decode_verify_gqa", "mla_absorbed", "chunked_gqa"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
@@ -336,6 +390,9 @@ def main():
     rpa.lib()
     torch.cuda.set_device(0)
     name = args.workload
+    if name == "chunked_gqa":
+        main_chunked(args)
+        return
     log(f"workload {name}: generating inputs")
     spec, meta, tensors = workloads.workload(name, device="cuda")
     torch.cuda.synchronize()
@@ -410,6 +467,47 @@ def main():
         "launches_per_step": {k: v[1] for k, v in kernels.items()},
         "plan_ms": plan_ms,
         "parts": parts,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def main_chunked(args):
+    """Chunked prefill of one 8192-token GQA prompt (16 chunks of 512): value
+    is the aggregate attention TFLOP/s over the 16 chunk steps."""
+    import workloads
+    spec = workloads.SPECS["chunked_gqa"]
+    log(f"workload chunked_gqa: timing each of 16 chunk steps, {args.steps} steps after "
+        f"{args.warmup} warmup")
+    per_chunk, one_shot = run_chunked(spec, args.steps, args.warmup)
+    flops = sum(c["flops"] for c in per_chunk)
+    attn_ms = sum(c["attention_ms"] for c in per_chunk)
+    step_ms = sum(c["ms_per_step"] for c in per_chunk)
+    pre_us = [c["kernels_us"].get("prefill", 0.0) * c["launches"].get("prefill", 0.0)
+              for c in per_chunk]
+    launches = sum(c["launches"].get("prefill", 0.0) for c in per_chunk)
+    achieved = flops / (sum(pre_us) * 1e-6) / 1e12 if sum(pre_us) > 0 else None
+    roof = None
+    if achieved is not None:
+        roof = {"kernel": "prefill", "bound": "mfma", "achieved": achieved,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                "traffic": measured_traffic("chunked_gqa", "prefill"),
+                "avg_launch_us": sum(pre_us) / launches,
+                "algorithmic_per_launch": {"flops": flops / launches}}
+    line = {
+        "metric": METRIC, "value": flops / (attn_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": "chunked_gqa", "prompt_len": spec.extra["prompt_len"],
+                   "chunk": spec.extra["chunk"], "num_qo_heads": spec.num_qo_heads,
+                   "num_kv_heads": spec.num_kv_heads, "head_dim_qk": spec.head_dim_qk,
+                   "head_dim_v": spec.head_dim_v, "page_size": spec.page_size,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof, "cpu_baseline": None,
+        "work": {"flops": flops},
+        "parts": {"chunks": [{k: c[k] for k in ("chunk", "kv_len", "tflops", "attention_ms",
+                                                "kernels_us")} for c in per_chunk],
+                  "one_shot": one_shot},
     }
     print(json.dumps(line), flush=True)
 

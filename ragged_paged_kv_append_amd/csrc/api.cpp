@@ -43,6 +43,8 @@ rpa::DevPlan dev_plan(const rpa_plan* plan) {
   for (int k = 0; k < rpa::KC_COUNT; ++k) {
     p.items[k] = base + plan->off_items[k];
     p.n_items[k] = plan->n_items[k];
+    p.wg_indptr[k] = base + plan->off_wg[k];
+    p.n_wgs[k] = plan->n_wgs[k];
   }
   p.merge_rows = base + plan->off_merge;
   p.n_merge_rows = plan->n_merge_rows;
@@ -412,6 +414,10 @@ RPA_EXPORT rpa_status rpa_plan_debug_dump(const rpa_plan* plan, const char* name
   } else if (nm == "append") {
     src = blob + plan->off_append;
     n = (int64_t)plan->total_q * 2;
+  } else if (nm == "wg_prefill" || nm == "wg_mla") {
+    const int k = nm == "wg_prefill" ? rpa::KC_PREFILL : rpa::KC_MLA;
+    src = blob + plan->off_wg[k];
+    n = plan->n_items[k] > 0 ? (int64_t)plan->n_wgs[k] + 1 : 0;
   } else if (nm == "merge_rows") {
     src = blob + plan->off_merge;
     n = plan->n_merge_rows;

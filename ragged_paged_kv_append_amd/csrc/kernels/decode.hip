@@ -59,8 +59,14 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // scalar cache and the wait covers only LDS/scalar operations, never the DMA
 // stream in flight.
 __device__ __forceinline__ int32_t load_scalar(const int32_t* ptr) {
+  // The address is wave-uniform; readfirstlane puts it in scalar registers
+  // even where the compiler holds it in vector registers.
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int32_t* sp = reinterpret_cast<const int32_t*>(lo | (hi << 32));
   int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sp) : "memory");
   return v;
 }
 

@@ -31,6 +31,14 @@ int32_t log2i(int32_t x) {
   return s;
 }
 
+int64_t wgs_per_cu(int32_t cls) {
+  switch (cls) {
+    case KC_PREFILL: return PRE_WGS_PER_CU;
+    case KC_MLA: return MLA_WGS_PER_CU;
+    default: return 1;
+  }
+}
+
 int32_t rows_per_item(int32_t cls, int32_t rows_total) {
   switch (cls) {
     case KC_DECODE: return DEC_MAX_ROWS;
@@ -181,23 +189,37 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
   // ---- split of kv ranges into pieces ----------------------------------------
   const int64_t cus = num_cus > 0 ? num_cus : 256;
   // Streaming classes (generic, decode): pieces sized so the whole batch makes
-  // about 8 items per compute unit.  Tile classes (prefill, latent): split only
-  // when the row tiles alone make fewer than 2 items per compute unit.
-  int64_t stream_work = 0, tiles = 0;
+  // about 8 items per compute unit.  Tile classes (prefill, latent): pieces
+  // sized so that one piece of a full row tile carries about the average load
+  // of one resident workgroup; the items are then packed onto the resident
+  // workgroups longest first (below).
+  int64_t stream_work = 0;
+  int64_t tile_work[KC_COUNT] = {0, 0, 0, 0};
   for (int32_t r = 0; r < B; ++r) {
     const int64_t n = (int64_t)qo[r + 1] - qo[r];
     if (n == 0) continue;
+    const int64_t R = rows_per_item(cls[r], (int32_t)(n * G));
     if (cls[r] == KC_GENERIC || cls[r] == KC_DECODE) {
-      stream_work += (int64_t)kvl[r] * c.num_kv_heads *
-                     ceil_div(n * G, rows_per_item(cls[r], (int32_t)(n * G)));
+      stream_work += (int64_t)kvl[r] * c.num_kv_heads * ceil_div(n * G, R);
     } else {
-      tiles += (int64_t)c.num_kv_heads * ceil_div(n * G, rows_per_item(cls[r], 0));
+      const int64_t cached = (int64_t)kvl[r] - n;
+      for (int64_t row0 = 0; row0 < n * G; row0 += R) {
+        const int64_t row1 = std::min(n * G, row0 + R);
+        const int64_t visible = c.causal ? cached + (row1 - 1) / G + 1 : kvl[r];
+        tile_work[cls[r]] += visible * round_up(row1 - row0, 32) * c.num_kv_heads;
+      }
     }
   }
   const int64_t stream_piece =
       std::max<int64_t>(KEY_ALIGN, round_up(ceil_div(std::max<int64_t>(stream_work, 1), 8 * cus),
                                             KEY_ALIGN));
-  const int64_t tile_split = tiles >= 2 * cus ? 1 : ceil_div(2 * cus, std::max<int64_t>(tiles, 1));
+  int64_t tile_piece[KC_COUNT] = {0, 0, 0, 0};
+  for (int k : {(int)KC_PREFILL, (int)KC_MLA}) {
+    const int64_t slots = wgs_per_cu(k) * cus;
+    tile_piece[k] = std::max<int64_t>(
+        4 * KEY_ALIGN, round_up(ceil_div(std::max<int64_t>(tile_work[k], 1),
+                                         slots * rows_per_item(k, 0)), KEY_ALIGN));
+  }
 
   std::vector<int32_t> split((size_t)B * SP_WORDS, 0);
   int64_t partial_rows = 0;
@@ -209,7 +231,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
       if (cls[r] == KC_GENERIC || cls[r] == KC_DECODE) {
         S = ceil_div(L, stream_piece);
       } else {
-        S = std::min<int64_t>(tile_split, ceil_div(L, 256));
+        S = ceil_div(L, tile_piece[cls[r]]);
       }
       S = std::max<int64_t>(S, 1);
       kc = round_up(ceil_div(L, S), KEY_ALIGN);
@@ -250,7 +272,9 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
           const int32_t it[IT_WORDS] = {r, g, (int32_t)row0, (int32_t)row1, (int32_t)k0,
                                         (int32_t)k1, (int32_t)s, k};
           items[k].insert(items[k].end(), it, it + IT_WORDS);
-          cost[k].push_back((std::min(k1, p_last + 1) - k0) * (row1 - row0));
+          const int64_t rows_cost = (k == KC_PREFILL || k == KC_MLA) ? round_up(row1 - row0, 32)
+                                                                      : row1 - row0;
+          cost[k].push_back((std::min(k1, p_last + 1) - k0) * rows_cost);
         }
       }
     }
@@ -266,6 +290,45 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
     for (size_t j = 0; j < m; ++j)
       std::memcpy(&sorted[j * IT_WORDS], &items[k][order[j] * IT_WORDS], IT_WORDS * sizeof(int32_t));
     items[k].swap(sorted);
+  }
+
+  // Tile classes: pack the items onto the resident workgroups, longest first,
+  // each to the workgroup with the least work so far.  Items are then stored
+  // grouped by workgroup; wg_indptr delimits each workgroup's list.
+  std::vector<std::vector<int32_t>> wg_indptr(KC_COUNT);
+  for (int k : {(int)KC_PREFILL, (int)KC_MLA}) {
+    const int64_t m = (int64_t)cost[k].size();
+    if (m == 0) continue;
+    const int64_t slots = std::min<int64_t>(m, wgs_per_cu(k) * cus);
+    std::vector<int64_t> load(slots, 0);
+    std::vector<std::vector<int64_t>> lists(slots);
+    // costs are already sorted in decreasing order
+    std::vector<std::pair<int64_t, int64_t>> heap;  // (load, slot), min-heap
+    heap.reserve(slots);
+    for (int64_t b = 0; b < slots; ++b) heap.push_back({0, b});
+    auto greater = [](const std::pair<int64_t, int64_t>& a, const std::pair<int64_t, int64_t>& b) {
+      return a > b;
+    };
+    std::make_heap(heap.begin(), heap.end(), greater);
+    std::vector<int64_t> sorted_cost(cost[k].begin(), cost[k].end());
+    std::sort(sorted_cost.begin(), sorted_cost.end(), std::greater<int64_t>());
+    for (int64_t j = 0; j < m; ++j) {
+      std::pop_heap(heap.begin(), heap.end(), greater);
+      auto& top = heap.back();
+      lists[top.second].push_back(j);
+      top.first += sorted_cost[j];
+      std::push_heap(heap.begin(), heap.end(), greater);
+    }
+    std::vector<int32_t> grouped;
+    grouped.reserve(items[k].size());
+    wg_indptr[k].push_back(0);
+    for (int64_t b = 0; b < slots; ++b) {
+      for (int64_t j : lists[b])
+        grouped.insert(grouped.end(), items[k].begin() + j * IT_WORDS,
+                       items[k].begin() + (j + 1) * IT_WORDS);
+      wg_indptr[k].push_back((int32_t)(grouped.size() / IT_WORDS));
+    }
+    items[k].swap(grouped);
   }
 
   // ---- append map and merge rows --------------------------------------------------
@@ -308,6 +371,8 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
   for (int k = 0; k < KC_COUNT; ++k) {
     plan->off_items[k] = push(items[k].data(), (int64_t)items[k].size());
     plan->n_items[k] = (int32_t)(items[k].size() / IT_WORDS);
+    plan->off_wg[k] = push(wg_indptr[k].data(), (int64_t)wg_indptr[k].size());
+    plan->n_wgs[k] = wg_indptr[k].empty() ? plan->n_items[k] : (int32_t)wg_indptr[k].size() - 1;
   }
   plan->off_merge = push(merge_rows.data(), (int64_t)merge_rows.size());
   plan->n_merge_rows = (int32_t)merge_rows.size();

@@ -19,6 +19,8 @@ struct rpa_plan {
   int64_t off_split = 0, off_append = 0, off_merge = 0;
   int64_t off_items[rpa::KC_COUNT] = {0, 0, 0, 0};
   int32_t n_items[rpa::KC_COUNT] = {0, 0, 0, 0};
+  int64_t off_wg[rpa::KC_COUNT] = {0, 0, 0, 0};   // wg_indptr tables (tile classes)
+  int32_t n_wgs[rpa::KC_COUNT] = {0, 0, 0, 0};
   int32_t n_merge_rows = 0;
   int64_t partial_rows = 0;
 

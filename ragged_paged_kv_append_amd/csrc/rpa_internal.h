@@ -34,9 +34,11 @@ enum SplitField : int32_t { SP_COUNT = 0, SP_CHUNK, SP_BASE, SP_WORDS };
 
 constexpr int GEN_ROWS = 4;        // rows per generic item (one wave each)
 constexpr int DEC_MAX_ROWS = 16;   // rows per decode item (one MFMA column block)
-constexpr int PRE_ROWS = 128;      // rows per prefill item
+constexpr int PRE_ROWS = 256;      // rows per prefill item
 constexpr int MLA_ROWS = 64;       // rows per latent-attention item
 constexpr int KEY_ALIGN = 64;      // split pieces start at multiples of this
+constexpr int PRE_WGS_PER_CU = 1;  // prefill workgroups resident per compute unit
+constexpr int MLA_WGS_PER_CU = 2;  // latent-attention workgroups resident per compute unit
 
 // Device view of an uploaded plan, passed to kernels by value.
 struct DevPlan {
@@ -47,10 +49,14 @@ struct DevPlan {
   const int32_t* split;         // [B][SP_WORDS]
   const int32_t* append;        // [total_q][2]: page id, slot
   const int32_t* items[KC_COUNT];
+  // Tile classes (prefill, latent): workgroup b runs items
+  // wg_indptr[b] .. wg_indptr[b + 1] - 1 of its class, in that order.
+  const int32_t* wg_indptr[KC_COUNT];
   const int32_t* merge_rows;    // tokens whose request has S_r > 1
   float* part_o;                // [partial rows][num_qo_heads][head_dim_v]
   float* part_lse;              // [partial rows][num_qo_heads]
   int32_t n_items[KC_COUNT];
+  int32_t n_wgs[KC_COUNT];      // workgroups of each class's launch
   int32_t n_merge_rows;
   int32_t batch_size;
   int32_t total_q;

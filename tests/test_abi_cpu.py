@@ -163,6 +163,51 @@ def test_planner_splits_long_requests(L):
         assert np.all(np.diff(ck) <= 0)
 
 
+@pytest.mark.parametrize("case", ["one_shot_8192", "mixed_7b", "mla_absorbed", "chunk_15"])
+def test_planner_packs_tile_items_onto_workgroups(L, case):
+    """Tile-class items are grouped per workgroup (wg_indptr); the grouping is a
+    longest-first packing, so no workgroup carries more than the average load
+    plus one item."""
+    if case == "one_shot_8192":
+        meta = workloads.make_meta([8192], [8192], 16, 3)
+        cfg = rpa.make_config(8, 1, 128, 128, 16, "bf16")
+        k, table = 2, "wg_prefill"
+    elif case == "chunk_15":
+        meta = workloads.make_meta([512], [8192], 16, 3)
+        cfg = rpa.make_config(8, 1, 128, 128, 16, "bf16")
+        k, table = 2, "wg_prefill"
+    else:
+        spec = workloads.SPECS[case]
+        qo, kv = workloads.lengths(case)
+        meta = workloads.make_meta(qo, kv, spec.page_size, spec.seed)
+        cfg = rpa.make_config(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim_qk,
+                              spec.head_dim_v, spec.page_size, spec.dtype, spec.causal,
+                              spec.sm_scale)
+        k, table = (3, "wg_mla") if case == "mla_absorbed" else (2, "wg_prefill")
+    for cus in (0, 7, 100000):
+        plan = plan_for(meta, cfg, cus)
+        items = rpa.rpa_plan_debug_dump(plan, "items").reshape(-1, 8)
+        items = items[items[:, 7] == k]
+        wg = rpa.rpa_plan_debug_dump(plan, table)
+        assert wg[0] == 0 and wg[-1] == len(items) and np.all(np.diff(wg) >= 1)
+        per_cu = {2: 1, 3: 2}[k]  # resident workgroups per compute unit of each class
+        slots = per_cu * (cus if cus > 0 else 256)
+        assert len(wg) - 1 == min(slots, len(items))
+        G = cfg.num_qo_heads // cfg.num_kv_heads
+        cached = {r: int(meta.kv_len[r]) - int(meta.qo_indptr[r + 1] - meta.qo_indptr[r])
+                  for r in range(meta.batch_size)}
+        cost = []
+        for r_, g, row0, row1, k0, k1, s, kc in items.tolist():
+            last = cached[r_] + (row1 - 1) // G if cfg.causal else int(meta.kv_len[r_]) - 1
+            cost.append((min(k1, last + 1) - k0) * (-(-(row1 - row0) // 32) * 32))
+        cost = np.array(cost)
+        loads = np.array([cost[wg[b]:wg[b + 1]].sum() for b in range(len(wg) - 1)])
+        assert loads.max() <= cost.sum() / len(loads) + cost.max()
+        # every list runs its items longest first
+        for b in range(len(wg) - 1):
+            assert np.all(np.diff(cost[wg[b]:wg[b + 1]]) <= 0)
+
+
 def test_planner_empty_batch_and_empty_requests(L):
     cfg = rpa.make_config(4, 2, 64, 64, 16, "f32")
     plan = rpa.rpa_plan_create(cfg, [0], [], [0], [], 0)
