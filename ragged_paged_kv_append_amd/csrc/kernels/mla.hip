@@ -8,17 +8,26 @@
 // speculation"), each latent row is used by 256 query rows: the work is bound
 // by the matrix cores, not by HBM.
 //
-// One workgroup (four wavefronts) takes 64 query rows (row = token * G +
-// head) and a key range.  Keys stream in tiles of 32 latent rows (36 KiB)
-// through LDS, read once from HBM and used for both products:
-//   S phase: wavefront w computes S^T for rows 16 w .. 16 w + 15 over the
-//     tile (mfma 16x16x32 bf16, 18 steps over the 576 dims, Q of its rows
-//     resident in registers), runs the online softmax for those rows and
-//     writes P (bf16) and the rescale factors to LDS;
-//   PV phase: wavefront w owns value dims 128 w .. 128 w + 127 of all 64 rows
-//     and accumulates O^T[d][row] += V^T[d][key] P^T[key][row] (mfma
-//     32x32x16 bf16), V^T read from the same latent tile with the transposing
-//     LDS read.
+// One workgroup of eight wavefronts (two per SIMD) takes a work item of up
+// to 128 query rows (row = token * G + head) and a key range; the planner
+// packs the items onto one resident workgroup per compute unit, longest
+// first.  Keys stream
+// in tiles of 32 latent rows (36 KiB) through a three-slot LDS ring fed by the
+// gfx950 global-to-LDS DMA (the next tile lands while the current one is
+// computed), each tile read from HBM once per item and used for both
+// products.  In a latent row, 16-byte chunk c sits at position
+// c ^ (row % 8), which keeps both LDS read patterns below conflict free.
+//
+// Per tile j, between two barriers:
+//   S phase: wave w computes S^T for rows 16 w .. 16 w + 15 over the tile
+//     (mfma 16x16x32 bf16, 18 steps over the 576 dims, Q of its rows resident
+//     in registers), runs the online softmax for those rows and writes P (bf16)
+//     and the per-row rescale factors into a double-buffered LDS area;
+//   PV phase: wave w owns value dims 64 w .. 64 w + 63 of all 128 rows and
+//     accumulates O^T[d][row] += V^T[d][key] P^T[key][row] (mfma 32x32x16
+//     bf16), V^T read from the latent tile with the transposing LDS read.
+// The PV phase of tile j and the S phase of tile j + 1 run back to back in one
+// inter-barrier step, so a barrier per tile suffices.
 
 #include "common.h"
 #include "../launch.h"
@@ -29,225 +38,376 @@ namespace {
 
 constexpr int kDQK = 576;
 constexpr int kDV = 512;
-constexpr int kRows = 64;    // query rows per workgroup
-constexpr int kKT = 32;      // keys per tile
-constexpr int kKRow = 584;   // latent tile row stride in LDS (elements)
-constexpr int kPRow = 36;    // P tile row stride in LDS (elements), [row][key]
-constexpr int kChunks = kDQK / 8;  // 16-byte chunks per latent row
+constexpr int kRows = 128;       // query rows per item
+constexpr int kWaves = 8;
+constexpr int kKT = 32;          // keys per tile
+constexpr int kRowBytes = kDQK * 2;            // 1152
+constexpr int kChunks = kDQK / 8;              // 72 chunks of 16 bytes per latent row
+constexpr int kTileBytes = kKT * kRowBytes;    // 36864
+constexpr int kSlots = 3;
+constexpr int kDmaInst = kTileBytes / 1024;    // 36 DMA instructions of 1 KiB per tile
+constexpr int kPRow = 36;                      // P row stride in LDS (bf16): 72 bytes
+constexpr int kPBytes = kRows * kPRow * 2;     // 9216
 constexpr float kMinusBig = -1.0e30f;
+constexpr float kRescaleSlack = 8.f;           // log2 units
+
+typedef __attribute__((address_space(3))) const bf16_t* lds_cptr_t;
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Blocking scalar load of one page id; the address is wave-uniform.
+__device__ __forceinline__ int32_t load_scalar(const int32_t* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int32_t* sp = reinterpret_cast<const int32_t*>(lo | (hi << 32));
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sp) : "memory");
+  return v;
+}
+
+// One global-to-LDS DMA instruction (gfx950 global_load_lds_dwordx4): every
+// lane copies 16 bytes from `src` to LDS byte address lds + 16 * lane.  It is
+// issued from inline assembly so that the compiler does not track it: left to
+// itself the compiler makes every later LDS read wait for all DMA in flight,
+// while the kernel waits for exactly the tile it needs (explicit vmcnt counts,
+// which operations the compiler adds can only make stricter).  M0, which
+// carries the LDS address, is saved and restored around the instruction.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// Two transposing reads (low and high key halves, + 8 rows) at one address,
+// with their own LDS wait (see the decode kernel: the compiler would
+// otherwise drain the DMA stream before them).
+__device__ __forceinline__ void read_vt2(uint32_t a, s16x4_t& lo, s16x4_t& hi) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo), "=&v"(hi)
+      : "v"(a), "n"(8 * kRowBytes)
+      : "memory");
+}
+
+// The lane index as a value the compiler cannot see through: addresses
+// derived from it are recomputed where they are used instead of being hoisted
+// out of the tile loop (registers are fully used by Q and the O accumulators,
+// and hoisted values would be spilled to scratch, whose reloads would also
+// wait for the DMA stream).
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void mla_kernel(DevPlan p, const bf16_t* __restrict__ q,
-                                                  const bf16_t* __restrict__ kvc, Strides ks,
-                                                  bf16_t* __restrict__ o,
-                                                  float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) bf16_t klds[kKT * kKRow];
-  __shared__ __attribute__((aligned(16))) bf16_t plds[kRows * kPRow];
-  __shared__ float alds[kRows];
-  __shared__ float mlds[kRows];
-  __shared__ float llds[kRows];
+__global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __restrict__ q,
+                                                     const bf16_t* __restrict__ kvc, Strides ks,
+                                                     bf16_t* __restrict__ o,
+                                                     float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots][kTileBytes];
+  __shared__ __attribute__((aligned(16))) bf16_t plds[2][kRows * kPRow];
+  __shared__ float alds[2][kRows];   // per-row rescale factor of the tile's P
+  __shared__ float mlds[kRows];      // final row max (log2 units)
+  __shared__ float llds[kRows];      // final row sum
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)ring;
 
-  const int32_t* it = p.items[KC_MLA] + (int64_t)blockIdx.x * IT_WORDS;
-  const int32_t r = it[IT_REQ], g = it[IT_KVHEAD], row0 = it[IT_ROW0], row1 = it[IT_ROW1];
-  const int32_t k0 = it[IT_K0], k1 = it[IT_K1], s = it[IT_SPLIT];
-  const int32_t G = p.group;
-  const int32_t q0 = p.qo_indptr[r];
-  const int32_t n = p.qo_indptr[r + 1] - q0;
-  const int32_t L = p.kv_len[r];
-  const int32_t cached = L - n;
-  auto key_end = [&](int32_t row) {
-    return min(k1, (p.causal ? cached + row / G : L - 1) + 1);
-  };
-  const int32_t kend = key_end(row1 - 1);
-
-  // ---- S-phase role: rows 16 wave + (lane % 16) -------------------------------------
+  // ---- S-phase role: rows 16 wave + scol ------------------------------------------
   const int scol = lane & 15, sgrp = lane >> 4;
-  const int32_t srow = row0 + 16 * wave + scol;
-  const bool srow_ok = srow < row1;
-  const int32_t st = srow_ok ? srow / G : 0;
-  const int32_t sh = g * G + (srow_ok ? srow % G : 0);
-  const int32_t kend_row = srow_ok ? key_end(srow) : k0;
-  u32x4_t qf[kDQK / 32];  // qf[j] = Q[srow][32 j + 8 sgrp .. + 8)
-  {
-    const bf16_t* qrow = q + ((int64_t)(q0 + st) * p.num_qo_heads + sh) * kDQK + 8 * sgrp;
+  // K operand of step j (dims 32 j .. 32 j + 31) for key row scol of a
+  // 16-key block: chunk 4 j + sgrp, at position (4 j + sgrp) ^ (scol % 8).
+  // With j = 2 m + jj that is 8 m + ((4 jj + sgrp) ^ (scol % 8)).
+  uint32_t k_rd[2];
 #pragma unroll
-    for (int j = 0; j < kDQK / 32; ++j)
-      qf[j] = srow_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-  const float sc = p.sm_scale * kLog2e;
-  float m = kMinusBig, lsum = 0.f;
-
-  // ---- PV-phase role: value dims 128 wave .. + 127, all rows -------------------------
+  for (int jj = 0; jj < 2; ++jj)
+    k_rd[jj] = scol * kRowBytes + 16 * ((4 * jj + sgrp) ^ (scol & 7));
+  // ---- PV-phase role: value dims 64 wave .. + 63, all rows ------------------------
   const int pcol = lane & 31, phalf = lane >> 5;
-  f32x16_t oacc[4][2];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[nb][rb][i] = 0.f;
-  const int tr_row = 4 * phalf + ((lane & 15) >> 2);
-  const int tr_col = 128 * wave + 16 * (pcol >> 4) + 4 * (lane & 3);
+  const int tr_row = 4 * phalf + ((lane & 15) >> 2);  // (+ 8 for the high half)
+  // Element column of block nb: 64 wave + 32 nb + 16 (pcol / 16) + 4 (lane % 4);
+  // its chunk is 8 wave + 4 nb + tr_c.
+  const int tr_c = 2 * (pcol >> 4) + ((lane & 3) >> 1);
+  // ---- DMA role: instructions wave, wave + 8, ... of the tile's 36 -----------------
+  // Instruction d moves chunks 64 d .. 64 d + 63 of the tile (72 chunks per
+  // key row); lane L carries chunk 64 d + L into its LDS position, fetching
+  // the global chunk (position) ^ (row % 8).
+  const int n_dma = (kDmaInst - wave + kWaves - 1) / kWaves;  // 5 or 4
 
-  const int32_t* pages = p.page_indices + p.page_indptr[r];
-  const int32_t ntiles = (kend - k0 + kKT - 1) / kKT;
-  for (int32_t tile = 0; tile < ntiles; ++tile) {
-    const int32_t kb = k0 + tile * kKT;
-    __syncthreads();  // previous tile and P fully consumed
-    // Latent tile: 32 rows x 72 chunks of 16 bytes; keys past k1 become zeros.
-#pragma unroll
-    for (int j = 0; j < (kKT * kChunks) / 256; ++j) {
-      const int c = tid + 256 * j;
-      const int key = c / kChunks, ch = c - key * kChunks;
-      const int32_t kk = kb + key;
-      const bool ok = kk < k1;
-      const int32_t kkc = ok ? kk : k1 - 1;
-      const int64_t page = pages[kkc >> p.page_shift];
-      const int64_t slot = kkc & (p.page_size - 1);
-      u32x4_t v = *reinterpret_cast<const u32x4_t*>(kvc + page * ks.page + (int64_t)g * ks.head +
-                                                    slot * ks.token + 8 * ch);
-      if (!ok) v = u32x4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t*>(&klds[key * kKRow + 8 * ch]) = v;
-    }
-    __syncthreads();
+  const int32_t wb0 = p.wg_indptr[KC_MLA][blockIdx.x];
+  const int32_t wb1 = p.wg_indptr[KC_MLA][blockIdx.x + 1];
+  for (int32_t idx = wb0; idx < wb1; ++idx) {
+    const int32_t* it = p.items[KC_MLA] + (int64_t)idx * IT_WORDS;
+    const int32_t r = it[IT_REQ], g = it[IT_KVHEAD], row0 = it[IT_ROW0], row1 = it[IT_ROW1];
+    const int32_t k0 = it[IT_K0], k1 = it[IT_K1], s = it[IT_SPLIT];
+    const int32_t G = p.group;
+    const int32_t q0 = p.qo_indptr[r];
+    const int32_t n = p.qo_indptr[r + 1] - q0;
+    const int32_t L = p.kv_len[r];
+    const int32_t cached = L - n;
+    auto key_end = [&](int32_t row) __attribute__((always_inline)) {
+      return min(k1, (p.causal ? cached + row / G : L - 1) + 1);
+    };
+    const int32_t kend = key_end(row1 - 1);
+    const int32_t ntiles = (kend - k0 + kKT - 1) / kKT;
 
-    // S phase.  sacc[b][i] = S^T[key 16 b + 4 sgrp + i][row scol].
-    f32x4_t sacc[2];
+    const int32_t* pages = p.page_indices + p.page_indptr[r];
+    const char* kvb = reinterpret_cast<const char*>(kvc + (int64_t)g * ks.head);
+    // DMA of the tile at key kb into ring slot `slot`.  Keys past k1 are
+    // fetched from the item's last key (finite values; they are masked).  A
+    // tile spans at most two pages (page size >= 16, tiles 32-aligned).
+    auto issue = [&](int32_t kb, int slot) __attribute__((always_inline)) {
+      const int32_t klast = k1 - 1;
+      const int32_t pa = load_scalar(pages + (min(kb, klast) >> p.page_shift));
+      const int32_t pb = load_scalar(pages + (min(kb + 16, klast) >> p.page_shift));
+      const int32_t page_a = min(kb, klast) >> p.page_shift;
+      const int ln = opaque_lane(lane);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      sacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const bf16_t* krow = &klds[(16 * b + scol) * kKRow + 8 * sgrp];
-#pragma unroll
-      for (int j = 0; j < kDQK / 32; ++j) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + 32 * j);
-        sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qf[j]), sacc[b],
-                                                          0, 0, 0);
-      }
-    }
-    float mx = kMinusBig;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t key = kb + 16 * b + 4 * sgrp + i;
-        const float v = key < kend_row ? sacc[b][i] * sc : kMinusBig;
-        sacc[b][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float e[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e[i] = sacc[b][i] > 0.5f * kMinusBig ? __builtin_amdgcn_exp2f(sacc[b][i] - m_new) : 0.f;
-        psum += e[i];
-      }
-      *reinterpret_cast<uint2*>(&plds[(16 * wave + scol) * kPRow + 16 * b + 4 * sgrp]) =
-          make_uint2(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]));
-    }
-    lsum = lsum * alpha + psum;
-    m = m_new;
-    if (sgrp == 0) alds[16 * wave + scol] = alpha;
-    __syncthreads();
-
-    // PV phase.
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float a = alds[32 * rb + pcol];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) oacc[nb][rb] *= a;
-    }
-#pragma unroll
-    for (int kc16 = 0; kc16 < 2; ++kc16) {
-      // P^T operand: row 32 rb + pcol, keys 16 kc16 + 8 (e / 4) + 4 phalf + e % 4.
-      u32x4_t pb[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16_t* prow = &plds[(32 * rb + pcol) * kPRow + 16 * kc16 + 4 * phalf];
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(prow);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(prow + 8);
-        pb[rb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-      }
-      const bf16_t* vsrc = &klds[(16 * kc16 + tr_row) * kKRow + tr_col];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const u32x2_t lo = __builtin_bit_cast(u32x2_t, lds_read_tr16(vsrc + 32 * nb));
-        const u32x2_t hi = __builtin_bit_cast(u32x2_t, lds_read_tr16(vsrc + 8 * kKRow + 32 * nb));
-        const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          oacc[nb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb[rb]),
-                                                                 oacc[nb][rb], 0, 0, 0);
-      }
-    }
-  }
-
-  // Row statistics from the S-phase owners, then every wave stores its dims.
-  float ltot = lsum + __shfl_xor(lsum, 16, 64);
-  ltot += __shfl_xor(ltot, 32, 64);
-  __syncthreads();
-  if (sgrp == 0) {
-    mlds[16 * wave + scol] = m;
-    llds[16 * wave + scol] = ltot;
-  }
-  const int32_t S = p.split[r * SP_WORDS + SP_COUNT];
-  if (sgrp == 0 && srow_ok) {
-    const float lse_nat = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
-    if (S == 1) {
-      if (lse) lse[(int64_t)(q0 + st) * p.num_qo_heads + sh] = lse_nat;
-    } else {
-      const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + st;
-      p.part_lse[prow * p.num_qo_heads + sh] = lse_nat;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int lrow = 32 * rb + pcol;
-    const int32_t row = row0 + lrow;
-    if (row >= row1) continue;
-    const int32_t t = row / G, h = g * G + row % G;
-    const float lt = llds[lrow];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    // Lane holds O^T[d][row] for d = 128 wave + 32 nb + 8 b + 4 phalf + j.
-    if (S == 1) {
-      bf16_t* orow = o + ((int64_t)(q0 + t) * p.num_qo_heads + h) * kDV + 128 * wave + 4 * phalf;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const f32x16_t& a = oacc[nb][rb];
-          *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * b) =
-              make_uint2(pack_bf16x2(a[4 * b] * inv, a[4 * b + 1] * inv),
-                         pack_bf16x2(a[4 * b + 2] * inv, a[4 * b + 3] * inv));
+      for (int x = 0; x < 5; ++x) {
+        if (x < n_dma) {
+          const int c = 64 * (wave + kWaves * x) + ln;
+          const int kr = c / kChunks, cc = c - kr * kChunks;
+          const int32_t key = min(kb + kr, klast);
+          const int64_t page = (key >> p.page_shift) == page_a ? pa : pb;
+          const char* src = kvb + (page * ks.page + (int64_t)(key & (p.page_size - 1)) * ks.token) * 2 +
+                            16 * (cc ^ (kr & 7));
+          dma16(src, __builtin_amdgcn_readfirstlane(ring_lds + slot * kTileBytes +
+                                                    1024 * (wave + kWaves * x)));
         }
-    } else {
-      const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + t;
-      float* orow = p.part_o + (prow * p.num_qo_heads + h) * kDV + 128 * wave + 4 * phalf;
+      }
+    };
+
+    // S-phase rows of this wave.
+    const int32_t srow = row0 + 16 * wave + scol;
+    const bool srow_ok = srow < row1;
+    const int32_t st = srow_ok ? srow / G : 0;
+    const int32_t sh = g * G + (srow_ok ? srow % G : 0);
+    const int32_t kend_row = srow_ok ? key_end(srow) : k0;
+    const bool s_active_wave = row0 + 16 * wave < row1;
+    const int32_t kend_wmin = s_active_wave ? key_end(row0 + 16 * wave) : k0;
+    const int32_t kend_wmax = s_active_wave ? key_end(min(row1, row0 + 16 * wave + 16) - 1) : k0;
+    const float sc = p.sm_scale * kLog2e;
+    float m = kMinusBig, lsum = 0.f;
+
+    f32x16_t oacc[2][4];  // [nb][rb]
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const f32x16_t& a = oacc[nb][rb];
-          *reinterpret_cast<float4*>(orow + 32 * nb + 8 * b) =
-              make_float4(a[4 * b] * inv, a[4 * b + 1] * inv, a[4 * b + 2] * inv,
-                          a[4 * b + 3] * inv);
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[nb][rb][i] = 0.f;
+
+    barrier();  // the previous item's waves are done with the ring and the P area
+    if (ntiles > 0) issue(k0, 0);
+
+    // Q operand: qf[j] = Q[srow][32 j + 8 sgrp .. + 8), loaded while the first
+    // tiles are in flight.
+    u32x4_t qf[kDQK / 32];
+    {
+      const bf16_t* qrow = q + ((int64_t)(q0 + st) * p.num_qo_heads + sh) * kDQK + 8 * sgrp;
+#pragma unroll
+      for (int j = 0; j < kDQK / 32; ++j)
+        qf[j] = srow_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < kDQK / 32; ++j) asm volatile("" ::"v"(qf[j]));
+    }
+
+    // S phase of the tile at key kb in `slot`: P and rescale factors into
+    // P buffer `pbuf`.
+    auto s_phase = [&](int32_t kb, int slot, int pbuf) __attribute__((always_inline)) {
+      const bool active = s_active_wave && kb < kend_wmax;
+      f32x4_t sacc[2];  // sacc[b][i] = S^T[key kb + 16 b + 4 sgrp + i][row scol]
+#pragma unroll
+      for (int b = 0; b < 2; ++b) sacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      float alpha = 1.f;
+      if (active) {
+        const char* kt = reinterpret_cast<const char*>(&ring[slot][0]);
+#pragma unroll
+        for (int j = 0; j < kDQK / 32; ++j) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kt + 16 * b * kRowBytes +
+                                                                k_rd[j & 1] + 128 * (j >> 1));
+            sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qf[j]),
+                                                              sacc[b], 0, 0, 0);
+          }
+          // Keep the compiler from hoisting all 36 K-operand reads: registers
+          // are fully used by Q and the O accumulators.
+          if (j & 1) __builtin_amdgcn_sched_barrier(0);
         }
+        const bool full = kb + kKT <= kend_wmin;
+        float mx = kMinusBig;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = sacc[b][i];
+            if (!full) v = (kb + 16 * b + 4 * sgrp + i < kend_row) ? v : kMinusBig;
+            sacc[b][i] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mt = mx > 0.5f * kMinusBig ? mx * sc : kMinusBig;
+        if (mt > m + kRescaleSlack) {
+          alpha = __builtin_amdgcn_exp2f(m - mt);
+          lsum *= alpha;
+          m = mt;
+        }
+        const float neg_m = -m;
+        float psum = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = sacc[b][i];
+            const float x =
+                v > 0.5f * kMinusBig ? __builtin_amdgcn_exp2f(__builtin_fmaf(v, sc, neg_m)) : 0.f;
+            sacc[b][i] = x;
+            psum += x;
+          }
+        lsum += psum;
+      }
+      // P[row][key 16 b + 4 sgrp + i] and the row's rescale factor.
+      bf16_t* prow = &plds[pbuf][(16 * wave + scol) * kPRow + 4 * sgrp];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        *reinterpret_cast<uint2*>(prow + 16 * b) =
+            make_uint2(pack_bf16x2(sacc[b][0], sacc[b][1]), pack_bf16x2(sacc[b][2], sacc[b][3]));
+      if (sgrp == 0) alds[pbuf][16 * wave + scol] = alpha;
+    };
+
+    // PV phase of the tile in `slot` with P buffer `pbuf`.
+    auto pv_phase = [&](int slot, int pbuf) __attribute__((always_inline)) {
+      const int ln = opaque_lane(lane);
+      const int pcol = ln & 31, phalf = ln >> 5;
+      const int tr_row = 4 * phalf + ((ln & 15) >> 2);
+      const int tr_c = 2 * (pcol >> 4) + ((ln & 3) >> 1);
+      // Rescale the rows whose reference max was raised with this tile.
+      float a[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) a[rb] = alds[pbuf][32 * rb + pcol];
+      if (__ballot(a[0] != 1.f || a[1] != 1.f || a[2] != 1.f || a[3] != 1.f)) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) oacc[nb][rb] *= a[rb];
+      }
+      const uint32_t slot_lds = ring_lds + slot * kTileBytes;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        u32x4_t va[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          s16x4_t lo, hi;
+          const int R = 16 * kc + tr_row;
+          read_vt2(slot_lds + R * kRowBytes + 16 * ((8 * wave + 4 * nb + tr_c) ^ (R & 7)) +
+                       8 * (ln & 1),
+                   lo, hi);
+          const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+          const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+          va[nb] = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+        }
+        // P^T operand of row block rb: row 32 rb + pcol, keys
+        // 16 kc + 8 (e / 4) + 4 phalf + e % 4.
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const bf16_t* prow = &plds[pbuf][(32 * rb + pcol) * kPRow + 16 * kc + 4 * phalf];
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(prow);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(prow + 8);
+          const u32x4_t pbv = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            oacc[nb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[nb]),
+                                                                   as_bf16x8(pbv), oacc[nb][rb],
+                                                                   0, 0, 0);
+        }
+      }
+    };
+
+    // Step j: [wait for tile j] barrier [DMA of tile j + 1] [PV of tile j - 1]
+    // [S of tile j].  The barrier publishes tile j and P of tile j - 1, and
+    // frees the ring slot and P buffer of tile j - 2; during step j the ring
+    // holds tiles j - 1 (its V, for PV), j (its K, for S) and j + 1 (landing).
+    for (int32_t tile = 0, slot = 0; tile <= ntiles; ++tile, slot = (slot == kSlots - 1) ? 0 : slot + 1) {
+      if (tile < ntiles) wait_vmem<0>();  // this wave's part of tile j has landed
+      barrier();
+      if (tile + 1 < ntiles) issue(k0 + (tile + 1) * kKT, slot == kSlots - 1 ? 0 : slot + 1);
+      if (tile > 0) pv_phase(slot == 0 ? kSlots - 1 : slot - 1, (tile - 1) & 1);
+      if (tile < ntiles) s_phase(k0 + tile * kKT, slot, tile & 1);
+    }
+
+    // Row statistics from the S-phase owners, then every wave stores its dims.
+    float ltot = lsum + __shfl_xor(lsum, 16, 64);
+    ltot += __shfl_xor(ltot, 32, 64);
+    if (sgrp == 0) {
+      mlds[16 * wave + scol] = m;
+      llds[16 * wave + scol] = ltot;
+    }
+    const int32_t S = p.split[r * SP_WORDS + SP_COUNT];
+    if (sgrp == 0 && srow_ok) {
+      const float lse_nat = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
+      if (S == 1) {
+        if (lse) lse[(int64_t)(q0 + st) * p.num_qo_heads + sh] = lse_nat;
+      } else {
+        const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + st;
+        p.part_lse[prow * p.num_qo_heads + sh] = lse_nat;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier();
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int lrow = 32 * rb + pcol;
+      const int32_t row = row0 + lrow;
+      if (row >= row1) continue;
+      const int32_t t = row / G, h = g * G + row % G;
+      const float lt = llds[lrow];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      // Lane holds O^T[d][row] for d = 64 wave + 32 nb + 8 b + 4 phalf + j.
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const f32x16_t& acc = oacc[nb][rb];
+        if (S == 1) {
+          bf16_t* orow = o + ((int64_t)(q0 + t) * p.num_qo_heads + h) * kDV + 64 * wave + 32 * nb +
+                         4 * phalf;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            *reinterpret_cast<uint2*>(orow + 8 * b) =
+                make_uint2(pack_bf16x2(acc[4 * b] * inv, acc[4 * b + 1] * inv),
+                           pack_bf16x2(acc[4 * b + 2] * inv, acc[4 * b + 3] * inv));
+        } else {
+          const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + t;
+          float* orow = p.part_o + (prow * p.num_qo_heads + h) * kDV + 64 * wave + 32 * nb + 4 * phalf;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            *reinterpret_cast<float4*>(orow + 8 * b) =
+                make_float4(acc[4 * b] * inv, acc[4 * b + 1] * inv, acc[4 * b + 2] * inv,
+                            acc[4 * b + 3] * inv);
+        }
+      }
     }
   }
 }
 
 hipError_t launch_mla(const DevPlan& p, const void* q, const void* kv_cache, Strides ks, void* o,
                       float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_kernel, dim3(p.n_items[KC_MLA]), dim3(256), 0, stream, p,
+  hipLaunchKernelGGL(mla_kernel, dim3(p.n_wgs[KC_MLA]), dim3(64 * kWaves), 0, stream, p,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(kv_cache), ks,
                      static_cast<bf16_t*>(o), lse);
   return hipGetLastError();

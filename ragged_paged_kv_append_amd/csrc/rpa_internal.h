@@ -35,10 +35,10 @@ enum SplitField : int32_t { SP_COUNT = 0, SP_CHUNK, SP_BASE, SP_WORDS };
 constexpr int GEN_ROWS = 4;        // rows per generic item (one wave each)
 constexpr int DEC_MAX_ROWS = 16;   // rows per decode item (one MFMA column block)
 constexpr int PRE_ROWS = 256;      // rows per prefill item
-constexpr int MLA_ROWS = 64;       // rows per latent-attention item
+constexpr int MLA_ROWS = 128;      // rows per latent-attention item
 constexpr int KEY_ALIGN = 64;      // split pieces start at multiples of this
 constexpr int PRE_WGS_PER_CU = 1;  // prefill workgroups resident per compute unit
-constexpr int MLA_WGS_PER_CU = 2;  // latent-attention workgroups resident per compute unit
+constexpr int MLA_WGS_PER_CU = 1;  // latent-attention workgroups resident per compute unit
 
 // Device view of an uploaded plan, passed to kernels by value.
 struct DevPlan {

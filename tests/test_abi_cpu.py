@@ -190,7 +190,7 @@ def test_planner_packs_tile_items_onto_workgroups(L, case):
         items = items[items[:, 7] == k]
         wg = rpa.rpa_plan_debug_dump(plan, table)
         assert wg[0] == 0 and wg[-1] == len(items) and np.all(np.diff(wg) >= 1)
-        per_cu = {2: 1, 3: 2}[k]  # resident workgroups per compute unit of each class
+        per_cu = {2: 1, 3: 1}[k]  # resident workgroups per compute unit of each class
         slots = per_cu * (cus if cus > 0 else 256)
         assert len(wg) - 1 == min(slots, len(items))
         G = cfg.num_qo_heads // cfg.num_kv_heads
