@@ -13,21 +13,20 @@
 // packs the items onto one resident workgroup per compute unit, longest
 // first.  Keys stream
 // in tiles of 32 latent rows (36 KiB) through a three-slot LDS ring fed by the
-// gfx950 global-to-LDS DMA (the next tile lands while the current one is
+// gfx950 global-to-LDS DMA (the next two tiles land while the current one is
 // computed), each tile read from HBM once per item and used for both
 // products.  In a latent row, 16-byte chunk c sits at position
 // c ^ (row % 8), which keeps both LDS read patterns below conflict free.
 //
-// Per tile j, between two barriers:
+// Per tile j:
 //   S phase: wave w computes S^T for rows 16 w .. 16 w + 15 over the tile
 //     (mfma 16x16x32 bf16, 18 steps over the 576 dims, Q of its rows resident
 //     in registers), runs the online softmax for those rows and writes P (bf16)
-//     and the per-row rescale factors into a double-buffered LDS area;
+//     and the per-row rescale factors into LDS;
 //   PV phase: wave w owns value dims 64 w .. 64 w + 63 of all 128 rows and
 //     accumulates O^T[d][row] += V^T[d][key] P^T[key][row] (mfma 32x32x16
 //     bf16), V^T read from the latent tile with the transposing LDS read.
-// The PV phase of tile j and the S phase of tile j + 1 run back to back in one
-// inter-barrier step, so a barrier per tile suffices.
+// A barrier separates the phases, and one more starts each tile.
 
 #include "common.h"
 #include "../launch.h"
@@ -120,8 +119,8 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
                                                      bf16_t* __restrict__ o,
                                                      float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots][kTileBytes];
-  __shared__ __attribute__((aligned(16))) bf16_t plds[2][kRows * kPRow];
-  __shared__ float alds[2][kRows];   // per-row rescale factor of the tile's P
+  __shared__ __attribute__((aligned(16))) bf16_t plds[1][kRows * kPRow];
+  __shared__ float alds[1][kRows];   // per-row rescale factor of the tile's P
   __shared__ float mlds[kRows];      // final row max (log2 units)
   __shared__ float llds[kRows];      // final row sum
   const int tid = threadIdx.x;
@@ -214,6 +213,7 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
 
     barrier();  // the previous item's waves are done with the ring and the P area
     if (ntiles > 0) issue(k0, 0);
+    if (ntiles > 1) issue(k0 + kKT, 1);
 
     // Q operand: qf[j] = Q[srow][32 j + 8 sgrp .. + 8), loaded while the first
     // tiles are in flight.
@@ -340,16 +340,22 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
       }
     };
 
-    // Step j: [wait for tile j] barrier [DMA of tile j + 1] [PV of tile j - 1]
-    // [S of tile j].  The barrier publishes tile j and P of tile j - 1, and
-    // frees the ring slot and P buffer of tile j - 2; during step j the ring
-    // holds tiles j - 1 (its V, for PV), j (its K, for S) and j + 1 (landing).
-    for (int32_t tile = 0, slot = 0; tile <= ntiles; ++tile, slot = (slot == kSlots - 1) ? 0 : slot + 1) {
-      if (tile < ntiles) wait_vmem<0>();  // this wave's part of tile j has landed
+    // Step j: [wait for tile j] barrier [DMA of tile j + 2] [S of tile j]
+    // barrier [PV of tile j].  The first barrier publishes tile j and frees
+    // the ring slot of tile j - 1 and the P area; the second publishes P.
+    // Two tiles (72 KiB) are in flight while one is computed.
+    for (int32_t tile = 0, slot = 0; tile < ntiles; ++tile, slot = (slot == kSlots - 1) ? 0 : slot + 1) {
+      if (tile + 1 < ntiles) {
+        if (n_dma == 5) wait_vmem<5>(); else wait_vmem<4>();  // tile j + 1 may be in flight
+      } else {
+        wait_vmem<0>();
+      }
       barrier();
-      if (tile + 1 < ntiles) issue(k0 + (tile + 1) * kKT, slot == kSlots - 1 ? 0 : slot + 1);
-      if (tile > 0) pv_phase(slot == 0 ? kSlots - 1 : slot - 1, (tile - 1) & 1);
-      if (tile < ntiles) s_phase(k0 + tile * kKT, slot, tile & 1);
+      if (tile + 2 < ntiles) issue(k0 + (tile + 2) * kKT, slot == 0 ? kSlots - 1 : slot - 1);
+      s_phase(k0 + tile * kKT, slot, 0);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's P is in LDS
+      barrier();
+      pv_phase(slot, 0);
     }
 
     // Row statistics from the S-phase owners, then every wave stores its dims.
