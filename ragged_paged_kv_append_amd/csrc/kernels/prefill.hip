@@ -12,24 +12,30 @@
 // Each wavefront owns 32 rows.  The planner packs the items onto one resident
 // workgroup per compute unit, longest first; a workgroup runs its list.
 //
-// K/V tiles of 64 keys (16 KiB each) move from HBM/L2 into a three-slot LDS
-// ring with the gfx950 global-to-LDS DMA; tiles j + 1 and j + 2 are in flight
-// while tile j is computed, and one barrier per tile both publishes the
-// landed tile and frees the slot the next DMA overwrites.  Rows are stored with their 16-byte
-// chunks permuted (K: chunk c of key row k at c ^ (k % 16); V: at
-// c ^ 4 (k % 4)) so both LDS read patterns below are bank-conflict free.
+// K/V tiles of 64 keys (16 KiB each) move from HBM/L2 into a four-slot LDS
+// ring with the gfx950 global-to-LDS DMA, issued four tiles ahead of the step
+// that uses them.  The V tile is transposed once per workgroup into a V^T
+// buffer (rows = head dims, keys in the order the PV product consumes them),
+// so that the per-wave PV operands are plain 16-byte LDS reads: the
+// transposing LDS read is four times slower than a 16-byte read, and each
+// wave would otherwise transpose the whole tile for itself.  K rows keep
+// chunk c at c ^ (k % 16), V rows at c ^ 4 (k % 4), V^T rows at
+// c ^ ((d / 2) % 8): every LDS read pattern below is bank-conflict free.
 //
-//   S^T[key][row] = K[key][:] . Q[row][:]        mfma 32x32x16 bf16, A operand
-//       read from LDS with ds_read_b128, Q resident in registers;
-//   online softmax on S^T (each lane holds 16 keys of one row per 32-key
-//       block), in log2 units with the scale folded into one FMA before the
-//       exp2.  The running max is raised only when a tile's max exceeds it by
-//       more than 8 (a factor of 256), so the O rescale is almost never run;
-//       the result is the same softmax, normalised by the same running sum.
-//       Only tiles that straddle a row's last visible key are masked;
-//   O^T[d][row] += V^T[d][key] . P^T[key][row]   mfma 32x32x16 bf16; the S^T
-//       accumulators are already the P^T operand, and V^T is read from the
-//       row-major V tile with the transposing LDS read.
+// A SIMD overlaps matrix products with vector ALU work only when both come
+// from the same wavefront's instruction stream, so each wavefront runs a
+// two-stage software pipeline.  Step j, after one workgroup barrier:
+//   transpose V of tile j + 1 (one eighth per wavefront);
+//   phase A: S^T_{j+1}[key][row] = K[key][:] . Q[row][:] (mfma 32x32x16
+//       bf16, K from LDS, Q resident in registers), interleaved with the
+//       exponentials of tile j: P_j = exp2(S_j * scale * log2 e - m), packed
+//       to bf16 (the S^T accumulators are already laid out as the P^T
+//       operand) and summed into the row sum;
+//   phase B: O^T[d][row] += V^T[d][key] . P^T_j[key][row] (mfma 32x32x16
+//       bf16), interleaved with the mask and row max of S_{j+1};
+//   the running max is raised only when tile j + 1's max exceeds it by more
+//   than 8 (a factor of 256, log2 units), so the O rescale is almost never
+//   run; only tiles that straddle a row's last visible key are masked.
 
 #include "common.h"
 #include "../launch.h"
@@ -39,37 +45,46 @@ namespace rpa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kKT = 64;                  // keys per tile
-constexpr int kTileElems = kKT * kD;     // 16 KiB of bf16
-constexpr int kTileBytes = kTileElems * 2;
+constexpr int kKT = 64;                     // keys per tile
+constexpr int kTileBytes = kKT * kD * 2;    // 16 KiB
 constexpr int kSlotBytes = 2 * kTileBytes;  // K tile + V tile
-constexpr int kSlots = 3;                   // ring depth
+constexpr int kSlots = 4;                   // ring depth
 constexpr int kWaves = 8;
-constexpr int kDmaRows = kKT / kWaves;      // key rows each wave moves per tile
+constexpr int kDmaRows = kKT / kWaves;      // key rows each wave moves per tile (8)
+constexpr int kDmaInst = 2 * kDmaRows / 4;  // its DMA instructions per tile, K and V (4)
 constexpr float kMinusBig = -1.0e30f;
-constexpr float kRescaleSlack = 8.f;     // log2 units
-constexpr int kNonTemporal = 2;          // DMA cache policy: streaming
+constexpr float kRescaleSlack = 8.f;        // log2 units
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) const bf16_t* lds_cptr_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
-// Workgroup barrier without the memory fences of __syncthreads: the only
-// cross-wave traffic is the DMA into the ring, whose completion each wave
-// establishes with its own vmcnt wait before the barrier, and LDS reads whose
-// values the wave has already consumed.  The fences would make the compiler
-// drain the DMA stream at every barrier.
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Hides x's value from the optimizer, so that addresses derived from it are
+// formed where they are used instead of being hoisted and kept live.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// 16-byte LDS read at byte address a.
+__device__ __forceinline__ u32x4_t lds_ld16(uint32_t a) {
+  return *reinterpret_cast<const lds_u32x4*>((uintptr_t)a);
+}
+
+// Workgroup barrier.  Cross-wave data are the DMA'd ring tiles (each wave
+// waits for its own part with vmcnt before the barrier) and the V^T writes
+// (covered here by the LDS count); no memory fence, which would make the
+// compiler drain the DMA in flight.
+__device__ __forceinline__ void barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Blocking scalar load of one page id (scalar cache; waits only for LDS and
-// scalar operations, never for the DMA in flight).
+// Blocking scalar load of one page id; the address is wave-uniform.
 __device__ __forceinline__ int32_t load_scalar(const int32_t* ptr) {
-  // The address is wave-uniform; readfirstlane puts it in scalar registers
-  // even where the compiler holds it in vector registers.
   const uint64_t a = reinterpret_cast<uint64_t>(ptr);
   const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
@@ -79,31 +94,48 @@ __device__ __forceinline__ int32_t load_scalar(const int32_t* ptr) {
   return v;
 }
 
-// Position of 16-byte chunk c of row k inside a tile row.
-__device__ __forceinline__ int k_pos(int c, int k) { return c ^ (k & 15); }
-__device__ __forceinline__ int v_pos(int c, int k) { return c ^ (4 * (k & 3)); }
-
-// Four transposing reads of one 16-key V chunk: two 32-dim blocks (base a0
-// and a1: LDS byte addresses of the blocks for chunk 0 of the slot), low and
-// high key halves (+ 8 rows = + 2048 bytes); kOff adds the chunk.  One asm
-// block with its own LDS wait: the compiler cannot tell these reads from the
-// DMA in flight and would otherwise drain it first.
-template <int kOff>
-__device__ __forceinline__ void read_vt4(uint32_t a0, uint32_t a1, s16x4_t (&v)[4]) {
+// One global-to-LDS DMA instruction (gfx950 global_load_lds_dwordx4): every
+// lane copies 16 bytes from `src` to LDS byte address lds + 16 * lane.  It is
+// issued from inline assembly so that the compiler does not track it: left to
+// itself the compiler makes later LDS reads wait for all DMA in flight, while
+// the kernel waits for exactly the tile it needs (explicit vmcnt counts,
+// which operations the compiler adds can only make stricter).  M0, which
+// carries the LDS address, is saved and restored around the instruction.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
-      "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
-      "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
-      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-      : "v"(a0), "v"(a1), "n"(kOff), "n"(kOff + 2048)
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
       : "memory");
 }
 
-template <int kSlot>
-struct SlotTag {
-  static constexpr int value = kSlot;
+// Positions of 16-byte chunk c inside a K row (key k), a V row (key k) and a
+// V^T row (head dim d).
+__device__ __forceinline__ int k_pos(int c, int k) { return c ^ (k & 15); }
+__device__ __forceinline__ int v_pos(int c, int k) { return c ^ (4 * (k & 3)); }
+__device__ __forceinline__ int vt_pos(int c, int d) { return c ^ ((d >> 1) & 7); }
+
+// Max over both halves of the wavefront (lanes l and l ^ 32).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// acc + lo + hi of the two bf16 values packed in w (fp32 accumulate).
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
 };
 
 }  // namespace
@@ -113,43 +145,59 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
                                                       const bf16_t* __restrict__ vc, Strides ks,
                                                       Strides vs, bf16_t* __restrict__ o,
                                                       float* __restrict__ lse) {
-  // ring[slot][0] = K tile, ring[slot][1] = V tile; rows of 128 bf16.
-  __shared__ __attribute__((aligned(1024))) bf16_t ring[kSlots][2][kTileElems];
+  // ring[slot]: K tile, then V tile (rows of 128 bf16).  vt[b]: V^T of a tile,
+  // 128 rows (head dims) of 64 keys; in a row, 16-byte chunk 2 c + hh holds
+  // the keys 16 c + 4 hh + (0..3) and 16 c + 8 + 4 hh + (0..3).
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots][kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vt[2][kTileBytes];
   const int tid = threadIdx.x;
   // The wave index is uniform within a wave; readfirstlane tells the compiler,
   // so everything derived from it stays in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31;   // query row of this lane within the wave (S^T / O^T column)
   const int half = lane >> 5;  // k-slot group of the 32x32x16 operands
+  const uint32_t ring_lds =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)ring;
+  const uint32_t vt_lds =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)vt;
 
   // ---- per-lane constants, shared by every item of this workgroup ----------
-  // LDS byte offsets (from the ring) of this lane's K operand reads: mfma i of
-  // a 32-key block reads chunk 2 i + half of key row col (+ 32 b2).
-  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_cptr_t)ring;
-  uint32_t k_rd[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) k_rd[i] = col * 256 + 16 * k_pos(2 * i + half, col);
-  // Transposing-read source of this lane inside a 16-key V chunk: row
-  // 4 half + (lane % 16) / 4 (+ 8 for the high half), element column
-  // 32 nb + 16 (col / 16) + 4 (lane % 4).
-  const int tr_row = 4 * half + ((lane & 15) >> 2);
-  const int tr_chunk = 2 * (col >> 4) + ((lane & 3) >> 1);
-  uint32_t v_rd[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    v_rd[nb] = kTileBytes + tr_row * 256 + 16 * v_pos(4 * nb + tr_chunk, tr_row) + 8 * (lane & 1);
+  // Buffer bases are multiples of 1024, so the XORs below, which touch bits
+  // 4..7 only, commute with adding them.
+  // K operand of mfma i of a 32-key block: chunk 2 i + half of key row col,
+  // at k_rd ^ 32 i (+ 32 rows = + 8192 bytes for the second block).
+  const uint32_t k_rd = col * 256 + 16 * k_pos(half, col);
+  // V^T operand of 16-key chunk kc16 and 32-dim block nb: chunk 2 kc16 + half
+  // of V^T row 32 nb + col, at vt_rd ^ 32 kc16 (+ 4096 bytes per nb).
+  const uint32_t vt_rd = col * 128 + 16 * vt_pos(half, col);
+  // Transpose role: instruction i = 2 ih + il of wave w handles unit
+  // u = 16 w + 4 i + lane / 16, i.e. keys 4 (u / 8) .. + 3 and head dims
+  // 16 (u % 8) .. + 15.  Lane c + 4 e of a 16-lane group reads key row
+  // 4 (u / 8) + e, dims 16 (u % 8) + 4 c .. + 3; the transposing read hands
+  // lane l of the group V^T[16 (u % 8) + l][4 keys], written as 8 bytes of
+  // V^T row 16 (u % 8) + l.  The source of instruction i is
+  // (tr_src ^ 128 il) + 1024 ih, its destination (tr_dst ^ 16 ih) + 8192 il.
+  uint32_t tr_src, tr_dst;
+  {
+    const int u = 16 * wave + (lane >> 4);
+    const int kq = u >> 3, cb = u & 7;
+    const int l16 = lane & 15, c = l16 & 3, e = l16 >> 2;
+    const int R = 4 * kq + e;                       // key row read by this lane
+    tr_src = kTileBytes + R * 256 + 16 * v_pos(2 * cb + (c >> 1), R) + 8 * (c & 1);
+    const int dd = 16 * cb + l16;                   // V^T row written by this lane
+    const int kc16 = kq >> 2, q4 = kq & 3;          // 16-key chunk and 4-key group in it
+    tr_dst = dd * 128 + 16 * vt_pos(2 * kc16 + (q4 & 1), dd) + 8 * (q4 >> 1);
+  }
   // DMA role: wave w moves key rows 8 w .. 8 w + 7 of every tile (a run of
   // keys inside one page for any page size >= 16); instruction i carries rows
-  // 8 w + 4 i + lane / 16, and lane % 16 is the 16-byte position in the row.
-  // dma_k[i] / dma_v[i]: element offset of that chunk from the row group's
-  // first key (the chunk placed at position lane % 16 is (lane % 16) ^ perm).
-  // (Byte offsets, unsigned, so that each DMA address is a scalar base plus a
-  // 32-bit lane offset.)
+  // 8 w + 4 i + lane / 16 and lane % 16 is the 16-byte position in the row,
+  // which holds chunk (lane % 16) ^ perm.  Byte offsets from the first key of
+  // the wave's rows.
   uint32_t dma_k[2], dma_v[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int rr = 4 * i + (lane >> 4);          // row within the wave's 8-row group
-    const int trow = 8 * (wave & 1) + rr;        // the row's index mod 16
+    const int rr = 4 * i + (lane >> 4);    // row within the wave's 8 rows
+    const int trow = 8 * (wave & 1) + rr;  // the row's index mod 16
     dma_k[i] = 2u * (uint32_t)(rr * ks.token + 8 * k_pos(lane & 15, trow));
     dma_v[i] = 2u * (uint32_t)(rr * vs.token + 8 * v_pos(lane & 15, trow));
   }
@@ -165,7 +213,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     const int32_t n = p.qo_indptr[r + 1] - q0;
     const int32_t L = p.kv_len[r];
     const int32_t cached = L - n;
-    auto key_end = [&](int32_t row) __attribute__((always_inline)) {  // one past the last key row `row` may see in this item
+    auto key_end = [&](int32_t row) __attribute__((always_inline)) {
       return min(k1, (p.causal ? cached + row / G : L - 1) + 1);
     };
 
@@ -178,45 +226,65 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     const int32_t wrow0 = row0 + wave * 32;
     const bool wave_has_rows = wrow0 < row1;
     const int32_t kend_wmin = wave_has_rows ? key_end(wrow0) : k0;
-    const int32_t kend_wmax = wave_has_rows ? key_end(min(row1, wrow0 + 32) - 1) : k0;
+    const int32_t ntiles = (kend - k0 + kKT - 1) / kKT;
 
     u32x4_t qf[8];  // Q operand, loaded once the first tiles are in flight
     const int32_t* pages = p.page_indices + p.page_indptr[r];
-    const int64_t k_head = (int64_t)g * ks.head;
-    const int64_t v_head = (int64_t)g * vs.head;
-    // Starts the DMA of the tile at key kb into ring slot `sl`.  Keys past k1
-    // are fetched from the item's last key (a written slot of the same page),
-    // so masked keys hold finite values.
+    const char* kbase = reinterpret_cast<const char*>(kc + (int64_t)g * ks.head);
+    const char* vbase = reinterpret_cast<const char*>(vc + (int64_t)g * vs.head);
+    // DMA of the tile at key kb into ring slot `slot`.  Keys past k1 are
+    // fetched from the item's last key (a written slot of the same page), so
+    // masked keys hold finite values.
     auto issue = [&](int32_t kb, int slot) __attribute__((always_inline)) {
       const int32_t gkey = min(kb + kDmaRows * wave, k1 - 1);  // first key of this wave's rows
       const int32_t rmax = k1 - 1 - gkey;                      // rows past it that exist
       const int64_t page = load_scalar(pages + (gkey >> p.page_shift));
       const int64_t in_page = gkey & (p.page_size - 1);
-      const bf16_t* kg = kc + page * ks.page + k_head + in_page * ks.token;
-      const bf16_t* vg = vc + page * vs.page + v_head + in_page * vs.token;
-      bf16_t* kl = &ring[slot][0][kDmaRows * wave * kD];
-      bf16_t* vl = &ring[slot][1][kDmaRows * wave * kD];
-      const char* kgb = reinterpret_cast<const char*>(kg);
-      const char* vgb = reinterpret_cast<const char*>(vg);
+      const char* kg = kbase + 2 * (page * ks.page + in_page * ks.token);
+      const char* vg = vbase + 2 * (page * vs.page + in_page * vs.token);
+      const uint32_t kl = __builtin_amdgcn_readfirstlane(ring_lds + slot * kSlotBytes +
+                                                         kDmaRows * wave * 256);
       if (rmax >= kDmaRows - 1) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          __builtin_amdgcn_global_load_lds(kgb + dma_k[i], (lds_void_t*)(kl + 4 * i * kD), 16, 0,
-                                           kNonTemporal);
-          __builtin_amdgcn_global_load_lds(vgb + dma_v[i], (lds_void_t*)(vl + 4 * i * kD), 16, 0,
-                                           kNonTemporal);
+          dma16(kg + dma_k[i], kl + 1024 * i);
+          dma16(vg + dma_v[i], kl + kTileBytes + 1024 * i);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int rr = 4 * i + (lane >> 4);
           const uint32_t back = (uint32_t)(rr - min(rr, rmax));  // rows clamped onto the last key
-          __builtin_amdgcn_global_load_lds(kgb + (dma_k[i] - 2u * back * (uint32_t)ks.token),
-                                           (lds_void_t*)(kl + 4 * i * kD), 16, 0, kNonTemporal);
-          __builtin_amdgcn_global_load_lds(vgb + (dma_v[i] - 2u * back * (uint32_t)vs.token),
-                                           (lds_void_t*)(vl + 4 * i * kD), 16, 0, kNonTemporal);
+          dma16(kg + (dma_k[i] - 2u * back * (uint32_t)ks.token), kl + 1024 * i);
+          dma16(vg + (dma_v[i] - 2u * back * (uint32_t)vs.token), kl + kTileBytes + 1024 * i);
         }
       }
+    };
+
+    // Transpose of the V tile in ring slot `slot` into vt[buf].
+    auto transpose = [&](int slot, int buf) __attribute__((always_inline)) {
+      const uint32_t src = opaque(ring_lds + slot * kSlotBytes + tr_src);
+      const uint32_t dst = opaque(vt_lds + buf * kTileBytes + tr_dst);
+      s16x4_t v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(uintptr_t)((src ^ (128u * (i & 1))) + 1024u * (i >> 1)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
+            (uintptr_t)((dst ^ (16u * (i >> 1))) + 8192u * (i & 1))) = v[i];
+    };
+
+    // Waits until this wave's part of tile `tile` has landed, when tiles up
+    // to `last` have been issued: each wave issues kDmaInst instructions per
+    // tile, in tile order.
+    auto wait_tile = [&](int32_t tile, int32_t last) __attribute__((always_inline)) {
+      const int32_t later = min(last, ntiles - 1) - tile;  // tiles issued after it
+      if (later >= 3) wait_vmem<3 * kDmaInst>();
+      else if (later == 2) wait_vmem<2 * kDmaInst>();
+      else if (later == 1) wait_vmem<kDmaInst>();
+      else wait_vmem<0>();
     };
 
     const float sc = p.sm_scale * kLog2e;
@@ -228,52 +296,20 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[nb][i] = 0.f;
 
-    // S^T of the tile in ring slot `sl` into sacc (two 32-key blocks).
-    f32x16_t sacc[2];
-    auto qk = [&](int slot) __attribute__((always_inline)) {
-      const char* kt = reinterpret_cast<const char*>(&ring[slot][0][0]);
+    // Element i of S^T block b2 of the tile at kb is key
+    // kb + 32 b2 + 8 (i / 4) + 4 half + i % 4 of row `col`.  Keys past the
+    // row's last visible key become kMinusBig.
+    auto mask = [&](f32x16_t (&sx)[2], int32_t kb) __attribute__((always_inline)) {
+      const int32_t lim = kend_row - kb - 4 * half;
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[b2][i] = 0.f;
-      // The two blocks' products alternate, so consecutive MFMAs never wait on
-      // each other, and only two K operands are live at a time.
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(kt + k_rd[i]);
-        const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(kt + k_rd[i] + 8192);
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qf[i]),
-                                                          sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qf[i]),
-                                                          sacc[1], 0, 0, 0);
-      }
+        for (int i = 0; i < 16; ++i)
+          sx[b2][i] = (32 * b2 + 8 * (i >> 2) + (i & 3)) < lim ? sx[b2][i] : kMinusBig;
     };
-
-    // Online softmax of sacc (the tile at key kb), then O^T += V^T P^T with
-    // the V tile of ring slot `sl`.
-    auto softmax_pv = [&](int32_t kb, int slot) __attribute__((always_inline)) {
-      const uint32_t slot_lds = ring_lds + slot * kSlotBytes;
-      // Element i of block b2 is key kb + 32 b2 + 8 (i / 4) + 4 half + i % 4 of row `col`.
-      const bool full = kb + kKT <= kend_wmin;  // every key of the tile visible to every row
-      float mx = kMinusBig;
-      if (full) {
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[b2][i]);
-      } else {
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int32_t key = kb + 32 * b2 + 8 * (i >> 2) + 4 * half + (i & 3);
-            sacc[b2][i] = key < kend_row ? sacc[b2][i] : kMinusBig;
-            mx = fmaxf(mx, sacc[b2][i]);
-          }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Raise the reference max only when the tile's max exceeds it by more
-      // than the slack; rows of the wave that need it are rescaled together.
+    // Raises the reference max for a tile whose row max (both halves
+    // combined) is mx, rescaling O and the row sum.
+    auto raise_max = [&](float mx) __attribute__((always_inline)) {
       const float mt = mx > 0.5f * kMinusBig ? mx * sc : kMinusBig;
       const bool raise = mt > m + kRescaleSlack;
       if (__ballot(raise)) {
@@ -284,82 +320,122 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
         for (int nb = 0; nb < 4; ++nb) oacc[nb] *= alpha;
         m = m_new;
       }
-      const float neg_m = -m;
+    };
+    // K operand i of block b2 of the tile whose K starts at LDS byte kt + k_rd.
+    auto kld = [&](uint32_t kt, int i, int b2) __attribute__((always_inline)) {
+      return lds_ld16((kt ^ (32u * i)) + 8192u * b2);
+    };
+    // P word w of tile sx (packed bf16 pair, the k-slot pair e = w % 4 of
+    // 16-key chunk w / 4), and its contribution to the row sum.
+    auto p_word = [&](const f32x16_t (&sx)[2], int w, float neg_m, float& psum)
+        __attribute__((always_inline)) {
+      const int kc16 = w >> 2, e = w & 3, b2 = kc16 >> 1, hb = kc16 & 1;
+      // key of k-slot (half, e) in a 16-key chunk: 16 kc16 + 8 (e / 4) + 4 half + e % 4
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[b2][8 * hb + 2 * e], sc, neg_m));
+      const float e1 =
+          __builtin_amdgcn_exp2f(__builtin_fmaf(sx[b2][8 * hb + 2 * e + 1], sc, neg_m));
+      const uint32_t wd = pack_bf16x2(e0, e1);
+      psum = sum_bf16x2(wd, psum);
+      return wd;
+    };
+
+    // One pipeline step: tile `tile`'s S^T is in `cur`; with has_next, tile
+    // tile + 1's S^T is produced into `nxt`.
+    auto step = [&](int32_t tile, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], auto has_next)
+        __attribute__((always_inline)) {
+      constexpr bool kNext = decltype(has_next)::value;
+      const int slot = tile & (kSlots - 1);
+      if (kNext) wait_tile(tile + 1, tile + 3);
+      // Publishes tile j + 1 and V^T of tile j; frees ring slot j (its K and
+      // V were consumed in step j - 1) and V^T of tile j - 1.
+      barrier();
+      if (tile + 4 < ntiles) issue(k0 + (tile + 4) * kKT, slot);
+      if (kNext) transpose((slot + 1) & (kSlots - 1), (tile + 1) & 1);
+      if (!wave_has_rows) return;
+
+      // A row with no visible key so far has m = kMinusBig; its masked
+      // entries (kMinusBig) then still map to exp2 = 0.
+      const float neg_m = m > 0.5f * kMinusBig ? -m : 0.f;
       float psum = 0.f;
-      if (full) {
+      u32x4_t pb[4];
+      if constexpr (kNext) {
+        // Phase A: S^T of tile j + 1, with the exponentials of tile j.
+        const uint32_t kt = opaque(ring_lds + ((slot + 1) & (kSlots - 1)) * kSlotBytes + k_rd);
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b2][i], sc, neg_m));
-            sacc[b2][i] = e;
-            psum += e;
+          for (int i = 0; i < 16; ++i) nxt[b2][i] = 0.f;
+        // Each product is issued together with the exponentials of one P
+        // word (the scheduling barriers keep the groups apart), and the K
+        // operands are read one product pair ahead.
+        u32x4_t ka[2][2];
+        ka[0][0] = kld(kt, 0, 0);
+        ka[0][1] = kld(kt, 0, 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i + 1 < 8) {
+            ka[(i + 1) & 1][0] = kld(kt, i + 1, 0);
+            ka[(i + 1) & 1][1] = kld(kt, i + 1, 1);
           }
+          nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i & 1][0]),
+                                                           as_bf16x8(qf[i]), nxt[0], 0, 0, 0);
+          const int w0 = 2 * i, w1 = 2 * i + 1;
+          pb[w0 >> 2][w0 & 3] = p_word(cur, w0, neg_m, psum);
+          __builtin_amdgcn_sched_barrier(0);
+          nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i & 1][1]),
+                                                           as_bf16x8(qf[i]), nxt[1], 0, 0, 0);
+          pb[w1 >> 2][w1 & 3] = p_word(cur, w1, neg_m, psum);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // The P words and the row sum are produced here, not sunk into
+        // phase B next to their uses.
+        asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(psum));
       } else {
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float v = sacc[b2][i];
-            const float e =
-                v > 0.5f * kMinusBig ? __builtin_amdgcn_exp2f(__builtin_fmaf(v, sc, neg_m)) : 0.f;
-            sacc[b2][i] = e;
-            psum += e;
-          }
+        for (int w = 0; w < 16; ++w) pb[w >> 2][w & 3] = p_word(cur, w, neg_m, psum);
       }
       lsum += psum;
 
-      // O^T += V^T P^T over the four 16-key chunks of the tile.
-      auto pv_chunk = [&](auto kct) __attribute__((always_inline)) {
-        constexpr int kc16 = decltype(kct)::value;
-        constexpr int b2 = kc16 >> 1, hb = kc16 & 1;
-        u32x4_t pb;
+      // Phase B: O^T += V^T P^T over the four 16-key chunks of tile j, with
+      // the mask and max of tile j + 1.
+      if constexpr (kNext) {
+        const int32_t kb1 = k0 + (tile + 1) * kKT;
+        if (kb1 + kKT > kend_wmin) mask(nxt, kb1);
+      }
+      const uint32_t vtb = opaque(vt_lds + (tile & 1) * kTileBytes + vt_rd);
+      auto vld = [&](int kc16, int nb) __attribute__((always_inline)) {
+        return lds_ld16((vtb ^ (32u * kc16)) + 4096u * nb);
+      };
+      u32x4_t va[2][4];
+      float mx = kMinusBig;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pb[e] = pack_bf16x2(sacc[b2][8 * hb + 2 * e], sacc[b2][8 * hb + 2 * e + 1]);
-        // key of k-slot (half, e) in this chunk: 16 kc16 + 8 (e / 4) + 4 half + e % 4
+      for (int nb = 0; nb < 4; ++nb) va[0][nb] = vld(0, nb);
 #pragma unroll
-        for (int np = 0; np < 2; ++np) {
-          s16x4_t vr[4];
-          read_vt4<kc16 * 16 * 256>(slot_lds + v_rd[2 * np], slot_lds + v_rd[2 * np + 1], vr);
+      for (int kc16 = 0; kc16 < 4; ++kc16) {
+        if (kc16 + 1 < 4) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int nb = 2 * np + j;
-            const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, vr[2 * j]);
-            const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, vr[2 * j + 1]);
-            const u32x4_t va = {lo2[0], lo2[1], hi2[0], hi2[1]};
-            oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb),
-                                                               oacc[nb], 0, 0, 0);
+          for (int nb = 0; nb < 4; ++nb) va[(kc16 + 1) & 1][nb] = vld(kc16 + 1, nb);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[kc16 & 1][nb]),
+                                                             as_bf16x8(pb[kc16]), oacc[nb], 0, 0, 0);
+          if constexpr (kNext) {
+            // 8 of the 32 entries per chunk, two per product
+            const int b2 = kc16 >> 1, i0 = 8 * (kc16 & 1) + 2 * nb;
+            mx = fmaxf(mx, fmaxf(nxt[b2][i0], nxt[b2][i0 + 1]));
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
-      };
-      pv_chunk(SlotTag<0>{});
-      pv_chunk(SlotTag<1>{});
-      pv_chunk(SlotTag<2>{});
-      pv_chunk(SlotTag<3>{});
-    };
-
-    // One step: wait for the tile (the next tile's DMA may still be in flight:
-    // each wave issues 4 instructions per tile), start the DMA of the tile two
-    // ahead into the slot freed by the previous tile, compute.
-    const int32_t ntiles = (kend - k0 + kKT - 1) / kKT;
-    auto step = [&](int32_t tile, int slot) __attribute__((always_inline)) {
-      const int32_t kb = k0 + tile * kKT;
-      if (tile + 1 < ntiles)
-        wait_vmem<4>();  // this wave's part of the tile has landed
-      else
-        wait_vmem<0>();
-      barrier();  // every part has landed, and every wave is done with tile - 1
-      if (tile + 2 < ntiles) issue(kb + 2 * kKT, slot == 0 ? 2 : slot - 1);
-      if (wave_has_rows && kb < kend_wmax) {
-        qk(slot);
-        softmax_pv(kb, slot);
       }
+      if constexpr (kNext) raise_max(max_halves(mx));
     };
 
-    barrier();  // the previous item's waves are done with the ring
-    if (ntiles > 0) issue(k0, 0);
-    if (ntiles > 1) issue(k0 + kKT, 1);
+    if (idx > wb0) wait_vmem<0>();  // the previous item's output stores
+    barrier();  // the previous item's waves are done with the ring and vt
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j)
+      if (j < ntiles) issue(k0 + j * kKT, j);
 
     // Q operand of the S^T products: qf[i] = Q[row][16 i + 8 half .. + 8),
     // loaded while the first tiles are in flight.
@@ -368,12 +444,51 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         qf[i] = row_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * i) : u32x4_t{0u, 0u, 0u, 0u};
-      // Complete the Q loads here: from now on the DMA owns the counter.
+      // Complete the Q loads here.
       asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
                    "v"(qf[6]), "v"(qf[7]));
     }
-    for (int32_t tile = 0, slot = 0; tile < ntiles; ++tile, slot = (slot == kSlots - 1) ? 0 : slot + 1)
-      step(tile, slot);
+    if (ntiles > 0) {
+      f32x16_t sa[2], sb[2];
+      // Prologue: tile 0 lands; V^T of tile 0, S^T of tile 0 and its max.
+      wait_tile(0, kSlots - 1);
+      barrier();
+      transpose(0, 0);
+      if (wave_has_rows) {
+        const uint32_t kt = opaque(ring_lds + k_rd);
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sa[b2][i] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kld(kt, i, 0)), as_bf16x8(qf[i]),
+                                                          sa[0], 0, 0, 0);
+          sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kld(kt, i, 1)), as_bf16x8(qf[i]),
+                                                          sa[1], 0, 0, 0);
+        }
+        if (k0 + kKT > kend_wmin) mask(sa, k0);
+        float mx = kMinusBig;
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sa[b2][i]);
+        raise_max(max_halves(mx));
+      }
+      // Steps, two per iteration so that the S^T buffers swap roles without
+      // copies.
+      int32_t tile = 0;
+      for (; tile + 2 < ntiles; tile += 2) {
+        step(tile, sa, sb, Flag<true>{});
+        step(tile + 1, sb, sa, Flag<true>{});
+      }
+      if (tile + 1 < ntiles) {
+        step(tile, sa, sb, Flag<true>{});
+        step(tile + 1, sb, sa, Flag<false>{});
+      } else {
+        step(tile, sa, sb, Flag<false>{});
+      }
+    }
 
     // Finish: the row sum is split over the two halves of the wave.
     const float ltot = lsum + __shfl_xor(lsum, 32, 64);
