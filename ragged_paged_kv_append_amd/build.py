@@ -30,6 +30,13 @@ DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
+# Per-file device flags.  The prefill kernel runs with the IEEE mode bit off:
+# its row maxima then need no NaN-quieting operand copies (no NaN reaches them:
+# masked keys carry a large negative finite value and unused key slots are
+# filled from a valid key).
+FILE_FLAGS = {"prefill.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def sources():
     out = []
     for root, _, files in os.walk(CSRC):
@@ -43,7 +50,8 @@ def _compile(src: str) -> tuple[str, str, int, str]:
     rel = os.path.relpath(src, CSRC).replace(os.sep, "_")
     obj = os.path.join(BUILD, rel + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-c", src, "-o", obj]
+        extra = FILE_FLAGS.get(os.path.basename(src), [])
+        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, *extra, "-c", src, "-o", obj]
     else:
         cmd = [HIPCC, *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", src, "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)

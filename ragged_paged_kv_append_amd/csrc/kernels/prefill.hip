@@ -22,20 +22,22 @@
 // chunk c at c ^ (k % 16), V rows at c ^ 4 (k % 4), V^T rows at
 // c ^ ((d / 2) % 8): every LDS read pattern below is bank-conflict free.
 //
-// A SIMD overlaps matrix products with vector ALU work only when both come
-// from the same wavefront's instruction stream, so each wavefront runs a
-// two-stage software pipeline.  Step j, after one workgroup barrier:
-//   transpose V of tile j + 1 (one eighth per wavefront);
-//   phase A: S^T_{j+1}[key][row] = K[key][:] . Q[row][:] (mfma 32x32x16
-//       bf16, K from LDS, Q resident in registers), interleaved with the
-//       exponentials of tile j: P_j = exp2(S_j * scale * log2 e - m), packed
-//       to bf16 (the S^T accumulators are already laid out as the P^T
-//       operand) and summed into the row sum;
-//   phase B: O^T[d][row] += V^T[d][key] . P^T_j[key][row] (mfma 32x32x16
-//       bf16), interleaved with the mask and row max of S_{j+1};
-//   the running max is raised only when tile j + 1's max exceeds it by more
-//   than 8 (a factor of 256, log2 units), so the O rescale is almost never
-//   run; only tiles that straddle a row's last visible key are masked.
+// Per wavefront, tile j goes through a matrix phase and a softmax phase:
+//   M(j): S^T_j[key][row] = K_j[key][:] . Q[row][:] and
+//         O^T[d][row] += V^T_{j-1}[d][key] . P^T_{j-1}[key][row]
+//         (mfma 32x32x16 bf16; K and V^T from LDS, Q resident in registers,
+//         the S^T accumulators laid out as the P^T operand);
+//   V(j): mask (only tiles that straddle a row's last visible key), row max,
+//         P_j = exp2(S_j * scale * log2 e - m) rounded to bf16, row sum of the
+//         rounded P.  The running max is raised only when a tile's max
+//         exceeds it by more than 8 (a factor of 256, log2 units), so the O
+//         rescale is almost never run.
+// The two wavefronts that share a SIMD (w and w + 4) belong to two groups
+// that run these phases half a step apart, one group's M beside the other
+// group's V, with a workgroup barrier between slots; each phase's inputs and
+// outputs are pinned to its slot so that the compiler cannot move work
+// across the barriers.  The page ids of a work item's tiles are loaded once
+// per item, one tile per lane.
 
 #include "common.h"
 #include "../launch.h"
@@ -74,8 +76,12 @@ __device__ __forceinline__ u32x4_t lds_ld16(uint32_t a) {
 // waits for its own part with vmcnt before the barrier) and the V^T writes
 // (covered here by the LDS count); no memory fence, which would make the
 // compiler drain the DMA in flight.
+// The scheduling barriers keep the compiler from moving register-only work
+// (exponentials, products) across it, which would undo the phase split below.
 __device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int N>
@@ -132,11 +138,6 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
   const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
 }
-
-template <bool B>
-struct Flag {
-  static constexpr bool value = B;
-};
 
 }  // namespace
 
@@ -202,16 +203,29 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     dma_v[i] = 2u * (uint32_t)(rr * vs.token + 8 * v_pos(lane & 15, trow));
   }
 
-  const int32_t wb0 = p.wg_indptr[KC_PREFILL][blockIdx.x];
-  const int32_t wb1 = p.wg_indptr[KC_PREFILL][blockIdx.x + 1];
+  // Both V^T buffers start as zeros, so that the first PV product of an item
+  // (P = 0) never meets a non-finite value.
+#pragma unroll
+  for (int i = 0; i < 2 * kTileBytes / (16 * 64 * kWaves); ++i)
+    *reinterpret_cast<lds_u32x4*>((uintptr_t)(vt_lds + 16 * (tid + 64 * kWaves * i))) =
+        u32x4_t{0u, 0u, 0u, 0u};
+
+  const int32_t wb0 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][blockIdx.x]);
+  const int32_t wb1 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][blockIdx.x + 1]);
   for (int32_t idx = wb0; idx < wb1; ++idx) {
+    // Item fields and request lengths are wave-uniform: readfirstlane keeps
+    // them, and the loop control derived from them, in scalar registers.
+    auto uni = [](int32_t x) __attribute__((always_inline)) {
+      return __builtin_amdgcn_readfirstlane(x);
+    };
     const int32_t* it = p.items[KC_PREFILL] + (int64_t)idx * IT_WORDS;
-    const int32_t r = it[IT_REQ], g = it[IT_KVHEAD], row0 = it[IT_ROW0], row1 = it[IT_ROW1];
-    const int32_t k0 = it[IT_K0], k1 = it[IT_K1], s = it[IT_SPLIT];
+    const int32_t r = uni(it[IT_REQ]), g = uni(it[IT_KVHEAD]);
+    const int32_t row0 = uni(it[IT_ROW0]), row1 = uni(it[IT_ROW1]);
+    const int32_t k0 = uni(it[IT_K0]), k1 = uni(it[IT_K1]), s = uni(it[IT_SPLIT]);
     const int32_t G = p.group;
-    const int32_t q0 = p.qo_indptr[r];
-    const int32_t n = p.qo_indptr[r + 1] - q0;
-    const int32_t L = p.kv_len[r];
+    const int32_t q0 = uni(p.qo_indptr[r]);
+    const int32_t n = uni(p.qo_indptr[r + 1]) - q0;
+    const int32_t L = uni(p.kv_len[r]);
     const int32_t cached = L - n;
     auto key_end = [&](int32_t row) __attribute__((always_inline)) {
       return min(k1, (p.causal ? cached + row / G : L - 1) + 1);
@@ -222,23 +236,34 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     const int32_t t = row_ok ? row / G : 0;
     const int32_t h = g * G + (row_ok ? row % G : 0);
     const int32_t kend_row = row_ok ? key_end(row) : k0;
-    const int32_t kend = key_end(row1 - 1);
+    const int32_t kend = uni(key_end(row1 - 1));
     const int32_t wrow0 = row0 + wave * 32;
     const bool wave_has_rows = wrow0 < row1;
-    const int32_t kend_wmin = wave_has_rows ? key_end(wrow0) : k0;
+    const int32_t kend_wmin = uni(wave_has_rows ? key_end(wrow0) : k0);
     const int32_t ntiles = (kend - k0 + kKT - 1) / kKT;
 
     u32x4_t qf[8];  // Q operand, loaded once the first tiles are in flight
     const int32_t* pages = p.page_indices + p.page_indptr[r];
     const char* kbase = reinterpret_cast<const char*>(kc + (int64_t)g * ks.head);
     const char* vbase = reinterpret_cast<const char*>(vc + (int64_t)g * vs.head);
-    // DMA of the tile at key kb into ring slot `slot`.  Keys past k1 are
-    // fetched from the item's last key (a written slot of the same page), so
-    // masked keys hold finite values.
-    auto issue = [&](int32_t kb, int slot) __attribute__((always_inline)) {
-      const int32_t gkey = min(kb + kDmaRows * wave, k1 - 1);  // first key of this wave's rows
-      const int32_t rmax = k1 - 1 - gkey;                      // rows past it that exist
-      const int64_t page = load_scalar(pages + (gkey >> p.page_shift));
+    if (idx > wb0) wait_vmem<0>();  // the previous item's output stores
+    // Page id of the first key row this wave moves for tile T, in lane T % 64
+    // of pid[T / 64] (the planner keeps an item within 128 tiles).  Rows past
+    // k1 are clamped onto the item's last key.
+    int32_t pid[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int32_t gkey = min(k0 + (lane + 64 * c) * kKT + kDmaRows * wave, k1 - 1);
+      pid[c] = (c == 0 || ntiles > 64) ? pages[gkey >> p.page_shift] : 0;
+    }
+    // DMA of tile T into ring slot `slot`.  Keys past k1 are fetched from the
+    // item's last key (a written slot of the same page), so masked keys hold
+    // finite values.
+    auto issue = [&](int32_t T, int slot) __attribute__((always_inline)) {
+      const int32_t gkey = min(k0 + T * kKT + kDmaRows * wave, k1 - 1);  // first key of this wave's rows
+      const int32_t rmax = k1 - 1 - gkey;                                // rows past it that exist
+      const int64_t page = T < 64 ? __builtin_amdgcn_readlane(pid[0], T)
+                                  : __builtin_amdgcn_readlane(pid[1], T - 64);
       const int64_t in_page = gkey & (p.page_size - 1);
       const char* kg = kbase + 2 * (page * ks.page + in_page * ks.token);
       const char* vg = vbase + 2 * (page * vs.page + in_page * vs.token);
@@ -261,26 +286,33 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
       }
     };
 
-    // Transpose of the V tile in ring slot `slot` into vt[buf].
-    auto transpose = [&](int slot, int buf) __attribute__((always_inline)) {
+    // Transpose of the V tile in ring slot `slot` into vt[buf]: this wave's
+    // four transposing reads, then its four writes.
+    auto transpose_read = [&](int slot, s16x4_t (&v)[4]) __attribute__((always_inline)) {
       const uint32_t src = opaque(ring_lds + slot * kSlotBytes + tr_src);
-      const uint32_t dst = opaque(vt_lds + buf * kTileBytes + tr_dst);
-      s16x4_t v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         v[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(uintptr_t)((src ^ (128u * (i & 1))) + 1024u * (i >> 1)));
+    };
+    auto transpose_write = [&](int buf, const s16x4_t (&v)[4]) __attribute__((always_inline)) {
+      const uint32_t dst = opaque(vt_lds + buf * kTileBytes + tr_dst);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
             (uintptr_t)((dst ^ (16u * (i >> 1))) + 8192u * (i & 1))) = v[i];
+    };
+    auto transpose = [&](int slot, int buf) __attribute__((always_inline)) {
+      s16x4_t v[4];
+      transpose_read(slot, v);
+      transpose_write(buf, v);
     };
 
     // Waits until this wave's part of tile `tile` has landed, when tiles up
     // to `last` have been issued: each wave issues kDmaInst instructions per
     // tile, in tile order.
     auto wait_tile = [&](int32_t tile, int32_t last) __attribute__((always_inline)) {
-      const int32_t later = min(last, ntiles - 1) - tile;  // tiles issued after it
+      const int32_t later = last - tile;  // tiles issued after it
       if (later >= 3) wait_vmem<3 * kDmaInst>();
       else if (later == 2) wait_vmem<2 * kDmaInst>();
       else if (later == 1) wait_vmem<kDmaInst>();
@@ -290,26 +322,97 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     const float sc = p.sm_scale * kLog2e;
     float m = kMinusBig;  // running reference max of this row, log2 units
     float lsum = 0.f;     // this lane's share of the running row sum
-    f32x16_t oacc[4];
+    f32x16_t oacc[4];     // O^T: element 4 b + j of block nb is head dim 32 nb + 8 b + 4 half + j
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[nb][i] = 0.f;
+    f32x16_t sacc[2];  // S^T of the current tile, two 32-key blocks
+    u32x4_t pb[4];     // P^T of the previous tile, bf16 pairs, one 16-key chunk each
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pb[c] = u32x4_t{0u, 0u, 0u, 0u};
 
-    // Element i of S^T block b2 of the tile at kb is key
-    // kb + 32 b2 + 8 (i / 4) + 4 half + i % 4 of row `col`.  Keys past the
-    // row's last visible key become kMinusBig.
-    auto mask = [&](f32x16_t (&sx)[2], int32_t kb) __attribute__((always_inline)) {
-      const int32_t lim = kend_row - kb - 4 * half;
+    // K operand i of block b2 of the tile in ring slot `slot`.
+    auto kld = [&](uint32_t kt, int i, int b2) __attribute__((always_inline)) {
+      return lds_ld16((kt ^ (32u * i)) + 8192u * b2);
+    };
+    // V^T operand of 16-key chunk kc16 and 32-dim block nb.
+    auto vld = [&](uint32_t vtb, int kc16, int nb) __attribute__((always_inline)) {
+      return lds_ld16((vtb ^ (32u * kc16)) + 4096u * nb);
+    };
+
+    // Matrix phase M(j): S^T_j = K_j Q^T into sacc, and
+    // O^T += V^T_{j-1} P^T_{j-1}.  The products of the two contractions
+    // alternate, with their LDS operands read one step ahead.  At j = 0, P is
+    // zero (and V^T finite); at j = ntiles, the S product reads a stale ring
+    // slot and its result is not used.
+    auto mphase = [&](int32_t j) __attribute__((always_inline)) {
+      const uint32_t kt = opaque(ring_lds + (j & (kSlots - 1)) * kSlotBytes + k_rd);
+      const uint32_t vtb = opaque(vt_lds + ((j - 1) & 1) * kTileBytes + vt_rd);
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          sx[b2][i] = (32 * b2 + 8 * (i >> 2) + (i & 3)) < lim ? sx[b2][i] : kMinusBig;
+        for (int i = 0; i < 16; ++i) sacc[b2][i] = 0.f;
+      // step i: S products i of both blocks, PV products (kc16 = i / 2,
+      // nb = 2 (i % 2) + 0, 1).  The operands of step i are read two steps
+      // ahead; the scheduling barrier at the end of each step keeps the
+      // compiler from sinking the reads next to their products.
+      constexpr int kAhead = 2;
+      u32x4_t ka[kAhead + 1][2], va[kAhead + 1][2];
+      auto fetch = [&](int i) __attribute__((always_inline)) {
+        const int b = i % (kAhead + 1);
+        ka[b][0] = kld(kt, i, 0);
+        ka[b][1] = kld(kt, i, 1);
+        va[b][0] = vld(vtb, i >> 1, 2 * (i & 1));
+        va[b][1] = vld(vtb, i >> 1, 2 * (i & 1) + 1);
+      };
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) fetch(i);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int b = i % (kAhead + 1), c = i & 1;
+        if (i + kAhead < 8) fetch(i + kAhead);
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[b][0]), as_bf16x8(qf[i]),
+                                                          sacc[0], 0, 0, 0);
+        oacc[2 * c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(va[b][0]), as_bf16x8(pb[i >> 1]), oacc[2 * c], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[b][1]), as_bf16x8(qf[i]),
+                                                          sacc[1], 0, 0, 0);
+        oacc[2 * c + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(va[b][1]), as_bf16x8(pb[i >> 1]), oacc[2 * c + 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
-    // Raises the reference max for a tile whose row max (both halves
-    // combined) is mx, rescaling O and the row sum.
-    auto raise_max = [&](float mx) __attribute__((always_inline)) {
+
+    // Softmax phase V(j): mask (tiles that straddle a row's last visible key),
+    // row max, lazy rescale, P^T_j = exp2(S^T_j * scale * log2 e - m) as bf16
+    // pairs, and the row sum of the rounded P.
+    // Element i of S^T block b2 of the tile at kb is key
+    // kb + 32 b2 + 8 (i / 4) + 4 half + i % 4 of row `col`.
+    auto vphase = [&](int32_t j) __attribute__((always_inline)) {
+      // S enters here and P leaves at the end through empty asm statements:
+      // the phase's arithmetic stays between the barriers that delimit it.
+      asm volatile("" : "+v"(sacc[0]), "+v"(sacc[1]));
+      const int32_t kb = k0 + j * kKT;
+      if (kb + kKT > kend_wmin) {
+        const int32_t lim = kend_row - kb - 4 * half;
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sacc[b2][i] = (32 * b2 + 8 * (i >> 2) + (i & 3)) < lim ? sacc[b2][i] : kMinusBig;
+      }
+      // Row max as a tree (independent operations for the scheduler).
+      float mx8[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        mx8[k] = fmaxf(fmaxf(sacc[k >> 2][4 * (k & 3)], sacc[k >> 2][4 * (k & 3) + 1]),
+                       fmaxf(sacc[k >> 2][4 * (k & 3) + 2], sacc[k >> 2][4 * (k & 3) + 3]));
+      float mx = fmaxf(fmaxf(fmaxf(mx8[0], mx8[1]), fmaxf(mx8[2], mx8[3])),
+                       fmaxf(fmaxf(mx8[4], mx8[5]), fmaxf(mx8[6], mx8[7])));
+      mx = max_halves(mx);
+      // The reference max is raised only when this tile's max exceeds it by
+      // more than kRescaleSlack; O and the row sum are rescaled then.
       const float mt = mx > 0.5f * kMinusBig ? mx * sc : kMinusBig;
       const bool raise = mt > m + kRescaleSlack;
       if (__ballot(raise)) {
@@ -320,173 +423,99 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
         for (int nb = 0; nb < 4; ++nb) oacc[nb] *= alpha;
         m = m_new;
       }
-    };
-    // K operand i of block b2 of the tile whose K starts at LDS byte kt + k_rd.
-    auto kld = [&](uint32_t kt, int i, int b2) __attribute__((always_inline)) {
-      return lds_ld16((kt ^ (32u * i)) + 8192u * b2);
-    };
-    // P word w of tile sx (packed bf16 pair, the k-slot pair e = w % 4 of
-    // 16-key chunk w / 4), and its contribution to the row sum.
-    auto p_word = [&](const f32x16_t (&sx)[2], int w, float neg_m, float& psum)
-        __attribute__((always_inline)) {
-      const int kc16 = w >> 2, e = w & 3, b2 = kc16 >> 1, hb = kc16 & 1;
-      // key of k-slot (half, e) in a 16-key chunk: 16 kc16 + 8 (e / 4) + 4 half + e % 4
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[b2][8 * hb + 2 * e], sc, neg_m));
-      const float e1 =
-          __builtin_amdgcn_exp2f(__builtin_fmaf(sx[b2][8 * hb + 2 * e + 1], sc, neg_m));
-      const uint32_t wd = pack_bf16x2(e0, e1);
-      psum = sum_bf16x2(wd, psum);
-      return wd;
-    };
-
-    // One pipeline step: tile `tile`'s S^T is in `cur`; with has_next, tile
-    // tile + 1's S^T is produced into `nxt`.
-    auto step = [&](int32_t tile, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], auto has_next)
-        __attribute__((always_inline)) {
-      constexpr bool kNext = decltype(has_next)::value;
-      const int slot = tile & (kSlots - 1);
-      if (kNext) wait_tile(tile + 1, tile + 3);
-      // Publishes tile j + 1 and V^T of tile j; frees ring slot j (its K and
-      // V were consumed in step j - 1) and V^T of tile j - 1.
-      barrier();
-      if (tile + 4 < ntiles) issue(k0 + (tile + 4) * kKT, slot);
-      if (kNext) transpose((slot + 1) & (kSlots - 1), (tile + 1) & 1);
-      if (!wave_has_rows) return;
-
       // A row with no visible key so far has m = kMinusBig; its masked
       // entries (kMinusBig) then still map to exp2 = 0.
       const float neg_m = m > 0.5f * kMinusBig ? -m : 0.f;
-      float psum = 0.f;
-      u32x4_t pb[4];
-      if constexpr (kNext) {
-        // Phase A: S^T of tile j + 1, with the exponentials of tile j.
-        const uint32_t kt = opaque(ring_lds + ((slot + 1) & (kSlots - 1)) * kSlotBytes + k_rd);
+      // P in place of S, each stage over all 32 entries so that the
+      // exponentials do not wait on one another's inputs.
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
+      for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) nxt[b2][i] = 0.f;
-        // Each product is issued together with the exponentials of one P
-        // word (the scheduling barriers keep the groups apart), and the K
-        // operands are read one product pair ahead.
-        u32x4_t ka[2][2];
-        ka[0][0] = kld(kt, 0, 0);
-        ka[0][1] = kld(kt, 0, 1);
+        for (int i = 0; i < 16; ++i) sacc[b2][i] = __builtin_fmaf(sacc[b2][i], sc, neg_m);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (i + 1 < 8) {
-            ka[(i + 1) & 1][0] = kld(kt, i + 1, 0);
-            ka[(i + 1) & 1][1] = kld(kt, i + 1, 1);
-          }
-          nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i & 1][0]),
-                                                           as_bf16x8(qf[i]), nxt[0], 0, 0, 0);
-          const int w0 = 2 * i, w1 = 2 * i + 1;
-          pb[w0 >> 2][w0 & 3] = p_word(cur, w0, neg_m, psum);
-          __builtin_amdgcn_sched_barrier(0);
-          nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i & 1][1]),
-                                                           as_bf16x8(qf[i]), nxt[1], 0, 0, 0);
-          pb[w1 >> 2][w1 & 3] = p_word(cur, w1, neg_m, psum);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // The P words and the row sum are produced here, not sunk into
-        // phase B next to their uses.
-        asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(psum));
-      } else {
+      for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int w = 0; w < 16; ++w) pb[w >> 2][w & 3] = p_word(cur, w, neg_m, psum);
+        for (int i = 0; i < 16; ++i) sacc[b2][i] = __builtin_amdgcn_exp2f(sacc[b2][i]);
+      __builtin_amdgcn_sched_barrier(0);
+      // word w = k-slot pair e = w % 4 of 16-key chunk kc16 = w / 4; the row
+      // sum is taken over the rounded P, in four partial sums.
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const int kc16 = w >> 2, e = w & 3, b2 = kc16 >> 1, hb = kc16 & 1;
+        const uint32_t wd = pack_bf16x2(sacc[b2][8 * hb + 2 * e], sacc[b2][8 * hb + 2 * e + 1]);
+        pb[kc16][e] = wd;
+        ps[e] = sum_bf16x2(wd, ps[e]);
       }
-      lsum += psum;
-
-      // Phase B: O^T += V^T P^T over the four 16-key chunks of tile j, with
-      // the mask and max of tile j + 1.
-      if constexpr (kNext) {
-        const int32_t kb1 = k0 + (tile + 1) * kKT;
-        if (kb1 + kKT > kend_wmin) mask(nxt, kb1);
-      }
-      const uint32_t vtb = opaque(vt_lds + (tile & 1) * kTileBytes + vt_rd);
-      auto vld = [&](int kc16, int nb) __attribute__((always_inline)) {
-        return lds_ld16((vtb ^ (32u * kc16)) + 4096u * nb);
-      };
-      u32x4_t va[2][4];
-      float mx = kMinusBig;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) va[0][nb] = vld(0, nb);
-#pragma unroll
-      for (int kc16 = 0; kc16 < 4; ++kc16) {
-        if (kc16 + 1 < 4) {
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) va[(kc16 + 1) & 1][nb] = vld(kc16 + 1, nb);
-        }
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[kc16 & 1][nb]),
-                                                             as_bf16x8(pb[kc16]), oacc[nb], 0, 0, 0);
-          if constexpr (kNext) {
-            // 8 of the 32 entries per chunk, two per product
-            const int b2 = kc16 >> 1, i0 = 8 * (kc16 & 1) + 2 * nb;
-            mx = fmaxf(mx, fmaxf(nxt[b2][i0], nxt[b2][i0 + 1]));
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-      if constexpr (kNext) raise_max(max_halves(mx));
+      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(lsum));
     };
 
-    if (idx > wb0) wait_vmem<0>();  // the previous item's output stores
-    barrier();  // the previous item's waves are done with the ring and vt
-#pragma unroll
-    for (int j = 0; j < kSlots; ++j)
-      if (j < ntiles) issue(k0 + j * kKT, j);
+    // This wave's eighth of the V transpose of tile j (ring slot j % kSlots
+    // into vt[j % 2]).
+    auto transpose_part = [&](int32_t j) __attribute__((always_inline)) {
+      transpose(j & (kSlots - 1), j & 1);
+    };
 
     // Q operand of the S^T products: qf[i] = Q[row][16 i + 8 half .. + 8),
-    // loaded while the first tiles are in flight.
+    // loaded together with the page ids.  Both are complete before the first
+    // DMA is issued, and the empty asm statement marks them as such: a load
+    // still pending in the compiler's view would make it wait for every
+    // untracked DMA in flight at the first use inside the loop.
     {
       const bf16_t* qrow = q + ((int64_t)(q0 + t) * p.num_qo_heads + h) * kD + 8 * half;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         qf[i] = row_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * i) : u32x4_t{0u, 0u, 0u, 0u};
-      // Complete the Q loads here.
-      asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
-                   "v"(qf[6]), "v"(qf[7]));
+      asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]),
+                   "+v"(qf[5]), "+v"(qf[6]), "+v"(qf[7]), "+v"(pid[0]), "+v"(pid[1]));
     }
-    if (ntiles > 0) {
-      f32x16_t sa[2], sb[2];
-      // Prologue: tile 0 lands; V^T of tile 0, S^T of tile 0 and its max.
-      wait_tile(0, kSlots - 1);
-      barrier();
-      transpose(0, 0);
-      if (wave_has_rows) {
-        const uint32_t kt = opaque(ring_lds + k_rd);
+
+    barrier();  // the previous item's waves are done with the ring and vt
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sa[b2][i] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kld(kt, i, 0)), as_bf16x8(qf[i]),
-                                                          sa[0], 0, 0, 0);
-          sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kld(kt, i, 1)), as_bf16x8(qf[i]),
-                                                          sa[1], 0, 0, 0);
+    for (int j = 0; j < kSlots; ++j)
+      if (j < ntiles) issue(j, j);
+
+    // Two groups of four wavefronts (one of each per SIMD) run the phases
+    // M(0) V(0) M(1) V(1) ... M(ntiles) half a step apart, so that one
+    // group's products overlap the other group's softmax.  Slot 2 j: group 0
+    // runs M(j), group 1 runs V(j - 1); slot 2 j + 1: group 0 runs V(j),
+    // group 1 runs M(j).  Each slot begins with a workgroup barrier.
+    //   K_j and V^T_{j-1} are read in slots 2 j and 2 j + 1;
+    //   V_j is transposed into vt[j % 2] in slots 2 j (group 1) and 2 j + 1
+    //   (group 0), each wave its eighth, in the slot of its softmax phase;
+    //   ring slot j % kSlots is refilled (tile j + kSlots) at slot 2 j + 2.
+    // Waits for tile j before slot 2 j: tiles up to j + kSlots - 2 (up to
+    // kSlots - 1 before the first) have been issued by then.
+    auto wait_for = [&](int32_t j) __attribute__((always_inline)) {
+      if (j < ntiles) wait_tile(j, min(j == 0 ? kSlots - 1 : j + kSlots - 2, ntiles - 1));
+    };
+    // At slot 2 j: refill ring slot (j - 1) % kSlots with tile j + kSlots - 1.
+    auto refill = [&](int32_t j) __attribute__((always_inline)) {
+      if (j >= 1 && j + kSlots - 1 < ntiles) issue(j + kSlots - 1, (j - 1) & (kSlots - 1));
+    };
+    if (wave < kWaves / 2) {
+      for (int32_t j = 0; j <= ntiles; ++j) {
+        wait_for(j);
+        barrier();  // slot 2 j
+        refill(j);
+        mphase(j);
+        barrier();  // slot 2 j + 1
+        if (j < ntiles) {
+          vphase(j);
+          transpose_part(j);
         }
-        if (k0 + kKT > kend_wmin) mask(sa, k0);
-        float mx = kMinusBig;
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sa[b2][i]);
-        raise_max(max_halves(mx));
       }
-      // Steps, two per iteration so that the S^T buffers swap roles without
-      // copies.
-      int32_t tile = 0;
-      for (; tile + 2 < ntiles; tile += 2) {
-        step(tile, sa, sb, Flag<true>{});
-        step(tile + 1, sb, sa, Flag<true>{});
-      }
-      if (tile + 1 < ntiles) {
-        step(tile, sa, sb, Flag<true>{});
-        step(tile + 1, sb, sa, Flag<false>{});
-      } else {
-        step(tile, sa, sb, Flag<false>{});
+    } else {
+      for (int32_t j = 0; j <= ntiles; ++j) {
+        wait_for(j);
+        barrier();  // slot 2 j
+        refill(j);
+        if (j >= 1) vphase(j - 1);
+        if (j < ntiles) transpose_part(j);
+        barrier();  // slot 2 j + 1
+        mphase(j);
       }
     }
 

@@ -35,6 +35,7 @@ enum SplitField : int32_t { SP_COUNT = 0, SP_CHUNK, SP_BASE, SP_WORDS };
 constexpr int GEN_ROWS = 4;        // rows per generic item (one wave each)
 constexpr int DEC_MAX_ROWS = 16;   // rows per decode item (one MFMA column block)
 constexpr int PRE_ROWS = 256;      // rows per prefill item
+constexpr int PRE_MAX_KEYS = 8192; // keys per prefill item (128 tiles: two page-id registers)
 constexpr int MLA_ROWS = 128;      // rows per latent-attention item
 constexpr int KEY_ALIGN = 64;      // split pieces start at multiples of this
 constexpr int PRE_WGS_PER_CU = 1;  // prefill workgroups resident per compute unit
