@@ -92,7 +92,13 @@ typedef enum rpa_dtype {
  *   value (v_cache == k_cache with the same strides).
  *   page_size: a power of two in [1, 256].
  *   causal: 1 = bottom-right causal (query t sees keys 0 .. c_r + t);
- *           0 = every query sees all kv_len keys.
+ *           0 = every query sees all kv_len keys.  Without causal masking
+ *           kv_len may be smaller than qo_len, down to 0: the new tokens then
+ *           attend to cached keys only (the cache half of the split execution
+ *           in "Chunked prefill", section "correctness"); a request with
+ *           kv_len = 0 gets the empty state o = 0, lse = -inf, and a plan
+ *           with any kv_len < qo_len cannot append (rpa_kv_append returns
+ *           RPA_ERR_INVALID_ARG).
  *   sm_scale: multiplier of q.k (e.g. 1/sqrt(head_dim_qk)). */
 typedef struct rpa_attn_config {
   int32_t num_qo_heads;
@@ -108,7 +114,8 @@ typedef struct rpa_attn_config {
 /* Ragged batch of one step.  Host int32 arrays, owned by the caller, read only
  * during rpa_plan_create.
  *   qo_indptr[batch_size+1]: starts at 0, non-decreasing; n_r = qo_indptr[r+1]-qo_indptr[r].
- *   kv_len[batch_size]: L_r >= n_r (the new tokens are the last n_r keys).
+ *   kv_len[batch_size]: L_r >= n_r (the new tokens are the last n_r keys);
+ *     with causal = 0, any L_r >= 0 (see rpa_attn_config).
  *   kv_page_indptr[batch_size+1], kv_page_indices[kv_page_indptr[batch_size]]:
  *     CSR page table; request r needs at least ceil(L_r / P) entries, extra
  *     entries are ignored.

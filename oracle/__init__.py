@@ -20,7 +20,9 @@ method is described on):
   chunked-prefill post (k4i.top), section "correctness" (position i sees keys
   j <= i, scores q.K^T/sqrt(d_k), softmax, times V);
 * softmax merge of two disjoint key partitions -- chunked-prefill post,
-  section "correctness" (softmax_merge of the cache part and the chunk part);
+  section "correctness" (softmax_merge of the cache part and the chunk part),
+  and the split execution built on it (the new tokens attend to the cache
+  and, causally, to their own keys; the two states are merged);
 * chunked driver over ceil(L/C) chunks -- chunked-prefill post, sections
   "core-idea" and "correctness";
 * FLOP and IO accounting -- chunked-prefill post, sections "flops" and
@@ -40,6 +42,7 @@ from .rpa_oracle import (  # noqa: F401
     attend,
     attend_dense,
     merge,
+    split_attention,
     chunked_prefill,
     one_shot_prefill,
     accounting,

@@ -294,6 +294,51 @@ def merge(o_a: np.ndarray, lse_a: np.ndarray, o_b: np.ndarray, lse_b: np.ndarray
 
 
 # ----------------------------------------------------------------------------
+# O3b: split execution (cache part + chunk part, merged)
+# ----------------------------------------------------------------------------
+
+
+def split_attention(q: np.ndarray, k_pool: np.ndarray, v_pool, k_new: np.ndarray, v_new,
+                    batch: Batch, num_qo_heads: int, num_kv_heads: int, sm_scale: float,
+                    head_dim_v: int | None = None):
+    """The chunked-prefill post's split form of one step (section "correctness").
+
+    The step's new tokens of request r attend to the c_r cached keys held in
+    the pages, each new token seeing all of them (the "history cache"), and,
+    causally, to the step's own keys k_new / v_new (token t sees new tokens
+    0 .. t: the "current chunk"); the two partial states are joined with the
+    softmax merge (O3).  The pages are read without the new tokens, so the
+    result does not depend on whether the append has run.  All inputs are
+    float64; k_new / v_new are token-major [total_q, num_kv_heads, d].
+    Returns (o, lse) like ``attend``.
+    """
+    group = num_qo_heads // num_kv_heads
+    d_v = head_dim_v if head_dim_v is not None else v_new.shape[-1]
+    cached = np.array([batch.cached_len(r) for r in range(batch.batch_size)], dtype=np.int64)
+    cache_batch = Batch(batch.qo_indptr, cached, batch.kv_page_indptr, batch.kv_page_indices,
+                        batch.page_size)
+    o_a, lse_a = attend(q, k_pool, v_pool, cache_batch, num_qo_heads, num_kv_heads, sm_scale,
+                        head_dim_v=d_v, causal=False)
+    o_b = np.zeros_like(o_a)
+    lse_b = np.full_like(lse_a, -np.inf)
+    for r in range(batch.batch_size):
+        n = batch.qo_len(r)
+        if n == 0:
+            continue
+        i0 = int(batch.qo_indptr[r])
+        visible = np.arange(n)[None, :] <= np.arange(n)[:, None]
+        for g in range(num_kv_heads):
+            kk = k_new[i0:i0 + n, g, :]
+            vv = v_new[i0:i0 + n, g, :d_v]
+            for hh in range(group):
+                h = g * group + hh
+                o_r, lse_r = attend_dense(q[i0:i0 + n, h, :], kk, vv, sm_scale, visible)
+                o_b[i0:i0 + n, h, :] = o_r
+                lse_b[i0:i0 + n, h] = lse_r
+    return merge(o_a, lse_a, o_b, lse_b)
+
+
+# ----------------------------------------------------------------------------
 # O4: chunked prefill driver
 # ----------------------------------------------------------------------------
 
@@ -398,6 +443,6 @@ def kv_write_bytes_per_chunk(chunk: int, n_layers: int, n_kv_heads: int, head_di
 
 __all__ = [
     "Batch", "bf16_bits_to_f64", "f32_to_bf16_bits_rne", "slot_of", "gather", "append",
-    "attend_dense", "attend", "merge", "chunked_prefill", "one_shot_prefill",
+    "attend_dense", "attend", "merge", "split_attention", "chunked_prefill", "one_shot_prefill",
     "accounting", "kv_write_bytes_per_chunk",
 ]

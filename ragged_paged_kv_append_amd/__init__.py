@@ -328,3 +328,78 @@ def merge_state(o_a, lse_a, o_b, lse_b, stream=None):
     dtype = RPA_DTYPE_BF16 if o_a.dtype == torch.bfloat16 else RPA_DTYPE_F32
     rpa_merge_state(o_a, lse_a, o_b, lse_b, o, lse, rows, heads, dim, dtype, stream)
     return o, lse
+
+
+class SplitChunkAttention:
+    """Split execution of a step's attention ("Chunked prefill", section
+    "correctness"): the new tokens of each request attend
+
+      (a) to the request's cached keys (c_r = kv_len - qo_len of them), every
+          new token seeing all of them: one cross-attention plan over the page
+          pool (causal masking off, kv_len = c_r);
+      (b) causally to the step's own keys and values, read straight from the
+          k_new / v_new buffers (token-major [total_q, num_kv_heads, d]) as a
+          pool of page_size-token pages: one causal plan per request with
+          kv_len = qo_len;
+
+    and the two states are combined by rpa_merge_state.  The result equals the
+    attention over the pages after rpa_kv_append, and the append may run
+    before, after or beside it.  Bottom-right causal attention only; not for
+    the shared-latent form (its values are a view of the keys).  Every step
+    runs in the library's kernels; this class only builds the plans and
+    chains the calls.
+    """
+
+    def __init__(self, cfg: rpa_attn_config, qo_indptr, kv_len, kv_page_indptr, kv_page_indices,
+                 num_pages: int, device="cuda", num_cus: int = 0):
+        if not cfg.causal:
+            raise RpaError(RPA_ERR_INVALID_ARG, "split execution is defined for causal attention")
+        if cfg.head_dim_qk == 576:
+            raise RpaError(RPA_ERR_UNSUPPORTED, "split execution of the shared latent form")
+        qo = np.asarray(qo_indptr, dtype=np.int64)
+        kv = np.asarray(kv_len, dtype=np.int64)
+        n = qo[1:] - qo[:-1]
+        cached = kv - n
+        if np.any(cached < 0):
+            raise RpaError(RPA_ERR_INVALID_ARG, "kv_len < qo_len")
+        self.cfg = cfg
+        self.qo = qo
+        self.total_q = int(qo[-1]) if len(qo) else 0
+        cross = rpa_attn_config(cfg.num_qo_heads, cfg.num_kv_heads, cfg.head_dim_qk,
+                                cfg.head_dim_v, cfg.page_size, cfg.dtype, 0, cfg.sm_scale)
+        self.cache_plan = Plan(cross, qo, cached, kv_page_indptr, kv_page_indices, num_pages,
+                               device=device, num_cus=num_cus)
+        P = cfg.page_size
+        self.chunk_plans = []
+        for r in range(len(n)):
+            if n[r] == 0:
+                continue
+            pages = -(-int(n[r]) // P)
+            plan = Plan(cfg, [0, int(n[r])], [int(n[r])], [0, pages], np.arange(pages), pages,
+                        device=device, num_cus=num_cus)
+            self.chunk_plans.append((int(qo[r]), int(n[r]), plan))
+
+    def run(self, q, k_new, v_new, k_cache, v_cache, o=None, lse=None, stream=None):
+        """o, lse of the step (o in q's dtype, lse float32, natural log)."""
+        import torch
+        H, d_v, P = self.cfg.num_qo_heads, self.cfg.head_dim_v, self.cfg.page_size
+        o_a, lse_a = self.cache_plan.attention(q, k_cache, v_cache, stream=stream)
+        o_b = torch.empty_like(o_a)
+        lse_b = torch.empty_like(lse_a)
+        es = q.element_size()
+        # token-major rows as pages of P tokens: page, head and token strides
+        ks = rpa_cache_strides(P * k_new.stride(0), k_new.stride(1), k_new.stride(0))
+        vs = rpa_cache_strides(P * v_new.stride(0), v_new.stride(1), v_new.stride(0))
+        for i0, n, plan in self.chunk_plans:
+            rpa_batch_attention(plan.handle, q.data_ptr() + i0 * q.stride(0) * es,
+                                k_new.data_ptr() + i0 * k_new.stride(0) * es,
+                                v_new.data_ptr() + i0 * v_new.stride(0) * es, ks, vs,
+                                o_b.data_ptr() + i0 * o_b.stride(0) * es,
+                                lse_b.data_ptr() + i0 * lse_b.stride(0) * 4, stream)
+        if o is None:
+            o = torch.empty_like(o_a)
+        if lse is None:
+            lse = torch.empty_like(lse_a)
+        dtype = RPA_DTYPE_BF16 if q.dtype == torch.bfloat16 else RPA_DTYPE_F32
+        rpa_merge_state(o_a, lse_a, o_b, lse_b, o, lse, self.total_q, H, d_v, dtype, stream)
+        return o, lse

@@ -254,6 +254,9 @@ RPA_EXPORT rpa_status rpa_kv_append(const rpa_plan* plan, const void* k_new, con
   const bool latent = shared_latent(c);
   std::string why;
   if (plan->total_q == 0) return RPA_OK;  // no new tokens: nothing to read or write
+  if (!plan->can_append)
+    return fail(RPA_ERR_INVALID_ARG,
+                "the plan has a request with kv_len < qo_len (cross attention): no append slots");
   if (!k_new || !k_cache) return fail(RPA_ERR_INVALID_ARG, "null k_new or k_cache");
   if (!aligned(k_new, 16) || !aligned(k_cache, 16))
     return fail(RPA_ERR_INVALID_ARG, "k_new and k_cache must be 16-byte aligned");

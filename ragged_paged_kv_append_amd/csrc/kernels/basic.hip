@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DevPlan p, T* __restric
   const int32_t S = p.split[r * SP_WORDS + SP_COUNT];
   const int32_t kc = p.split[r * SP_WORDS + SP_CHUNK];
   const int64_t base = p.split[r * SP_WORDS + SP_BASE];
-  const int32_t S_eff = min(S, pmax / kc + 1);
+  const int32_t S_eff = pmax < 0 ? 0 : min(S, pmax / kc + 1);  // no key: empty state
   const int32_t h = x / per_head;
   const int32_t d0 = (x - h * per_head) * 8;
   float mx = -INFINITY;

@@ -226,6 +226,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     const int32_t q0 = uni(p.qo_indptr[r]);
     const int32_t n = uni(p.qo_indptr[r + 1]) - q0;
     const int32_t L = uni(p.kv_len[r]);
+    const int32_t S = uni(p.split[r * SP_WORDS + SP_COUNT]);     // pieces of this request
+    const int32_t part0 = uni(p.split[r * SP_WORDS + SP_BASE]);  // its first partial row
     const int32_t cached = L - n;
     auto key_end = [&](int32_t row) __attribute__((always_inline)) {
       return min(k1, (p.causal ? cached + row / G : L - 1) + 1);
@@ -525,7 +527,6 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
       const float lse_nat = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
       const int32_t i_tok = q0 + t;
-      const int32_t S = p.split[r * SP_WORDS + SP_COUNT];
       // Lane holds O^T[d][row] for d = 32 nb + 8 b + 4 half + j (element 4 b + j of block nb).
       if (S == 1) {
         bf16_t* orow = o + ((int64_t)i_tok * p.num_qo_heads + h) * kD + 4 * half;
@@ -539,7 +540,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
           }
         if (half == 0 && lse) lse[(int64_t)i_tok * p.num_qo_heads + h] = lse_nat;
       } else {
-        const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + t;
+        const int64_t prow = (int64_t)part0 + (int64_t)s * n + t;
         float* orow = p.part_o + (prow * p.num_qo_heads + h) * kD + 4 * half;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)

@@ -120,8 +120,9 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
       *err = "qo_indptr must be non-decreasing (request " + std::to_string(r) + ")";
       return RPA_ERR_INVALID_ARG;
     }
-    if (kvl[r] < n) {
-      *err = "kv_len < qo_len for request " + std::to_string(r);
+    if (kvl[r] < 0 || (c.causal && kvl[r] < n)) {
+      *err = (kvl[r] < 0 ? "kv_len < 0" : "kv_len < qo_len with causal attention") +
+             std::string(" for request ") + std::to_string(r);
       return RPA_ERR_INVALID_ARG;
     }
     if (pip[r + 1] < pip[r]) {
@@ -154,7 +155,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
     }
     for (int32_t r = 0; r < B; ++r) {
       const int64_t n = (int64_t)qo[r + 1] - qo[r];
-      if (n == 0) continue;
+      if (n == 0 || kvl[r] < n) continue;  // nothing to append (cross attention)
       const int64_t cached = kvl[r] - n;
       for (int64_t j = cached / P; j <= (kvl[r] - 1) / P; ++j) {
         const int32_t pg = pix[pip[r] + j];
@@ -333,17 +334,26 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
   }
 
   // ---- append map and merge rows --------------------------------------------------
-  std::vector<int32_t> append((size_t)total_q * 2);
+  // A request with kv_len < qo_len (allowed without causal masking: the new
+  // tokens attend to cached keys only) has no append slots, so such a plan
+  // cannot append.  Its rows with kv_len = 0 have no work item; the merge
+  // pass writes them as empty states (O = 0, lse = -inf).
+  std::vector<int32_t> append((size_t)total_q * 2, -1);
   std::vector<int32_t> merge_rows;
+  plan->can_append = true;
   for (int32_t r = 0; r < B; ++r) {
     const int64_t n = (int64_t)qo[r + 1] - qo[r];
     const int64_t cached = (int64_t)kvl[r] - n;
+    if (cached < 0) plan->can_append = false;
     for (int64_t t = 0; t < n; ++t) {
       const int64_t p = cached + t;
       const int64_t i = qo[r] + t;
-      append[(size_t)i * 2 + 0] = pix[pip[r] + p / P];
-      append[(size_t)i * 2 + 1] = (int32_t)(p % P);
-      if (split[(size_t)r * SP_WORDS + SP_COUNT] > 1) merge_rows.push_back((int32_t)i);
+      if (p >= 0) {
+        append[(size_t)i * 2 + 0] = pix[pip[r] + p / P];
+        append[(size_t)i * 2 + 1] = (int32_t)(p % P);
+      }
+      if (split[(size_t)r * SP_WORDS + SP_COUNT] > 1 || kvl[r] == 0)
+        merge_rows.push_back((int32_t)i);
     }
   }
 

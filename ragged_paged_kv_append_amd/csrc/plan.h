@@ -12,6 +12,7 @@ struct rpa_plan {
   int32_t total_q = 0;
   int32_t num_pages = 0;
   int32_t group = 1;
+  bool can_append = true;  // false if a request has kv_len < qo_len
 
   // Metadata in the order it is laid out in the device workspace (int32 words).
   std::vector<int32_t> blob;

@@ -251,7 +251,8 @@ def test_plan_create_error_paths(L):
     call()  # the baseline is valid
     expect(rpa.RPA_ERR_INVALID_ARG, lambda: call(qo=[1, 2, 3]))            # indptr not from 0
     expect(rpa.RPA_ERR_INVALID_ARG, lambda: call(qo=[0, 3, 1]))            # decreasing
-    expect(rpa.RPA_ERR_INVALID_ARG, lambda: call(kv=[0, 20]))              # kv_len < qo_len
+    expect(rpa.RPA_ERR_INVALID_ARG, lambda: call(kv=[0, 20]))              # kv_len < qo_len, causal
+    expect(rpa.RPA_ERR_INVALID_ARG, lambda: call(kv=[-1, 20]))             # negative kv_len
     expect(rpa.RPA_ERR_INVALID_ARG, lambda: call(pip=[0, 2, 1]))           # page indptr decreasing
     expect(rpa.RPA_ERR_PAGE_OOB, lambda: call(kv=[17, 20]))                # missing page
     expect(rpa.RPA_ERR_PAGE_OOB, lambda: call(pix=[0, 1, 4]))              # page id >= num_pages
@@ -321,3 +322,18 @@ def test_plan_debug_dump_append_matches_oracle(L):
         for t in range(batch.qo_len(r)):
             assert tuple(app[i]) == oracle.slot_of(batch, r, batch.cached_len(r) + t)
             i += 1
+
+
+def test_cross_attention_plan_without_causal_mask(L):
+    """Without causal masking kv_len may be below qo_len (the new tokens attend
+    to cached keys only); kv_len = 0 rows go to the merge pass as empty states."""
+    cfg = rpa.make_config(4, 2, 64, 64, 16, "f32", causal=False)
+    plan = rpa.rpa_plan_create(cfg, [0, 3, 8, 9], [0, 2, 40], [0, 0, 1, 4], [3, 0, 1, 2], 4)
+    items = rpa.rpa_plan_debug_dump(plan, "items").reshape(-1, 8)
+    assert 0 not in set(items[:, 0].tolist())          # kv_len 0: no work item
+    assert {1, 2} <= set(items[:, 0].tolist())
+    merge = set(rpa.rpa_plan_debug_dump(plan, "merge_rows").tolist())
+    assert {0, 1, 2} <= merge                          # rows of the kv_len = 0 request
+    noncausal = rpa.make_config(4, 2, 64, 64, 16, "f32", causal=False)
+    with pytest.raises(rpa.RpaError):
+        rpa.rpa_plan_create(noncausal, [0, 3], [-2], [0, 0], [0], 1)

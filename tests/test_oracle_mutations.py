@@ -36,6 +36,9 @@ MUTATIONS = {
     "pairs_off_by_one": ("pairs += sum(c + t + 1 for t in range(n))",
                          "pairs += sum(c + t for t in range(n))"),
     "io_drops_v": ("return chunk * 2 * n_layers", "return chunk * n_layers"),
+    "split_cache_part_causal": ("head_dim_v=d_v, causal=False)", "head_dim_v=d_v, causal=True)"),
+    "split_chunk_part_sees_all": ("visible = np.arange(n)[None, :] <= np.arange(n)[:, None]",
+                                  "visible = np.ones((n, n), dtype=bool)"),
     "bf16_truncates": ("rounded = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)",
                        "rounded = u >> np.uint64(16)"),
 }
@@ -74,6 +77,8 @@ def _pin_calls(golden):
         lambda: pins.test_p8_flop_identity(golden),
         pins.test_p8_accounting_counts_visible_pairs,
         lambda: pins.test_p9_io_worked_example(golden),
+        lambda: pins.test_p2s_split_execution_equals_attention_after_append(
+            [1, 16, 0, 5], [37, 36, 4, 5], 4, 2, 16),
     ]
     return calls
 

@@ -18,6 +18,9 @@ Each test names the pin it implements:
   P9 the pages' IO worked example (section "io-overhead");
   P10 verify shapes: n drafts give qo_len n + 1; MTP verify gives 2 rows per
      request.
+  P2s split execution (cache part over the pages before the append, chunk
+     part over the new keys, merged) == attention after the append, and == the
+     torch SDPA reference over the concatenated keys.
 """
 
 import json
@@ -294,6 +297,45 @@ def test_p2_merge_equals_union():
         np.testing.assert_allclose(l_m, l_u, rtol=0, atol=1e-13)
         o_m2, l_m2 = oracle.merge(o_b, l_b, o_a, l_a)    # symmetric
         np.testing.assert_allclose(o_m2, o_u, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("qo,kv,hq,hkv,P", [
+    ([1, 16, 0, 5], [37, 36, 4, 5], 4, 2, 16),     # decode, chunk on a cache, empty, first chunk
+    ([3, 7], [40, 7], 8, 1, 4),
+    ([2, 1, 6], [9, 64, 70], 2, 2, 64),
+])
+def test_p2s_split_execution_equals_attention_after_append(qo, kv, hq, hkv, P):
+    rng = np.random.default_rng(sum(kv))
+    d, dv, scale = 16, 8, 0.3
+    seqs_k = [rng.standard_normal((L, hkv, d)) for L in kv]
+    seqs_v = [rng.standard_normal((L, hkv, dv)) for L in kv]
+    seed = int(rng.integers(1 << 30))
+    kp, indptr, indices = place(seqs_k, P, hkv, d, np.random.default_rng(seed))
+    vp, _, _ = place(seqs_v, P, hkv, dv, np.random.default_rng(seed))
+    qo_indptr = np.concatenate([[0], np.cumsum(qo)])
+    batch = Batch(qo_indptr, kv, indptr, indices, P)
+    # the pool before the append: the new tokens' slots are NaN, so the split
+    # form must not read them
+    kp0 = kp.copy()
+    vp0 = vp.copy()
+    for r, (n, L) in enumerate(zip(qo, kv)):
+        for t in range(L - n, L):
+            pg, sl = oracle.slot_of(batch, r, t)
+            kp0[pg, :, sl, :] = np.nan
+            vp0[pg, :, sl, :] = np.nan
+    k_new = np.concatenate([s[L - n:] for s, L, n in zip(seqs_k, kv, qo)])
+    v_new = np.concatenate([s[L - n:] for s, L, n in zip(seqs_v, kv, qo)])
+    q = rng.standard_normal((int(qo_indptr[-1]), hq, d))
+    o_s, l_s = oracle.split_attention(q, kp0, vp0, k_new, v_new, batch, hq, hkv, scale)
+    kp1, vp1 = oracle.append(kp0, vp0, k_new, v_new, batch)
+    np.testing.assert_array_equal(kp1, kp)           # the append restores the full pool
+    o_a, l_a = oracle.attend(q, kp1, vp1, batch, hq, hkv, scale)
+    np.testing.assert_allclose(o_s, o_a, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_s, l_a, rtol=0, atol=1e-12)
+    o_t, l_t = torch_reference(q, seqs_k, seqs_v, qo, kv, hq, hkv, scale)
+    rows = np.concatenate([np.arange(qo_indptr[r], qo_indptr[r + 1]) for r in range(len(qo))])
+    np.testing.assert_allclose(o_s[rows], o_t, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_s[rows], l_t, rtol=0, atol=1e-12)
 
 
 def test_p2_merge_of_two_empty_partials_is_empty():
