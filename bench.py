@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 METRIC = "decode KV-read HBM GB/s + prefill-chunk attention TFLOP/s (1 GPU, % roofline)"
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
-KERNELS = ("append", "generic", "decode", "prefill", "mla", "merge")
+KERNELS = ("append", "generic", "decode", "prefill", "mla", "merge", "merge_state")
 
 
 def log(msg):
@@ -283,6 +283,26 @@ def run_chunked(spec, steps, warmup):
                           "flops": w["flops"], "tflops": w["flops"] / (attn_ms * 1e-3) / 1e12,
                           "kernels_us": {kk: t * 1e3 for kk, (t, c) in kernels.items()},
                           "launches": {kk: c for kk, (t, c) in kernels.items()}})
+    # the same chunks in split form: cache part (cross attention over the
+    # pages), chunk part (causal, over the chunk's own K/V) and their merge
+    o_s = torch.empty_like(o)
+    lse_s = torch.empty_like(lse)
+    split_chunks = []
+    for i in range(len(chunks)):
+        a = i * C
+        n = min(C, L - a)
+        sp = rpa.SplitChunkAttention(cfg, [0, n], [a + n], [0, len(pages)], pages, meta.num_pages)
+
+        def st(sp=sp, a=a, n=n):
+            sp.run(q[a:a + n], k[a:a + n], v[a:a + n], k_pool, v_pool, o=o_s[a:a + n],
+                   lse=lse_s[a:a + n])
+        ms, kernels = timed_steps(st, steps, warmup)
+        w = work(spec, [n], [a + n])
+        attn_ms = sum(t * c for name, (t, c) in kernels.items())
+        split_chunks.append({"chunk": i, "kv_len": a + n, "attention_ms": attn_ms,
+                             "flops": w["flops"], "tflops": w["flops"] / (attn_ms * 1e-3) / 1e12,
+                             "kernels_us": {kk: t * 1e3 for kk, (t, c) in kernels.items()},
+                             "launches": {kk: c for kk, (t, c) in kernels.items()}})
     one = step_of(0, L)
     ms1, k1 = timed_steps(one, max(3, steps // 4), 1)
     w1 = work(spec, [L], [L])
@@ -290,7 +310,7 @@ def run_chunked(spec, steps, warmup):
     one_shot = {"ms_per_step": ms1, "attention_ms": attn1, "flops": w1["flops"],
                 "tflops": w1["flops"] / (attn1 * 1e-3) / 1e12,
                 "kernels_us": {kk: t * 1e3 for kk, (t, c) in k1.items()}}
-    return per_chunk, one_shot
+    return per_chunk, one_shot, split_chunks
 
 
 # ----------------------------------------------------------------------------
@@ -478,7 +498,7 @@ def main_chunked(args):
     spec = workloads.SPECS["chunked_gqa"]
     log(f"workload chunked_gqa: timing each of 16 chunk steps, {args.steps} steps after "
         f"{args.warmup} warmup")
-    per_chunk, one_shot = run_chunked(spec, args.steps, args.warmup)
+    per_chunk, one_shot, split_chunks = run_chunked(spec, args.steps, args.warmup)
     flops = sum(c["flops"] for c in per_chunk)
     attn_ms = sum(c["attention_ms"] for c in per_chunk)
     step_ms = sum(c["ms_per_step"] for c in per_chunk)
@@ -507,7 +527,11 @@ def main_chunked(args):
         "work": {"flops": flops},
         "parts": {"chunks": [{k: c[k] for k in ("chunk", "kv_len", "tflops", "attention_ms",
                                                 "kernels_us")} for c in per_chunk],
-                  "one_shot": one_shot},
+                  "one_shot": one_shot,
+                  "split": {"tflops": sum(c["flops"] for c in split_chunks)
+                            / (sum(c["attention_ms"] for c in split_chunks) * 1e-3) / 1e12,
+                            "chunks": [{k: c[k] for k in ("chunk", "tflops", "attention_ms",
+                                                          "kernels_us")} for c in split_chunks]}},
     }
     print(json.dumps(line), flush=True)
 

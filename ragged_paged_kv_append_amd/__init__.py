@@ -383,9 +383,15 @@ class SplitChunkAttention:
         """o, lse of the step (o in q's dtype, lse float32, natural log)."""
         import torch
         H, d_v, P = self.cfg.num_qo_heads, self.cfg.head_dim_v, self.cfg.page_size
-        o_a, lse_a = self.cache_plan.attention(q, k_cache, v_cache, stream=stream)
-        o_b = torch.empty_like(o_a)
-        lse_b = torch.empty_like(lse_a)
+        key = (q.dtype, q.device)
+        if getattr(self, "_tmp_key", None) != key:
+            # the two partial states, kept for later calls with this plan
+            mk = lambda: (torch.empty((self.total_q, H, d_v), dtype=q.dtype, device=q.device),
+                          torch.empty((self.total_q, H), dtype=torch.float32, device=q.device))
+            self._tmp = mk() + mk()
+            self._tmp_key = key
+        o_a, lse_a, o_b, lse_b = self._tmp
+        self.cache_plan.attention(q, k_cache, v_cache, o=o_a, lse=lse_a, stream=stream)
         es = q.element_size()
         # token-major rows as pages of P tokens: page, head and token strides
         ks = rpa_cache_strides(P * k_new.stride(0), k_new.stride(1), k_new.stride(0))

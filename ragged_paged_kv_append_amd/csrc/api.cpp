@@ -47,6 +47,7 @@ rpa::DevPlan dev_plan(const rpa_plan* plan) {
     p.n_wgs[k] = plan->n_wgs[k];
   }
   p.merge_rows = base + plan->off_merge;
+  p.merge_req = base + plan->off_merge_req;
   p.n_merge_rows = plan->n_merge_rows;
   char* ws = static_cast<char*>(plan->d_ws);
   p.part_o = reinterpret_cast<float*>(ws + plan->part_o_off);

@@ -233,19 +233,21 @@ hipError_t launch_generic(const DevPlan& p, const void* q, const void* k_cache,
 // ----------------------------------------------------------------------------
 
 // Block (x, y) merges row p.merge_rows[x]; a thread owns 8 consecutive output
-// elements of one head (task y * 256 + thread of the row's H * d_v / 8).
+// elements of one head (task y * blockDim.x + thread of the row's H * d_v / 8).
 // Piece s of a row contributes only if it holds a key the row sees
-// (s * chunk <= last visible key).
+// (s * chunk <= last visible key).  The pieces are read eight at a time, with
+// a running maximum, so their loads are in flight together.
 template <typename T>
 __global__ __launch_bounds__(256) void merge_rows_kernel(DevPlan p, T* __restrict__ o,
                                                          float* __restrict__ lse) {
-  const int32_t i = p.merge_rows[blockIdx.x];
+  constexpr int kGroup = 8;
   const int32_t DV = p.head_dim_v;
   const int32_t per_head = DV / 8;
   const int32_t H = p.num_qo_heads;
   const int32_t x = blockIdx.y * blockDim.x + threadIdx.x;
   if (x >= H * per_head) return;
-  const int32_t r = request_of_row(p.qo_indptr, p.batch_size, i);
+  const int32_t i = p.merge_rows[blockIdx.x];
+  const int32_t r = p.merge_req[blockIdx.x];
   const int32_t q0 = p.qo_indptr[r];
   const int32_t n = p.qo_indptr[r + 1] - q0;
   const int32_t t = i - q0;
@@ -257,31 +259,52 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DevPlan p, T* __restric
   const int32_t S_eff = pmax < 0 ? 0 : min(S, pmax / kc + 1);  // no key: empty state
   const int32_t h = x / per_head;
   const int32_t d0 = (x - h * per_head) * 8;
-  float mx = -INFINITY;
-  for (int32_t s = 0; s < S_eff; ++s)
-    mx = fmaxf(mx, p.part_lse[(base + (int64_t)s * n + t) * H + h]);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;  // running maximum of the pieces' lse
   float tot = 0.f;
-  for (int32_t s = 0; s < S_eff; ++s) {
-    const int64_t prow = base + (int64_t)s * n + t;
-    const float ls = p.part_lse[prow * H + h];
-    const float w = (ls == -INFINITY) ? 0.f : __expf(ls - mx);
-    tot += w;
-    float v[8];
-    load8(p.part_o + (prow * H + h) * DV + d0, v);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int32_t s0 = 0; s0 < S_eff; s0 += kGroup) {
+    float ls[kGroup];
+    float v[kGroup][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, v[e], acc[e]);
+    for (int u = 0; u < kGroup; ++u) {
+      if (s0 + u < S_eff) {
+        const int64_t prow = base + (int64_t)(s0 + u) * n + t;
+        ls[u] = p.part_lse[prow * H + h];
+        load8(p.part_o + (prow * H + h) * DV + d0, v[u]);
+      } else {
+        ls[u] = -INFINITY;
+      }
+    }
+    float mg = m;
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) mg = fmaxf(mg, ls[u]);
+    if (mg == -INFINITY) continue;  // nothing seen yet
+    const float a = (m == -INFINITY) ? 0.f : __expf(m - mg);
+    tot *= a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= a;
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      if (s0 + u < S_eff && ls[u] != -INFINITY) {
+        const float w = __expf(ls[u] - mg);
+        tot += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
+      }
+    }
+    m = mg;
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] *= inv;
   store8(o + ((int64_t)i * H + h) * DV + d0, acc);
-  if (lse && d0 == 0) lse[(int64_t)i * H + h] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
+  if (lse && d0 == 0) lse[(int64_t)i * H + h] = tot > 0.f ? m + __logf(tot) : -INFINITY;
 }
 
 hipError_t launch_merge_rows(const DevPlan& p, void* o, float* lse, hipStream_t stream) {
   const int tasks = p.num_qo_heads * (p.head_dim_v / 8);
-  const dim3 grid(p.n_merge_rows, (tasks + 255) / 256), block(256);
+  const int bs = tasks >= 256 ? 256 : (tasks + 63) / 64 * 64;
+  const dim3 grid(p.n_merge_rows, (tasks + bs - 1) / bs), block(bs);
   if (p.dtype == RPA_DTYPE_BF16)
     hipLaunchKernelGGL(merge_rows_kernel<bf16_t>, grid, block, 0, stream, p,
                        static_cast<bf16_t*>(o), lse);

@@ -103,15 +103,4 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Request that owns global query row i (binary search over qo_indptr).
-__device__ __forceinline__ int32_t request_of_row(const int32_t* qo_indptr, int32_t batch_size,
-                                                  int32_t i) {
-  int32_t lo = 0, hi = batch_size - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (qo_indptr[mid] <= i) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 }  // namespace rpa

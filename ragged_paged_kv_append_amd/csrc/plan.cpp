@@ -339,7 +339,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
   // cannot append.  Its rows with kv_len = 0 have no work item; the merge
   // pass writes them as empty states (O = 0, lse = -inf).
   std::vector<int32_t> append((size_t)total_q * 2, -1);
-  std::vector<int32_t> merge_rows;
+  std::vector<int32_t> merge_rows, merge_req;
   plan->can_append = true;
   for (int32_t r = 0; r < B; ++r) {
     const int64_t n = (int64_t)qo[r + 1] - qo[r];
@@ -353,7 +353,10 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
         append[(size_t)i * 2 + 1] = (int32_t)(p % P);
       }
       if (split[(size_t)r * SP_WORDS + SP_COUNT] > 1 || kvl[r] == 0)
+      {
         merge_rows.push_back((int32_t)i);
+        merge_req.push_back(r);
+      }
     }
   }
 
@@ -386,6 +389,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
     plan->n_wgs[k] = wg_indptr[k].empty() ? plan->n_items[k] : (int32_t)wg_indptr[k].size() - 1;
   }
   plan->off_merge = push(merge_rows.data(), (int64_t)merge_rows.size());
+  plan->off_merge_req = push(merge_req.data(), (int64_t)merge_req.size());
   plan->n_merge_rows = (int32_t)merge_rows.size();
   plan->partial_rows = partial_rows;
 

@@ -53,7 +53,8 @@ struct DevPlan {
   // Tile classes (prefill, latent): workgroup b runs items
   // wg_indptr[b] .. wg_indptr[b + 1] - 1 of its class, in that order.
   const int32_t* wg_indptr[KC_COUNT];
-  const int32_t* merge_rows;    // tokens whose request has S_r > 1
+  const int32_t* merge_rows;    // tokens whose request has S_r > 1 (or kv_len 0)
+  const int32_t* merge_req;     // the request of each of those tokens
   float* part_o;                // [partial rows][num_qo_heads][head_dim_v]
   float* part_lse;              // [partial rows][num_qo_heads]
   int32_t n_items[KC_COUNT];
