@@ -151,6 +151,29 @@ typedef struct rpa_plan rpa_plan;
 rpa_status rpa_plan_create(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
                            int32_t num_cus, rpa_plan** out);
 
+/* rpa_plan_create for a batch whose speculative drafts form trees
+ * ("Accelerating Sonar through speculation", Perplexity: a draft tree is
+ * verified in one pass, each draft token attending to the context and to its
+ * own ancestors in the tree, under a custom attention mask).  Attention stays
+ * causal (cfg->causal must be 1) except among the new tokens of a request
+ * that has a mask: there new token t sees new token u iff bit u of its mask
+ * row is set, while every cached key stays visible.
+ *   tree_indptr[batch_size+1]: word offsets into tree_words, starting at 0;
+ *     request r has a mask iff tree_indptr[r+1] > tree_indptr[r], and then
+ *     exactly n_r * ceil(n_r/32) words (n_r <= 64);
+ *   tree_words: row t of request r is the ceil(n_r/32) words at
+ *     tree_indptr[r] + t * ceil(n_r/32); bit u % 32 of word u / 32 is set iff
+ *     new token t sees new token u.  Every token must see itself; bits past
+ *     n_r must be clear.
+ * Both arrays are host memory owned by the caller, read only during the call.
+ * A chain mask (row t = bits 0..t) reproduces the causal result.  Requests of
+ * the absorbed latent form that carry a mask run on the generic kernel.
+ * Errors: as rpa_plan_create; INVALID_ARG for a malformed mask, UNSUPPORTED
+ * for a mask over more than 64 new tokens. */
+rpa_status rpa_plan_create_tree(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                                const int32_t* tree_indptr, const uint32_t* tree_words,
+                                int32_t num_cus, rpa_plan** out);
+
 /* Device bytes the plan needs in its workspace: metadata plus float32 partial
  * outputs of split pieces.  Host only. */
 rpa_status rpa_plan_workspace_size(const rpa_plan* plan, size_t* bytes);

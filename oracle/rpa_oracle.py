@@ -218,7 +218,7 @@ def attend_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 def attend(q: np.ndarray, k_pool: np.ndarray, v_pool, batch: Batch,
            num_qo_heads: int, num_kv_heads: int, sm_scale: float,
-           head_dim_v: int | None = None, causal: bool = True):
+           head_dim_v: int | None = None, causal: bool = True, tree=None):
     """Batched ragged causal attention over a paged KV cache, in float64.
 
     q: [total_q, num_qo_heads, d_qk] (float64).  k_pool / v_pool: HND pools
@@ -227,6 +227,12 @@ def attend(q: np.ndarray, k_pool: np.ndarray, v_pool, batch: Batch,
 
     Query token t of request r, head h, attends to keys j = 0 .. c_r + t of KV
     head h // G of its own request (all kv_len keys when causal is False).
+
+    ``tree``: optional list with one entry per request, None or a boolean
+    [n_r, n_r] matrix; for such a request new token t sees every cached key
+    and new token u iff tree[r][t, u] (verification of a draft tree under a
+    custom attention mask, "Accelerating Sonar through speculation", EAGLE
+    section).
     Returns (o [total_q, num_qo_heads, d_v], lse [total_q, num_qo_heads]).
     """
     if num_qo_heads % num_kv_heads != 0:
@@ -247,6 +253,9 @@ def attend(q: np.ndarray, k_pool: np.ndarray, v_pool, batch: Batch,
         t_idx = np.arange(n)[:, None]
         j_idx = np.arange(L)[None, :]
         visible = (j_idx <= c + t_idx) if causal else np.ones((n, L), dtype=bool)
+        if tree is not None and tree[r] is not None:
+            among_new = np.asarray(tree[r], dtype=bool)
+            visible = np.concatenate([np.ones((n, c), dtype=bool), among_new], axis=1)
         for g in range(num_kv_heads):
             kk = gather(k_pool, batch, r, g, L)
             if v_pool is None:

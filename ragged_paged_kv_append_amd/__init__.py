@@ -37,8 +37,9 @@ RPA_DTYPE_BF16 = 1
 KC_GENERIC, KC_DECODE, KC_PREFILL, KC_MLA = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
-    "rpa_plan_create", "rpa_plan_workspace_size", "rpa_plan_upload", "rpa_kv_append",
-    "rpa_batch_attention", "rpa_merge_state", "rpa_plan_destroy", "rpa_status_string",
+    "rpa_plan_create", "rpa_plan_create_tree", "rpa_plan_workspace_size", "rpa_plan_upload",
+    "rpa_kv_append", "rpa_batch_attention", "rpa_merge_state", "rpa_plan_destroy",
+    "rpa_status_string",
     "rpa_last_error_message", "rpa_abi_version", "rpa_plan_debug_dump", "rpa_profile_enable",
     "rpa_profile_read", "rpa_profile_reset",
 )
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     P = ctypes.POINTER
     L.rpa_plan_create.argtypes = [P(rpa_attn_config), P(rpa_batch_desc), i32, P(vp)]
+    L.rpa_plan_create_tree.argtypes = [P(rpa_attn_config), P(rpa_batch_desc),
+                                       P(ctypes.c_int32), P(ctypes.c_uint32), i32, P(vp)]
     L.rpa_plan_workspace_size.argtypes = [vp, P(sz)]
     L.rpa_plan_upload.argtypes = [vp, vp, sz, vp]
     L.rpa_kv_append.argtypes = [vp, vp, vp, vp, vp, P(rpa_cache_strides), P(rpa_cache_strides), vp]
@@ -197,6 +200,47 @@ def rpa_plan_create(cfg: rpa_attn_config, qo_indptr, kv_len, kv_page_indptr, kv_
     return _PlanHandle(out.value, arrays)
 
 
+def rpa_plan_create_tree(cfg: rpa_attn_config, qo_indptr, kv_len, kv_page_indptr,
+                         kv_page_indices, num_pages: int, tree_indptr, tree_words,
+                         num_cus: int = 0) -> _PlanHandle:
+    """rpa_plan_create with per-request tree masks among the new tokens."""
+    L = lib()
+    arrays = [_i32(qo_indptr), _i32(kv_len), _i32(kv_page_indptr), _i32(kv_page_indices)]
+    ti = _i32(tree_indptr)
+    tw = np.ascontiguousarray(np.asarray(tree_words, dtype=np.uint32))
+    if tw.size == 0:
+        tw = np.zeros(1, dtype=np.uint32)
+    batch = rpa_batch_desc(len(arrays[1]), _i32p(arrays[0]), _i32p(arrays[1]), _i32p(arrays[2]),
+                           _i32p(arrays[3]), int(num_pages))
+    out = ctypes.c_void_p()
+    _check(L.rpa_plan_create_tree(ctypes.byref(cfg), ctypes.byref(batch), _i32p(ti),
+                                  tw.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                  int(num_cus), ctypes.byref(out)))
+    return _PlanHandle(out.value, arrays + [ti, tw])
+
+
+def tree_mask_words(masks) -> tuple[np.ndarray, np.ndarray]:
+    """Pack per-request boolean masks ([n_r, n_r] arrays, or None for no mask)
+    into (tree_indptr, tree_words) for rpa_plan_create_tree: row t of a
+    request is ceil(n_r/32) words, bit u set iff new token t sees new token u."""
+    indptr = [0]
+    words = []
+    for m in masks:
+        if m is None:
+            indptr.append(indptr[-1])
+            continue
+        m = np.asarray(m, dtype=bool)
+        n = m.shape[0]
+        wpr = (n + 31) // 32
+        for t in range(n):
+            row = [0] * wpr
+            for u in np.nonzero(m[t])[0]:
+                row[int(u) // 32] |= 1 << (int(u) % 32)
+            words.extend(row)
+        indptr.append(indptr[-1] + n * wpr)
+    return np.array(indptr, dtype=np.int32), np.array(words, dtype=np.uint32)
+
+
 def rpa_plan_workspace_size(plan: _PlanHandle) -> int:
     n = ctypes.c_size_t()
     _check(lib().rpa_plan_workspace_size(plan.handle, ctypes.byref(n)))
@@ -281,11 +325,18 @@ class Plan:
     """A plan plus its device workspace (a torch uint8 tensor on ``device``)."""
 
     def __init__(self, cfg: rpa_attn_config, qo_indptr, kv_len, kv_page_indptr, kv_page_indices,
-                 num_pages: int, device="cuda", num_cus: int = 0, stream=None):
+                 num_pages: int, device="cuda", num_cus: int = 0, stream=None, tree_masks=None):
+        """tree_masks: optional list with one [n_r, n_r] boolean array (or None)
+        per request; see rpa_plan_create_tree."""
         import torch
         self.cfg = cfg
-        self.handle = rpa_plan_create(cfg, qo_indptr, kv_len, kv_page_indptr, kv_page_indices,
-                                      num_pages, num_cus)
+        if tree_masks is None:
+            self.handle = rpa_plan_create(cfg, qo_indptr, kv_len, kv_page_indptr,
+                                          kv_page_indices, num_pages, num_cus)
+        else:
+            ti, tw = tree_mask_words(tree_masks)
+            self.handle = rpa_plan_create_tree(cfg, qo_indptr, kv_len, kv_page_indptr,
+                                               kv_page_indices, num_pages, ti, tw, num_cus)
         self.total_q = int(np.asarray(qo_indptr)[-1]) if len(qo_indptr) else 0
         self.ws_bytes = rpa_plan_workspace_size(self.handle)
         self.workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)

@@ -48,6 +48,9 @@ rpa::DevPlan dev_plan(const rpa_plan* plan) {
   }
   p.merge_rows = base + plan->off_merge;
   p.merge_req = base + plan->off_merge_req;
+  p.tree_req = plan->off_tree_req >= 0 ? base + plan->off_tree_req : nullptr;
+  p.tree_mask = plan->off_tree_mask >= 0
+                    ? reinterpret_cast<const uint32_t*>(base + plan->off_tree_mask) : nullptr;
   p.n_merge_rows = plan->n_merge_rows;
   char* ws = static_cast<char*>(plan->d_ws);
   p.part_o = reinterpret_cast<float*>(ws + plan->part_o_off);
@@ -178,8 +181,11 @@ RPA_EXPORT const char* rpa_status_string(rpa_status s) {
 
 RPA_EXPORT const char* rpa_last_error_message(void) { return g_last_error.c_str(); }
 
-RPA_EXPORT rpa_status rpa_plan_create(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
-                                      int32_t num_cus, rpa_plan** out) {
+namespace {
+
+rpa_status create_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                       const int32_t* tree_indptr, const uint32_t* tree_words, int32_t num_cus,
+                       rpa_plan** out) {
   if (!out) return fail(RPA_ERR_INVALID_ARG, "null output pointer");
   *out = nullptr;
   rpa_plan* plan = new (std::nothrow) rpa_plan();
@@ -187,7 +193,7 @@ RPA_EXPORT rpa_status rpa_plan_create(const rpa_attn_config* cfg, const rpa_batc
   std::string err;
   rpa_status s;
   try {
-    s = rpa::build_plan(cfg, batch, num_cus, plan, &err);
+    s = rpa::build_plan(cfg, batch, tree_indptr, tree_words, num_cus, plan, &err);
   } catch (const std::bad_alloc&) {
     s = RPA_ERR_INVALID_ARG;
     err = "out of host memory while planning";
@@ -199,6 +205,22 @@ RPA_EXPORT rpa_status rpa_plan_create(const rpa_attn_config* cfg, const rpa_batc
   *out = plan;
   g_last_error.clear();
   return RPA_OK;
+}
+
+}  // namespace
+
+RPA_EXPORT rpa_status rpa_plan_create(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                                      int32_t num_cus, rpa_plan** out) {
+  return create_plan(cfg, batch, nullptr, nullptr, num_cus, out);
+}
+
+RPA_EXPORT rpa_status rpa_plan_create_tree(const rpa_attn_config* cfg,
+                                           const rpa_batch_desc* batch,
+                                           const int32_t* tree_indptr,
+                                           const uint32_t* tree_words, int32_t num_cus,
+                                           rpa_plan** out) {
+  if (!tree_indptr) return fail(RPA_ERR_INVALID_ARG, "null tree_indptr");
+  return create_plan(cfg, batch, tree_indptr, tree_words, num_cus, out);
 }
 
 RPA_EXPORT rpa_status rpa_plan_workspace_size(const rpa_plan* plan, size_t* bytes) {

@@ -132,7 +132,13 @@ __global__ __launch_bounds__(256) void generic_kernel(DevPlan p, const T* __rest
   if (row >= row1) return;  // no block-level barrier after this point
   const int32_t t = row / G, h = g * G + row % G;
   const int32_t i = q0 + t;
-  const int32_t pmax = p.causal ? cached + t : L - 1;
+  // A request with a tree mask sees every key up to L - 1, filtered among the
+  // new tokens by its 64-bit mask row.
+  const bool tree = p.tree_mask != nullptr && p.tree_req[r] != 0;
+  const uint64_t tmask = tree ? ((uint64_t)p.tree_mask[2 * (int64_t)i + 1] << 32) |
+                                    p.tree_mask[2 * (int64_t)i]
+                              : 0ull;
+  const int32_t pmax = (p.causal && !tree) ? cached + t : L - 1;
   const int32_t kend = min(k1, pmax + 1);
   const int32_t* pages = p.page_indices + p.page_indptr[r];
   const float sc = p.sm_scale * kLog2e;  // scores kept in log2 units
@@ -144,7 +150,8 @@ __global__ __launch_bounds__(256) void generic_kernel(DevPlan p, const T* __rest
 
   for (int32_t kb = k0; kb < kend; kb += 64) {
     const int32_t key = kb + lane;
-    const bool valid = key < kend;
+    const bool valid = key < kend && !(tree && key >= cached &&
+                                       !((tmask >> (uint32_t)(key - cached)) & 1ull));
     float sv = -INFINITY;
     int64_t voff = 0;
     if (valid) {
@@ -252,7 +259,8 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DevPlan p, T* __restric
   const int32_t n = p.qo_indptr[r + 1] - q0;
   const int32_t t = i - q0;
   const int32_t L = p.kv_len[r];
-  const int32_t pmax = p.causal ? L - n + t : L - 1;
+  const bool tree = p.tree_mask != nullptr && p.tree_req[r] != 0;
+  const int32_t pmax = (p.causal && !tree) ? L - n + t : L - 1;
   const int32_t S = p.split[r * SP_WORDS + SP_COUNT];
   const int32_t kc = p.split[r * SP_WORDS + SP_CHUNK];
   const int64_t base = p.split[r * SP_WORDS + SP_BASE];

@@ -122,13 +122,19 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
   const int32_t L = p.kv_len[r];
   const int32_t cached = L - n;
 
+  // A request with a tree mask sees every key up to L - 1, filtered among
+  // the new tokens by its mask row (at most 16 new tokens here).
+  const bool tree = p.tree_mask != nullptr && p.tree_req[r] != 0;
+  const bool causal = p.causal && !tree;
+
   // This lane's query row (as a column of S^T).
   const bool row_ok = col < rows;
   const int32_t t = row_ok ? col / G : 0;
   const int32_t h = g * G + (row_ok ? col % G : 0);
-  const int32_t kend_row = row_ok ? min(k1, (p.causal ? cached + t : L - 1) + 1) : k0;
+  const int32_t kend_row = row_ok ? min(k1, (causal ? cached + t : L - 1) + 1) : k0;
   const int32_t t_last = (rows - 1) / G;
-  const int32_t kend = min(k1, (p.causal ? cached + t_last : L - 1) + 1);
+  const int32_t kend = min(k1, (causal ? cached + t_last : L - 1) + 1);
+  const uint32_t tmask = (tree && row_ok) ? p.tree_mask[2 * (int64_t)(q0 + t)] : 0u;
 
   // Q operand: qf[j] = Q[row][32 grp + 8 j .. + 8), the dims of chunk 4 grp + j.
   u32x4_t qf[4];
@@ -212,7 +218,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
     float mx = kMinusBig;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool ok = kb + 4 * grp + e < kend_row;
+      const int32_t key = kb + 4 * grp + e;
+      bool ok = key < kend_row;
+      if (tree && key >= cached) ok = ok && ((tmask >> (uint32_t)(key - cached)) & 1u);
       sv[e] = ok ? sacc[e] * sc : kMinusBig;
       mx = fmaxf(mx, sv[e]);
     }

@@ -229,8 +229,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     const int32_t S = uni(p.split[r * SP_WORDS + SP_COUNT]);     // pieces of this request
     const int32_t part0 = uni(p.split[r * SP_WORDS + SP_BASE]);  // its first partial row
     const int32_t cached = L - n;
+    // A request with a tree mask sees every key up to L - 1, filtered among
+    // the new tokens by its 64-bit mask row.
+    const bool tree = p.tree_mask != nullptr && uni(p.tree_req[r]) != 0;
+    const bool causal = p.causal && !tree;
     auto key_end = [&](int32_t row) __attribute__((always_inline)) {
-      return min(k1, (p.causal ? cached + row / G : L - 1) + 1);
+      return min(k1, (causal ? cached + row / G : L - 1) + 1);
     };
 
     const int32_t row = row0 + wave * 32 + col;
@@ -242,6 +246,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     const int32_t wrow0 = row0 + wave * 32;
     const bool wave_has_rows = wrow0 < row1;
     const int32_t kend_wmin = uni(wave_has_rows ? key_end(wrow0) : k0);
+    // Tiles from mask_from on need the element mask.
+    const int32_t mask_from = tree ? min(kend_wmin, max(cached, k0)) : kend_wmin;
+    const uint64_t tmask = (tree && row_ok)
+                               ? ((uint64_t)p.tree_mask[2 * (int64_t)(q0 + t) + 1] << 32) |
+                                     p.tree_mask[2 * (int64_t)(q0 + t)]
+                               : 0ull;
     const int32_t ntiles = (kend - k0 + kKT - 1) / kKT;
 
     u32x4_t qf[8];  // Q operand, loaded once the first tiles are in flight
@@ -396,13 +406,19 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
       // the phase's arithmetic stays between the barriers that delimit it.
       asm volatile("" : "+v"(sacc[0]), "+v"(sacc[1]));
       const int32_t kb = k0 + j * kKT;
-      if (kb + kKT > kend_wmin) {
+      if (kb + kKT > mask_from) {
         const int32_t lim = kend_row - kb - 4 * half;
+        const int32_t rel = kb + 4 * half - cached;  // new-token index of element offset 0
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            sacc[b2][i] = (32 * b2 + 8 * (i >> 2) + (i & 3)) < lim ? sacc[b2][i] : kMinusBig;
+          for (int i = 0; i < 16; ++i) {
+            const int idx = 32 * b2 + 8 * (i >> 2) + (i & 3);
+            bool ok = idx < lim;
+            if (tree && rel + idx >= 0)
+              ok = ok && ((tmask >> (uint32_t)(rel + idx)) & 1ull);
+            sacc[b2][i] = ok ? sacc[b2][i] : kMinusBig;
+          }
       }
       // Row max as a tree (independent operations for the scheduler).
       float mx8[8];

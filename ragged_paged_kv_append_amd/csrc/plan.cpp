@@ -51,7 +51,8 @@ int32_t rows_per_item(int32_t cls, int32_t rows_total) {
 
 }  // namespace
 
-rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, int32_t num_cus,
+rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                      const int32_t* tree_indptr, const uint32_t* tree_words, int32_t num_cus,
                       rpa_plan* plan, std::string* err) {
   if (!cfg || !batch || !plan) {
     *err = "null cfg, batch or plan pointer";
@@ -143,6 +144,57 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
       }
     }
   }
+  // Tree masks ("Accelerating Sonar through speculation", tree drafts: the
+  // verification attends each draft token to its ancestors only).  Request r
+  // has a mask iff tree_indptr[r + 1] > tree_indptr[r]; it then holds n_r rows
+  // of ceil(n_r / 32) words, row t bit u set iff new token t sees new token u.
+  const bool has_tree = tree_indptr != nullptr || tree_words != nullptr;
+  std::vector<uint8_t> tree_req;
+  if (has_tree) {
+    if (!tree_indptr || (!tree_words && B > 0 && tree_indptr[B] > 0)) {
+      *err = "tree masks need both tree_indptr and tree_words";
+      return RPA_ERR_INVALID_ARG;
+    }
+    if (!c.causal) {
+      *err = "tree masks refine causal attention (causal must be 1)";
+      return RPA_ERR_INVALID_ARG;
+    }
+    if (B > 0 && tree_indptr[0] != 0) {
+      *err = "tree_indptr[0] must be 0";
+      return RPA_ERR_INVALID_ARG;
+    }
+    tree_req.assign((size_t)B, 0);
+    for (int32_t r = 0; r < B; ++r) {
+      const int64_t n = (int64_t)qo[r + 1] - qo[r];
+      const int64_t words = (int64_t)tree_indptr[r + 1] - tree_indptr[r];
+      if (words == 0) continue;
+      const int64_t wpr = (n + 31) / 32;
+      if (n > TREE_MAX_NEW) {
+        *err = "request " + std::to_string(r) + " has a tree mask over more than " +
+               std::to_string(TREE_MAX_NEW) + " new tokens";
+        return RPA_ERR_UNSUPPORTED;
+      }
+      if (words != n * wpr) {
+        *err = "tree mask of request " + std::to_string(r) + " must hold qo_len * ceil(qo_len/32) words";
+        return RPA_ERR_INVALID_ARG;
+      }
+      for (int64_t t = 0; t < n; ++t) {
+        const uint32_t* row = tree_words + tree_indptr[r] + t * wpr;
+        if (!((row[t / 32] >> (t % 32)) & 1u)) {
+          *err = "tree mask of request " + std::to_string(r) + ": token " + std::to_string(t) +
+                 " must see itself";
+          return RPA_ERR_INVALID_ARG;
+        }
+        for (int64_t u = n; u < wpr * 32; ++u)
+          if ((row[u / 32] >> (u % 32)) & 1u) {
+            *err = "tree mask of request " + std::to_string(r) + " has bits past qo_len";
+            return RPA_ERR_INVALID_ARG;
+          }
+      }
+      tree_req[(size_t)r] = 1;
+    }
+  }
+
   // A page the append writes must be referenced exactly once in the batch.
   if (B > 0) {
     std::vector<uint8_t> refs((size_t)batch->num_pages, 0);
@@ -184,6 +236,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
       }
     }
     if (!class_available(k, c)) k = KC_GENERIC;
+    if (k == KC_MLA && has_tree && tree_req[(size_t)r]) k = KC_GENERIC;
     cls[r] = k;
   }
 
@@ -206,7 +259,8 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
       const int64_t cached = (int64_t)kvl[r] - n;
       for (int64_t row0 = 0; row0 < n * G; row0 += R) {
         const int64_t row1 = std::min(n * G, row0 + R);
-        const int64_t visible = c.causal ? cached + (row1 - 1) / G + 1 : kvl[r];
+        const int64_t visible = (c.causal && !(has_tree && tree_req[(size_t)r]))
+                                    ? cached + (row1 - 1) / G + 1 : kvl[r];
         tile_work[cls[r]] += visible * round_up(row1 - row0, 32) * c.num_kv_heads;
       }
     }
@@ -266,7 +320,8 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
       for (int64_t row0 = 0; row0 < rows_total; row0 += R) {
         const int64_t row1 = std::min(rows_total, row0 + R);
         const int64_t t_last = (row1 - 1) / G;
-        const int64_t p_last = c.causal ? cached + t_last : L - 1;
+        const bool masked = has_tree && tree_req[(size_t)r];
+        const int64_t p_last = (c.causal && !masked) ? cached + t_last : L - 1;
         for (int64_t s = 0; s < S; ++s) {
           const int64_t k0 = s * kc;
           if (k0 > p_last) break;
@@ -390,6 +445,23 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, i
   }
   plan->off_merge = push(merge_rows.data(), (int64_t)merge_rows.size());
   plan->off_merge_req = push(merge_req.data(), (int64_t)merge_req.size());
+  plan->off_tree_mask = plan->off_tree_req = -1;
+  if (has_tree) {
+    std::vector<int32_t> treq(tree_req.begin(), tree_req.end());
+    std::vector<int32_t> tmask((size_t)total_q * 2, 0);
+    for (int32_t r = 0; r < B; ++r) {
+      if (!tree_req[(size_t)r]) continue;
+      const int64_t n = (int64_t)qo[r + 1] - qo[r];
+      const int64_t wpr = (n + 31) / 32;
+      for (int64_t t = 0; t < n; ++t) {
+        const uint32_t* row = tree_words + tree_indptr[r] + t * wpr;
+        tmask[(size_t)(qo[r] + t) * 2 + 0] = (int32_t)row[0];
+        tmask[(size_t)(qo[r] + t) * 2 + 1] = wpr > 1 ? (int32_t)row[1] : 0;
+      }
+    }
+    plan->off_tree_req = push(treq.data(), (int64_t)treq.size());
+    plan->off_tree_mask = push(tmask.data(), (int64_t)tmask.size());
+  }
   plan->n_merge_rows = (int32_t)merge_rows.size();
   plan->partial_rows = partial_rows;
 

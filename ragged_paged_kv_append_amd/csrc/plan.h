@@ -18,6 +18,7 @@ struct rpa_plan {
   std::vector<int32_t> blob;
   int64_t off_qo_indptr = 0, off_kv_len = 0, off_page_indptr = 0, off_page_indices = 0;
   int64_t off_split = 0, off_append = 0, off_merge = 0, off_merge_req = 0;
+  int64_t off_tree_mask = -1, off_tree_req = -1;  // -1: the plan has no tree masks
   int64_t off_items[rpa::KC_COUNT] = {0, 0, 0, 0};
   int32_t n_items[rpa::KC_COUNT] = {0, 0, 0, 0};
   int64_t off_wg[rpa::KC_COUNT] = {0, 0, 0, 0};   // wg_indptr tables (tile classes)
@@ -42,7 +43,10 @@ namespace rpa {
 
 // Validates cfg and batch and fills `plan` (metadata, offsets, sizes).
 // On failure returns the status and sets *err.
-rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch, int32_t num_cus,
+// tree_indptr / tree_words: optional per-request visibility masks among the
+// new tokens (both NULL for plain causal or non-causal attention).
+rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                      const int32_t* tree_indptr, const uint32_t* tree_words, int32_t num_cus,
                       rpa_plan* plan, std::string* err);
 
 // Whether a specialised kernel class is available in this build; the planner

@@ -36,6 +36,7 @@ constexpr int GEN_ROWS = 4;        // rows per generic item (one wave each)
 constexpr int DEC_MAX_ROWS = 16;   // rows per decode item (one MFMA column block)
 constexpr int PRE_ROWS = 256;      // rows per prefill item
 constexpr int PRE_MAX_KEYS = 8192; // keys per prefill item (128 tiles: two page-id registers)
+constexpr int TREE_MAX_NEW = 64;   // new tokens of a request with a tree mask (one 64-bit row)
 constexpr int MLA_ROWS = 128;      // rows per latent-attention item
 constexpr int KEY_ALIGN = 64;      // split pieces start at multiples of this
 constexpr int PRE_WGS_PER_CU = 1;  // prefill workgroups resident per compute unit
@@ -55,6 +56,11 @@ struct DevPlan {
   const int32_t* wg_indptr[KC_COUNT];
   const int32_t* merge_rows;    // tokens whose request has S_r > 1 (or kv_len 0)
   const int32_t* merge_req;     // the request of each of those tokens
+  // Tree masks (nullptr when the plan has none).  tree_req[r] = 1 if request
+  // r has a mask; then tree_mask[2 i], tree_mask[2 i + 1] are the low and high
+  // 32 bits of new token i's row: bit u = it sees new token u of its request.
+  const int32_t* tree_req;
+  const uint32_t* tree_mask;
   float* part_o;                // [partial rows][num_qo_heads][head_dim_v]
   float* part_lse;              // [partial rows][num_qo_heads]
   int32_t n_items[KC_COUNT];

@@ -337,3 +337,33 @@ def test_cross_attention_plan_without_causal_mask(L):
     noncausal = rpa.make_config(4, 2, 64, 64, 16, "f32", causal=False)
     with pytest.raises(rpa.RpaError):
         rpa.rpa_plan_create(noncausal, [0, 3], [-2], [0, 0], [0], 1)
+
+
+def test_tree_mask_plan_validation(L):
+    cfg = rpa.make_config(8, 2, 128, 128, 16, "bf16")
+    qo, kv, pip, pix = [0, 4, 5], [40, 9], [0, 3, 4], [0, 1, 2, 3]
+    tree = np.array([[1, 0, 0, 0], [1, 1, 0, 0], [1, 0, 1, 0], [1, 0, 1, 1]], dtype=bool)
+    ti, tw = rpa.tree_mask_words([tree, None])
+    assert ti.tolist() == [0, 4, 4] and tw.tolist() == [0b1, 0b11, 0b101, 0b1101]
+    plan = rpa.rpa_plan_create_tree(cfg, qo, kv, pip, pix, 4, ti, tw)
+    items = rpa.rpa_plan_debug_dump(plan, "items").reshape(-1, 8)
+    # the masked request's items reach its last key (the tree may see any draft token)
+    assert items[items[:, 0] == 0][:, 5].max() == 40
+    bad_diag = tw.copy()
+    bad_diag[1] = 0b01
+    expect(rpa.RPA_ERR_INVALID_ARG,
+           lambda: rpa.rpa_plan_create_tree(cfg, qo, kv, pip, pix, 4, ti, bad_diag))
+    past = tw.copy()
+    past[0] |= 1 << 7
+    expect(rpa.RPA_ERR_INVALID_ARG,
+           lambda: rpa.rpa_plan_create_tree(cfg, qo, kv, pip, pix, 4, ti, past))
+    expect(rpa.RPA_ERR_INVALID_ARG,
+           lambda: rpa.rpa_plan_create_tree(cfg, qo, kv, pip, pix, 4, [0, 3, 3], tw[:3]))
+    noncausal = rpa.make_config(8, 2, 128, 128, 16, "bf16", causal=False)
+    expect(rpa.RPA_ERR_INVALID_ARG,
+           lambda: rpa.rpa_plan_create_tree(noncausal, qo, kv, pip, pix, 4, ti, tw))
+    big = np.tril(np.ones((65, 65), dtype=bool))
+    ti2, tw2 = rpa.tree_mask_words([big])
+    expect(rpa.RPA_ERR_UNSUPPORTED,
+           lambda: rpa.rpa_plan_create_tree(cfg, [0, 65], [70], [0, 5], [0, 1, 2, 3, 4], 5,
+                                            ti2, tw2))

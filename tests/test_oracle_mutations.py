@@ -39,6 +39,10 @@ MUTATIONS = {
     "split_cache_part_causal": ("head_dim_v=d_v, causal=False)", "head_dim_v=d_v, causal=True)"),
     "split_chunk_part_sees_all": ("visible = np.arange(n)[None, :] <= np.arange(n)[:, None]",
                                   "visible = np.ones((n, n), dtype=bool)"),
+    "tree_mask_transposed": ("among_new = np.asarray(tree[r], dtype=bool)",
+                             "among_new = np.asarray(tree[r], dtype=bool).T"),
+    "tree_hides_cache": ("visible = np.concatenate([np.ones((n, c), dtype=bool), among_new], axis=1)",
+                         "visible = np.concatenate([np.zeros((n, c), dtype=bool), among_new], axis=1)"),
     "bf16_truncates": ("rounded = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)",
                        "rounded = u >> np.uint64(16)"),
 }
@@ -77,6 +81,7 @@ def _pin_calls(golden):
         lambda: pins.test_p8_flop_identity(golden),
         pins.test_p8_accounting_counts_visible_pairs,
         lambda: pins.test_p9_io_worked_example(golden),
+        pins.test_pt_tree_mask_matches_torch_sdpa,
         lambda: pins.test_p2s_split_execution_equals_attention_after_append(
             [1, 16, 0, 5], [37, 36, 4, 5], 4, 2, 16),
     ]

@@ -21,6 +21,9 @@ Each test names the pin it implements:
   P2s split execution (cache part over the pages before the append, chunk
      part over the new keys, merged) == attention after the append, and == the
      torch SDPA reference over the concatenated keys.
+  PT tree masks among the new tokens: a chain mask == causal attention; any
+     mask == torch SDPA with the test's own boolean mask; relabeling the draft
+     nodes permutes the outputs.
 """
 
 import json
@@ -83,7 +86,8 @@ def random_case(rng, qo_lens, kv_lens, hq, hkv, d, dv, page_size, extra_pages=0)
     return q, seqs_k, seqs_v, k_pool, v_pool, batch
 
 
-def torch_reference(q, seqs_k, seqs_v, qo_lens, kv_lens, hq, hkv, scale, causal=True):
+def torch_reference(q, seqs_k, seqs_v, qo_lens, kv_lens, hq, hkv, scale, causal=True,
+                    new_masks=None):
     """Attention by torch's SDPA (float64) on contiguous logical K/V."""
     G = hq // hkv
     outs, lses = [], []
@@ -98,6 +102,9 @@ def torch_reference(q, seqs_k, seqs_v, qo_lens, kv_lens, hq, hkv, scale, causal=
         t = torch.arange(n)[:, None]
         j = torch.arange(L)[None, :]
         mask = (j <= c + t) if causal else torch.ones(n, L, dtype=torch.bool)
+        if new_masks is not None and new_masks[len(outs)] is not None:
+            mask = mask.clone()
+            mask[:, c:] = torch.from_numpy(np.asarray(new_masks[len(outs)], dtype=bool))
         o = torch.nn.functional.scaled_dot_product_attention(
             qt, kt, vt, attn_mask=mask, scale=scale)
         s = (qt @ kt.transpose(1, 2)) * scale
@@ -584,3 +591,73 @@ def test_p10_verify_shapes():
     assert int(qo5.sum()) == 2 * len(qo5) == 128
     qo2, kv2 = workloads.lengths("mixed_7b")
     assert qo2[-1] == 512 and kv2[-1] == 1536 and np.all(qo2[:-1] == 1)
+
+
+
+# ----------------------------------------------------------------------------
+# PT: tree masks among the new tokens
+# ----------------------------------------------------------------------------
+
+
+def random_tree(rng, n):
+    """Ancestor-or-self mask of a random rooted tree on n nodes labelled in
+    creation order (a node's parent has a smaller label)."""
+    parent = [-1] + [int(rng.integers(0, u)) for u in range(1, n)]
+    m = np.zeros((n, n), dtype=bool)
+    for t in range(n):
+        u = t
+        while u >= 0:
+            m[t, u] = True
+            u = parent[u]
+    return m
+
+
+def test_pt_chain_mask_equals_causal():
+    rng = np.random.default_rng(41)
+    qo, kv = [4, 1, 7], [40, 9, 7]
+    q, sk, sv, kp, vp, batch = random_case(rng, qo, kv, 8, 2, 16, 16, 16)
+    chains = [np.tril(np.ones((n, n), dtype=bool)) for n in qo]
+    o_t, l_t = oracle.attend(q, kp, vp, batch, 8, 2, 0.4, tree=chains)
+    o_c, l_c = oracle.attend(q, kp, vp, batch, 8, 2, 0.4)
+    np.testing.assert_allclose(o_t, o_c, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l_t, l_c, rtol=0, atol=1e-13)
+
+
+def test_pt_tree_mask_matches_torch_sdpa():
+    rng = np.random.default_rng(42)
+    qo, kv = [5, 0, 9, 3], [30, 4, 9, 70]
+    q, sk, sv, kp, vp, batch = random_case(rng, qo, kv, 4, 2, 16, 8, 4)
+    masks = [random_tree(rng, 5), None, random_tree(rng, 9), None]
+    o, lse = oracle.attend(q, kp, vp, batch, 4, 2, 0.3, tree=masks)
+    o_t, l_t = torch_reference(q, sk, sv, qo, kv, 4, 2, 0.3,
+                               new_masks=[m for m, n in zip(masks, qo) if n > 0])
+    np.testing.assert_allclose(o, o_t, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l_t, rtol=0, atol=1e-12)
+    # a non-causal pattern (a node seeing a later sibling) is honoured too
+    odd = [np.eye(5, dtype=bool) | np.eye(5, k=1, dtype=bool), None, random_tree(rng, 9), None]
+    o2, l2 = oracle.attend(q, kp, vp, batch, 4, 2, 0.3, tree=odd)
+    o_t2, l_t2 = torch_reference(q, sk, sv, qo, kv, 4, 2, 0.3,
+                                 new_masks=[m for m, n in zip(odd, qo) if n > 0])
+    np.testing.assert_allclose(o2, o_t2, rtol=0, atol=1e-12)
+
+
+def test_pt_relabeling_draft_nodes_permutes_outputs():
+    rng = np.random.default_rng(43)
+    n, c, hq, hkv, d = 6, 25, 4, 1, 8
+    k_all = rng.standard_normal((c + n, hkv, d))
+    v_all = rng.standard_normal((c + n, hkv, d))
+    q = rng.standard_normal((n, hq, d))
+    m = random_tree(rng, n)
+    perm = rng.permutation(n)          # new label of node u is perm[u]
+    inv = np.argsort(perm)
+    k2 = np.concatenate([k_all[:c], k_all[c:][inv]])
+    v2 = np.concatenate([v_all[:c], v_all[c:][inv]])
+    m2 = m[np.ix_(inv, inv)]
+    outs = []
+    for kk, vv, qq, mm in ((k_all, v_all, q, m), (k2, v2, q[inv], m2)):
+        kp, indptr, indices = place([kk], 4, hkv, d, np.random.default_rng(1))
+        vp, _, _ = place([vv], 4, hkv, d, np.random.default_rng(1))
+        b = Batch([0, n], [c + n], indptr, indices, 4)
+        outs.append(oracle.attend(qq, kp, vp, b, hq, hkv, 0.5, tree=[mm]))
+    np.testing.assert_allclose(outs[1][0], outs[0][0][inv], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(outs[1][1], outs[0][1][inv], rtol=0, atol=1e-13)
