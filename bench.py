@@ -101,12 +101,25 @@ def sub_batch(meta, requests, tensors):
     return sub, t
 
 
-def make_plan(spec, meta):
+def make_plan(spec, meta, tree_masks=None):
     import ragged_paged_kv_append_amd as rpa
     cfg = rpa.make_config(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim_qk, spec.head_dim_v,
                           spec.page_size, spec.dtype, spec.causal, spec.sm_scale)
     return rpa.Plan(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices,
-                    meta.num_pages)
+                    meta.num_pages, tree_masks=tree_masks)
+
+
+def tree_of(parents):
+    """Ancestor-or-self mask of a draft tree given each node's parent (-1: root)."""
+    import numpy as np
+    n = len(parents)
+    m = np.zeros((n, n), dtype=bool)
+    for t in range(n):
+        u = t
+        while u >= 0:
+            m[t, u] = True
+            u = parents[u]
+    return m
 
 
 def plan_host_ms(spec, meta, reps=20):
@@ -159,8 +172,8 @@ def timed_steps(step, steps, warmup):
     return 1e3 * (t1 - t0) / steps, kernels
 
 
-def run_batch(spec, meta, tensors, steps, warmup):
-    plan = make_plan(spec, meta)
+def run_batch(spec, meta, tensors, steps, warmup, tree_masks=None):
+    plan = make_plan(spec, meta, tree_masks)
 
     def step():
         plan.append(tensors["k_new"], tensors["v_new"], tensors["k_pool"], tensors["v_pool"])
@@ -450,6 +463,22 @@ def main():
                 tf = sw["flops"] / (attn_ms * 1e-3) / 1e12
                 entry.update({"tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS})
             parts[label] = entry
+
+    if name == "decode_verify_gqa":
+        # the same step with every verify request's 4 new tokens as a draft
+        # tree (root, two children of the root, one grandchild) instead of a
+        # chain: the mask applies to the tiles holding new tokens only
+        masks = [tree_of([-1, 0, 0, 1]) if qo[r] == 4 else None for r in range(meta.batch_size)]
+        log("part tree_verify: verify requests as draft trees")
+        _, tms, tk = run_batch(spec, meta, tensors, args.steps, args.warmup, tree_masks=masks)
+        attn_ms = sum(v[0] * v[1] for k, v in tk.items() if k != "append")
+        gbps = (w["kv_bytes"] + w["qo_bytes"]) / (attn_ms * 1e-3) / 1e9
+        base_ms = sum(v[0] * v[1] for k, v in kernels.items() if k != "append")
+        parts["tree_verify"] = {"ms_per_step": tms, "attention_ms": attn_ms,
+                                "kernels_us": {k: v[0] * 1e3 for k, v in tk.items()},
+                                "kv_read_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+                                "slowdown_vs_chain": attn_ms / base_ms,
+                                "tree_parents": [-1, 0, 0, 1]}
 
     cpu = None
     if not args.no_cpu_baseline:
