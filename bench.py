@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 METRIC = "decode KV-read HBM GB/s + prefill-chunk attention TFLOP/s (1 GPU, % roofline)"
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
-KERNELS = ("append", "generic", "decode", "prefill", "mla", "merge", "merge_state")
+KERNELS = ("append", "generic", "decode", "prefill", "mla", "merge", "merge_state", "page_copy")
 
 
 def log(msg):

@@ -221,6 +221,34 @@ rpa_status rpa_merge_state(const void* o_a, const float* lse_a, const void* o_b,
                            const float* lse_b, void* o, float* lse, int64_t rows,
                            int32_t heads, int32_t dim, int32_t dtype, void* stream);
 
+/* Page copy between paged pools and transfer buffers.
+ * "Disaggregated prefill and decode" (Perplexity), sharded-transfer section:
+ * when prefill and decode shard the KV cache differently, pages are split or
+ * reconstructed by the shard ratio (a decoder rebuilds full pages from the
+ * halves two prefill devices send), and the HND layout keeps a head range of
+ * a page contiguous so that it moves as one write.  "Chunked prefill",
+ * prefix-cache section: cached prefix blocks are reused; a shared block that
+ * is only partly filled must be copied before two requests append to it.
+ * For i in [0, num_pages), copies heads [src_head0, src_head0 + num_heads)
+ * of page src_pages[i] of `src` into heads [dst_head0, dst_head0 + num_heads)
+ * of page dst_pages[i] of `dst`: all page_size slots, `dim` elements per row.
+ * A raw copy of the stored bits.
+ *   src_pages / dst_pages: DEVICE int32 arrays of num_pages page ids, or NULL
+ *     for the identity (page i); the caller owns them.
+ *   strides (elements, as rpa_cache_strides): any layout, e.g. an HND pool,
+ *     an NHD buffer (head_stride = dim, token_stride = heads * dim) or a
+ *     packed shard buffer of num_heads heads.
+ *   dtype: RPA_DTYPE_F32 or RPA_DTYPE_BF16; dim fills whole 16-byte chunks.
+ * Regions written must not overlap regions read; ids and head ranges must lie
+ * inside the pools (not checked: the call knows only strides).  num_pages = 0
+ * is a no-op.  Errors: INVALID_ARG, HIP. */
+rpa_status rpa_page_copy(const void* src, const rpa_cache_strides* src_strides,
+                         const int32_t* src_pages, void* dst,
+                         const rpa_cache_strides* dst_strides, const int32_t* dst_pages,
+                         int32_t num_pages, int32_t src_head0, int32_t dst_head0,
+                         int32_t num_heads, int32_t page_size, int32_t dim, int32_t dtype,
+                         void* stream);
+
 /* Free a plan.  Waits for the plan's last upload copy to finish reading the
  * staging buffer.  NULL is ignored. */
 void rpa_plan_destroy(rpa_plan* plan);
@@ -239,7 +267,7 @@ int32_t rpa_abi_version(void);
  * every kernel it launches.  rpa_profile_read waits for the recorded events,
  * folds them into per-kernel totals and returns the total milliseconds and
  * launch count of one kernel: "append", "generic", "decode", "prefill",
- * "mla", "merge" or "merge_state".  rpa_profile_reset clears the totals.
+ * "mla", "merge", "merge_state" or "page_copy".  rpa_profile_reset clears the totals.
  * Process-wide and thread-safe; off by default.  Errors: INVALID_ARG, HIP. */
 rpa_status rpa_profile_enable(int32_t on);
 rpa_status rpa_profile_read(const char* kernel, double* total_ms, int64_t* launches);

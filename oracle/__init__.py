@@ -23,6 +23,10 @@ method is described on):
   section "correctness" (softmax_merge of the cache part and the chunk part),
   and the split execution built on it (the new tokens attend to the cache
   and, causally, to their own keys; the two states are merged);
+* page copies: head ranges of pages between pools and transfer buffers --
+  disaggregation post, sharded-transfer section (pages split and rebuilt by
+  the shard ratio; HND keeps a head range contiguous), and the copy of a
+  shared partly filled prefix block (chunked-prefill post, prefix cache);
 * chunked driver over ceil(L/C) chunks -- chunked-prefill post, sections
   "core-idea" and "correctness";
 * FLOP and IO accounting -- chunked-prefill post, sections "flops" and
@@ -47,4 +51,6 @@ from .rpa_oracle import (  # noqa: F401
     one_shot_prefill,
     accounting,
     kv_write_bytes_per_chunk,
+    copy_pages,
+    hnd_to_nhd,
 )

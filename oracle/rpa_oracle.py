@@ -402,6 +402,37 @@ def one_shot_prefill(q, k_new, v_new, k_pool, v_pool, pages, page_size,
 
 
 # ----------------------------------------------------------------------------
+# O6: page copies (sharded transfer, prefix reuse)
+# ----------------------------------------------------------------------------
+
+
+def copy_pages(src: np.ndarray, dst: np.ndarray, src_pages, dst_pages, src_head0: int,
+               dst_head0: int, num_heads: int) -> np.ndarray:
+    """Copy head ranges of whole pages; returns the new destination.
+
+    ``src`` and ``dst`` are indexed [page, head, slot, dim] whatever their
+    storage order (an NHD buffer is passed as its [page, head, slot, dim]
+    view).  For each i, heads src_head0 .. src_head0 + num_heads - 1 of page
+    src_pages[i] go to heads dst_head0 .. of page dst_pages[i]; nothing else
+    of the destination changes.  This is the page split and reconstruction of
+    "Disaggregated prefill and decode" (sharded-transfer section: a decoder
+    rebuilds full pages from the halves sent by two prefill devices, and HND
+    keeps a head range of a page contiguous), and the copy of a shared,
+    partly filled prefix block before two requests append to it (chunked-
+    prefill post, prefix-cache section).  Raw elements move unchanged.
+    """
+    out = np.array(dst, copy=True)
+    for sp, dp in zip(np.asarray(src_pages).tolist(), np.asarray(dst_pages).tolist()):
+        out[dp, dst_head0:dst_head0 + num_heads] = src[sp, src_head0:src_head0 + num_heads]
+    return out
+
+
+def hnd_to_nhd(pages: np.ndarray) -> np.ndarray:
+    """Pages [n, heads, slots, dim] (HND) re-laid as [n, slots, heads, dim] (NHD)."""
+    return np.ascontiguousarray(np.swapaxes(pages, 1, 2))
+
+
+# ----------------------------------------------------------------------------
 # O5: accounting
 # ----------------------------------------------------------------------------
 
@@ -453,5 +484,5 @@ def kv_write_bytes_per_chunk(chunk: int, n_layers: int, n_kv_heads: int, head_di
 __all__ = [
     "Batch", "bf16_bits_to_f64", "f32_to_bf16_bits_rne", "slot_of", "gather", "append",
     "attend_dense", "attend", "merge", "split_attention", "chunked_prefill", "one_shot_prefill",
-    "accounting", "kv_write_bytes_per_chunk",
+    "accounting", "kv_write_bytes_per_chunk", "copy_pages", "hnd_to_nhd",
 ]

@@ -38,7 +38,8 @@ KC_GENERIC, KC_DECODE, KC_PREFILL, KC_MLA = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
     "rpa_plan_create", "rpa_plan_create_tree", "rpa_plan_workspace_size", "rpa_plan_upload",
-    "rpa_kv_append", "rpa_batch_attention", "rpa_merge_state", "rpa_plan_destroy",
+    "rpa_kv_append", "rpa_batch_attention", "rpa_merge_state", "rpa_page_copy",
+    "rpa_plan_destroy",
     "rpa_status_string",
     "rpa_last_error_message", "rpa_abi_version", "rpa_plan_debug_dump", "rpa_profile_enable",
     "rpa_profile_read", "rpa_profile_reset",
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.rpa_batch_attention.argtypes = [vp, vp, vp, vp, P(rpa_cache_strides),
                                       P(rpa_cache_strides), vp, vp, vp]
     L.rpa_merge_state.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
+    L.rpa_page_copy.argtypes = [vp, P(rpa_cache_strides), vp, vp, P(rpa_cache_strides), vp, i32,
+                                i32, i32, i32, i32, i32, i32, vp]
     L.rpa_plan_destroy.argtypes = [vp]
     L.rpa_plan_destroy.restype = None
     L.rpa_status_string.argtypes = [i32]
@@ -270,6 +273,31 @@ def rpa_merge_state(o_a, lse_a, o_b, lse_b, o, lse, rows: int, heads: int, dim: 
     _check(lib().rpa_merge_state(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o),
                                  _ptr(lse), int(rows), int(heads), int(dim), int(dtype),
                                  _stream(stream)))
+
+
+def rpa_page_copy(src, src_strides: rpa_cache_strides, src_pages, dst,
+                  dst_strides: rpa_cache_strides, dst_pages, num_pages: int, src_head0: int,
+                  dst_head0: int, num_heads: int, page_size: int, dim: int, dtype: int,
+                  stream=None):
+    """Raw copy of head ranges of pages (page id arrays are device tensors or None)."""
+    _check(lib().rpa_page_copy(_ptr(src), ctypes.byref(src_strides), _ptr(src_pages), _ptr(dst),
+                               ctypes.byref(dst_strides), _ptr(dst_pages), int(num_pages),
+                               int(src_head0), int(dst_head0), int(num_heads), int(page_size),
+                               int(dim), int(dtype), _stream(stream)))
+
+
+def copy_pages(src, dst, src_pages=None, dst_pages=None, src_head0=0, dst_head0=0,
+               num_heads=None, stream=None):
+    """Copy head ranges of pages between two 4-D views [pages, heads, slots, dim]
+    (any strides, e.g. an HND pool, or an NHD buffer permuted to that order).
+    Page id lists are device int32 tensors (or None for 0, 1, ...)."""
+    import torch
+    n = int(src_pages.numel()) if src_pages is not None else (
+        int(dst_pages.numel()) if dst_pages is not None else int(src.shape[0]))
+    heads = int(num_heads if num_heads is not None else src.shape[1] - src_head0)
+    dtype = RPA_DTYPE_BF16 if src.dtype == torch.bfloat16 else RPA_DTYPE_F32
+    rpa_page_copy(src, strides_of(src), src_pages, dst, strides_of(dst), dst_pages, n, src_head0,
+                  dst_head0, heads, int(src.shape[2]), int(src.shape[3]), dtype, stream)
 
 
 def rpa_plan_destroy(plan: _PlanHandle):

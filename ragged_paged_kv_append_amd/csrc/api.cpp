@@ -385,6 +385,44 @@ RPA_EXPORT rpa_status rpa_merge_state(const void* o_a, const float* lse_a, const
   return RPA_OK;
 }
 
+RPA_EXPORT rpa_status rpa_page_copy(const void* src, const rpa_cache_strides* src_strides,
+                                    const int32_t* src_pages, void* dst,
+                                    const rpa_cache_strides* dst_strides,
+                                    const int32_t* dst_pages, int32_t num_pages,
+                                    int32_t src_head0, int32_t dst_head0, int32_t num_heads,
+                                    int32_t page_size, int32_t dim, int32_t dtype, void* stream) {
+  if (dtype != RPA_DTYPE_F32 && dtype != RPA_DTYPE_BF16)
+    return fail(RPA_ERR_INVALID_ARG, "dtype must be RPA_DTYPE_F32 or RPA_DTYPE_BF16");
+  if (num_pages < 0 || num_heads <= 0 || page_size <= 0 || dim <= 0 || src_head0 < 0 ||
+      dst_head0 < 0)
+    return fail(RPA_ERR_INVALID_ARG, "bad num_pages, heads, page_size or dim");
+  const int32_t vec = dtype == RPA_DTYPE_BF16 ? 8 : 4;
+  if (dim % vec) return fail(RPA_ERR_INVALID_ARG, "dim must fill whole 16-byte chunks");
+  if (num_pages == 0) return RPA_OK;
+  if (!src || !dst) return fail(RPA_ERR_INVALID_ARG, "null src or dst");
+  if (!aligned(src, 16) || !aligned(dst, 16))
+    return fail(RPA_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  if ((src_pages && !aligned(src_pages, 4)) || (dst_pages && !aligned(dst_pages, 4)))
+    return fail(RPA_ERR_INVALID_ARG, "page id arrays must be 4-byte aligned");
+  std::string why;
+  if (!strides_ok(src_strides, dim, dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "src: " + why);
+  if (!strides_ok(dst_strides, dim, dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "dst: " + why);
+  const int64_t es = dtype == RPA_DTYPE_BF16 ? 2 : 4;
+  if ((int64_t)num_heads * page_size * (dim * es / 16) > INT32_MAX)
+    return fail(RPA_ERR_INVALID_ARG, "page too large");
+  const rpa::Strides sb{src_strides->page_stride * es, src_strides->head_stride * es,
+                        src_strides->token_stride * es};
+  const rpa::Strides db{dst_strides->page_stride * es, dst_strides->head_stride * es,
+                        dst_strides->token_stride * es};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("page_copy", st, [&] {
+    return rpa::launch_page_copy(src, sb, src_pages, dst, db, dst_pages, num_pages, src_head0,
+                                 dst_head0, num_heads, page_size, (int32_t)(dim * es), st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "page_copy launch");
+  return RPA_OK;
+}
+
 RPA_EXPORT rpa_status rpa_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lock(g_prof_mu);
   g_prof_on = on != 0;

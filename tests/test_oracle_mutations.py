@@ -43,6 +43,10 @@ MUTATIONS = {
                              "among_new = np.asarray(tree[r], dtype=bool).T"),
     "tree_hides_cache": ("visible = np.concatenate([np.ones((n, c), dtype=bool), among_new], axis=1)",
                          "visible = np.concatenate([np.zeros((n, c), dtype=bool), among_new], axis=1)"),
+    "copy_pages_wrong_head_offset": (
+        "out[dp, dst_head0:dst_head0 + num_heads] = src[sp, src_head0:src_head0 + num_heads]",
+        "out[dp, dst_head0:dst_head0 + num_heads] = src[sp, dst_head0:dst_head0 + num_heads]"),
+    "nhd_wrong_axes": ("np.swapaxes(pages, 1, 2)", "np.swapaxes(pages, 2, 3)"),
     "bf16_truncates": ("rounded = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)",
                        "rounded = u >> np.uint64(16)"),
 }
@@ -82,6 +86,8 @@ def _pin_calls(golden):
         pins.test_p8_accounting_counts_visible_pairs,
         lambda: pins.test_p9_io_worked_example(golden),
         pins.test_pt_tree_mask_matches_torch_sdpa,
+        pins.test_pc_copy_pages_element_loop_and_untouched_bytes,
+        pins.test_pc_half_shards_rebuild_full_pages_and_nhd_is_a_transpose,
         lambda: pins.test_p2s_split_execution_equals_attention_after_append(
             [1, 16, 0, 5], [37, 36, 4, 5], 4, 2, 16),
     ]

@@ -21,6 +21,11 @@ Each test names the pin it implements:
   P2s split execution (cache part over the pages before the append, chunk
      part over the new keys, merged) == attention after the append, and == the
      torch SDPA reference over the concatenated keys.
+  PC page copies: an element loop over (page, head, slot, dim) with its own
+     index arithmetic; two half-head shards rebuild the full pages; NHD is the
+     slot/head transpose (element loop); nothing outside the target changes;
+     copying a shared partly filled prefix page before two requests append
+     gives the attention of private copies (torch SDPA reference).
   PT tree masks among the new tokens: a chain mask == causal attention; any
      mask == torch SDPA with the test's own boolean mask; relabeling the draft
      nodes permutes the outputs.
@@ -661,3 +666,80 @@ def test_pt_relabeling_draft_nodes_permutes_outputs():
         outs.append(oracle.attend(qq, kp, vp, b, hq, hkv, 0.5, tree=[mm]))
     np.testing.assert_allclose(outs[1][0], outs[0][0][inv], rtol=0, atol=1e-13)
     np.testing.assert_allclose(outs[1][1], outs[0][1][inv], rtol=0, atol=1e-13)
+
+
+
+# ----------------------------------------------------------------------------
+# PC: page copies
+# ----------------------------------------------------------------------------
+
+
+def test_pc_copy_pages_element_loop_and_untouched_bytes():
+    rng = np.random.default_rng(51)
+    src = rng.standard_normal((7, 4, 8, 6))
+    dst = np.full((9, 4, 8, 6), np.nan)
+    sp, dp = [3, 0, 6], [8, 2, 5]
+    out = oracle.copy_pages(src, dst, sp, dp, 1, 2, 2)
+    want = dst.copy()
+    for i in range(3):
+        for hh in range(2):
+            for sl in range(8):
+                for e in range(6):
+                    want[dp[i], 2 + hh, sl, e] = src[sp[i], 1 + hh, sl, e]
+    np.testing.assert_array_equal(out, want)
+    assert np.isnan(out[[0, 1, 3, 4, 6, 7]]).all()
+    assert np.isnan(out[dp][:, [0, 1]]).all()
+
+
+def test_pc_half_shards_rebuild_full_pages_and_nhd_is_a_transpose():
+    rng = np.random.default_rng(52)
+    H, P, d = 8, 16, 4
+    pool = rng.standard_normal((20, H, P, d))
+    pages = rng.permutation(20)[:6]
+    ident = np.arange(6)
+    lo = oracle.copy_pages(pool, np.zeros((6, H // 2, P, d)), pages, ident, 0, 0, H // 2)
+    hi = oracle.copy_pages(pool, np.zeros((6, H // 2, P, d)), pages, ident, H // 2, 0, H // 2)
+    rebuilt = np.full((30, H, P, d), np.nan)
+    dst_pages = rng.permutation(30)[:6]
+    rebuilt = oracle.copy_pages(lo, rebuilt, ident, dst_pages, 0, 0, H // 2)
+    rebuilt = oracle.copy_pages(hi, rebuilt, ident, dst_pages, 0, H // 2, H // 2)
+    np.testing.assert_array_equal(rebuilt[dst_pages], pool[pages])
+    nhd = oracle.hnd_to_nhd(pool[pages])
+    for i in range(6):
+        for sl in range(P):
+            for h in range(H):
+                np.testing.assert_array_equal(nhd[i, sl, h], pool[pages[i], h, sl])
+
+
+def test_pc_copy_shared_tail_page_then_append_matches_private_copies():
+    # Two requests share a 40-token prefix over pages of 16: pages 0, 1 are
+    # full and shared read-only; the tail page (8 tokens) is copied for the
+    # second request before both append their own tokens.
+    rng = np.random.default_rng(53)
+    H, P, d, hq = 2, 16, 8, 4
+    prefix_k = rng.standard_normal((40, H, d))
+    prefix_v = rng.standard_normal((40, H, d))
+    own = [rng.standard_normal((n, H, d)) for n in (5, 12)]
+    own_v = [rng.standard_normal((n, H, d)) for n in (5, 12)]
+    kp, indptr, indices = place([prefix_k], P, H, d, np.random.default_rng(3), slack=4)
+    vp, _, _ = place([prefix_v], P, H, d, np.random.default_rng(3), slack=4)
+    shared = [int(x) for x in indices]            # 3 pages
+    free = [x for x in range(kp.shape[0]) if x not in shared]
+    tail_copy = free[0]
+    kp = oracle.copy_pages(kp, kp, [shared[2]], [tail_copy], 0, 0, H)
+    vp = oracle.copy_pages(vp, vp, [shared[2]], [tail_copy], 0, 0, H)
+    extra = free[1:3]                             # the second request grows past its tail
+    tables = [shared, shared[:2] + [tail_copy, extra[0]]]
+    batch = Batch([0, 5, 17], [45, 52], [0, 3, 7], tables[0] + tables[1], P)
+    k_new = np.concatenate(own)
+    v_new = np.concatenate(own_v)
+    kp2, vp2 = oracle.append(kp, vp, k_new, v_new, batch)
+    q = rng.standard_normal((17, hq, d))
+    o, lse = oracle.attend(q, kp2, vp2, batch, hq, H, 0.35)
+    seqs_k = [np.concatenate([prefix_k, own[0]]), np.concatenate([prefix_k, own[1]])]
+    seqs_v = [np.concatenate([prefix_v, own_v[0]]), np.concatenate([prefix_v, own_v[1]])]
+    o_t, l_t = torch_reference(q, seqs_k, seqs_v, [5, 12], [45, 52], hq, H, 0.35)
+    np.testing.assert_allclose(o, o_t, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l_t, rtol=0, atol=1e-12)
+    # the shared full pages are unchanged by either append
+    np.testing.assert_array_equal(kp2[shared[:2]], kp[shared[:2]])
