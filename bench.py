@@ -480,6 +480,33 @@ def main():
                                 "slowdown_vs_chain": attn_ms / base_ms,
                                 "tree_parents": [-1, 0, 0, 1]}
 
+    if name == "decode_verify_gqa":
+        # page export for a sharded transfer: the K and V pages of the first 64
+        # requests, each as two half-head shards, gathered from the HND pools
+        # into packed shard buffers (one contiguous run per page and shard)
+        reqs = list(range(64))
+        pages = np.concatenate([meta.kv_page_indices[meta.kv_page_indptr[r]:
+                                                     meta.kv_page_indptr[r + 1]] for r in reqs])
+        pid = torch.as_tensor(pages.astype(np.int32), device="cuda")
+        H = spec.num_kv_heads
+        bufs = [torch.empty((len(pages), H // 2, spec.page_size, spec.head_dim_qk),
+                            dtype=tensors["k_pool"].dtype, device="cuda") for _ in range(4)]
+
+        def export_step():
+            for j, pool in enumerate((tensors["k_pool"], tensors["v_pool"])):
+                for s_ in range(2):
+                    rpa.copy_pages(pool, bufs[2 * j + s_], src_pages=pid,
+                                   src_head0=s_ * (H // 2), num_heads=H // 2)
+        log(f"part page_export: {len(pages)} pages x 2 pools x 2 shards")
+        ems, ek = timed_steps(export_step, args.steps, args.warmup)
+        copied = 2 * len(pages) * H * spec.page_size * spec.head_dim_qk * spec.elem_bytes
+        cms = ek["page_copy"][0] * ek["page_copy"][1]
+        parts["page_export"] = {"pages": int(len(pages)), "bytes_copied": copied,
+                                "ms_per_step": ems, "kernel_ms": cms,
+                                "hbm_gbps": 2 * copied / (cms * 1e-3) / 1e9,
+                                "hbm_frac": 2 * copied / (cms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                "launches": ek["page_copy"][1]}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on a bounded sample")
