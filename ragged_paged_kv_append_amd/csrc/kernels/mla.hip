@@ -59,17 +59,6 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Blocking scalar load of one page id; the address is wave-uniform.
-__device__ __forceinline__ int32_t load_scalar(const int32_t* ptr) {
-  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const int32_t* sp = reinterpret_cast<const int32_t*>(lo | (hi << 32));
-  int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sp) : "memory");
-  return v;
-}
-
 // One global-to-LDS DMA instruction (gfx950 global_load_lds_dwordx4): every
 // lane copies 16 bytes from `src` to LDS byte address lds + 16 * lane.  It is
 // issued from inline assembly so that the compiler does not track it: left to
@@ -123,6 +112,9 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
   __shared__ float alds[1][kRows];   // per-row rescale factor of the tile's P
   __shared__ float mlds[kRows];      // final row max (log2 units)
   __shared__ float llds[kRows];      // final row sum
+  // Page ids of the current item's keys (the planner keeps an item within
+  // MLA_MAX_KEYS keys, i.e. at most MLA_MAX_KEYS / 16 pages).
+  __shared__ int32_t pglds[MLA_MAX_KEYS / 16];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)ring;
@@ -167,28 +159,51 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
 
     const int32_t* pages = p.page_indices + p.page_indptr[r];
     const char* kvb = reinterpret_cast<const char*>(kvc + (int64_t)g * ks.head);
+    // The item's page ids go to LDS once (coalesced), so a tile's DMA looks
+    // them up there instead of waiting on a scalar load per tile.
+    const int32_t pg0 = k0 >> p.page_shift;
+    const int32_t npg = ((max(k1, k0 + 1) - 1) >> p.page_shift) - pg0 + 1;
     // DMA of the tile at key kb into ring slot `slot`.  Keys past k1 are
     // fetched from the item's last key (finite values; they are masked).  A
     // tile spans at most two pages (page size >= 16, tiles 32-aligned).
-    auto issue = [&](int32_t kb, int slot) __attribute__((always_inline)) {
+    // Row addresses are formed from two wave-uniform bases (keys kb and
+    // kb + 16: the second half of a tile is in the same page for page sizes
+    // >= 32, in the next one for 16) plus a 32-bit per-lane offset.
+    struct DmaPlan {
+      const char* base_a;
+      const char* base_b;
+      uint32_t rlim;  // last row of the tile that exists
+      uint32_t lds;   // LDS byte address of the ring slot
+    };
+    auto dma_plan = [&](int32_t kb, int slot) __attribute__((always_inline)) {
       const int32_t klast = k1 - 1;
-      const int32_t pa = load_scalar(pages + (min(kb, klast) >> p.page_shift));
-      const int32_t pb = load_scalar(pages + (min(kb + 16, klast) >> p.page_shift));
-      const int32_t page_a = min(kb, klast) >> p.page_shift;
-      const int ln = opaque_lane(lane);
+      const int32_t pa = __builtin_amdgcn_readfirstlane(
+          pglds[(min(kb, klast) >> p.page_shift) - pg0]);
+      const int32_t pb = __builtin_amdgcn_readfirstlane(
+          pglds[(min(kb + 16, klast) >> p.page_shift) - pg0]);
+      DmaPlan d;
+      d.base_a = kvb + 2 * ((int64_t)pa * ks.page + (int64_t)(kb & (p.page_size - 1)) * ks.token);
+      d.base_b =
+          kvb + 2 * ((int64_t)pb * ks.page + (int64_t)((kb + 16) & (p.page_size - 1)) * ks.token);
+      d.rlim = (uint32_t)(klast - kb);
+      d.lds = ring_lds + slot * kTileBytes;
+      return d;
+    };
+    // DMA instruction x (of this wave's n_dma) of a tile.
+    auto dma_one = [&](const DmaPlan& d, int x) __attribute__((always_inline)) {
+      const uint32_t tok2 = 2u * (uint32_t)ks.token;
+      const uint32_t c = 64u * (wave + kWaves * x) + (uint32_t)opaque_lane(lane);  // < 2304
+      const uint32_t kr = c / kChunks, cc = c - kr * kChunks;
+      const uint32_t kq = min(kr, d.rlim);  // rows past the last key repeat it
+      const uint32_t off = (kq & 15u) * tok2 + 16u * (cc ^ (kr & 7u));
+      dma16((kq >= 16u ? d.base_b : d.base_a) + off,
+            __builtin_amdgcn_readfirstlane(d.lds + 1024 * (wave + kWaves * x)));
+    };
+    auto issue = [&](int32_t kb, int slot) __attribute__((always_inline)) {
+      const DmaPlan d = dma_plan(kb, slot);
 #pragma unroll
-      for (int x = 0; x < 5; ++x) {
-        if (x < n_dma) {
-          const int c = 64 * (wave + kWaves * x) + ln;
-          const int kr = c / kChunks, cc = c - kr * kChunks;
-          const int32_t key = min(kb + kr, klast);
-          const int64_t page = (key >> p.page_shift) == page_a ? pa : pb;
-          const char* src = kvb + (page * ks.page + (int64_t)(key & (p.page_size - 1)) * ks.token) * 2 +
-                            16 * (cc ^ (kr & 7));
-          dma16(src, __builtin_amdgcn_readfirstlane(ring_lds + slot * kTileBytes +
-                                                    1024 * (wave + kWaves * x)));
-        }
-      }
+      for (int x = 0; x < 5; ++x)
+        if (x < n_dma) dma_one(d, x);
     };
 
     // S-phase rows of this wave.
@@ -211,7 +226,10 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[nb][rb][i] = 0.f;
 
-    barrier();  // the previous item's waves are done with the ring and the P area
+    barrier();  // the previous item's waves are done with the ring, P area and page table
+    for (int32_t i = tid; i < npg; i += 64 * kWaves) pglds[i] = pages[pg0 + i];
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    barrier();  // the page table is in LDS
     if (ntiles > 0) issue(k0, 0);
     if (ntiles > 1) issue(k0 + kKT, 1);
 
@@ -229,12 +247,22 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
 
     // S phase of the tile at key kb in `slot`: P and rescale factors into
     // P buffer `pbuf`.
-    auto s_phase = [&](int32_t kb, int slot, int pbuf) __attribute__((always_inline)) {
+    // With dma, this wave's DMA instructions of the tile at dkb (ring slot
+    // dslot) are spread over the products, one after every second step.
+    auto s_phase = [&](int32_t kb, int slot, int pbuf, bool dma, int32_t dkb, int dslot)
+        __attribute__((always_inline)) {
       const bool active = s_active_wave && kb < kend_wmax;
       f32x4_t sacc[2];  // sacc[b][i] = S^T[key kb + 16 b + 4 sgrp + i][row scol]
 #pragma unroll
       for (int b = 0; b < 2; ++b) sacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       float alpha = 1.f;
+      DmaPlan dp{};
+      if (dma) dp = dma_plan(dkb, dslot);
+      if (!active && dma) {
+#pragma unroll
+        for (int x = 0; x < 5; ++x)
+          if (x < n_dma) dma_one(dp, x);
+      }
       if (active) {
         const char* kt = reinterpret_cast<const char*>(&ring[slot][0]);
 #pragma unroll
@@ -246,6 +274,7 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
             sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qf[j]),
                                                               sacc[b], 0, 0, 0);
           }
+          if ((j & 1) && dma && (j >> 1) < n_dma) dma_one(dp, j >> 1);
           // Keep the compiler from hoisting all 36 K-operand reads: registers
           // are fully used by Q and the O accumulators.
           if (j & 1) __builtin_amdgcn_sched_barrier(0);
@@ -351,8 +380,8 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
         wait_vmem<0>();
       }
       barrier();
-      if (tile + 2 < ntiles) issue(k0 + (tile + 2) * kKT, slot == 0 ? kSlots - 1 : slot - 1);
-      s_phase(k0 + tile * kKT, slot, 0);
+      s_phase(k0 + tile * kKT, slot, 0, tile + 2 < ntiles, k0 + (tile + 2) * kKT,
+              slot == 0 ? kSlots - 1 : slot - 1);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's P is in LDS
       barrier();
       pv_phase(slot, 0);

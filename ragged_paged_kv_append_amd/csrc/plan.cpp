@@ -288,6 +288,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
       } else {
         S = ceil_div(L, tile_piece[cls[r]]);
         if (cls[r] == KC_PREFILL) S = std::max<int64_t>(S, ceil_div(L, PRE_MAX_KEYS));
+        if (cls[r] == KC_MLA) S = std::max<int64_t>(S, ceil_div(L, MLA_MAX_KEYS));
       }
       S = std::max<int64_t>(S, 1);
       kc = round_up(ceil_div(L, S), KEY_ALIGN);

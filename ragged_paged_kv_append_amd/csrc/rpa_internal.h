@@ -36,6 +36,7 @@ constexpr int GEN_ROWS = 4;        // rows per generic item (one wave each)
 constexpr int DEC_MAX_ROWS = 16;   // rows per decode item (one MFMA column block)
 constexpr int PRE_ROWS = 256;      // rows per prefill item
 constexpr int PRE_MAX_KEYS = 8192; // keys per prefill item (128 tiles: two page-id registers)
+constexpr int MLA_MAX_KEYS = 32768; // keys per latent item (its page ids fit an LDS table)
 constexpr int TREE_MAX_NEW = 64;   // new tokens of a request with a tree mask (one 64-bit row)
 constexpr int MLA_ROWS = 128;      // rows per latent-attention item
 constexpr int KEY_ALIGN = 64;      // split pieces start at multiples of this
