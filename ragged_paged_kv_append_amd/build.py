@@ -34,7 +34,10 @@ DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-p
 # its row maxima then need no NaN-quieting operand copies (no NaN reaches them:
 # masked keys carry a large negative finite value and unused key slots are
 # filled from a valid key).
-FILE_FLAGS = {"prefill.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+FILE_FLAGS = {
+    "prefill.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+    "mla.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+}
 
 
 def sources():

@@ -8,24 +8,28 @@
 // speculation"), each latent row is used by 256 query rows: the work is bound
 // by the matrix cores, not by HBM.
 //
-// One workgroup of eight wavefronts (two per SIMD) takes a work item of up
-// to 128 query rows (row = token * G + head) and a key range; the planner
-// packs the items onto one resident workgroup per compute unit, longest
-// first.  Keys stream
-// in tiles of 32 latent rows (36 KiB) through a three-slot LDS ring fed by the
-// gfx950 global-to-LDS DMA (the next two tiles land while the current one is
-// computed), each tile read from HBM once per item and used for both
-// products.  In a latent row, 16-byte chunk c sits at position
-// c ^ (row % 8), which keeps both LDS read patterns below conflict free.
+// One workgroup of four wavefronts (one per SIMD, so each wave has the whole
+// 512-entry register file: Q of its rows in VGPRs, its O accumulators in
+// AGPRs) takes a work item of up to 128 query rows (row = token * G + head)
+// and a key range; the planner packs the items onto one resident workgroup
+// per compute unit, longest first.  Keys stream in tiles of 32 latent rows
+// through a two-slot LDS ring fed by the gfx950 global-to-LDS DMA (the next
+// tile lands while the current one is computed), each tile read from HBM
+// once per item and used for both products.  A latent row takes 73 chunks of
+// 16 bytes in LDS (72 of data and one of padding), which keeps the K-operand
+// reads (16 rows, one chunk each) and the transposing V reads conflict free.
 //
 // Per tile j:
-//   S phase: wave w computes S^T for rows 16 w .. 16 w + 15 over the tile
-//     (mfma 16x16x32 bf16, 18 steps over the 576 dims, Q of its rows resident
-//     in registers), runs the online softmax for those rows and writes P (bf16)
-//     and the per-row rescale factors into LDS;
-//   PV phase: wave w owns value dims 64 w .. 64 w + 63 of all 128 rows and
+//   S phase: wave w computes S^T for rows 32 w .. 32 w + 31 over the tile as
+//     four independent 16x16 blocks (mfma 16x16x32 bf16, 18 steps over the
+//     576 dims, K operands read three steps ahead), runs the online softmax
+//     for those rows and writes P (bf16) and the per-row rescale factors into
+//     LDS;
+//   PV phase: wave w owns value dims 128 w .. 128 w + 127 of all 128 rows and
 //     accumulates O^T[d][row] += V^T[d][key] P^T[key][row] (mfma 32x32x16
 //     bf16), V^T read from the latent tile with the transposing LDS read.
+// Each wave's share of the DMA of tile j + 1 is issued one instruction at a
+// time between the first S products.
 // A barrier separates the phases, and one more starts each tile.
 
 #include "common.h"
@@ -38,19 +42,22 @@ namespace {
 constexpr int kDQK = 576;
 constexpr int kDV = 512;
 constexpr int kRows = 128;       // query rows per item
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kKT = 32;          // keys per tile
-constexpr int kRowBytes = kDQK * 2;            // 1152
-constexpr int kChunks = kDQK / 8;              // 72 chunks of 16 bytes per latent row
-constexpr int kTileBytes = kKT * kRowBytes;    // 36864
-constexpr int kSlots = 3;
-constexpr int kDmaInst = kTileBytes / 1024;    // 36 DMA instructions of 1 KiB per tile
+constexpr int kChunks = kDQK / 8;              // 72 data chunks of 16 bytes per latent row
+constexpr int kRowChunks = kChunks + 1;        // 73 with the padding chunk
+constexpr int kRowBytes = 16 * kRowChunks;     // 1168
+constexpr int kDmaInst = (kKT * kRowChunks + 63) / 64;  // 37 DMA instructions of 1 KiB per tile
+constexpr int kTileBytes = 1024 * kDmaInst;    // 37888 (the last instruction's tail is slack)
+constexpr int kSlots = 2;
+constexpr int kSteps = kDQK / 32;              // 18 steps of 32 dims per S tile
+constexpr int kAhead = 3;                      // steps of K-operand reads in flight
 constexpr int kPRow = 36;                      // P row stride in LDS (bf16): 72 bytes
-constexpr int kPBytes = kRows * kPRow * 2;     // 9216
 constexpr float kMinusBig = -1.0e30f;
-constexpr float kRescaleSlack = 8.f;           // log2 units
-
-typedef __attribute__((address_space(3))) const bf16_t* lds_cptr_t;
+// A row's reference max only moves when a tile beats it by more than this
+// (log2 units); P then stays below 2^64 and O below 2^79 |V|max (keys per item
+// <= 2^15), far inside fp32 range.
+constexpr float kRestartSlack = 64.f;
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -65,12 +72,14 @@ __device__ __forceinline__ void wait_vmem() {
 // itself the compiler makes every later LDS read wait for all DMA in flight,
 // while the kernel waits for exactly the tile it needs (explicit vmcnt counts,
 // which operations the compiler adds can only make stricter).  M0, which
-// carries the LDS address, is saved and restored around the instruction.
+// carries the LDS address, is saved and restored around the instruction; the
+// DMA reads M0 one wait state after the write that sets it.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -78,9 +87,27 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
       : "memory");
 }
 
+// The same DMA with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// offset (the saddr form: no per-lane address arithmetic).  The base usually
+// comes straight from v_readfirstlane, and a memory instruction reads an SGPR
+// that a VALU instruction wrote only five wait states later: s_nop 4 first.
+__device__ __forceinline__ void dma16_base(const void* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+
 // Two transposing reads (low and high key halves, + 8 rows) at one address,
-// with their own LDS wait (see the decode kernel: the compiler would
-// otherwise drain the DMA stream before them).
+// with their own LDS wait (the compiler would otherwise drain the DMA stream
+// before them).
 __device__ __forceinline__ void read_vt2(uint32_t a, s16x4_t& lo, s16x4_t& hi) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %2\n\t"
@@ -93,56 +120,73 @@ __device__ __forceinline__ void read_vt2(uint32_t a, s16x4_t& lo, s16x4_t& hi) {
 
 // The lane index as a value the compiler cannot see through: addresses
 // derived from it are recomputed where they are used instead of being hoisted
-// out of the tile loop (registers are fully used by Q and the O accumulators,
-// and hoisted values would be spilled to scratch, whose reloads would also
-// wait for the DMA stream).
+// out of the tile loop and kept in registers for the whole item.
 __device__ __forceinline__ int opaque_lane(int lane) {
   asm volatile("" : "+v"(lane));
   return lane;
 }
 
+// The S products are issued from inline assembly so that their accumulators
+// stay in VGPRs (the compiler puts every matrix-core result of a kernel that
+// uses AGPRs into AGPRs, and the O accumulators already fill them).  A chain
+// of products on one accumulator needs no wait states between its links;
+// s_wait_products covers the results' latency before any other instruction
+// touches the accumulators.
+__device__ __forceinline__ void mfma16_first(f32x4_t& d, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16(f32x4_t& d, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void s_wait_products(f32x4_t (&acc)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+}
+
 }  // namespace
 
-__global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __restrict__ q,
-                                                     const bf16_t* __restrict__ kvc, Strides ks,
-                                                     bf16_t* __restrict__ o,
-                                                     float* __restrict__ lse) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_kernel(
+    DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kvc, Strides ks,
+    bf16_t* __restrict__ o, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots][kTileBytes];
-  __shared__ __attribute__((aligned(16))) bf16_t plds[1][kRows * kPRow];
-  __shared__ float alds[1][kRows];   // per-row rescale factor of the tile's P
-  __shared__ float mlds[kRows];      // final row max (log2 units)
-  __shared__ float llds[kRows];      // final row sum
+  __shared__ __attribute__((aligned(16))) bf16_t plds[kRows * kPRow];
+  __shared__ int32_t restart;     // set when a tile moved a row's reference max
+  __shared__ float llds[kRows];   // final row sum
   // Page ids of the current item's keys (the planner keeps an item within
   // MLA_MAX_KEYS keys, i.e. at most MLA_MAX_KEYS / 16 pages).
   __shared__ int32_t pglds[MLA_MAX_KEYS / 16];
+  // Per-thread byte offsets (from the tile's first key) of this thread's DMA
+  // chunks, x = 0..9, for a tile of 32 keys in one page.
+  __shared__ uint32_t doff[10][64 * kWaves];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)ring;
 
-  // ---- S-phase role: rows 16 wave + scol ------------------------------------------
-  const int scol = lane & 15, sgrp = lane >> 4;
-  // K operand of step j (dims 32 j .. 32 j + 31) for key row scol of a
-  // 16-key block: chunk 4 j + sgrp, at position (4 j + sgrp) ^ (scol % 8).
-  // With j = 2 m + jj that is 8 m + ((4 jj + sgrp) ^ (scol % 8)).
-  uint32_t k_rd[2];
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
-    k_rd[jj] = scol * kRowBytes + 16 * ((4 * jj + sgrp) ^ (scol & 7));
-  // ---- PV-phase role: value dims 64 wave .. + 63, all rows ------------------------
+  // ---- S-phase role: rows 32 wave + 16 rb + kq, keys 16 kb + 4 kg + i -------------
+  const int kq = lane & 15, kg = lane >> 4;
+  // ---- PV-phase role: value dims 128 wave .. + 127, all rows -----------------------
   const int pcol = lane & 31, phalf = lane >> 5;
-  const int tr_row = 4 * phalf + ((lane & 15) >> 2);  // (+ 8 for the high half)
-  // Element column of block nb: 64 wave + 32 nb + 16 (pcol / 16) + 4 (lane % 4);
-  // its chunk is 8 wave + 4 nb + tr_c.
-  const int tr_c = 2 * (pcol >> 4) + ((lane & 3) >> 1);
-  // ---- DMA role: instructions wave, wave + 8, ... of the tile's 36 -----------------
-  // Instruction d moves chunks 64 d .. 64 d + 63 of the tile (72 chunks per
-  // key row); lane L carries chunk 64 d + L into its LDS position, fetching
-  // the global chunk (position) ^ (row % 8).
-  const int n_dma = (kDmaInst - wave + kWaves - 1) / kWaves;  // 5 or 4
+  // ---- DMA role: instructions wave, wave + 4, ... of the tile's 37 -----------------
+  // Instruction d fills LDS chunk positions 64 d .. 64 d + 63 of the slot;
+  // position c is chunk c % 73 of key row c / 73 (chunk 72 is padding and
+  // takes a copy of chunk 71; positions past the 32 rows are slack).
+  const int n_dma = (kDmaInst - wave + kWaves - 1) / kWaves;  // 10 or 9
+  {
+    const uint32_t tok2 = 2u * (uint32_t)ks.token;
+#pragma unroll
+    for (int x = 0; x < 10; ++x) {
+      const uint32_t c = 64u * (wave + kWaves * x) + (uint32_t)lane;
+      const uint32_t kr = c / kRowChunks, cc = min(c - kr * kRowChunks, (uint32_t)kChunks - 1);
+      doff[x][tid] = kr < (uint32_t)kKT ? kr * tok2 + 16u * cc : 0u;
+    }
+  }
 
   const int32_t wb0 = p.wg_indptr[KC_MLA][blockIdx.x];
   const int32_t wb1 = p.wg_indptr[KC_MLA][blockIdx.x + 1];
-  for (int32_t idx = wb0; idx < wb1; ++idx) {
+  // References kept when an item starts over (see the tile loop).
+  float m_keep[2] = {kMinusBig, kMinusBig};
+  bool again = false;
+  for (int32_t idx = wb0; idx < wb1;) {
     const int32_t* it = p.items[KC_MLA] + (int64_t)idx * IT_WORDS;
     const int32_t r = it[IT_REQ], g = it[IT_KVHEAD], row0 = it[IT_ROW0], row1 = it[IT_ROW1];
     const int32_t k0 = it[IT_K0], k1 = it[IT_K1], s = it[IT_SPLIT];
@@ -165,10 +209,10 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
     const int32_t npg = ((max(k1, k0 + 1) - 1) >> p.page_shift) - pg0 + 1;
     // DMA of the tile at key kb into ring slot `slot`.  Keys past k1 are
     // fetched from the item's last key (finite values; they are masked).  A
-    // tile spans at most two pages (page size >= 16, tiles 32-aligned).
-    // Row addresses are formed from two wave-uniform bases (keys kb and
-    // kb + 16: the second half of a tile is in the same page for page sizes
-    // >= 32, in the next one for 16) plus a 32-bit per-lane offset.
+    // tile spans at most two pages (page size >= 16, tiles 32-aligned): row
+    // addresses are formed from two wave-uniform bases (keys kb and kb + 16:
+    // the second half of a tile is in the same page for page sizes >= 32, in
+    // the next one for 16) plus a 32-bit per-lane offset.
     struct DmaPlan {
       const char* base_a;
       const char* base_b;
@@ -192,35 +236,41 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
     // DMA instruction x (of this wave's n_dma) of a tile.
     auto dma_one = [&](const DmaPlan& d, int x) __attribute__((always_inline)) {
       const uint32_t tok2 = 2u * (uint32_t)ks.token;
-      const uint32_t c = 64u * (wave + kWaves * x) + (uint32_t)opaque_lane(lane);  // < 2304
-      const uint32_t kr = c / kChunks, cc = c - kr * kChunks;
-      const uint32_t kq = min(kr, d.rlim);  // rows past the last key repeat it
-      const uint32_t off = (kq & 15u) * tok2 + 16u * (cc ^ (kr & 7u));
+      const uint32_t c = 64u * (wave + kWaves * x) + (uint32_t)opaque_lane(lane);  // < 2368
+      const uint32_t kr = c / kRowChunks, cc = min(c - kr * kRowChunks, (uint32_t)kChunks - 1);
+      const uint32_t kq = min(kr, d.rlim);  // rows past the last key (or the slot) repeat it
+      const uint32_t off = (kq & 15u) * tok2 + 16u * cc;
       dma16((kq >= 16u ? d.base_b : d.base_a) + off,
             __builtin_amdgcn_readfirstlane(d.lds + 1024 * (wave + kWaves * x)));
     };
     auto issue = [&](int32_t kb, int slot) __attribute__((always_inline)) {
       const DmaPlan d = dma_plan(kb, slot);
 #pragma unroll
-      for (int x = 0; x < 5; ++x)
+      for (int x = 0; x < 10; ++x)
         if (x < n_dma) dma_one(d, x);
     };
 
-    // S-phase rows of this wave.
-    const int32_t srow = row0 + 16 * wave + scol;
-    const bool srow_ok = srow < row1;
-    const int32_t st = srow_ok ? srow / G : 0;
-    const int32_t sh = g * G + (srow_ok ? srow % G : 0);
-    const int32_t kend_row = srow_ok ? key_end(srow) : k0;
-    const bool s_active_wave = row0 + 16 * wave < row1;
-    const int32_t kend_wmin = s_active_wave ? key_end(row0 + 16 * wave) : k0;
-    const int32_t kend_wmax = s_active_wave ? key_end(min(row1, row0 + 16 * wave + 16) - 1) : k0;
-    const float sc = p.sm_scale * kLog2e;
-    float m = kMinusBig, lsum = 0.f;
-
-    f32x16_t oacc[2][4];  // [nb][rb]
+    // S-phase rows of this lane (rb = 0, 1).
+    int32_t st[2], sh[2], kend_row[2];
+    bool srow_ok[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int rb = 0; rb < 2; ++rb) {
+      const int32_t srow = row0 + 32 * wave + 16 * rb + kq;
+      srow_ok[rb] = srow < row1;
+      st[rb] = srow_ok[rb] ? srow / G : 0;
+      sh[rb] = g * G + (srow_ok[rb] ? srow % G : 0);
+      kend_row[rb] = srow_ok[rb] ? key_end(srow) : k0;
+    }
+    const bool s_active_wave = row0 + 32 * wave < row1;
+    const int32_t kend_wmin = s_active_wave ? key_end(row0 + 32 * wave) : k0;
+    const int32_t kend_wmax = s_active_wave ? key_end(min(row1, row0 + 32 * wave + 32) - 1) : k0;
+    const float sc = p.sm_scale * kLog2e;
+    float m[2] = {again ? m_keep[0] : kMinusBig, again ? m_keep[1] : kMinusBig};
+    float lsum[2] = {0.f, 0.f};
+
+    f32x16_t oacc[4][4];  // [nb][rb]: O^T[dims 128 wave + 32 nb ..][rows 32 rb ..]
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -228,180 +278,269 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
 
     barrier();  // the previous item's waves are done with the ring, P area and page table
     for (int32_t i = tid; i < npg; i += 64 * kWaves) pglds[i] = pages[pg0 + i];
+    if (tid == 0) restart = 0;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     barrier();  // the page table is in LDS
     if (ntiles > 0) issue(k0, 0);
-    if (ntiles > 1) issue(k0 + kKT, 1);
 
-    // Q operand: qf[j] = Q[srow][32 j + 8 sgrp .. + 8), loaded while the first
-    // tiles are in flight.
-    u32x4_t qf[kDQK / 32];
-    {
-      const bf16_t* qrow = q + ((int64_t)(q0 + st) * p.num_qo_heads + sh) * kDQK + 8 * sgrp;
+    // Q operand: qf[rb][j] = Q[row 32 wave + 16 rb + kq][32 j + 8 kg .. + 8),
+    // loaded while the first tiles are in flight.
+    u32x4_t qf[2][kSteps];
 #pragma unroll
-      for (int j = 0; j < kDQK / 32; ++j)
-        qf[j] = srow_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int rb = 0; rb < 2; ++rb) {
+      const bf16_t* qrow =
+          q + ((int64_t)(q0 + st[rb]) * p.num_qo_heads + sh[rb]) * kDQK + 8 * kg;
 #pragma unroll
-      for (int j = 0; j < kDQK / 32; ++j) asm volatile("" ::"v"(qf[j]));
+      for (int j = 0; j < kSteps; ++j)
+        qf[rb][j] = srow_ok[rb] ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * j)
+                                : u32x4_t{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int j = 0; j < kSteps; ++j) asm volatile("" ::"v"(qf[rb][j]));
 
-    // S phase of the tile at key kb in `slot`: P and rescale factors into
-    // P buffer `pbuf`.
-    // With dma, this wave's DMA instructions of the tile at dkb (ring slot
-    // dslot) are spread over the products, one after every second step.
-    auto s_phase = [&](int32_t kb, int slot, int pbuf, bool dma, int32_t dkb, int dslot)
-        __attribute__((always_inline)) {
-      const bool active = s_active_wave && kb < kend_wmax;
-      f32x4_t sacc[2];  // sacc[b][i] = S^T[key kb + 16 b + 4 sgrp + i][row scol]
-#pragma unroll
-      for (int b = 0; b < 2; ++b) sacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      float alpha = 1.f;
-      DmaPlan dp{};
-      if (dma) dp = dma_plan(dkb, dslot);
-      if (!active && dma) {
-#pragma unroll
-        for (int x = 0; x < 5; ++x)
-          if (x < n_dma) dma_one(dp, x);
+    // DMA of the next tile, one instruction after each of the first S steps.
+    // Issuing it stalls the wave while many transfers are outstanding, so the
+    // ring holds two slots and keeps one tile in flight, which covers the
+    // memory latency.  A tile of 32 existing keys in one page (page size
+    // >= 32) takes the table offsets and one SGPR base; other tiles clamp rows
+    // per lane.
+    bool dma_on = false, dma_fast = false;
+    int32_t dma_kb = 0;
+    int32_t dma_pid = 0;
+    uint32_t dma_off = 0, dma_lds = 0;
+    const char* dma_base = nullptr;
+    DmaPlan dma_dp{};
+    auto dma_begin = [&](bool on, int32_t kb, int slot) __attribute__((always_inline)) {
+      dma_on = on;
+      dma_kb = kb;
+      dma_fast = on && p.page_size >= 2 * 16 && kb + kKT <= k1;
+      if (on && !dma_fast) dma_dp = dma_plan(kb, slot);
+      if (dma_fast) {
+        dma_pid = pglds[(kb >> p.page_shift) - pg0];
+        dma_off = doff[0][tid];
       }
-      if (active) {
-        const char* kt = reinterpret_cast<const char*>(&ring[slot][0]);
-#pragma unroll
-        for (int j = 0; j < kDQK / 32; ++j) {
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kt + 16 * b * kRowBytes +
-                                                                k_rd[j & 1] + 128 * (j >> 1));
-            sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qf[j]),
-                                                              sacc[b], 0, 0, 0);
-          }
-          if ((j & 1) && dma && (j >> 1) < n_dma) dma_one(dp, j >> 1);
-          // Keep the compiler from hoisting all 36 K-operand reads: registers
-          // are fully used by Q and the O accumulators.
-          if (j & 1) __builtin_amdgcn_sched_barrier(0);
-        }
-        const bool full = kb + kKT <= kend_wmin;
-        float mx = kMinusBig;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = sacc[b][i];
-            if (!full) v = (kb + 16 * b + 4 * sgrp + i < kend_row) ? v : kMinusBig;
-            sacc[b][i] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mt = mx > 0.5f * kMinusBig ? mx * sc : kMinusBig;
-        if (mt > m + kRescaleSlack) {
-          alpha = __builtin_amdgcn_exp2f(m - mt);
-          lsum *= alpha;
-          m = mt;
-        }
-        const float neg_m = -m;
-        float psum = 0.f;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = sacc[b][i];
-            const float x =
-                v > 0.5f * kMinusBig ? __builtin_amdgcn_exp2f(__builtin_fmaf(v, sc, neg_m)) : 0.f;
-            sacc[b][i] = x;
-            psum += x;
-          }
-        lsum += psum;
+      dma_lds = ring_lds + slot * kTileBytes + 1024 * wave;
+    };
+    auto dma_x = [&](int x) __attribute__((always_inline)) {
+      if (!dma_on || x >= n_dma) return;
+      if (dma_fast) {
+        if (x == 0)
+          dma_base = kvb + 2 * ((int64_t)__builtin_amdgcn_readfirstlane(dma_pid) * ks.page +
+                                (int64_t)(dma_kb & (p.page_size - 1)) * ks.token);
+        // (readfirstlane returns int: widen through uint32_t, not by sign)
+        const uint64_t b = reinterpret_cast<uint64_t>(dma_base);
+        const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+        const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+        const uint64_t bu = ((uint64_t)b_hi << 32) | (uint64_t)b_lo;
+        dma16_base(reinterpret_cast<const void*>(bu), dma_off,
+                   __builtin_amdgcn_readfirstlane(dma_lds + 1024 * kWaves * x));
+        if (x + 1 < 10) dma_off = doff[x + 1][tid];
+      } else {
+        dma_one(dma_dp, x);
       }
-      // P[row][key 16 b + 4 sgrp + i] and the row's rescale factor.
-      bf16_t* prow = &plds[pbuf][(16 * wave + scol) * kPRow + 4 * sgrp];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        *reinterpret_cast<uint2*>(prow + 16 * b) =
-            make_uint2(pack_bf16x2(sacc[b][0], sacc[b][1]), pack_bf16x2(sacc[b][2], sacc[b][3]));
-      if (sgrp == 0) alds[pbuf][16 * wave + scol] = alpha;
     };
 
-    // PV phase of the tile in `slot` with P buffer `pbuf`.
-    auto pv_phase = [&](int slot, int pbuf) __attribute__((always_inline)) {
-      const int ln = opaque_lane(lane);
-      const int pcol = ln & 31, phalf = ln >> 5;
-      const int tr_row = 4 * phalf + ((ln & 15) >> 2);
-      const int tr_c = 2 * (pcol >> 4) + ((ln & 3) >> 1);
-      // Rescale the rows whose reference max was raised with this tile.
-      float a[4];
+    // S phase of the tile at key kb in `slot`, with this wave's DMA of the
+    // next tile between its first products.
+    auto s_phase = [&](int32_t kb, int slot) __attribute__((always_inline)) {
+      const bool active = s_active_wave && kb < kend_wmax;
+      // sacc[kb][rb][i] = S^T[key kb + 16 kb + 4 kg + i][row 16 rb + kq]
+      f32x4_t sacc[2][2];
+      bool moved = false;
+      if (!active) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) a[rb] = alds[pbuf][32 * rb + pcol];
-      if (__ballot(a[0] != 1.f || a[1] != 1.f || a[2] != 1.f || a[3] != 1.f)) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) oacc[nb][rb] *= a[rb];
+        for (int x = 0; x < 10; ++x) dma_x(x);
       }
-      const uint32_t slot_lds = ring_lds + slot * kTileBytes;
+      if (active) {
+        // K operand of step j, key block b: key 16 b + kq, chunk 4 j + kg.
+        const uint32_t krd = ring_lds + slot * kTileBytes +
+                             (uint32_t)(opaque_lane(lane) & 15) * kRowBytes + 16u * kg;
+        typedef __attribute__((address_space(3))) const u32x4_t* lds_u32x4_t;
+        auto kread = [&](int j, int b) __attribute__((always_inline)) {
+          return *reinterpret_cast<lds_u32x4_t>((uintptr_t)(krd + 16 * b * kRowBytes + 64 * j));
+        };
+        u32x4_t kbuf[kAhead][2];
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) kbuf[j][b] = kread(j, b);
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) {
+          const u32x4_t a0 = kbuf[j % kAhead][0], a1 = kbuf[j % kAhead][1];
+          if (j + kAhead < kSteps) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) kbuf[j % kAhead][b] = kread(j + kAhead, b);
+          }
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            if (j == 0) {
+              mfma16_first(sacc[0][rb], a0, qf[rb][0]);
+              mfma16_first(sacc[1][rb], a1, qf[rb][0]);
+            } else {
+              mfma16(sacc[0][rb], a0, qf[rb][j]);
+              mfma16(sacc[1][rb], a1, qf[rb][j]);
+            }
+          }
+          if (j < 10) dma_x(j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        s_wait_products(sacc);
+        if (kb + kKT > kend_wmin) {
+          asm volatile("" ::: "memory");  // a real (uniform) branch, not selects
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                sacc[b][rb][i] =
+                    (kb + 16 * b + 4 * kg + i < kend_row[rb]) ? sacc[b][rb][i] : kMinusBig;
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float mx = kMinusBig;
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[b][rb][i]);
+          mx = max_halves(max_rows16(mx));  // over the four lane groups kg
+          const float mt = mx > 0.5f * kMinusBig ? mx * sc : kMinusBig;
+          if (mt > m[rb] + kRestartSlack) {
+            // While the row has seen no key its O and sum are still zero:
+            // the first reference costs nothing.
+            if (m[rb] > 0.5f * kMinusBig) moved = true;
+            m[rb] = mt;
+          }
+          // Masked scores sit at kMinusBig: against a finite reference their
+          // exponent is hugely negative (P = 0); a row with no key yet takes
+          // reference 0 here, which gives the same.
+          const float neg_m = m[rb] > 0.5f * kMinusBig ? -m[rb] : 0.f;
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sacc[b][rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][rb][i], sc, neg_m));
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) sacc[b][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      // P[row][key 16 b + 4 kg + i] in bf16.  The row sums add the rounded
+      // values, the weights the PV products actually use, so that a row whose
+      // mass sits on one key returns that key's value row exactly.
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        bf16_t* prow = &plds[(32 * wave + 16 * rb + kq) * kPRow + 4 * kg];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const uint32_t u0 = pack_bf16x2(sacc[b][rb][0], sacc[b][rb][1]);
+          const uint32_t u1 = pack_bf16x2(sacc[b][rb][2], sacc[b][rb][3]);
+          *reinterpret_cast<uint2*>(prow + 16 * b) = make_uint2(u0, u1);
+          lsum[rb] = sum_bf16x2(u1, sum_bf16x2(u0, lsum[rb]));
+        }
+      }
+      if (moved) restart = 1;
+    };
+
+    // PV phase of the tile in `slot`.
+    // PV products of the tile in `slot`.
+    auto pv_phase = [&](int slot) __attribute__((always_inline)) {
+      const int ln = opaque_lane(lane);
+      const int pc = ln & 31, ph = ln >> 5;
+      // Transposing read: lane ln reads row 4 ph + (ln % 16) / 4 (+ 8 for the
+      // high half) of a 16-key block, 4 value dims at element column
+      // 32 nb + 16 (pc / 16) + 4 (ln % 4) of the wave's 128.
+      const int tr_row = 4 * ph + ((ln & 15) >> 2);
+      const uint32_t vt = ring_lds + slot * kTileBytes + (uint32_t)tr_row * kRowBytes +
+                          2u * (128 * wave + 16 * (pc >> 4) + 4 * (ln & 3));
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        u32x4_t va[2];
+        u32x4_t va[4];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          s16x4_t lo, hi;
-          const int R = 16 * kc + tr_row;
-          read_vt2(slot_lds + R * kRowBytes + 16 * ((8 * wave + 4 * nb + tr_c) ^ (R & 7)) +
-                       8 * (ln & 1),
-                   lo, hi);
+        for (int nb = 0; nb < 4; ++nb) {
+          const uint32_t a = vt + 16 * kc * kRowBytes + 64 * nb;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a);
+          const s16x4_t hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(a + 8 * kRowBytes));
           const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
           const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
           va[nb] = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
         }
-        // P^T operand of row block rb: row 32 rb + pcol, keys
-        // 16 kc + 8 (e / 4) + 4 phalf + e % 4.
+        // P^T operand of row block rb: row 32 rb + pc, keys
+        // 16 kc + 8 (e / 4) + 4 ph + e % 4.
+        u32x4_t pbv[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          const bf16_t* prow = &plds[pbuf][(32 * rb + pcol) * kPRow + 16 * kc + 4 * phalf];
+          const bf16_t* prow = &plds[(32 * rb + pc) * kPRow + 16 * kc + 4 * ph];
           const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(prow);
           const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(prow + 8);
-          const u32x4_t pbv = {lo[0], lo[1], hi[0], hi[1]};
+          pbv[rb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
+        for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
             oacc[nb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[nb]),
-                                                                   as_bf16x8(pbv), oacc[nb][rb],
+                                                                   as_bf16x8(pbv[rb]), oacc[nb][rb],
                                                                    0, 0, 0);
         }
       }
     };
 
-    // Step j: [wait for tile j] barrier [DMA of tile j + 2] [S of tile j]
+    // Step j: [wait for tile j] barrier [S of tile j, DMA of tile j + 1]
     // barrier [PV of tile j].  The first barrier publishes tile j and frees
     // the ring slot of tile j - 1 and the P area; the second publishes P.
-    // Two tiles (72 KiB) are in flight while one is computed.
-    for (int32_t tile = 0, slot = 0; tile < ntiles; ++tile, slot = (slot == kSlots - 1) ? 0 : slot + 1) {
-      if (tile + 1 < ntiles) {
-        if (n_dma == 5) wait_vmem<5>(); else wait_vmem<4>();  // tile j + 1 may be in flight
-      } else {
-        wait_vmem<0>();
-      }
+    //
+    // O is never rescaled: P is taken against a per-row reference that moves
+    // only when a tile beats it by more than kRestartSlack.  When that happens
+    // the whole workgroup finishes the pass and then does the item over with
+    // the new references (which no tile can beat again by that much).
+    // This keeps O touched by the matrix cores alone, in AGPRs.
+    bool restarted = false;
+    for (int32_t tile = 0, slot = 0; tile < ntiles;) {
+      wait_vmem<0>();  // this wave's share of tile j has landed
       barrier();
-      s_phase(k0 + tile * kKT, slot, 0, tile + 2 < ntiles, k0 + (tile + 2) * kKT,
-              slot == 0 ? kSlots - 1 : slot - 1);
+      dma_begin(tile + 1 < ntiles, k0 + (tile + 1) * kKT, slot ^ 1);
+      s_phase(k0 + tile * kKT, slot);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's P is in LDS
       barrier();
-      pv_phase(slot, 0);
+      restarted |= __builtin_amdgcn_readfirstlane(restart) != 0;
+      pv_phase(slot);
+      ++tile;
+      slot ^= 1;
     }
 
-    // Row statistics from the S-phase owners, then every wave stores its dims.
-    float ltot = lsum + __shfl_xor(lsum, 16, 64);
-    ltot += __shfl_xor(ltot, 32, 64);
-    if (sgrp == 0) {
-      mlds[16 * wave + scol] = m;
-      llds[16 * wave + scol] = ltot;
+    if (restarted) {
+      // The item start's barrier orders this behind every wave's DMA and
+      // read of the flag; the flag is cleared there.
+      m_keep[0] = m[0];
+      m_keep[1] = m[1];
+      again = true;
+      continue;
     }
+    again = false;
+    ++idx;
+
+    // Row statistics from the S-phase owners, then every wave stores its dims.
     const int32_t S = p.split[r * SP_WORDS + SP_COUNT];
-    if (sgrp == 0 && srow_ok) {
-      const float lse_nat = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
-      if (S == 1) {
-        if (lse) lse[(int64_t)(q0 + st) * p.num_qo_heads + sh] = lse_nat;
-      } else {
-        const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + st;
-        p.part_lse[prow * p.num_qo_heads + sh] = lse_nat;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float ltot = lsum[rb] + __shfl_xor(lsum[rb], 16, 64);
+      ltot += __shfl_xor(ltot, 32, 64);
+      if (kg == 0) llds[32 * wave + 16 * rb + kq] = ltot;
+      if (kg == 0 && srow_ok[rb]) {
+        const float lse_nat = ltot > 0.f ? (m[rb] + log2f(ltot)) * kLn2 : -INFINITY;
+        if (S == 1) {
+          if (lse) lse[(int64_t)(q0 + st[rb]) * p.num_qo_heads + sh[rb]] = lse_nat;
+        } else {
+          const int64_t prow =
+              (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + st[rb];
+          p.part_lse[prow * p.num_qo_heads + sh[rb]] = lse_nat;
+        }
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -414,13 +553,13 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
       const int32_t t = row / G, h = g * G + row % G;
       const float lt = llds[lrow];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      // Lane holds O^T[d][row] for d = 64 wave + 32 nb + 8 b + 4 phalf + j.
+      // Lane holds O^T[d][row] for d = 128 wave + 32 nb + 8 b + 4 phalf + j.
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < 4; ++nb) {
         const f32x16_t& acc = oacc[nb][rb];
         if (S == 1) {
-          bf16_t* orow = o + ((int64_t)(q0 + t) * p.num_qo_heads + h) * kDV + 64 * wave + 32 * nb +
-                         4 * phalf;
+          bf16_t* orow = o + ((int64_t)(q0 + t) * p.num_qo_heads + h) * kDV + 128 * wave +
+                         32 * nb + 4 * phalf;
 #pragma unroll
           for (int b = 0; b < 4; ++b)
             *reinterpret_cast<uint2*>(orow + 8 * b) =
@@ -428,7 +567,8 @@ __global__ __launch_bounds__(512, 1) void mla_kernel(DevPlan p, const bf16_t* __
                            pack_bf16x2(acc[4 * b + 2] * inv, acc[4 * b + 3] * inv));
         } else {
           const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + t;
-          float* orow = p.part_o + (prow * p.num_qo_heads + h) * kDV + 64 * wave + 32 * nb + 4 * phalf;
+          float* orow =
+              p.part_o + (prow * p.num_qo_heads + h) * kDV + 128 * wave + 32 * nb + 4 * phalf;
 #pragma unroll
           for (int b = 0; b < 4; ++b)
             *reinterpret_cast<float4*>(orow + 8 * b) =

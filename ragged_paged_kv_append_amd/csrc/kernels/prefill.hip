@@ -106,12 +106,14 @@ __device__ __forceinline__ int32_t load_scalar(const int32_t* ptr) {
 // itself the compiler makes later LDS reads wait for all DMA in flight, while
 // the kernel waits for exactly the tile it needs (explicit vmcnt counts,
 // which operations the compiler adds can only make stricter).  M0, which
-// carries the LDS address, is saved and restored around the instruction.
+// carries the LDS address, is saved and restored around the instruction; the
+// DMA reads M0 one wait state after the write that sets it.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -124,20 +126,6 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
 __device__ __forceinline__ int k_pos(int c, int k) { return c ^ (k & 15); }
 __device__ __forceinline__ int v_pos(int c, int k) { return c ^ (4 * (k & 3)); }
 __device__ __forceinline__ int vt_pos(int c, int d) { return c ^ ((d >> 1) & 7); }
-
-// Max over both halves of the wavefront (lanes l and l ^ 32).
-__device__ __forceinline__ float max_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// acc + lo + hi of the two bf16 values packed in w (fp32 accumulate).
-__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
-}
 
 }  // namespace
 

@@ -180,6 +180,44 @@ def test_merge_state_matches_oracle():
         assert torch.equal(o_alias, o)
 
 
+GROWING = [
+    # (dtype, hq, hkv, dqk, dv, P, qo, kv, num_cus, key scale per 512-key segment)
+    ("bf16", 128, 1, 576, 512, 64, [2, 1, 2], [3000, 1800, 700], 4, [1, 32, 1024]),  # latent
+    ("bf16", 128, 1, 576, 512, 64, [2, 1, 2], [3000, 1800, 700], 0, [1, 32, 1024]),  # split
+    ("bf16", 16, 2, 128, 128, 16, [1, 5, 40], [2500, 1200, 900], 4, [1, 32, 1024]),  # GQA
+    # fp32 keeps the scores small enough for its 1e-4 bound (fp32 dot products)
+    ("f32", 8, 2, 64, 64, 16, [1, 3], [1100, 600], 0, [1, 8]),                      # generic
+]
+
+
+@pytest.mark.parametrize("case", GROWING, ids=[f"g{i}" for i in range(len(GROWING))])
+def test_scores_jump_far_above_the_first_tiles(case):
+    # Later keys are scaled up by powers of two (values are not): a row's max
+    # rises by tens to hundreds of log2 units after its first tiles, far past
+    # any lazy-rescale slack, so every kernel must move its reference (or redo
+    # its pass).
+    dtype, hq, hkv, dqk, dv, P, qo, kv, num_cus, scales = case
+    spec = small_spec(dtype, hq, hkv, dqk, dv, P, True, 31)
+    meta = workloads.make_meta(qo, kv, P, 31)
+    tensors = workloads.make_tensors(spec, meta, 31, device="cuda")
+    # Near one-hot rows return a single value row: values of magnitude <~ 1
+    # keep the bf16 output rounding (half an ulp) well inside the bound.
+    for name in (("k_pool", "k_new") if dqk == 576 else ("v_pool", "v_new")):
+        tensors[name] *= 0.25
+    for r in range(meta.batch_size):
+        ids = meta.kv_page_indices[meta.kv_page_indptr[r]:meta.kv_page_indptr[r + 1]]
+        for i, pg in enumerate(ids):
+            f = float(scales[min((i * P) // 512, len(scales) - 1)])
+            if dqk == 576:
+                # the latent's values are its first 512 dims: scale only the
+                # 64 key-only dims so O keeps its magnitude
+                tensors["k_pool"][int(pg), :, :, 512:] *= f
+            else:
+                tensors["k_pool"][int(pg)] *= f
+    log(f"case {case}")
+    check_full(spec, meta, tensors, num_cus=num_cus, label=f"growing {dtype} d{dqk}")
+
+
 def test_invalid_calls_launch_nothing():
     spec = small_spec("bf16", 4, 2, 128, 128, 16, True, 1)
     meta = workloads.make_meta([2], [10], 16, 1)
