@@ -12,6 +12,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstring>
 #include <numeric>
@@ -47,6 +48,88 @@ int32_t rows_per_item(int32_t cls, int32_t rows_total) {
     default: return GEN_ROWS;
   }
   (void)rows_total;
+}
+
+// Latent packing with XCD pairs.  `items` are sorted by decreasing cost and
+// `cost` holds the same costs in any order.  Items with the same request, KV
+// head and key range form units of two; units go longest first to the pair of
+// workgroups (b, b + 8) with the least work, one item to each.  Returns false
+// (and changes nothing) when no unit has two items or the workgroup count is
+// not a multiple of 16.
+bool pack_latent_pairs(std::vector<int32_t>& items, const std::vector<int64_t>& cost,
+                       int64_t max_wgs, std::vector<int32_t>* wg_indptr) {
+  const int64_t m = (int64_t)cost.size();
+  if (max_wgs < 16 || max_wgs % 16 != 0) return false;
+  std::vector<int64_t> c(cost);
+  std::sort(c.begin(), c.end(), std::greater<int64_t>());
+  // units: consecutive pairing within each (request, head, k0, k1) group, in
+  // decreasing cost order
+  struct Unit {
+    int64_t a, b;  // item indices (b < 0: single)
+    int64_t cost;
+  };
+  std::vector<Unit> units;
+  std::vector<int64_t> open;  // per group: index of the unit waiting for a partner
+  std::vector<std::array<int32_t, 4>> keys;
+  bool any_pair = false;
+  for (int64_t j = 0; j < m; ++j) {
+    const int32_t* it = &items[(size_t)j * IT_WORDS];
+    const std::array<int32_t, 4> key = {it[IT_REQ], it[IT_KVHEAD], it[IT_K0], it[IT_K1]};
+    size_t g = 0;
+    while (g < keys.size() && keys[g] != key) ++g;
+    if (g == keys.size()) {
+      keys.push_back(key);
+      open.push_back(-1);
+    }
+    if (open[g] >= 0) {
+      units[(size_t)open[g]].b = j;
+      open[g] = -1;
+      any_pair = true;
+    } else {
+      open[g] = (int64_t)units.size();
+      units.push_back({j, -1, c[(size_t)j]});
+    }
+  }
+  if (!any_pair) return false;
+  const int64_t npairs = std::min<int64_t>(max_wgs / 2, round_up((int64_t)units.size(), 8));
+  const int64_t n_wgs = 2 * npairs;
+  std::vector<int64_t> load((size_t)n_wgs, 0);
+  std::vector<std::vector<int64_t>> lists((size_t)n_wgs);
+  auto wg_of = [](int64_t pair, int side) { return 16 * (pair / 8) + pair % 8 + 8 * side; };
+  std::vector<std::pair<int64_t, int64_t>> heap;  // (pair load, pair), min-heap
+  for (int64_t q = 0; q < npairs; ++q) heap.push_back({0, q});
+  auto greater = [](const std::pair<int64_t, int64_t>& x, const std::pair<int64_t, int64_t>& y) {
+    return x > y;
+  };
+  std::make_heap(heap.begin(), heap.end(), greater);
+  for (const Unit& u : units) {
+    std::pop_heap(heap.begin(), heap.end(), greater);
+    auto& top = heap.back();
+    const int64_t w0 = wg_of(top.second, 0), w1 = wg_of(top.second, 1);
+    if (u.b >= 0) {
+      lists[(size_t)w0].push_back(u.a);
+      lists[(size_t)w1].push_back(u.b);
+      load[(size_t)w0] += c[(size_t)u.a];
+      load[(size_t)w1] += c[(size_t)u.b];
+    } else {
+      const int64_t w = load[(size_t)w0] <= load[(size_t)w1] ? w0 : w1;
+      lists[(size_t)w].push_back(u.a);
+      load[(size_t)w] += c[(size_t)u.a];
+    }
+    top.first = std::max(load[(size_t)w0], load[(size_t)w1]);
+    std::push_heap(heap.begin(), heap.end(), greater);
+  }
+  std::vector<int32_t> grouped;
+  grouped.reserve(items.size());
+  wg_indptr->assign(1, 0);
+  for (int64_t b = 0; b < n_wgs; ++b) {
+    for (int64_t j : lists[(size_t)b])
+      grouped.insert(grouped.end(), items.begin() + j * IT_WORDS,
+                     items.begin() + (j + 1) * IT_WORDS);
+    wg_indptr->push_back((int32_t)(grouped.size() / IT_WORDS));
+  }
+  items.swap(grouped);
+  return true;
 }
 
 }  // namespace
@@ -353,10 +436,18 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
   // Tile classes: pack the items onto the resident workgroups, longest first,
   // each to the workgroup with the least work so far.  Items are then stored
   // grouped by workgroup; wg_indptr delimits each workgroup's list.
+  //
+  // Latent items that read the same key range (the row tiles of one request:
+  // its query tokens all read the one latent head) are packed as a pair onto
+  // workgroups b and b + 8.  Workgroups are dealt to the eight XCDs round
+  // robin, so both run on one XCD, start together and stream the same latent
+  // tiles in step: the second read of each tile is served by that XCD's L2.
   std::vector<std::vector<int32_t>> wg_indptr(KC_COUNT);
   for (int k : {(int)KC_PREFILL, (int)KC_MLA}) {
     const int64_t m = (int64_t)cost[k].size();
     if (m == 0) continue;
+    if (k == KC_MLA && pack_latent_pairs(items[k], cost[k], wgs_per_cu(k) * cus, &wg_indptr[k]))
+      continue;
     const int64_t slots = std::min<int64_t>(m, wgs_per_cu(k) * cus);
     std::vector<int64_t> load(slots, 0);
     std::vector<std::vector<int64_t>> lists(slots);
