@@ -73,14 +73,15 @@ __device__ __forceinline__ void wait_vmem() {
 // while the kernel waits for exactly the tile it needs (explicit vmcnt counts,
 // which operations the compiler adds can only make stricter).  M0, which
 // carries the LDS address, is saved and restored around the instruction; the
-// DMA reads M0 one wait state after the write that sets it.
+// DMA reads M0 one wait state after the write that sets it.  No non-temporal
+// hint: the workgroup paired on the same XCD reads the same lines from L2.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(lds)
@@ -98,7 +99,7 @@ __device__ __forceinline__ void dma16_base(const void* base, uint32_t off, uint3
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(off), "s"(base), "s"(lds)
