@@ -43,6 +43,7 @@ constexpr int kD = 128;
 constexpr int kTile = 16;    // keys per tile
 constexpr int kTileElems = kTile * kD;
 constexpr float kMinusBig = -1.0e30f;
+constexpr float kRescaleSlack = 8.f;  // log2 units
 constexpr int kNonTemporal = 2;  // cache-policy bit of the DMA loads: streaming data
 
 // Waits until at most N vector-memory operations of this wave are in flight.
@@ -134,6 +135,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
   const int32_t kend_row = row_ok ? min(k1, (causal ? cached + t : L - 1) + 1) : k0;
   const int32_t t_last = (rows - 1) / G;
   const int32_t kend = min(k1, (causal ? cached + t_last : L - 1) + 1);
+  // Last key (exclusive) of the item's first row: tiles below it need no mask.
+  const int32_t kend_first = min(k1, (causal ? cached : L - 1) + 1);
   const uint32_t tmask = (tree && row_ok) ? p.tree_mask[2 * (int64_t)(q0 + t)] : 0u;
 
   // Q operand: qf[j] = Q[row][32 grp + 8 j .. + 8), the dims of chunk 4 grp + j.
@@ -149,15 +152,61 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
   }
 
   const int32_t* pages = p.page_indices + p.page_indptr[r];
+  // The item's first 256 page ids, one per lane of pidv[c] (page pg0 + 64 c +
+  // lane), loaded with Q before the DMA stream starts: a tile then takes its
+  // page id with v_readlane instead of a scalar load and wait.  Pages past
+  // the first 256 (items longer than 4096 keys at page size 16) use the
+  // scalar load.
+  const int32_t pg0 = k0 >> p.page_shift;
+  const int32_t npg_req = p.page_indptr[r + 1] - p.page_indptr[r];
+  int32_t pidv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int32_t pi = pg0 + 64 * c + lane;
+    pidv[c] = pi < npg_req ? pages[pi] : 0;
+  }
+  asm volatile("" ::"v"(pidv[0]), "v"(pidv[1]), "v"(pidv[2]), "v"(pidv[3]));
   // DMA role: instruction i of a tile moves rows 4 (i % 4) + lane / 16, chunk
   // (lane % 16) ^ row into LDS position lane % 16 of that row.
   const int drow = lane >> 4;
   const int64_t k_head = (int64_t)g * ks.head;
   const int64_t v_head = (int64_t)g * vs.head;
+  auto page_of = [&](int32_t kb) __attribute__((always_inline)) -> int64_t {
+    const int32_t i = (kb >> p.page_shift) - pg0;  // wave-uniform
+    if (i < 64) return __builtin_amdgcn_readlane(pidv[0], i);
+    if (i < 128) return __builtin_amdgcn_readlane(pidv[1], i - 64);
+    if (i < 192) return __builtin_amdgcn_readlane(pidv[2], i - 128);
+    if (i < 256) return __builtin_amdgcn_readlane(pidv[3], i - 192);
+    return load_scalar(pages + (kb >> p.page_shift));
+  };
+  // Byte offsets, from the tile's first key, of this lane's four K and four V
+  // chunks: the same for every tile that lies inside its page and the item,
+  // whose DMA then needs only a wave-uniform base per tile.
+  uint32_t koff[4], voffs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * i + drow;
+    const uint32_t chunk = (uint32_t)((lane & 15) ^ row);
+    koff[i] = (uint32_t)row * 2u * (uint32_t)ks.token + 16u * chunk;
+    voffs[i] = (uint32_t)row * 2u * (uint32_t)vs.token + 16u * chunk;
+  }
   auto issue = [&](int32_t kb, int slot) {
-    const int64_t page = load_scalar(pages + (kb >> p.page_shift));
+    const int64_t page = page_of(kb);
     const bf16_t* kpage = kc + page * ks.page + k_head;
     const bf16_t* vpage = vc + page * vs.page + v_head;
+    if (kb + kTile <= k1) {
+      const int64_t in_page = kb & (p.page_size - 1);
+      const char* kbase = reinterpret_cast<const char*>(kpage + in_page * ks.token);
+      const char* vbase = reinterpret_cast<const char*>(vpage + in_page * vs.token);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_global_load_lds(kbase + koff[i], (lds_void_t*)&ring[slot][0][512 * i], 16,
+                                         0, kNonTemporal);
+        __builtin_amdgcn_global_load_lds(vbase + voffs[i], (lds_void_t*)&ring[slot][1][512 * i],
+                                         16, 0, kNonTemporal);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * i + drow;
@@ -214,33 +263,43 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
                                                      0);
     }
     // Online softmax for query row `col`; this lane holds keys kb + 4*grp + e.
+    // Only a tile that reaches past some row's last key, or a tree-masked
+    // request, needs the mask.
     float sv[4];
-    float mx = kMinusBig;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int32_t key = kb + 4 * grp + e;
-      bool ok = key < kend_row;
-      if (tree && key >= cached) ok = ok && ((tmask >> (uint32_t)(key - cached)) & 1u);
-      sv[e] = ok ? sacc[e] * sc : kMinusBig;
-      mx = fmaxf(mx, sv[e]);
+    for (int e = 0; e < 4; ++e) sv[e] = sacc[e] * sc;
+    if (tree || kb + kTile > kend_first) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int32_t key = kb + 4 * grp + e;
+        bool ok = key < kend_row;
+        if (tree && key >= cached) ok = ok && ((tmask >> (uint32_t)(key - cached)) & 1u);
+        sv[e] = ok ? sv[e] : kMinusBig;
+      }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = max_halves(max_rows16(mx));
+    // The reference max moves only when the tile beats it by more than the
+    // slack (P then stays below 2^8), so O is rescaled on few tiles.
+    float alpha = 1.f;
+    if (mx > m + kRescaleSlack) {
+      if (m > 0.5f * kMinusBig) alpha = __builtin_amdgcn_exp2f(m - mx);
+      m = mx;
+    }
+    // Masked keys sit at kMinusBig; a row with no key yet takes reference 0,
+    // so they still come out as 0.
+    const float neg_m = m > 0.5f * kMinusBig ? -m : 0.f;
     float pv[4];
-    float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pv[e] = sv[e] > 0.5f * kMinusBig ? __builtin_amdgcn_exp2f(sv[e] - m_new) : 0.f;
-      psum += pv[e];
-    }
-    lsum = lsum * alpha + psum;
-    m = m_new;
+    for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(sv[e] + neg_m);
     const u32x2_t pw = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+    // The row sum adds the rounded P, the weights the PV product uses.
+    lsum = sum_bf16x2(pw[1], sum_bf16x2(pw[0], lsum * alpha));
     const s16x4_t pb = __builtin_bit_cast(s16x4_t, pw);
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[nb] *= alpha;
+      for (int nb = 0; nb < 8; ++nb) acc[nb] *= alpha;
+    }
 
     // O^T += V^T P^T, V^T of block nb through the transposing read.
     s16x4_t va[8];
