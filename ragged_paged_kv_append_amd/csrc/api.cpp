@@ -118,7 +118,10 @@ hipError_t prof_event(hipEvent_t* ev) {
     g_prof_free.pop_back();
     return hipSuccess;
   }
-  return hipEventCreate(ev);
+  // Timing-only events: no system-scope fence (cache writeback and
+  // invalidate) when they are recorded, which otherwise costs several
+  // microseconds per event between the kernels being timed.
+  return hipEventCreateWithFlags(ev, hipEventDisableSystemFence);
 }
 
 // Runs `launch`, bracketed by timing events when profiling is on.

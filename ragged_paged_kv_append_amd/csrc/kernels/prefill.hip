@@ -464,24 +464,28 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
       transpose(j & (kSlots - 1), j & 1);
     };
 
+    // The page ids are complete before the first DMA is issued (the DMA
+    // addresses need them); the empty asm statement marks them as such.
+    asm volatile("" : "+v"(pid[0]), "+v"(pid[1]));
+    barrier();  // the previous item's waves are done with the ring and vt
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j)
+      if (j < ntiles) issue(j, j);
+
     // Q operand of the S^T products: qf[i] = Q[row][16 i + 8 half .. + 8),
-    // loaded together with the page ids.  Both are complete before the first
-    // DMA is issued, and the empty asm statement marks them as such: a load
-    // still pending in the compiler's view would make it wait for every
-    // untracked DMA in flight at the first use inside the loop.
+    // loaded while the first tiles are in flight.  The empty asm statement
+    // makes the compiler complete these loads here (its wait also covers the
+    // first tiles, whose latency the Q loads now share); a load still pending
+    // in its view would make it wait for every untracked DMA in flight at
+    // the first use inside the loop.
     {
       const bf16_t* qrow = q + ((int64_t)(q0 + t) * p.num_qo_heads + h) * kD + 8 * half;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         qf[i] = row_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * i) : u32x4_t{0u, 0u, 0u, 0u};
       asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]),
-                   "+v"(qf[5]), "+v"(qf[6]), "+v"(qf[7]), "+v"(pid[0]), "+v"(pid[1]));
+                   "+v"(qf[5]), "+v"(qf[6]), "+v"(qf[7]));
     }
-
-    barrier();  // the previous item's waves are done with the ring and vt
-#pragma unroll
-    for (int j = 0; j < kSlots; ++j)
-      if (j < ntiles) issue(j, j);
 
     // Two groups of four wavefronts (one of each per SIMD) run the phases
     // M(0) V(0) M(1) V(1) ... M(ntiles) half a step apart, so that one
