@@ -218,6 +218,37 @@ def test_scores_jump_far_above_the_first_tiles(case):
     check_full(spec, meta, tensors, num_cus=num_cus, label=f"growing {dtype} d{dqk}")
 
 
+@pytest.mark.parametrize("dqk", [576, 128])
+def test_pool_base_with_bit_31_of_its_low_word_set(dqk):
+    # Kernels that keep a wave-uniform 64-bit base in scalar registers must
+    # widen its halves without sign extension: put the pool at an address
+    # whose low 32 bits are >= 2^31 (and, for contrast, below it).
+    dv = 512 if dqk == 576 else 128
+    hq, hkv, P = (16, 1, 64) if dqk == 576 else (8, 2, 16)
+    spec = small_spec("bf16", hq, hkv, dqk, dv, P, True, 41)
+    meta = workloads.make_meta([2, 1, 9], [900, 700, 300], P, 41)
+    base_tensors = workloads.make_tensors(spec, meta, 41, device="cuda")
+    pool = base_tensors["k_pool"]
+    need = pool.numel() * 2
+    for high in (True, False):
+        buf = torch.empty(need + (1 << 32) + 4096, dtype=torch.uint8, device="cuda")
+        addr = buf.data_ptr()
+        want = (addr & ~0xFFFFFFFF) + (0x80000000 if high else 0)
+        while want < addr:
+            want += 1 << 32
+        off = want - addr
+        assert off + need <= buf.numel() and ((want & 0xFFFFFFFF) >= 0x80000000) == high
+        k_pool = buf[off:off + need].view(torch.bfloat16).view(pool.shape)
+        k_pool.copy_(pool)
+        tensors = dict(base_tensors, k_pool=k_pool)
+        if base_tensors["v_pool"] is not None:
+            tensors["v_pool"] = base_tensors["v_pool"].clone()
+        log(f"dqk {dqk} pool at {want:#x} (bit 31 of the low word {'set' if high else 'clear'})")
+        check_full(spec, meta, tensors, num_cus=4, label=f"pool-address d{dqk} high={high}")
+        del buf, k_pool, tensors
+        torch.cuda.empty_cache()
+
+
 def test_invalid_calls_launch_nothing():
     spec = small_spec("bf16", 4, 2, 128, 128, 16, True, 1)
     meta = workloads.make_meta([2], [10], 16, 1)
