@@ -218,6 +218,24 @@ def test_scores_jump_far_above_the_first_tiles(case):
     check_full(spec, meta, tensors, num_cus=num_cus, label=f"growing {dtype} d{dqk}")
 
 
+LONG = [
+    # (dtype, hq, hkv, dqk, dv, P, qo, kv, num_cus): few compute units, so pieces stay long
+    ("bf16", 32, 8, 128, 128, 16, [1, 4], [40000, 9000], 1),    # decode pieces past 256 pages
+    ("bf16", 8, 1, 128, 128, 16, [300], [12000], 2),            # prefill split at 8192 keys
+    ("bf16", 16, 1, 576, 512, 64, [2], [40000], 1),             # latent split at 32768 keys
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=[f"long{i}" for i in range(len(LONG))])
+def test_long_requests(case):
+    dtype, hq, hkv, dqk, dv, P, qo, kv, num_cus = case
+    spec = small_spec(dtype, hq, hkv, dqk, dv, P, True, 43)
+    meta = workloads.make_meta(qo, kv, P, 43)
+    tensors = workloads.make_tensors(spec, meta, 43, device="cuda")
+    log(f"case {case}")
+    check_full(spec, meta, tensors, num_cus=num_cus, label=f"long d{dqk}")
+
+
 @pytest.mark.parametrize("dqk", [576, 128])
 def test_pool_base_with_bit_31_of_its_low_word_set(dqk):
     # Kernels that keep a wave-uniform 64-bit base in scalar registers must
