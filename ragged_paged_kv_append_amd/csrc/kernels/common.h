@@ -47,13 +47,6 @@ __device__ __forceinline__ float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// acc + lo + hi of the two bf16 values packed in w (fp32 accumulate).
-__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
-}
-
 // Max over lanes l and l ^ 16.
 __device__ __forceinline__ float max_rows16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,

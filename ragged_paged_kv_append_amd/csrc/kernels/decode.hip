@@ -293,8 +293,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
 #pragma unroll
     for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(sv[e] + neg_m);
     const u32x2_t pw = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-    // The row sum adds the rounded P, the weights the PV product uses.
-    lsum = sum_bf16x2(pw[1], sum_bf16x2(pw[0], lsum * alpha));
+    // Plain adds for the row sum: v_dot2 would serialise against the matrix
+    // products of the other waves on this SIMD.
+    lsum = lsum * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
     const s16x4_t pb = __builtin_bit_cast(s16x4_t, pw);
     if (__ballot(alpha != 1.f)) {
 #pragma unroll

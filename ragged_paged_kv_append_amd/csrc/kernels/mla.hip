@@ -430,9 +430,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) sacc[b][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-      // P[row][key 16 b + 4 kg + i] in bf16.  The row sums add the rounded
-      // values, the weights the PV products actually use, so that a row whose
-      // mass sits on one key returns that key's value row exactly.
+      // P[row][key 16 b + 4 kg + i] in bf16; the row sums add the fp32 P
+      // with plain adds (v_dot2 would hold up the matrix pipe).
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         bf16_t* prow = &plds[(32 * wave + 16 * rb + kq) * kPRow + 4 * kg];
@@ -441,7 +440,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const uint32_t u0 = pack_bf16x2(sacc[b][rb][0], sacc[b][rb][1]);
           const uint32_t u1 = pack_bf16x2(sacc[b][rb][2], sacc[b][rb][3]);
           *reinterpret_cast<uint2*>(prow + 16 * b) = make_uint2(u0, u1);
-          lsum[rb] = sum_bf16x2(u1, sum_bf16x2(u0, lsum[rb]));
+          lsum[rb] += (sacc[b][rb][0] + sacc[b][rb][1]) + (sacc[b][rb][2] + sacc[b][rb][3]);
         }
       }
       if (moved) restart = 1;

@@ -445,14 +445,16 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
         for (int i = 0; i < 16; ++i) sacc[b2][i] = __builtin_amdgcn_exp2f(sacc[b2][i]);
       __builtin_amdgcn_sched_barrier(0);
       // word w = k-slot pair e = w % 4 of 16-key chunk kc16 = w / 4; the row
-      // sum is taken over the rounded P, in four partial sums.
+      // sum is taken over the fp32 P, in four partial sums, with plain adds:
+      // v_dot2 would serialise against the other wave's matrix products on
+      // this SIMD, the adds overlap them.
       float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < 16; ++w) {
         const int kc16 = w >> 2, e = w & 3, b2 = kc16 >> 1, hb = kc16 & 1;
-        const uint32_t wd = pack_bf16x2(sacc[b2][8 * hb + 2 * e], sacc[b2][8 * hb + 2 * e + 1]);
-        pb[kc16][e] = wd;
-        ps[e] = sum_bf16x2(wd, ps[e]);
+        const float x0 = sacc[b2][8 * hb + 2 * e], x1 = sacc[b2][8 * hb + 2 * e + 1];
+        pb[kc16][e] = pack_bf16x2(x0, x1);
+        ps[e] += x0 + x1;
       }
       lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(lsum));
