@@ -52,8 +52,8 @@ constexpr int kTileBytes = kKT * kD * 2;    // 16 KiB
 constexpr int kSlotBytes = 2 * kTileBytes;  // K tile + V tile
 constexpr int kSlots = 4;                   // ring depth
 constexpr int kWaves = 8;
-constexpr int kDmaRows = kKT / kWaves;      // key rows each wave moves per tile (8)
-constexpr int kDmaInst = 2 * kDmaRows / 4;  // its DMA instructions per tile, K and V (4)
+constexpr int kDmaRows = kKT / (kWaves / 2);  // key rows each DMA wave moves per tile (16)
+constexpr int kDmaInst = 2 * kDmaRows / 4;    // its DMA instructions per tile, K and V (8)
 constexpr float kMinusBig = -1.0e30f;
 constexpr float kRescaleSlack = 8.f;        // log2 units
 
@@ -177,19 +177,16 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     const int kc16 = kq >> 2, q4 = kq & 3;          // 16-key chunk and 4-key group in it
     tr_dst = dd * 128 + 16 * vt_pos(2 * kc16 + (q4 & 1), dd) + 8 * (q4 >> 1);
   }
-  // DMA role: wave w moves key rows 8 w .. 8 w + 7 of every tile (a run of
-  // keys inside one page for any page size >= 16); instruction i carries rows
-  // 8 w + 4 i + lane / 16 and lane % 16 is the 16-byte position in the row,
-  // which holds chunk (lane % 16) ^ perm.  Byte offsets from the first key of
-  // the wave's rows.
-  uint32_t dma_k[2], dma_v[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rr = 4 * i + (lane >> 4);    // row within the wave's 8 rows
-    const int trow = 8 * (wave & 1) + rr;  // the row's index mod 16
-    dma_k[i] = 2u * (uint32_t)(rr * ks.token + 8 * k_pos(lane & 15, trow));
-    dma_v[i] = 2u * (uint32_t)(rr * vs.token + 8 * v_pos(lane & 15, trow));
-  }
+  // DMA role (waves of the first group only, so that the DMA issue, which
+  // stalls the issuing wave while many transfers are outstanding, sits among
+  // that wave's matrix products): wave w < 4 moves key rows 16 w .. 16 w + 15
+  // of every tile (a run of keys inside one page for any page size >= 16);
+  // instruction i carries rows 16 w + 4 i + lane / 16 and lane % 16 is the
+  // 16-byte position in the row, which holds chunk (lane % 16) ^ perm.  Byte
+  // offsets from the first key of the wave's rows.
+  // The offsets are recomputed at each instruction (a few vector operations
+  // beside the matrix products) rather than held in registers.
+  const bool dma_wave = wave < kWaves / 2;
 
   // Both V^T buffers start as zeros, so that the first PV product of an item
   // (P = 0) never meets a non-finite value.
@@ -254,36 +251,45 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int32_t gkey = min(k0 + (lane + 64 * c) * kKT + kDmaRows * wave, k1 - 1);
-      pid[c] = (c == 0 || ntiles > 64) ? pages[gkey >> p.page_shift] : 0;
+      pid[c] = dma_wave && (c == 0 || ntiles > 64) ? pages[gkey >> p.page_shift] : 0;
     }
-    // DMA of tile T into ring slot `slot`.  Keys past k1 are fetched from the
+    // DMA of tile T into ring slot `slot` by a wave of the first group: 4 K
+    // and 4 V instructions, x = 0..7.  Keys past k1 are fetched from the
     // item's last key (a written slot of the same page), so masked keys hold
     // finite values.
-    auto issue = [&](int32_t T, int slot) __attribute__((always_inline)) {
+    struct DmaTile {
+      const char* kg;
+      const char* vg;
+      uint32_t kl;
+      int32_t rmax;  // rows past the first that exist
+    };
+    auto dma_setup = [&](int32_t T, int slot) __attribute__((always_inline)) {
       const int32_t gkey = min(k0 + T * kKT + kDmaRows * wave, k1 - 1);  // first key of this wave's rows
-      const int32_t rmax = k1 - 1 - gkey;                                // rows past it that exist
       const int64_t page = T < 64 ? __builtin_amdgcn_readlane(pid[0], T)
                                   : __builtin_amdgcn_readlane(pid[1], T - 64);
       const int64_t in_page = gkey & (p.page_size - 1);
-      const char* kg = kbase + 2 * (page * ks.page + in_page * ks.token);
-      const char* vg = vbase + 2 * (page * vs.page + in_page * vs.token);
-      const uint32_t kl = __builtin_amdgcn_readfirstlane(ring_lds + slot * kSlotBytes +
-                                                         kDmaRows * wave * 256);
-      if (rmax >= kDmaRows - 1) {
+      DmaTile d;
+      d.kg = kbase + 2 * (page * ks.page + in_page * ks.token);
+      d.vg = vbase + 2 * (page * vs.page + in_page * vs.token);
+      d.kl = __builtin_amdgcn_readfirstlane(ring_lds + slot * kSlotBytes + kDmaRows * wave * 256);
+      d.rmax = k1 - 1 - gkey;
+      return d;
+    };
+    auto dma_x = [&](const DmaTile& d, int x) __attribute__((always_inline)) {
+      const int i = x & 3;
+      const bool v = x >= 4;
+      const int ln = (int)opaque((uint32_t)lane);
+      const int rr = 4 * i + (ln >> 4);  // row within the wave's 16 rows (= its index mod 16)
+      const int row = min(rr, d.rmax);   // rows past the last key repeat it
+      const uint32_t off =
+          v ? 2u * (uint32_t)(row * vs.token + 8 * v_pos(ln & 15, rr))
+            : 2u * (uint32_t)(row * ks.token + 8 * k_pos(ln & 15, rr));
+      dma16((v ? d.vg : d.kg) + off, d.kl + (v ? kTileBytes : 0) + 1024 * i);
+    };
+    auto issue = [&](int32_t T, int slot) __attribute__((always_inline)) {
+      const DmaTile d = dma_setup(T, slot);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          dma16(kg + dma_k[i], kl + 1024 * i);
-          dma16(vg + dma_v[i], kl + kTileBytes + 1024 * i);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int rr = 4 * i + (lane >> 4);
-          const uint32_t back = (uint32_t)(rr - min(rr, rmax));  // rows clamped onto the last key
-          dma16(kg + (dma_k[i] - 2u * back * (uint32_t)ks.token), kl + 1024 * i);
-          dma16(vg + (dma_v[i] - 2u * back * (uint32_t)vs.token), kl + kTileBytes + 1024 * i);
-        }
-      }
+      for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
     };
 
     // Transpose of the V tile in ring slot `slot` into vt[buf]: this wave's
@@ -346,7 +352,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     // alternate, with their LDS operands read one step ahead.  At j = 0, P is
     // zero (and V^T finite); at j = ntiles, the S product reads a stale ring
     // slot and its result is not used.
-    auto mphase = [&](int32_t j) __attribute__((always_inline)) {
+    // With refill, this (first-group) wave's DMA of tile j + kSlots - 1 into
+    // ring slot (j - 1) % kSlots goes between the products, one instruction
+    // per step.
+    auto mphase = [&](int32_t j, bool refill) __attribute__((always_inline)) {
+      DmaTile rd{};
+      if (refill) rd = dma_setup(j + kSlots - 1, (j - 1) & (kSlots - 1));
       const uint32_t kt = opaque(ring_lds + (j & (kSlots - 1)) * kSlotBytes + k_rd);
       const uint32_t vtb = opaque(vt_lds + ((j - 1) & 1) * kTileBytes + vt_rd);
 #pragma unroll
@@ -380,6 +391,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
                                                           sacc[1], 0, 0, 0);
         oacc[2 * c + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(va[b][1]), as_bf16x8(pb[i >> 1]), oacc[2 * c + 1], 0, 0, 0);
+        if (refill) dma_x(rd, i);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -470,9 +482,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     // addresses need them); the empty asm statement marks them as such.
     asm volatile("" : "+v"(pid[0]), "+v"(pid[1]));
     barrier();  // the previous item's waves are done with the ring and vt
+    if (dma_wave) {
 #pragma unroll
-    for (int j = 0; j < kSlots; ++j)
-      if (j < ntiles) issue(j, j);
+      for (int j = 0; j < kSlots; ++j)
+        if (j < ntiles) issue(j, j);
+    }
 
     // Q operand of the S^T products: qf[i] = Q[row][16 i + 8 half .. + 8),
     // loaded while the first tiles are in flight.  The empty asm statement
@@ -500,19 +514,21 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     //   ring slot j % kSlots is refilled (tile j + kSlots) at slot 2 j + 2.
     // Waits for tile j before slot 2 j: tiles up to j + kSlots - 2 (up to
     // kSlots - 1 before the first) have been issued by then.
+    // Only the first group issues DMA; the second sees each tile through the
+    // barrier that follows the first group's wait.
     auto wait_for = [&](int32_t j) __attribute__((always_inline)) {
       if (j < ntiles) wait_tile(j, min(j == 0 ? kSlots - 1 : j + kSlots - 2, ntiles - 1));
     };
-    // At slot 2 j: refill ring slot (j - 1) % kSlots with tile j + kSlots - 1.
-    auto refill = [&](int32_t j) __attribute__((always_inline)) {
-      if (j >= 1 && j + kSlots - 1 < ntiles) issue(j + kSlots - 1, (j - 1) & (kSlots - 1));
+    // In slot 2 j the first group refills ring slot (j - 1) % kSlots with tile
+    // j + kSlots - 1 (inside its matrix phase).
+    auto refill_due = [&](int32_t j) __attribute__((always_inline)) {
+      return j >= 1 && j + kSlots - 1 < ntiles;
     };
     if (wave < kWaves / 2) {
       for (int32_t j = 0; j <= ntiles; ++j) {
         wait_for(j);
         barrier();  // slot 2 j
-        refill(j);
-        mphase(j);
+        mphase(j, refill_due(j));
         barrier();  // slot 2 j + 1
         if (j < ntiles) {
           vphase(j);
@@ -521,13 +537,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
       }
     } else {
       for (int32_t j = 0; j <= ntiles; ++j) {
-        wait_for(j);
         barrier();  // slot 2 j
-        refill(j);
         if (j >= 1) vphase(j - 1);
         if (j < ntiles) transpose_part(j);
         barrier();  // slot 2 j + 1
-        mphase(j);
+        mphase(j, false);
       }
     }
 
