@@ -51,6 +51,9 @@ constexpr int kKT = 64;                     // keys per tile
 constexpr int kTileBytes = kKT * kD * 2;    // 16 KiB
 constexpr int kSlotBytes = 2 * kTileBytes;  // K tile + V tile
 constexpr int kSlots = 4;                   // ring depth
+// Tiles in flight ahead of the one being computed.  Two cover the memory
+// latency; more outstanding DMA only makes each issue stall longer.
+constexpr int kLookahead = 2;
 constexpr int kWaves = 8;
 constexpr int kDmaRows = kKT / (kWaves / 2);  // key rows each DMA wave moves per tile (16)
 constexpr int kDmaInst = 2 * kDmaRows / 4;    // its DMA instructions per tile, K and V (8)
@@ -352,12 +355,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     // alternate, with their LDS operands read one step ahead.  At j = 0, P is
     // zero (and V^T finite); at j = ntiles, the S product reads a stale ring
     // slot and its result is not used.
-    // With refill, this (first-group) wave's DMA of tile j + kSlots - 1 into
-    // ring slot (j - 1) % kSlots goes between the products, one instruction
-    // per step.
+    // With refill, this (first-group) wave's DMA of tile j + kLookahead into
+    // its ring slot goes between the products, one instruction per step.
     auto mphase = [&](int32_t j, bool refill) __attribute__((always_inline)) {
       DmaTile rd{};
-      if (refill) rd = dma_setup(j + kSlots - 1, (j - 1) & (kSlots - 1));
+      if (refill) rd = dma_setup(j + kLookahead, (j + kLookahead) & (kSlots - 1));
       const uint32_t kt = opaque(ring_lds + (j & (kSlots - 1)) * kSlotBytes + k_rd);
       const uint32_t vtb = opaque(vt_lds + ((j - 1) & 1) * kTileBytes + vt_rd);
 #pragma unroll
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     barrier();  // the previous item's waves are done with the ring and vt
     if (dma_wave) {
 #pragma unroll
-      for (int j = 0; j < kSlots; ++j)
+      for (int j = 0; j < kLookahead; ++j)
         if (j < ntiles) issue(j, j);
     }
 
@@ -511,18 +513,18 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
     //   K_j and V^T_{j-1} are read in slots 2 j and 2 j + 1;
     //   V_j is transposed into vt[j % 2] in slots 2 j (group 1) and 2 j + 1
     //   (group 0), each wave its eighth, in the slot of its softmax phase;
-    //   ring slot j % kSlots is refilled (tile j + kSlots) at slot 2 j + 2.
-    // Waits for tile j before slot 2 j: tiles up to j + kSlots - 2 (up to
-    // kSlots - 1 before the first) have been issued by then.
-    // Only the first group issues DMA; the second sees each tile through the
-    // barrier that follows the first group's wait.
+    //   tile j + kLookahead is loaded into ring slot (j + kLookahead) % kSlots
+    //   in slot 2 j (the tile that slot held was last read in slot 2 j - 3).
+    // Waits for tile j before slot 2 j: tiles up to j + kLookahead - 1 have
+    // been issued by then.  Only the first group issues DMA; the second sees
+    // each tile through the barrier that follows the first group's wait.
     auto wait_for = [&](int32_t j) __attribute__((always_inline)) {
-      if (j < ntiles) wait_tile(j, min(j == 0 ? kSlots - 1 : j + kSlots - 2, ntiles - 1));
+      if (j < ntiles) wait_tile(j, min(j + kLookahead - 1, ntiles - 1));
     };
-    // In slot 2 j the first group refills ring slot (j - 1) % kSlots with tile
-    // j + kSlots - 1 (inside its matrix phase).
+    // In slot 2 j the first group loads tile j + kLookahead (inside its
+    // matrix phase).
     auto refill_due = [&](int32_t j) __attribute__((always_inline)) {
-      return j >= 1 && j + kSlots - 1 < ntiles;
+      return j + kLookahead < ntiles;
     };
     if (wave < kWaves / 2) {
       for (int32_t j = 0; j <= ntiles; ++j) {
