@@ -22,9 +22,9 @@
 // Per tile j:
 //   S phase: wave w computes S^T for rows 32 w .. 32 w + 31 over the tile as
 //     four independent 16x16 blocks (mfma 16x16x32 bf16, 18 steps over the
-//     576 dims, K operands read three steps ahead), runs the online softmax
-//     for those rows and writes P (bf16) and the per-row rescale factors into
-//     LDS;
+//     576 dims, K operands read three steps ahead), runs the softmax for
+//     those rows against their reference max (moved only far above it: see
+//     the tile loop) and writes P (bf16) into LDS;
 //   PV phase: wave w owns value dims 128 w .. 128 w + 127 of all 128 rows and
 //     accumulates O^T[d][row] += V^T[d][key] P^T[key][row] (mfma 32x32x16
 //     bf16), V^T read from the latent tile with the transposing LDS read.
@@ -103,19 +103,6 @@ __device__ __forceinline__ void dma16_base(const void* base, uint32_t off, uint3
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(off), "s"(base), "s"(lds)
-      : "memory");
-}
-
-// Two transposing reads (low and high key halves, + 8 rows) at one address,
-// with their own LDS wait (the compiler would otherwise drain the DMA stream
-// before them).
-__device__ __forceinline__ void read_vt2(uint32_t a, s16x4_t& lo, s16x4_t& hi) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %2\n\t"
-      "ds_read_b64_tr_b16 %1, %2 offset:%3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(lo), "=&v"(hi)
-      : "v"(a), "n"(8 * kRowBytes)
       : "memory");
 }
 

@@ -92,17 +92,6 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Blocking scalar load of one page id; the address is wave-uniform.
-__device__ __forceinline__ int32_t load_scalar(const int32_t* ptr) {
-  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const int32_t* sp = reinterpret_cast<const int32_t*>(lo | (hi << 32));
-  int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sp) : "memory");
-  return v;
-}
-
 // One global-to-LDS DMA instruction (gfx950 global_load_lds_dwordx4): every
 // lane copies 16 bytes from `src` to LDS byte address lds + 16 * lane.  It is
 // issued from inline assembly so that the compiler does not track it: left to
