@@ -398,18 +398,31 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
       asm volatile("" : "+v"(sacc[0]), "+v"(sacc[1]));
       const int32_t kb = k0 + j * kKT;
       if (kb + kKT > mask_from) {
+        // Two uniform branches, each one compare and one select per element
+        // (plus the bit test for trees), with no per-element control flow.
         const int32_t lim = kend_row - kb - 4 * half;
-        const int32_t rel = kb + 4 * half - cached;  // new-token index of element offset 0
+        if (!tree) {
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
+          for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int idx = 32 * b2 + 8 * (i >> 2) + (i & 3);
-            bool ok = idx < lim;
-            if (tree && rel + idx >= 0)
-              ok = ok && ((tmask >> (uint32_t)(rel + idx)) & 1ull);
-            sacc[b2][i] = ok ? sacc[b2][i] : kMinusBig;
-          }
+            for (int i = 0; i < 16; ++i) {
+              const int idx = 32 * b2 + 8 * (i >> 2) + (i & 3);
+              sacc[b2][i] = idx < lim ? sacc[b2][i] : kMinusBig;
+            }
+        } else {
+          const int32_t rel = kb + 4 * half - cached;  // new-token index of element offset 0
+          const uint32_t tlo = (uint32_t)tmask, thi = (uint32_t)(tmask >> 32);
+#pragma unroll
+          for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int idx = 32 * b2 + 8 * (i >> 2) + (i & 3);
+              const int32_t bi = rel + idx;  // < 0: a cached key, always visible
+              const uint32_t word = bi >= 32 ? thi : tlo;
+              const bool in_tree = bi < 0 || ((word >> (bi & 31)) & 1u) != 0;
+              sacc[b2][i] = (idx < lim) & in_tree ? sacc[b2][i] : kMinusBig;
+            }
+        }
       }
       // Row max as a tree (independent operations for the scheduler).
       float mx8[8];
