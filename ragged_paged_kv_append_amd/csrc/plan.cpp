@@ -468,11 +468,31 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
       top.first += sorted_cost[j];
       std::push_heap(heap.begin(), heap.end(), greater);
     }
+    // Workgroup w runs on XCD w % 8.  Lists are handed to the workgroups of
+    // XCD 0 first, then XCD 1, ..., in the order of the request, KV head, key
+    // range and row tile of their first (longest) item: the row tiles that
+    // read one key range, and the pieces of one KV head, then share an XCD, so
+    // the K/V tiles (and Q rows) they have in common come from HBM once and
+    // from that XCD's L2 after.
+    std::vector<int64_t> by_key((size_t)slots);
+    for (int64_t b = 0; b < slots; ++b) by_key[(size_t)b] = b;
+    auto key_of = [&](int64_t b) {
+      const int32_t* it = &items[k][(size_t)lists[(size_t)b][0] * IT_WORDS];
+      return std::array<int32_t, 4>{it[IT_REQ], it[IT_KVHEAD], it[IT_K0], it[IT_ROW0]};
+    };
+    std::stable_sort(by_key.begin(), by_key.end(),
+                     [&](int64_t a, int64_t b) { return key_of(a) < key_of(b); });
+    std::vector<int64_t> list_of_wg((size_t)slots);
+    {
+      int64_t i = 0;
+      for (int64_t x = 0; x < 8; ++x)
+        for (int64_t w = x; w < slots; w += 8) list_of_wg[(size_t)w] = by_key[(size_t)i++];
+    }
     std::vector<int32_t> grouped;
     grouped.reserve(items[k].size());
     wg_indptr[k].push_back(0);
-    for (int64_t b = 0; b < slots; ++b) {
-      for (int64_t j : lists[b])
+    for (int64_t w = 0; w < slots; ++w) {
+      for (int64_t j : lists[(size_t)list_of_wg[(size_t)w]])
         grouped.insert(grouped.end(), items[k].begin() + j * IT_WORDS,
                        items[k].begin() + (j + 1) * IT_WORDS);
       wg_indptr[k].push_back((int32_t)(grouped.size() / IT_WORDS));
