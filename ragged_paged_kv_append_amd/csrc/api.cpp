@@ -47,7 +47,7 @@ rpa::DevPlan dev_plan(const rpa_plan* plan) {
     p.n_wgs[k] = plan->n_wgs[k];
   }
   p.merge_rows = base + plan->off_merge;
-  p.merge_req = base + plan->off_merge_req;
+  p.merge_info = base + plan->off_merge_info;
   p.tree_req = plan->off_tree_req >= 0 ? base + plan->off_tree_req : nullptr;
   p.tree_mask = plan->off_tree_mask >= 0
                     ? reinterpret_cast<const uint32_t*>(base + plan->off_tree_mask) : nullptr;

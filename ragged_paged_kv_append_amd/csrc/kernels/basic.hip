@@ -241,8 +241,9 @@ hipError_t launch_generic(const DevPlan& p, const void* q, const void* k_cache,
 
 // Block (x, y) merges row p.merge_rows[x]; a thread owns 8 consecutive output
 // elements of one head (task y * blockDim.x + thread of the row's H * d_v / 8).
-// Piece s of a row contributes only if it holds a key the row sees
-// (s * chunk <= last visible key).  The pieces are read eight at a time, with
+// The plan gives each merge row its first partial row, the stride between its
+// pieces and how many pieces hold a key the row sees, so the partial loads
+// depend on one table load only.  The pieces are read eight at a time, with
 // a running maximum, so their loads are in flight together.
 template <typename T>
 __global__ __launch_bounds__(256) void merge_rows_kernel(DevPlan p, T* __restrict__ o,
@@ -254,17 +255,10 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DevPlan p, T* __restric
   const int32_t x = blockIdx.y * blockDim.x + threadIdx.x;
   if (x >= H * per_head) return;
   const int32_t i = p.merge_rows[blockIdx.x];
-  const int32_t r = p.merge_req[blockIdx.x];
-  const int32_t q0 = p.qo_indptr[r];
-  const int32_t n = p.qo_indptr[r + 1] - q0;
-  const int32_t t = i - q0;
-  const int32_t L = p.kv_len[r];
-  const bool tree = p.tree_mask != nullptr && p.tree_req[r] != 0;
-  const int32_t pmax = (p.causal && !tree) ? L - n + t : L - 1;
-  const int32_t S = p.split[r * SP_WORDS + SP_COUNT];
-  const int32_t kc = p.split[r * SP_WORDS + SP_CHUNK];
-  const int64_t base = p.split[r * SP_WORDS + SP_BASE];
-  const int32_t S_eff = pmax < 0 ? 0 : min(S, pmax / kc + 1);  // no key: empty state
+  const int4 info = *reinterpret_cast<const int4*>(p.merge_info + 4 * (int64_t)blockIdx.x);
+  const int64_t prow0 = info.x;
+  const int32_t n = info.y;
+  const int32_t S_eff = info.z;  // 0: no key, an empty state
   const int32_t h = x / per_head;
   const int32_t d0 = (x - h * per_head) * 8;
   float m = -INFINITY;  // running maximum of the pieces' lse
@@ -276,7 +270,7 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DevPlan p, T* __restric
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
       if (s0 + u < S_eff) {
-        const int64_t prow = base + (int64_t)(s0 + u) * n + t;
+        const int64_t prow = prow0 + (int64_t)(s0 + u) * n;
         ls[u] = p.part_lse[prow * H + h];
         load8(p.part_o + (prow * H + h) * DV + d0, v[u]);
       } else {

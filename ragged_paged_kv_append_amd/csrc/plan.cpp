@@ -506,7 +506,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
   // cannot append.  Its rows with kv_len = 0 have no work item; the merge
   // pass writes them as empty states (O = 0, lse = -inf).
   std::vector<int32_t> append((size_t)total_q * 2, -1);
-  std::vector<int32_t> merge_rows, merge_req;
+  std::vector<int32_t> merge_rows, merge_info;
   plan->can_append = true;
   for (int32_t r = 0; r < B; ++r) {
     const int64_t n = (int64_t)qo[r + 1] - qo[r];
@@ -519,10 +519,19 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
         append[(size_t)i * 2 + 0] = pix[pip[r] + p / P];
         append[(size_t)i * 2 + 1] = (int32_t)(p % P);
       }
-      if (split[(size_t)r * SP_WORDS + SP_COUNT] > 1 || kvl[r] == 0)
-      {
+      const int32_t S = split[(size_t)r * SP_WORDS + SP_COUNT];
+      if (S > 1 || kvl[r] == 0) {
+        // Piece s holds keys [s chunk, (s + 1) chunk); the row sees keys up to
+        // pmax, so pieces past pmax / chunk hold nothing for it.
+        const bool masked = c.causal && !(has_tree && tree_req[(size_t)r]);
+        const int64_t pmax = masked ? p : (int64_t)kvl[r] - 1;
+        const int64_t chunk = split[(size_t)r * SP_WORDS + SP_CHUNK];
+        const int64_t s_eff = pmax < 0 ? 0 : std::min<int64_t>(S, pmax / chunk + 1);
         merge_rows.push_back((int32_t)i);
-        merge_req.push_back(r);
+        merge_info.push_back(split[(size_t)r * SP_WORDS + SP_BASE] + (int32_t)t);
+        merge_info.push_back((int32_t)n);
+        merge_info.push_back((int32_t)s_eff);
+        merge_info.push_back(0);
       }
     }
   }
@@ -556,7 +565,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
     plan->n_wgs[k] = wg_indptr[k].empty() ? plan->n_items[k] : (int32_t)wg_indptr[k].size() - 1;
   }
   plan->off_merge = push(merge_rows.data(), (int64_t)merge_rows.size());
-  plan->off_merge_req = push(merge_req.data(), (int64_t)merge_req.size());
+  plan->off_merge_info = push(merge_info.data(), (int64_t)merge_info.size());
   plan->off_tree_mask = plan->off_tree_req = -1;
   if (has_tree) {
     std::vector<int32_t> treq(tree_req.begin(), tree_req.end());

@@ -17,7 +17,7 @@ struct rpa_plan {
   // Metadata in the order it is laid out in the device workspace (int32 words).
   std::vector<int32_t> blob;
   int64_t off_qo_indptr = 0, off_kv_len = 0, off_page_indptr = 0, off_page_indices = 0;
-  int64_t off_split = 0, off_append = 0, off_merge = 0, off_merge_req = 0;
+  int64_t off_split = 0, off_append = 0, off_merge = 0, off_merge_info = 0;
   int64_t off_tree_mask = -1, off_tree_req = -1;  // -1: the plan has no tree masks
   int64_t off_items[rpa::KC_COUNT] = {0, 0, 0, 0};
   int32_t n_items[rpa::KC_COUNT] = {0, 0, 0, 0};

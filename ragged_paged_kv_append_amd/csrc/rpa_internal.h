@@ -56,7 +56,10 @@ struct DevPlan {
   // wg_indptr[b] .. wg_indptr[b + 1] - 1 of its class, in that order.
   const int32_t* wg_indptr[KC_COUNT];
   const int32_t* merge_rows;    // tokens whose request has S_r > 1 (or kv_len 0)
-  const int32_t* merge_req;     // the request of each of those tokens
+  // merge_info[4 x + 0..3] for merge row x: its first partial row, the
+  // partial-row stride between pieces (qo_len of its request), and the number
+  // of pieces that hold a key the row sees (0: an empty state).
+  const int32_t* merge_info;
   // Tree masks (nullptr when the plan has none).  tree_req[r] = 1 if request
   // r has a mask; then tree_mask[2 i], tree_mask[2 i + 1] are the low and high
   // 32 bits of new token i's row: bit u = it sees new token u of its request.
