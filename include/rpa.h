@@ -270,6 +270,11 @@ int32_t rpa_abi_version(void);
  * "mla", "merge", "merge_state" or "page_copy".  rpa_profile_reset clears the totals.
  * Process-wide and thread-safe; off by default.  Errors: INVALID_ARG, HIP. */
 rpa_status rpa_profile_enable(int32_t on);
+/* Restricts the timing to the kernels named in `kernels`, a comma-separated
+ * list of the names above (NULL or "" again times every kernel), so that a
+ * timed loop carries events around its dominant kernel only.  Takes effect
+ * for later launches; the totals are kept.  Errors: none. */
+rpa_status rpa_profile_select(const char* kernels);
 rpa_status rpa_profile_read(const char* kernel, double* total_ms, int64_t* launches);
 rpa_status rpa_profile_reset(void);
 

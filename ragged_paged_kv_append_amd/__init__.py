@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "rpa_plan_destroy",
     "rpa_status_string",
     "rpa_last_error_message", "rpa_abi_version", "rpa_plan_debug_dump", "rpa_profile_enable",
-    "rpa_profile_read", "rpa_profile_reset",
+    "rpa_profile_read", "rpa_profile_reset", "rpa_profile_select",
 )
 
 
@@ -110,9 +110,11 @@ def lib() -> ctypes.CDLL:
     L.rpa_profile_enable.argtypes = [i32]
     L.rpa_profile_read.argtypes = [ctypes.c_char_p, P(ctypes.c_double), P(i64)]
     L.rpa_profile_reset.argtypes = []
+    L.rpa_profile_select.argtypes = [ctypes.c_char_p]
     for name in ("rpa_plan_create", "rpa_plan_workspace_size", "rpa_plan_upload", "rpa_kv_append",
                  "rpa_batch_attention", "rpa_merge_state", "rpa_plan_debug_dump",
-                 "rpa_profile_enable", "rpa_profile_read", "rpa_profile_reset"):
+                 "rpa_profile_enable", "rpa_profile_read", "rpa_profile_reset",
+                 "rpa_profile_select"):
         getattr(L, name).restype = i32
     _lib_handle = L
     return L
@@ -342,6 +344,11 @@ def rpa_profile_read(kernel: str) -> tuple[float, int]:
 
 def rpa_profile_reset():
     _check(lib().rpa_profile_reset())
+
+
+def rpa_profile_select(kernels=None):
+    """Times only the named kernels (a list of names, or None for all)."""
+    _check(lib().rpa_profile_select(",".join(kernels).encode() if kernels else None))
 
 
 # ----------------------------------------------------------------------------

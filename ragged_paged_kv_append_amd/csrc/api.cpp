@@ -5,6 +5,7 @@
 
 #include <cstring>
 #include <map>
+#include <set>
 #include <mutex>
 #include <new>
 #include <string>
@@ -108,6 +109,7 @@ struct ProfRecord {
 
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+std::set<std::string> g_prof_only;  // kernels to time (empty: all)
 std::vector<ProfRecord> g_prof_pending;
 std::vector<hipEvent_t> g_prof_free;
 std::map<std::string, std::pair<double, int64_t>> g_prof_totals;
@@ -128,7 +130,7 @@ hipError_t prof_event(hipEvent_t* ev) {
 template <class F>
 hipError_t timed(const char* name, hipStream_t st, F&& launch) {
   std::unique_lock<std::mutex> lock(g_prof_mu);
-  if (!g_prof_on) {
+  if (!g_prof_on || (!g_prof_only.empty() && g_prof_only.count(name) == 0)) {
     lock.unlock();
     return launch();
   }
@@ -429,6 +431,23 @@ RPA_EXPORT rpa_status rpa_page_copy(const void* src, const rpa_cache_strides* sr
 RPA_EXPORT rpa_status rpa_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lock(g_prof_mu);
   g_prof_on = on != 0;
+  return RPA_OK;
+}
+
+RPA_EXPORT rpa_status rpa_profile_select(const char* kernels) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof_only.clear();
+  if (kernels == nullptr) return RPA_OK;
+  std::string cur;
+  for (const char* c = kernels;; ++c) {
+    if (*c == ',' || *c == '\0') {
+      if (!cur.empty()) g_prof_only.insert(cur);
+      cur.clear();
+      if (*c == '\0') break;
+    } else {
+      cur.push_back(*c);
+    }
+  }
   return RPA_OK;
 }
 
