@@ -99,6 +99,37 @@ __device__ __forceinline__ void read_vt(const bf16_t* row_base, int vrow, int vh
       : "memory");
 }
 
+// O^T += V^T P^T for the eight 16-dim blocks, issued from inline assembly so
+// that the accumulators are VGPR operands: left to the compiler they live in
+// AGPRs and are copied to VGPRs and back around every tile (the lazy rescale
+// reads them with vector instructions), about a hundred extra instructions
+// per tile.  The compiler does not see these as matrix instructions, so the
+// wait states it would add are written here: two before the first product
+// (P, and maybe a copy of an accumulator, were just written by vector
+// instructions) and 24 after the last, more than any product needs before a
+// vector instruction reads or overwrites its registers (the compiler may
+// copy the accumulators right after this block).
+__device__ __forceinline__ void pv_products(f32x4_t (&acc)[8], const s16x4_t (&va)[8],
+                                            s16x4_t pb) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x16_bf16 %0, %8, %16, %0\n\t"
+      "v_mfma_f32_16x16x16_bf16 %1, %9, %16, %1\n\t"
+      "v_mfma_f32_16x16x16_bf16 %2, %10, %16, %2\n\t"
+      "v_mfma_f32_16x16x16_bf16 %3, %11, %16, %3\n\t"
+      "v_mfma_f32_16x16x16_bf16 %4, %12, %16, %4\n\t"
+      "v_mfma_f32_16x16x16_bf16 %5, %13, %16, %5\n\t"
+      "v_mfma_f32_16x16x16_bf16 %6, %14, %16, %6\n\t"
+      "v_mfma_f32_16x16x16_bf16 %7, %15, %16, %7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7"
+      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
+        "+v"(acc[6]), "+v"(acc[7])
+      : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]),
+        "v"(va[7]), "v"(pb));
+}
+
 }  // namespace
 
 // kStages: LDS ring depth in tiles (8 KiB each); kStages - 1 tiles are in flight.
@@ -305,9 +336,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
     // O^T += V^T P^T, V^T of block nb through the transposing read.
     s16x4_t va[8];
     read_vt(vt + vrow * kD + voff, vrow, vhalf, va);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[nb], pb, acc[nb], 0, 0, 0);
+    pv_products(acc, va, pb);
   }
 
   // Row sum over the four lane groups, then normalise and store.
@@ -348,7 +377,7 @@ hipError_t launch_decode(const DevPlan& p, const void* q, const void* k_cache, c
   static const int stages = [] {
     const char* e = getenv("RPA_DECODE_STAGES");
     const int v = e ? atoi(e) : 3;
-    return (v == 4 || v == 6) ? v : 3;
+    return (v == 2 || v == 4 || v == 6) ? v : 3;
   }();
   const dim3 grid(p.n_items[KC_DECODE]), block(64);
   const bf16_t* qq = static_cast<const bf16_t*>(q);
@@ -357,6 +386,8 @@ hipError_t launch_decode(const DevPlan& p, const void* q, const void* k_cache, c
   bf16_t* oo = static_cast<bf16_t*>(o);
   if (stages == 3)
     hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
+  else if (stages == 2)
+    hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
   else if (stages == 6)
     hipLaunchKernelGGL(decode_kernel<6>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
   else
