@@ -284,7 +284,10 @@ rpa_status rpa_profile_reset(void);
  * kv head, first row, end row, first key, end key, split index, kernel
  * class), "splits" (3 int32 per request: number of pieces, keys per piece,
  * first partial row), "append" (2 int32 per new token: page id, slot),
- * "merge_rows" (rows whose pieces are merged), "summary" (batch_size,
+ * "wg_prefill" / "wg_mla" (workgroup b runs items [v[b], v[b + 1]) of that
+ * class), "merge_rows" (rows whose pieces are merged), "merge_info" (4 int32
+ * per merge row: first partial row, partial-row stride between pieces,
+ * pieces holding a key the row sees, 0), "summary" (batch_size,
  * total_q, num items, partial rows, number of items per kernel class 0..3).
  * Errors: INVALID_ARG for an unknown name. */
 rpa_status rpa_plan_debug_dump(const rpa_plan* plan, const char* name, int32_t* dst,

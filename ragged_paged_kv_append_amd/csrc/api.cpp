@@ -507,6 +507,9 @@ RPA_EXPORT rpa_status rpa_plan_debug_dump(const rpa_plan* plan, const char* name
   } else if (nm == "merge_rows") {
     src = blob + plan->off_merge;
     n = plan->n_merge_rows;
+  } else if (nm == "merge_info") {
+    src = blob + plan->off_merge_info;
+    n = (int64_t)plan->n_merge_rows * 4;
   } else if (nm == "summary") {
     int32_t total = 0;
     for (int k = 0; k < rpa::KC_COUNT; ++k) total += plan->n_items[k];

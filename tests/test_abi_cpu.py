@@ -110,6 +110,19 @@ def check_plan(plan, meta, cfg):
             i = int(meta.qo_indptr[r_]) + t
             assert (i in merge_rows) == (S > 1)
             assert tuple(app[i]) == oracle.slot_of(batch, r_, c + t)
+    # each merge row's first partial row, piece stride and live piece count
+    mrows = rpa.rpa_plan_debug_dump(plan, "merge_rows").tolist()
+    minfo = rpa.rpa_plan_debug_dump(plan, "merge_info").reshape(-1, 4)
+    assert len(minfo) == len(mrows)
+    for x, i in enumerate(mrows):
+        r_ = int(np.searchsorted(np.asarray(meta.qo_indptr), i, side="right")) - 1
+        n = batch.qo_len(r_)
+        t = i - int(meta.qo_indptr[r_])
+        Lr = int(meta.kv_len[r_])
+        S, chunk, base = splits[r_]
+        pmax = Lr - n + t if cfg.causal else Lr - 1
+        live = 0 if pmax < 0 else min(S, pmax // chunk + 1)
+        assert tuple(minfo[x].tolist()) == (base + t, n, live, 0), (i, minfo[x])
     return items, splits
 
 
@@ -224,6 +237,12 @@ def test_planner_packs_tile_items_onto_workgroups(L, case):
         # every list runs its items longest first
         for b in range(len(wg) - 1):
             assert np.all(np.diff(cost[wg[b]:wg[b + 1]]) <= 0)
+        # lists are handed out XCD by XCD (workgroup w runs on XCD w % 8) in the
+        # order of (request, KV head, first key, first row) of their first item
+        n_wgs = len(wg) - 1
+        order = [w for x in range(8) for w in range(x, n_wgs, 8)]
+        firsts = [tuple(items[wg[w]][[0, 1, 4, 2]].tolist()) for w in order]
+        assert firsts == sorted(firsts)
 
 
 def test_planner_empty_batch_and_empty_requests(L):
