@@ -166,8 +166,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
   const int32_t kend_row = row_ok ? min(k1, (causal ? cached + t : L - 1) + 1) : k0;
   const int32_t t_last = (rows - 1) / G;
   const int32_t kend = min(k1, (causal ? cached + t_last : L - 1) + 1);
-  // Last key (exclusive) of the item's first row: tiles below it need no mask.
+  // Last key (exclusive) of the item's first row: tiles below it need no
+  // mask, except that a tree mask filters the new tokens (keys >= cached).
   const int32_t kend_first = min(k1, (causal ? cached : L - 1) + 1);
+  const int32_t mask_from = tree ? min(kend_first, cached) : kend_first;
   const uint32_t tmask = (tree && row_ok) ? p.tree_mask[2 * (int64_t)(q0 + t)] : 0u;
 
   // Q operand: qf[j] = Q[row][32 grp + 8 j .. + 8), the dims of chunk 4 grp + j.
@@ -294,18 +296,24 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
                                                      0);
     }
     // Online softmax for query row `col`; this lane holds keys kb + 4*grp + e.
-    // Only a tile that reaches past some row's last key, or a tree-masked
-    // request, needs the mask.
+    // Only a tile that reaches past some row's last key, or holds new tokens
+    // of a tree-masked request, needs the mask: one compare and one select
+    // per key (plus the bit test for trees), with no per-key branches.
     float sv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) sv[e] = sacc[e] * sc;
-    if (tree || kb + kTile > kend_first) {
+    if (kb + kTile > mask_from) {
+      if (!tree) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int32_t key = kb + 4 * grp + e;
-        bool ok = key < kend_row;
-        if (tree && key >= cached) ok = ok && ((tmask >> (uint32_t)(key - cached)) & 1u);
-        sv[e] = ok ? sv[e] : kMinusBig;
+        for (int e = 0; e < 4; ++e) sv[e] = kb + 4 * grp + e < kend_row ? sv[e] : kMinusBig;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int32_t key = kb + 4 * grp + e;
+          const int32_t u = key - cached;  // new-token index (< 0: a cached key)
+          const bool in_tree = u < 0 || ((tmask >> (uint32_t)(u & 31)) & 1u) != 0;
+          sv[e] = (key < kend_row) & in_tree ? sv[e] : kMinusBig;
+        }
       }
     }
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
