@@ -536,6 +536,40 @@ def main():
                                 "hbm_frac": 2 * copied / (cms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                 "launches": ek["page_copy"][1]}
 
+    if name == "decode_verify_gqa":
+        # prefix-cache page sharing: the first 64 requests read one common
+        # 960-token prefix (60 read-only pages of request 0, page aligned, so
+        # no shared page is appended to) and their own pages after it; timed
+        # against the same batch with every request on its own pages.  The
+        # logical KV bytes are the same; the shared pages are read from HBM
+        # once and from the caches after.
+        import dataclasses
+        reqs = list(range(64))
+        sm, st = sub_batch(meta, reqs, tensors)
+        share = 960 // spec.page_size
+        idx = sm.kv_page_indices.copy()
+        shared = idx[sm.kv_page_indptr[0]:sm.kv_page_indptr[0] + share].copy()
+        for i in range(len(reqs)):
+            idx[sm.kv_page_indptr[i]:sm.kv_page_indptr[i] + share] = shared
+        shm = dataclasses.replace(sm, kv_page_indices=idx)
+        sqo = [int(sm.qo_indptr[r + 1] - sm.qo_indptr[r]) for r in range(sm.batch_size)]
+        sw = work(spec, sqo, sm.kv_len)
+        per_tok = spec.num_kv_heads * (spec.head_dim_qk + spec.head_dim_v) * spec.elem_bytes
+        unique = sw["kv_bytes"] - (len(reqs) - 1) * share * spec.page_size * per_tok
+        entry = {"requests": len(reqs), "shared_prefix_tokens": share * spec.page_size,
+                 "logical_kv_bytes": sw["kv_bytes"], "unique_kv_bytes": int(unique)}
+        for label, m_ in (("own_pages", sm), ("shared_prefix", shm)):
+            log(f"part prefix_share: {label}")
+            _, pms, pk = run_batch(spec, m_, st, args.steps, args.warmup)
+            attn_ms = sum(v[0] * v[1] for k, v in pk.items() if k != "append")
+            entry[label] = {"ms_per_step": pms, "attention_ms": attn_ms,
+                            "kernels_us": {k: v[0] * 1e3 for k, v in pk.items()},
+                            "logical_kv_gbps": (sw["kv_bytes"] + sw["qo_bytes"]) /
+                                               (attn_ms * 1e-3) / 1e9}
+        entry["shared_prefix"]["unique_kv_gbps"] = (unique + sw["qo_bytes"]) / (
+            entry["shared_prefix"]["attention_ms"] * 1e-3) / 1e9
+        parts["prefix_share"] = entry
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on a bounded sample")
