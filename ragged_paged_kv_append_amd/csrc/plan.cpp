@@ -359,6 +359,64 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
                                          slots * rows_per_item(k, 0)), KEY_ALIGN));
   }
 
+  // Latent requests of two row tiles (a query token pair over 128 heads, run
+  // as a pair of workgroups on one XCD) are cut so that every workgroup pair
+  // gets the same number of keys: the requests, longest first, are laid end
+  // to end and cut into equal runs, one per pair, at multiples of KEY_ALIGN
+  // (no piece under kMinPiece keys, none over MLA_MAX_KEYS).  Uniform pieces
+  // packed longest first left the busiest pair with 40% more keys than the
+  // average on the latent workload.  cut_k0[r] holds the first key of each
+  // piece of a cut request and cut_pair[r] its pair.
+  std::vector<std::vector<int64_t>> cut_k0((size_t)B), cut_pair((size_t)B);
+  int64_t cut_pairs = 0;
+  {
+    const int64_t max_wgs = wgs_per_cu(KC_MLA) * cus;
+    bool ok = max_wgs >= 16 && max_wgs % 16 == 0;
+    std::vector<int32_t> reqs;
+    int64_t total = 0;
+    for (int32_t r = 0; r < B && ok; ++r) {
+      const int64_t n = (int64_t)qo[r + 1] - qo[r];
+      if (cls[r] != KC_MLA || n == 0 || kvl[r] == 0) continue;
+      if (n * G <= MLA_ROWS || n * G > 2 * MLA_ROWS) ok = false;  // two row tiles each
+      reqs.push_back(r);
+      total += kvl[r];
+    }
+    if (!ok || reqs.empty() || c.num_kv_heads != 1) reqs.clear();
+    const int64_t kMinPiece = 4 * KEY_ALIGN;
+    if (!reqs.empty()) {
+      cut_pairs = std::min<int64_t>(max_wgs / 2, std::max<int64_t>(1, total / kMinPiece));
+      const int64_t cap = round_up(ceil_div(total, cut_pairs), KEY_ALIGN);
+      std::stable_sort(reqs.begin(), reqs.end(),
+                       [&](int32_t a, int32_t b) { return kvl[a] > kvl[b]; });
+      int64_t pair = 0, room = cap;
+      for (int32_t r : reqs) {
+        const int64_t L = kvl[r];
+        for (int64_t k0 = 0; k0 < L;) {
+          // Pieces start at multiples of KEY_ALIGN: a pair takes whole
+          // KEY_ALIGN runs of what it has left, or a request's whole rest.
+          int64_t avail = std::max<int64_t>(room, 0) / KEY_ALIGN * KEY_ALIGN;
+          // A run that would start a pair's list with a sliver goes to the next pair.
+          if (avail < kMinPiece && avail < L - k0 && pair + 1 < cut_pairs) {
+            ++pair;
+            room = avail = cap;
+          }
+          const bool last_pair = pair + 1 == cut_pairs;
+          int64_t take = last_pair ? L - k0 : std::min(L - k0, avail);
+          if (L - (k0 + take) < kMinPiece) take = L - k0;  // no sliver at the end either
+          take = std::min<int64_t>(take, MLA_MAX_KEYS);
+          cut_k0[(size_t)r].push_back(k0);
+          cut_pair[(size_t)r].push_back(pair);
+          k0 += take;
+          room -= take;
+          if (room <= 0 && !last_pair) {
+            ++pair;
+            room = cap;
+          }
+        }
+      }
+    }
+  }
+
   std::vector<int32_t> split((size_t)B * SP_WORDS, 0);
   int64_t partial_rows = 0;
   for (int32_t r = 0; r < B; ++r) {
@@ -376,6 +434,10 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
       S = std::max<int64_t>(S, 1);
       kc = round_up(ceil_div(L, S), KEY_ALIGN);
       S = ceil_div(L, kc);
+      if (!cut_k0[(size_t)r].empty()) {
+        S = (int64_t)cut_k0[(size_t)r].size();
+        kc = 0;  // pieces of unequal length: cut_k0
+      }
     }
     split[(size_t)r * SP_WORDS + SP_COUNT] = (int32_t)S;
     split[(size_t)r * SP_WORDS + SP_CHUNK] = (int32_t)kc;
@@ -406,10 +468,12 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
         const int64_t t_last = (row1 - 1) / G;
         const bool masked = has_tree && tree_req[(size_t)r];
         const int64_t p_last = (c.causal && !masked) ? cached + t_last : L - 1;
+        const std::vector<int64_t>& cuts = cut_k0[(size_t)r];
         for (int64_t s = 0; s < S; ++s) {
-          const int64_t k0 = s * kc;
+          const int64_t k0 = kc > 0 ? s * kc : cuts[(size_t)s];
           if (k0 > p_last) break;
-          const int64_t k1 = std::min(L, k0 + kc);
+          const int64_t k1 =
+              kc > 0 ? std::min(L, k0 + kc) : (s + 1 < S ? cuts[(size_t)s + 1] : L);
           const int32_t it[IT_WORDS] = {r, g, (int32_t)row0, (int32_t)row1, (int32_t)k0,
                                         (int32_t)k1, (int32_t)s, k};
           items[k].insert(items[k].end(), it, it + IT_WORDS);
@@ -446,6 +510,29 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
   for (int k : {(int)KC_PREFILL, (int)KC_MLA}) {
     const int64_t m = (int64_t)cost[k].size();
     if (m == 0) continue;
+    if (k == KC_MLA && cut_pairs > 0) {
+      // Cut latent requests: each piece's two row tiles go to its pair's
+      // workgroups b and b + 8 (one XCD); a pair runs its pieces in turn.
+      const int64_t n_wgs = 16 * ceil_div(cut_pairs, 8);
+      std::vector<std::vector<int64_t>> lists((size_t)n_wgs);
+      for (int64_t j = 0; j < m; ++j) {
+        const int32_t* it = &items[k][(size_t)j * IT_WORDS];
+        const int64_t pr = cut_pair[(size_t)it[IT_REQ]][(size_t)it[IT_SPLIT]];
+        const int64_t side = it[IT_ROW0] / MLA_ROWS;
+        lists[(size_t)(16 * (pr / 8) + pr % 8 + 8 * side)].push_back(j);
+      }
+      std::vector<int32_t> grouped;
+      grouped.reserve(items[k].size());
+      wg_indptr[k].push_back(0);
+      for (int64_t w = 0; w < n_wgs; ++w) {
+        for (int64_t j : lists[(size_t)w])
+          grouped.insert(grouped.end(), items[k].begin() + j * IT_WORDS,
+                         items[k].begin() + (j + 1) * IT_WORDS);
+        wg_indptr[k].push_back((int32_t)(grouped.size() / IT_WORDS));
+      }
+      items[k].swap(grouped);
+      continue;
+    }
     if (k == KC_MLA && pack_latent_pairs(items[k], cost[k], wgs_per_cu(k) * cus, &wg_indptr[k]))
       continue;
     const int64_t slots = std::min<int64_t>(m, wgs_per_cu(k) * cus);
@@ -521,12 +608,18 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
       }
       const int32_t S = split[(size_t)r * SP_WORDS + SP_COUNT];
       if (S > 1 || kvl[r] == 0) {
-        // Piece s holds keys [s chunk, (s + 1) chunk); the row sees keys up to
-        // pmax, so pieces past pmax / chunk hold nothing for it.
+        // Piece s holds keys [s chunk, (s + 1) chunk) (or from cut_k0[s] for a
+        // cut request); the row sees keys up to pmax, so pieces that start
+        // past pmax hold nothing for it.
         const bool masked = c.causal && !(has_tree && tree_req[(size_t)r]);
         const int64_t pmax = masked ? p : (int64_t)kvl[r] - 1;
         const int64_t chunk = split[(size_t)r * SP_WORDS + SP_CHUNK];
-        const int64_t s_eff = pmax < 0 ? 0 : std::min<int64_t>(S, pmax / chunk + 1);
+        int64_t s_eff = 0;
+        if (pmax >= 0 && chunk > 0) {
+          s_eff = std::min<int64_t>(S, pmax / chunk + 1);
+        } else if (pmax >= 0) {
+          for (int64_t k0c : cut_k0[(size_t)r]) s_eff += k0c <= pmax ? 1 : 0;
+        }
         merge_rows.push_back((int32_t)i);
         merge_info.push_back(split[(size_t)r * SP_WORDS + SP_BASE] + (int32_t)t);
         merge_info.push_back((int32_t)n);

@@ -75,6 +75,7 @@ def check_plan(plan, meta, cfg):
     batch = oracle.Batch(meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices,
                          meta.page_size)
     cover = {}
+    piece = {}  # (request, piece) -> its key range, the same in every item
     for r_, g, row0, row1, k0, k1, s, kc in items.tolist():
         n = batch.qo_len(r_)
         Lr = int(meta.kv_len[r_])
@@ -82,10 +83,31 @@ def check_plan(plan, meta, cfg):
         assert 0 <= row0 < row1 <= n * G
         assert 0 <= k0 < k1 <= Lr
         S, chunk, base = splits[r_]
-        assert 0 <= s < S and k0 == s * chunk and k1 == min(Lr, k0 + chunk)
+        assert 0 <= s < S and piece.setdefault((r_, s), (k0, k1)) == (k0, k1)
+        if chunk > 0:  # equal pieces
+            assert k0 == s * chunk and k1 == min(Lr, k0 + chunk)
         for row in range(row0, row1):
             key = (r_, g, row)
             cover.setdefault(key, []).append((k0, k1))
+    # pieces of unequal length (chunk 0) tile the request in order, starting at
+    # multiples of 64
+    starts = {}
+    for r_ in range(B):
+        S, chunk, base = splits[r_]
+        if chunk == 0 and S > 0:
+            rng = [piece[(r_, s)] for s in range(S)]
+            assert rng[0][0] == 0 and rng[-1][1] == int(meta.kv_len[r_])
+            assert all(a[1] == b[0] for a, b in zip(rng, rng[1:]))
+            assert all(a[0] % 64 == 0 for a in rng)
+            starts[r_] = [a[0] for a in rng]
+
+    def live(r_, S, chunk, pmax):
+        """Pieces that hold a key at or below pmax."""
+        if pmax < 0:
+            return 0
+        if chunk > 0:
+            return min(S, pmax // chunk + 1)
+        return sum(1 for k0 in starts[r_] if k0 <= pmax)
     for r_ in range(B):
         n = batch.qo_len(r_)
         Lr = int(meta.kv_len[r_])
@@ -105,7 +127,7 @@ def check_plan(plan, meta, cfg):
                 for (a0, a1), (b0, b1) in zip(ranges, ranges[1:]):
                     assert a1 == b0
                 assert ranges[-1][1] > pmax
-                assert len(ranges) == min(S, pmax // chunk + 1)
+                assert len(ranges) == live(r_, S, chunk, pmax)
         for t in range(n):
             i = int(meta.qo_indptr[r_]) + t
             assert (i in merge_rows) == (S > 1)
@@ -121,8 +143,7 @@ def check_plan(plan, meta, cfg):
         Lr = int(meta.kv_len[r_])
         S, chunk, base = splits[r_]
         pmax = Lr - n + t if cfg.causal else Lr - 1
-        live = 0 if pmax < 0 else min(S, pmax // chunk + 1)
-        assert tuple(minfo[x].tolist()) == (base + t, n, live, 0), (i, minfo[x])
+        assert tuple(minfo[x].tolist()) == (base + t, n, live(r_, S, chunk, pmax), 0), (i, minfo[x])
     return items, splits
 
 
