@@ -282,7 +282,8 @@ rpa_status rpa_profile_reset(void);
  * `cap` int32 values of the named table into `dst` and stores the table's
  * full length in *len.  Names: "items" (8 int32 per work item: request,
  * kv head, first row, end row, first key, end key, split index, kernel
- * class), "splits" (3 int32 per request: number of pieces, keys per piece,
+ * class), "splits" (3 int32 per request: number of pieces, keys per piece
+ * (0 when the pieces differ in length; the items then give their bounds),
  * first partial row), "append" (2 int32 per new token: page id, slot),
  * "wg_prefill" / "wg_mla" (workgroup b runs items [v[b], v[b + 1]) of that
  * class), "merge_rows" (rows whose pieces are merged), "merge_info" (4 int32

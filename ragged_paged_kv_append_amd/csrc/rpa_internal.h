@@ -27,7 +27,8 @@ enum ItemField : int32_t {
 
 // Per-request split record: 3 int32 values.
 //   number of pieces S_r, keys per piece (pieces are [s*kc, (s+1)*kc) clipped
-//   to kv_len), first partial row of the request (partial row of token t in
+//   to kv_len; 0 when the pieces differ in length, whose bounds the items
+//   carry), first partial row of the request (partial row of token t in
 //   piece s is base + s * n_r + t).  S_r == 1 means items write the final
 //   output directly and there is nothing to merge.
 enum SplitField : int32_t { SP_COUNT = 0, SP_CHUNK, SP_BASE, SP_WORDS };
