@@ -500,8 +500,9 @@ RPA_EXPORT rpa_status rpa_plan_debug_dump(const rpa_plan* plan, const char* name
   } else if (nm == "append") {
     src = blob + plan->off_append;
     n = (int64_t)plan->total_q * 2;
-  } else if (nm == "wg_prefill" || nm == "wg_mla") {
-    const int k = nm == "wg_prefill" ? rpa::KC_PREFILL : rpa::KC_MLA;
+  } else if (nm == "wg_prefill" || nm == "wg_mla" || nm == "wg_decode") {
+    const int k = nm == "wg_prefill" ? rpa::KC_PREFILL
+                                     : (nm == "wg_mla" ? rpa::KC_MLA : rpa::KC_DECODE);
     src = blob + plan->off_wg[k];
     n = plan->n_items[k] > 0 ? (int64_t)plan->n_wgs[k] + 1 : 0;
   } else if (nm == "merge_rows") {

@@ -145,7 +145,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
   const int col = lane & 15;  // query row of S^T / P^T / O^T columns; key row of the K operand
   const int grp = lane >> 4;  // which 32-element quarter of a row this lane reads
 
-  const int32_t* it = p.items[KC_DECODE] + (int64_t)blockIdx.x * IT_WORDS;
+  // This workgroup's items (its wg_indptr range), in turn.
+  const int32_t wb0 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_DECODE][blockIdx.x]);
+  const int32_t wb1 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_DECODE][blockIdx.x + 1]);
+  for (int32_t idx = wb0; idx < wb1; ++idx) {
+  const int32_t* it = p.items[KC_DECODE] + (int64_t)idx * IT_WORDS;
   const int32_t r = it[IT_REQ], g = it[IT_KVHEAD], rows = it[IT_ROW1];
   const int32_t k0 = it[IT_K0], k1 = it[IT_K1], s = it[IT_SPLIT];
   const int32_t G = p.group;
@@ -269,6 +273,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
   const int voff = 4 * (col & 1);
 
   const int32_t ntiles = (kend - k0 + kTile - 1) / kTile;
+  // The previous item's output stores count in the same vector-memory counter
+  // and may complete after later loads, which would let the counted waits
+  // below pass early: drain them before this item's DMA stream starts.
+  if (idx > wb0) wait_vmem<0>();
 #pragma unroll
   for (int j = 0; j < kStages - 1; ++j)
     if (j < ntiles) issue(k0 + j * kTile, j);
@@ -350,7 +358,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
   // Row sum over the four lane groups, then normalise and store.
   float ltot = lsum + __shfl_xor(lsum, 16, 64);
   ltot += __shfl_xor(ltot, 32, 64);
-  if (!row_ok) return;
+  if (row_ok) {
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   const float lse_nat = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
   const int32_t i = q0 + t;
@@ -375,6 +383,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
           make_float4(acc[nb][0] * inv, acc[nb][1] * inv, acc[nb][2] * inv, acc[nb][3] * inv);
     if (grp == 0) p.part_lse[prow * p.num_qo_heads + h] = lse_nat;
   }
+  }  // row_ok
+  }  // items
 }
 
 hipError_t launch_decode(const DevPlan& p, const void* q, const void* k_cache, const void* v_cache,
@@ -387,7 +397,7 @@ hipError_t launch_decode(const DevPlan& p, const void* q, const void* k_cache, c
     const int v = e ? atoi(e) : 3;
     return (v == 2 || v == 4 || v == 6) ? v : 3;
   }();
-  const dim3 grid(p.n_items[KC_DECODE]), block(64);
+  const dim3 grid(p.n_wgs[KC_DECODE]), block(64);
   const bf16_t* qq = static_cast<const bf16_t*>(q);
   const bf16_t* kk = static_cast<const bf16_t*>(k_cache);
   const bf16_t* vv = static_cast<const bf16_t*>(v_cache);

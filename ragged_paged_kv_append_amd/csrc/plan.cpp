@@ -359,62 +359,64 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
                                          slots * rows_per_item(k, 0)), KEY_ALIGN));
   }
 
-  // Latent requests of two row tiles (a query token pair over 128 heads, run
-  // as a pair of workgroups on one XCD) are cut so that every workgroup pair
-  // gets the same number of keys: the requests, longest first, are laid end
-  // to end and cut into equal runs, one per pair, at multiples of KEY_ALIGN
-  // (no piece under kMinPiece keys, none over MLA_MAX_KEYS).  Uniform pieces
-  // packed longest first left the busiest pair with 40% more keys than the
-  // average on the latent workload.  cut_k0[r] holds the first key of each
-  // piece of a cut request and cut_pair[r] its pair.
-  std::vector<std::vector<int64_t>> cut_k0((size_t)B), cut_pair((size_t)B);
-  int64_t cut_pairs = 0;
+  // Requests cut into equal runs of keys, one run per "bin" of workgroups
+  // that run side by side: the requests, longest first, are laid end to end
+  // and cut at multiples of KEY_ALIGN (no piece under kMinPiece keys unless
+  // the request is shorter, none over max_piece; kMinPiece is 4 KEY_ALIGN for
+  // latent pieces, each of which costs a 144 KiB Q load and a 256 KiB partial).  cut_k0[r] holds the first
+  // key of each piece of a cut request and cut_bin[r] its bin.
+  //   Latent requests of two row tiles (a query token pair over 128 heads):
+  //   a bin is a pair of workgroups on one XCD.  Equal pieces packed longest
+  //   first left the busiest pair with 40% more keys than the average.
+  std::vector<std::vector<int64_t>> cut_k0((size_t)B), cut_bin((size_t)B);
+  int64_t cut_bins[KC_COUNT] = {0, 0, 0, 0};
+  auto cut_requests = [&](std::vector<int32_t> reqs, int64_t bins, int64_t max_piece,
+                          int64_t kMinPiece) {
+    int64_t total = 0;
+    for (int32_t r : reqs) total += kvl[r];
+    bins = std::min<int64_t>(bins, std::max<int64_t>(1, total / kMinPiece));
+    const int64_t cap = round_up(ceil_div(total, bins), KEY_ALIGN);
+    std::stable_sort(reqs.begin(), reqs.end(), [&](int32_t a, int32_t b) { return kvl[a] > kvl[b]; });
+    int64_t bin = 0, room = cap;
+    for (int32_t r : reqs) {
+      const int64_t L = kvl[r];
+      for (int64_t k0 = 0; k0 < L;) {
+        // Pieces start at multiples of KEY_ALIGN: a bin takes whole KEY_ALIGN
+        // runs of what it has left, or a request's whole rest.
+        int64_t avail = std::max<int64_t>(room, 0) / KEY_ALIGN * KEY_ALIGN;
+        // A run that would start a bin's list with a sliver goes to the next bin.
+        if (avail < kMinPiece && avail < L - k0 && bin + 1 < bins) {
+          ++bin;
+          room = avail = cap;
+        }
+        const bool last_bin = bin + 1 == bins;
+        int64_t take = last_bin ? L - k0 : std::min(L - k0, avail);
+        if (L - (k0 + take) < kMinPiece) take = L - k0;  // no sliver at the end either
+        take = std::min<int64_t>(take, max_piece);
+        cut_k0[(size_t)r].push_back(k0);
+        cut_bin[(size_t)r].push_back(bin);
+        k0 += take;
+        room -= take;
+        if (room <= 0 && !last_bin) {
+          ++bin;
+          room = cap;
+        }
+      }
+    }
+    return bins;
+  };
   {
     const int64_t max_wgs = wgs_per_cu(KC_MLA) * cus;
-    bool ok = max_wgs >= 16 && max_wgs % 16 == 0;
+    bool ok = max_wgs >= 16 && max_wgs % 16 == 0 && c.num_kv_heads == 1;
     std::vector<int32_t> reqs;
-    int64_t total = 0;
     for (int32_t r = 0; r < B && ok; ++r) {
       const int64_t n = (int64_t)qo[r + 1] - qo[r];
       if (cls[r] != KC_MLA || n == 0 || kvl[r] == 0) continue;
       if (n * G <= MLA_ROWS || n * G > 2 * MLA_ROWS) ok = false;  // two row tiles each
       reqs.push_back(r);
-      total += kvl[r];
     }
-    if (!ok || reqs.empty() || c.num_kv_heads != 1) reqs.clear();
-    const int64_t kMinPiece = 4 * KEY_ALIGN;
-    if (!reqs.empty()) {
-      cut_pairs = std::min<int64_t>(max_wgs / 2, std::max<int64_t>(1, total / kMinPiece));
-      const int64_t cap = round_up(ceil_div(total, cut_pairs), KEY_ALIGN);
-      std::stable_sort(reqs.begin(), reqs.end(),
-                       [&](int32_t a, int32_t b) { return kvl[a] > kvl[b]; });
-      int64_t pair = 0, room = cap;
-      for (int32_t r : reqs) {
-        const int64_t L = kvl[r];
-        for (int64_t k0 = 0; k0 < L;) {
-          // Pieces start at multiples of KEY_ALIGN: a pair takes whole
-          // KEY_ALIGN runs of what it has left, or a request's whole rest.
-          int64_t avail = std::max<int64_t>(room, 0) / KEY_ALIGN * KEY_ALIGN;
-          // A run that would start a pair's list with a sliver goes to the next pair.
-          if (avail < kMinPiece && avail < L - k0 && pair + 1 < cut_pairs) {
-            ++pair;
-            room = avail = cap;
-          }
-          const bool last_pair = pair + 1 == cut_pairs;
-          int64_t take = last_pair ? L - k0 : std::min(L - k0, avail);
-          if (L - (k0 + take) < kMinPiece) take = L - k0;  // no sliver at the end either
-          take = std::min<int64_t>(take, MLA_MAX_KEYS);
-          cut_k0[(size_t)r].push_back(k0);
-          cut_pair[(size_t)r].push_back(pair);
-          k0 += take;
-          room -= take;
-          if (room <= 0 && !last_pair) {
-            ++pair;
-            room = cap;
-          }
-        }
-      }
-    }
+    if (ok && !reqs.empty())
+      cut_bins[KC_MLA] = cut_requests(reqs, max_wgs / 2, MLA_MAX_KEYS, 4 * KEY_ALIGN);
   }
 
   std::vector<int32_t> split((size_t)B * SP_WORDS, 0);
@@ -510,14 +512,14 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
   for (int k : {(int)KC_PREFILL, (int)KC_MLA}) {
     const int64_t m = (int64_t)cost[k].size();
     if (m == 0) continue;
-    if (k == KC_MLA && cut_pairs > 0) {
+    if (k == KC_MLA && cut_bins[KC_MLA] > 0) {
       // Cut latent requests: each piece's two row tiles go to its pair's
       // workgroups b and b + 8 (one XCD); a pair runs its pieces in turn.
-      const int64_t n_wgs = 16 * ceil_div(cut_pairs, 8);
+      const int64_t n_wgs = 16 * ceil_div(cut_bins[KC_MLA], 8);
       std::vector<std::vector<int64_t>> lists((size_t)n_wgs);
       for (int64_t j = 0; j < m; ++j) {
         const int32_t* it = &items[k][(size_t)j * IT_WORDS];
-        const int64_t pr = cut_pair[(size_t)it[IT_REQ]][(size_t)it[IT_SPLIT]];
+        const int64_t pr = cut_bin[(size_t)it[IT_REQ]][(size_t)it[IT_SPLIT]];
         const int64_t side = it[IT_ROW0] / MLA_ROWS;
         lists[(size_t)(16 * (pr / 8) + pr % 8 + 8 * side)].push_back(j);
       }
@@ -585,6 +587,16 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
       wg_indptr[k].push_back((int32_t)(grouped.size() / IT_WORDS));
     }
     items[k].swap(grouped);
+  }
+
+  // Decode: one item per workgroup, in the heaviest-first order above, so
+  // the dispatcher hands each freed slot the next item.  (Cutting the
+  // requests into one equal run per resident workgroup, each running its
+  // pieces in turn, was 5% faster on long GQA verify batches but 10% slower
+  // on the 7B decode batch.)
+  if (!items[KC_DECODE].empty()) {
+    const int32_t m = (int32_t)(items[KC_DECODE].size() / IT_WORDS);
+    for (int32_t j = 0; j <= m; ++j) wg_indptr[KC_DECODE].push_back(j);
   }
 
   // ---- append map and merge rows --------------------------------------------------

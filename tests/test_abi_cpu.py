@@ -132,6 +132,11 @@ def check_plan(plan, meta, cfg):
             i = int(meta.qo_indptr[r_]) + t
             assert (i in merge_rows) == (S > 1)
             assert tuple(app[i]) == oracle.slot_of(batch, r_, c + t)
+    # every decode item sits in exactly one workgroup list
+    n_dec = int(np.sum(items[:, 7] == 1))
+    if n_dec:
+        wg = rpa.rpa_plan_debug_dump(plan, "wg_decode")
+        assert wg[0] == 0 and wg[-1] == n_dec and np.all(np.diff(wg) >= 0)
     # each merge row's first partial row, piece stride and live piece count
     mrows = rpa.rpa_plan_debug_dump(plan, "merge_rows").tolist()
     minfo = rpa.rpa_plan_debug_dump(plan, "merge_info").reshape(-1, 4)
@@ -191,10 +196,18 @@ def test_planner_splits_long_requests(L):
     assert splits[0][0] > 1 and splits[1][0] == 1
     items = rpa.rpa_plan_debug_dump(plan, "items").reshape(-1, 8)
     costs = (items[:, 5] - items[:, 4]) * (items[:, 3] - items[:, 2])
-    # heaviest items are listed first within each kernel class
+    # heaviest items are listed first within each kernel class, or within each
+    # workgroup's list where the class has them
+    lists = {1: "wg_decode", 2: "wg_prefill", 3: "wg_mla"}
     for k in set(items[:, 7].tolist()):
         ck = costs[items[:, 7] == k]
-        assert np.all(np.diff(ck) <= 0)
+        if k in lists:
+            wg = rpa.rpa_plan_debug_dump(plan, lists[k])
+            assert wg[0] == 0 and wg[-1] == len(ck)
+            for b in range(len(wg) - 1):
+                assert np.all(np.diff(ck[wg[b]:wg[b + 1]]) <= 0)
+        else:
+            assert np.all(np.diff(ck) <= 0)
 
 
 @pytest.mark.parametrize("case", ["one_shot_8192", "mixed_7b", "mla_absorbed", "chunk_15"])
