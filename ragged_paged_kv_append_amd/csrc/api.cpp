@@ -53,6 +53,7 @@ rpa::DevPlan dev_plan(const rpa_plan* plan) {
   p.tree_mask = plan->off_tree_mask >= 0
                     ? reinterpret_cast<const uint32_t*>(base + plan->off_tree_mask) : nullptr;
   p.n_merge_rows = plan->n_merge_rows;
+  p.dec_stages = plan->dec_stages;
   char* ws = static_cast<char*>(plan->d_ws);
   p.part_o = reinterpret_cast<float*>(ws + plan->part_o_off);
   p.part_lse = reinterpret_cast<float*>(ws + plan->part_lse_off);

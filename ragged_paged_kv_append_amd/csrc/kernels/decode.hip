@@ -389,14 +389,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
 
 hipError_t launch_decode(const DevPlan& p, const void* q, const void* k_cache, const void* v_cache,
                          Strides ks, Strides vs, void* o, float* lse, hipStream_t stream) {
-  // Ring depth: 3 tiles by default (24 KiB of LDS per wave, so six waves fit a
-  // compute unit with two tiles each in flight); RPA_DECODE_STAGES in
-  // {3, 4, 6} overrides it (a tuning knob, read once).
-  static const int stages = [] {
+  // Ring depth: the planner's choice (3 tiles, 24 KiB of LDS per wave, six
+  // waves per CU, for one item per workgroup; 2 tiles, 16 KiB, for the cut
+  // lists it sizes for eight resident waves per CU).  RPA_DECODE_STAGES in
+  // {2, 3, 4, 6} overrides it (a tuning knob, read once).
+  static const int forced = [] {
     const char* e = getenv("RPA_DECODE_STAGES");
-    const int v = e ? atoi(e) : 3;
-    return (v == 2 || v == 4 || v == 6) ? v : 3;
+    const int v = e ? atoi(e) : 0;
+    return (v == 2 || v == 3 || v == 4 || v == 6) ? v : 0;
   }();
+  const int stages = forced ? forced : (p.dec_stages == 2 ? 2 : 3);
   const dim3 grid(p.n_wgs[KC_DECODE]), block(64);
   const bf16_t* qq = static_cast<const bf16_t*>(q);
   const bf16_t* kk = static_cast<const bf16_t*>(k_cache);

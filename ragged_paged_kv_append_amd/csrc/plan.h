@@ -24,6 +24,7 @@ struct rpa_plan {
   int64_t off_wg[rpa::KC_COUNT] = {0, 0, 0, 0};   // wg_indptr tables (tile classes)
   int32_t n_wgs[rpa::KC_COUNT] = {0, 0, 0, 0};
   int32_t n_merge_rows = 0;
+  int32_t dec_stages = 3;  // decode ring depth the plan's decode lists are sized for
   int64_t partial_rows = 0;
 
   // Workspace layout (bytes from the workspace base).

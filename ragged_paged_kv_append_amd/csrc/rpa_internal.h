@@ -71,6 +71,7 @@ struct DevPlan {
   int32_t n_items[KC_COUNT];
   int32_t n_wgs[KC_COUNT];      // workgroups of each class's launch
   int32_t n_merge_rows;
+  int32_t dec_stages;           // decode LDS ring depth (2 or 3) chosen by the planner
   int32_t batch_size;
   int32_t total_q;
   int32_t num_qo_heads;
