@@ -281,7 +281,7 @@ def roofline_for(spec, meta, plan, kernels):
             "avg_launch_us": avg_ms * 1e3, "algorithmic_per_launch": {"bytes": nbytes}}
 
 
-def run_chunked(spec, steps, warmup):
+def run_chunked(spec, steps, warmup, parts=True):
     """The 8192-token GQA prompt run as 16 chunks of 512 (append, then
     attention over the pages, per chunk) and one-shot.  Every chunk step is
     timed on its own after the whole prompt has been appended once (the append
@@ -330,7 +330,7 @@ def run_chunked(spec, steps, warmup):
     o_s = torch.empty_like(o)
     lse_s = torch.empty_like(lse)
     split_chunks = []
-    for i in range(len(chunks)):
+    for i in range(len(chunks) if parts else 0):
         a = i * C
         n = min(C, L - a)
         sp = rpa.SplitChunkAttention(cfg, [0, n], [a + n], [0, len(pages)], pages, meta.num_pages)
@@ -345,6 +345,8 @@ def run_chunked(spec, steps, warmup):
                              "flops": w["flops"], "tflops": w["flops"] / (attn_ms * 1e-3) / 1e12,
                              "kernels_us": {kk: t * 1e3 for kk, (t, c) in kernels.items()},
                              "launches": {kk: c for kk, (t, c) in kernels.items()}})
+    if not parts:
+        return per_chunk, None, split_chunks
     one = step_of(0, L)
     ms1, k1 = timed_steps(one, max(3, steps // 4), 1)
     w1 = work(spec, [L], [L])
@@ -432,6 +434,9 @@ def main():
     ap.add_argument("--workload", default="mixed_7b",
                     choices=["mixed_7b", "decode_verify_gqa", "mla_absorbed", "chunked_gqa"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parts", action="store_true",
+                    help="time the workload's step only (no sub-batch or variant parts), "
+                         "so that a profiler's per-kernel averages cover that step alone")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                          "kernel that FETCH_SIZE / WRITE_SIZE counter readings are scaled by)")
@@ -473,7 +478,7 @@ def main():
         value = w["flops"] / (ms * 1e-3) / 1e12
 
     parts = {}
-    if name == "mixed_7b":
+    if name == "mixed_7b" and not args.no_parts:
         dec = [r for r in range(meta.batch_size) if qo[r] == 1]
         pre = [r for r in range(meta.batch_size) if qo[r] > 1]
         for label, reqs in (("decode", dec), ("prefill_chunk", pre)):
@@ -493,7 +498,7 @@ def main():
                 entry.update({"tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS})
             parts[label] = entry
 
-    if name == "decode_verify_gqa":
+    if name == "decode_verify_gqa" and not args.no_parts:
         # the same step with every verify request's 4 new tokens as a draft
         # tree (root, two children of the root, one grandchild) instead of a
         # chain: the mask applies to the tiles holding new tokens only
@@ -509,7 +514,7 @@ def main():
                                 "slowdown_vs_chain": attn_ms / base_ms,
                                 "tree_parents": [-1, 0, 0, 1]}
 
-    if name == "decode_verify_gqa":
+    if name == "decode_verify_gqa" and not args.no_parts:
         # page export for a sharded transfer: the K and V pages of the first 64
         # requests, each as two half-head shards, gathered from the HND pools
         # into packed shard buffers (one contiguous run per page and shard)
@@ -536,7 +541,7 @@ def main():
                                 "hbm_frac": 2 * copied / (cms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                 "launches": ek["page_copy"][1]}
 
-    if name == "decode_verify_gqa":
+    if name == "decode_verify_gqa" and not args.no_parts:
         # prefix-cache page sharing: the first 64 requests read one common
         # 960-token prefix (60 read-only pages of request 0, page aligned, so
         # no shared page is appended to) and their own pages after it; timed
@@ -617,7 +622,8 @@ def main_chunked(args):
     spec = workloads.SPECS["chunked_gqa"]
     log(f"workload chunked_gqa: timing each of 16 chunk steps, {args.steps} steps after "
         f"{args.warmup} warmup")
-    per_chunk, one_shot, split_chunks = run_chunked(spec, args.steps, args.warmup)
+    per_chunk, one_shot, split_chunks = run_chunked(spec, args.steps, args.warmup,
+                                                    parts=not args.no_parts)
     flops = sum(c["flops"] for c in per_chunk)
     attn_ms = sum(c["attention_ms"] for c in per_chunk)
     step_ms = sum(c["ms_per_step"] for c in per_chunk)
@@ -647,10 +653,11 @@ def main_chunked(args):
         "parts": {"chunks": [{k: c[k] for k in ("chunk", "kv_len", "tflops", "attention_ms",
                                                 "kernels_us")} for c in per_chunk],
                   "one_shot": one_shot,
-                  "split": {"tflops": sum(c["flops"] for c in split_chunks)
-                            / (sum(c["attention_ms"] for c in split_chunks) * 1e-3) / 1e12,
-                            "chunks": [{k: c[k] for k in ("chunk", "tflops", "attention_ms",
-                                                          "kernels_us")} for c in split_chunks]}},
+                  "split": None if not split_chunks else {
+                      "tflops": sum(c["flops"] for c in split_chunks)
+                      / (sum(c["attention_ms"] for c in split_chunks) * 1e-3) / 1e12,
+                      "chunks": [{k: c[k] for k in ("chunk", "tflops", "attention_ms",
+                                                    "kernels_us")} for c in split_chunks]}},
     }
     print(json.dumps(line), flush=True)
 
