@@ -1,4 +1,4 @@
-// Which specialised kernel classes this build provides.  Pure C++ so the
+// Which specialised kernel classes the compiled library provides.  Pure C++ so the
 // planner links without HIP.
 #include "plan.h"
 
