@@ -148,18 +148,59 @@ def request_classes(plan):
 
 
 ATTN_KERNELS = ("generic", "decode", "prefill", "mla")
+SCRUB_BYTES = 1 << 30   # > 2x the 256 MB MALL: evicts it (and every L2) between timed steps
+
+_hip = None
+_scrub = None
+
+
+def hip_events(n):
+    """n timing events without the system-scope fence (creating them through
+    torch would add a cache flush of several microseconds to each record)."""
+    import ctypes
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        _hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        _hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                             ctypes.c_void_p]
+        _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        if _hip.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        evs.append(e)
+    return evs
+
+
+def scrub():
+    """Writes SCRUB_BYTES of device memory (outside the timed events), so that
+    no step finds the previous step's data in the MALL or an L2."""
+    import torch
+    global _scrub
+    if _scrub is None:
+        _scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.int32, device="cuda")
+    _scrub.fill_(int(time.perf_counter_ns() & 0xffff))
 
 
 def timed_steps(step, steps, warmup):
-    """Runs warmup steps, then times exactly `steps` steps; returns (ms/step,
-    {kernel: (avg ms, launches per step)}) with per-kernel HIP-event timings.
+    """Runs `warmup` steps, then times exactly `steps` steps.  Each timed step
+    is bracketed by its own pair of HIP events on the launch stream, with a
+    SCRUB_BYTES write before it (outside the events).  Returns a dict with the
+    median, minimum and mean step time (ms), the wall-clock time of the whole
+    timed loop per step (scrubs included), and per-kernel timings
+    {kernel: (avg ms, launches per step)}.
 
-    A short profiling pass (every kernel bracketed by events, outside the
-    timed region) finds the attention kernel that takes the most time per
-    step; the timed steps then carry events around that kernel only, so the
-    step time holds one event pair per launch of it rather than one per
-    kernel.  The dominant kernel's figures come from the timed steps, the
-    others' from the profiling pass."""
+    A short profiling pass first (every kernel bracketed by events, scrubbed
+    steps, outside the timed loop) finds the attention kernel that takes the
+    most time per step; the timed steps carry library events around that
+    kernel only, which give its average launch time over the timed region.
+    The other kernels' figures come from the profiling pass."""
+    import ctypes
+    import statistics
     import torch
     import ragged_paged_kv_append_amd as rpa
     for _ in range(warmup):
@@ -179,26 +220,43 @@ def timed_steps(step, steps, warmup):
     rpa.rpa_profile_select(None)
     rpa.rpa_profile_enable(True)
     for _ in range(prof_steps):
+        scrub()
         step()
     torch.cuda.synchronize()
     rpa.rpa_profile_enable(False)
     kernels = read_all(prof_steps)
     attn = [k for k in kernels if k in ATTN_KERNELS]
-    only = [max(attn, key=lambda k: kernels[k][0] * kernels[k][1])] if attn else None
+    only = [max(attn, key=lambda k: kernels[k][0] * kernels[k][1])] if attn else ["append"]
 
+    evs = hip_events(2 * steps)
+    stream = torch.cuda.current_stream().cuda_stream
     rpa.rpa_profile_reset()
     rpa.rpa_profile_select(only)
     rpa.rpa_profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
+        scrub()
+        _hip.hipEventRecord(evs[2 * i], stream)
         step()
+        _hip.hipEventRecord(evs[2 * i + 1], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     rpa.rpa_profile_enable(False)
     rpa.rpa_profile_select(None)
     kernels.update(read_all(steps))
-    return 1e3 * (t1 - t0) / steps, kernels
+    per_step = []
+    for i in range(steps):
+        ms = ctypes.c_float()
+        _hip.hipEventSynchronize(evs[2 * i + 1])
+        if _hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * i], evs[2 * i + 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        per_step.append(float(ms.value))
+    for e in evs:
+        _hip.hipEventDestroy(e)
+    return {"median_ms": statistics.median(per_step), "min_ms": min(per_step),
+            "mean_ms": statistics.fmean(per_step), "wall_ms": 1e3 * (t1 - t0) / steps,
+            "kernels": kernels}
 
 
 def run_batch(spec, meta, tensors, steps, warmup, tree_masks=None):
@@ -214,10 +272,10 @@ def run_batch(spec, meta, tensors, steps, warmup, tree_masks=None):
                             dtype=tensors["q"].dtype, device=tensors["q"].device),
            "lse": torch.empty((meta.total_q, spec.num_qo_heads), dtype=torch.float32,
                               device=tensors["q"].device)}
-    ms, kernels = timed_steps(step, steps, warmup)
+    tm = timed_steps(step, steps, warmup)
     if not torch.isfinite(out["o"].float()).all():
         raise RuntimeError("non-finite attention output")
-    return plan, ms, kernels
+    return plan, tm
 
 
 KERNEL_SOURCES = {"generic": "basic.hip", "decode": "decode.hip", "prefill": "prefill.hip",
@@ -250,6 +308,16 @@ def measured_traffic(workload, kernel):
     if not entry or entry.get("src_hash") != kernel_source_hash(kernel):
         return None
     return entry["traffic_bytes"]
+
+
+def append_entry(w, kernels):
+    """KV append as bandwidth: every appended byte is read once and written once."""
+    if "append" not in kernels:
+        return None
+    us = kernels["append"][0] * 1e3
+    nbytes = w["append_bytes"]
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"us": us, "bytes": nbytes, "gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS}
 
 
 def roofline_for(spec, meta, plan, kernels):
@@ -318,10 +386,12 @@ def run_chunked(spec, steps, warmup, parts=True):
     for i, st in enumerate(chunks):
         a = i * C
         n = min(C, L - a)
-        ms, kernels = timed_steps(st, steps, warmup)
+        tm = timed_steps(st, steps, warmup)
+        kernels = tm["kernels"]
         w = work(spec, [n], [a + n])
         attn_ms = sum(t * c for name, (t, c) in kernels.items() if name != "append")
-        per_chunk.append({"chunk": i, "kv_len": a + n, "ms_per_step": ms, "attention_ms": attn_ms,
+        per_chunk.append({"chunk": i, "kv_len": a + n, "ms_per_step": tm["median_ms"],
+                          "ms_per_step_min": tm["min_ms"], "attention_ms": attn_ms,
                           "flops": w["flops"], "tflops": w["flops"] / (attn_ms * 1e-3) / 1e12,
                           "kernels_us": {kk: t * 1e3 for kk, (t, c) in kernels.items()},
                           "launches": {kk: c for kk, (t, c) in kernels.items()}})
@@ -338,7 +408,8 @@ def run_chunked(spec, steps, warmup, parts=True):
         def st(sp=sp, a=a, n=n):
             sp.run(q[a:a + n], k[a:a + n], v[a:a + n], k_pool, v_pool, o=o_s[a:a + n],
                    lse=lse_s[a:a + n])
-        ms, kernels = timed_steps(st, steps, warmup)
+        tm = timed_steps(st, steps, warmup)
+        kernels = tm["kernels"]
         w = work(spec, [n], [a + n])
         attn_ms = sum(t * c for name, (t, c) in kernels.items())
         split_chunks.append({"chunk": i, "kv_len": a + n, "attention_ms": attn_ms,
@@ -348,10 +419,11 @@ def run_chunked(spec, steps, warmup, parts=True):
     if not parts:
         return per_chunk, None, split_chunks
     one = step_of(0, L)
-    ms1, k1 = timed_steps(one, max(3, steps // 4), 1)
+    tm1 = timed_steps(one, max(3, steps // 4), 1)
+    k1 = tm1["kernels"]
     w1 = work(spec, [L], [L])
     attn1 = sum(t * c for name, (t, c) in k1.items() if name != "append")
-    one_shot = {"ms_per_step": ms1, "attention_ms": attn1, "flops": w1["flops"],
+    one_shot = {"ms_per_step": tm1["median_ms"], "attention_ms": attn1, "flops": w1["flops"],
                 "tflops": w1["flops"] / (attn1 * 1e-3) / 1e12,
                 "kernels_us": {kk: t * 1e3 for kk, (t, c) in k1.items()}}
     return per_chunk, one_shot, split_chunks
@@ -365,11 +437,12 @@ def run_chunked(spec, steps, warmup, parts=True):
 def cpu_baseline(spec, meta, tensors, requests, unit):
     import numpy as np
     import oracle
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        threads = 1
+        blas_threads = None
 
     def raw(t):
         import torch
@@ -398,8 +471,8 @@ def cpu_baseline(spec, meta, tensors, requests, unit):
     qo = [int(sub.qo_indptr[r + 1] - sub.qo_indptr[r]) for r in range(sub.batch_size)]
     w = work(spec, qo, sub.kv_len)
     value = (w["kv_bytes"] / secs / 1e9) if unit == "GB/s" else (w["flops"] / secs / 1e12)
-    return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
-            "seconds": secs,
+    return {"value": value, "unit": unit, "cores": cores, "blas_threads": blas_threads,
+            "kind": "oracle", "seconds": secs,
             "sample": f"fp64 numpy oracle attention over {len(requests)} of {meta.batch_size} "
                       f"requests of the same workload ({w['kv_bytes'] / 1e9:.3f} GB of KV, "
                       f"{w['flops'] / 1e9:.2f} GFLOP)"}
@@ -467,7 +540,8 @@ def main():
     w = work(spec, qo, meta.kv_len)
 
     log(f"workload {name}: timing {args.steps} steps after {args.warmup} warmup")
-    plan, ms, kernels = run_batch(spec, meta, tensors, args.steps, args.warmup)
+    plan, tm = run_batch(spec, meta, tensors, args.steps, args.warmup)
+    ms, kernels = tm["median_ms"], tm["kernels"]
     roof = roofline_for(spec, meta, plan, kernels)
     plan_ms = plan_host_ms(spec, meta)
 
@@ -486,7 +560,8 @@ def main():
             log(f"part {label}: {len(reqs)} requests")
             sqo = [int(sm.qo_indptr[r + 1] - sm.qo_indptr[r]) for r in range(sm.batch_size)]
             sw = work(spec, sqo, sm.kv_len)
-            _, pms, pk = run_batch(spec, sm, st, args.steps, args.warmup)
+            _, ptm = run_batch(spec, sm, st, args.steps, args.warmup)
+            pms, pk = ptm["median_ms"], ptm["kernels"]
             attn_ms = sum(v[0] * v[1] for k, v in pk.items() if k != "append")
             entry = {"requests": len(reqs), "ms_per_step": pms, "attention_ms": attn_ms,
                      "kernels_us": {k: v[0] * 1e3 for k, v in pk.items()}}
@@ -504,7 +579,8 @@ def main():
         # chain: the mask applies to the tiles holding new tokens only
         masks = [tree_of([-1, 0, 0, 1]) if qo[r] == 4 else None for r in range(meta.batch_size)]
         log("part tree_verify: verify requests as draft trees")
-        _, tms, tk = run_batch(spec, meta, tensors, args.steps, args.warmup, tree_masks=masks)
+        _, ttm = run_batch(spec, meta, tensors, args.steps, args.warmup, tree_masks=masks)
+        tms, tk = ttm["median_ms"], ttm["kernels"]
         attn_ms = sum(v[0] * v[1] for k, v in tk.items() if k != "append")
         gbps = (w["kv_bytes"] + w["qo_bytes"]) / (attn_ms * 1e-3) / 1e9
         base_ms = sum(v[0] * v[1] for k, v in kernels.items() if k != "append")
@@ -532,7 +608,8 @@ def main():
                     rpa.copy_pages(pool, bufs[2 * j + s_], src_pages=pid,
                                    src_head0=s_ * (H // 2), num_heads=H // 2)
         log(f"part page_export: {len(pages)} pages x 2 pools x 2 shards")
-        ems, ek = timed_steps(export_step, args.steps, args.warmup)
+        etm = timed_steps(export_step, args.steps, args.warmup)
+        ems, ek = etm["median_ms"], etm["kernels"]
         copied = 2 * len(pages) * H * spec.page_size * spec.head_dim_qk * spec.elem_bytes
         cms = ek["page_copy"][0] * ek["page_copy"][1]
         parts["page_export"] = {"pages": int(len(pages)), "bytes_copied": copied,
@@ -565,7 +642,8 @@ def main():
                  "logical_kv_bytes": sw["kv_bytes"], "unique_kv_bytes": int(unique)}
         for label, m_ in (("own_pages", sm), ("shared_prefix", shm)):
             log(f"part prefix_share: {label}")
-            _, pms, pk = run_batch(spec, m_, st, args.steps, args.warmup)
+            _, ptm = run_batch(spec, m_, st, args.steps, args.warmup)
+            pms, pk = ptm["median_ms"], ptm["kernels"]
             attn_ms = sum(v[0] * v[1] for k, v in pk.items() if k != "append")
             entry[label] = {"ms_per_step": pms, "attention_ms": attn_ms,
                             "kernels_us": {k: v[0] * 1e3 for k, v in pk.items()},
@@ -594,6 +672,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_min": tm["min_ms"],
+        "ms_per_step_mean": tm["mean_ms"],
+        "timing": f"median of {args.steps} steps, each between its own pair of HIP events, "
+                  f"after a {SCRUB_BYTES >> 20} MiB device write outside the events "
+                  f"(wall clock of the timed loop, writes included: {tm['wall_ms']:.4f} ms/step)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -610,6 +693,7 @@ def main():
         "kernels_us": {k: v[0] * 1e3 for k, v in kernels.items()},
         "launches_per_step": {k: v[1] for k, v in kernels.items()},
         "plan_ms": plan_ms,
+        "append": append_entry(w, kernels),
         "parts": parts,
     }
     print(json.dumps(line), flush=True)

@@ -55,7 +55,8 @@
  * Arguments are validated on the host before anything is launched: on an
  * error nothing is launched and no output is touched.  A thread-local message
  * (rpa_last_error_message) describes the last failure.  No C++ exception
- * crosses this interface.
+ * crosses this interface: every entry point catches them and returns
+ * RPA_ERR_HOST_ALLOC (host memory ran out) or RPA_ERR_INTERNAL.
  */
 #ifndef RPA_H_
 #define RPA_H_
@@ -67,7 +68,7 @@
 extern "C" {
 #endif
 
-#define RPA_ABI_VERSION 1
+#define RPA_ABI_VERSION 2
 
 typedef enum rpa_status {
   RPA_OK = 0,
@@ -77,7 +78,9 @@ typedef enum rpa_status {
   RPA_ERR_PAGE_OOB = -4,            /* a page id outside [0, num_pages), or too few pages */
   RPA_ERR_DUPLICATE_WRITE_PAGE = -5,/* a page written by the append is referenced twice */
   RPA_ERR_HIP = -6,                 /* a HIP runtime call failed */
-  RPA_ERR_NOT_UPLOADED = -7         /* the plan has not been uploaded to a workspace */
+  RPA_ERR_NOT_UPLOADED = -7,        /* the plan has not been uploaded to a workspace */
+  RPA_ERR_HOST_ALLOC = -8,          /* host memory ran out inside the call */
+  RPA_ERR_INTERNAL = -9             /* any other failure inside the library */
 } rpa_status;
 
 typedef enum rpa_dtype {
@@ -145,9 +148,20 @@ typedef struct rpa_plan rpa_plan;
 /* Validate a batch and build its plan on the host: the per-token append map,
  * the attention work items (long kv_len split into pieces so that the GPU's
  * num_cus compute units get balanced work; 0 means 256), and the merge map of
- * the split pieces.  No device work; may be called without a GPU.  On success
- * *out receives a plan owned by the library (free with rpa_plan_destroy).
- * Errors: INVALID_ARG, UNSUPPORTED, PAGE_OOB, DUPLICATE_WRITE_PAGE. */
+ * the split pieces.
+ * Source: "Accelerating Sonar through speculation" (Perplexity), section on
+ * inference with speculative decoding: for every step the host allocates KV
+ * pages for the new tokens, packs tokens and page information for the GPU and
+ * builds the attention metadata once, for prefill, decode and verification
+ * alike; "Disaggregated prefill and decode" (Perplexity), performance
+ * section: each request has its own qo_len and kv_len, and the work
+ * parallelises over requests and over kv_len.
+ * Arguments: cfg and batch as described above (read during the call only);
+ * num_cus: compute units to balance for (0 = 256); out: receives the plan.
+ * No device work; may be called without a GPU.  On success *out receives a
+ * plan owned by the library (free with rpa_plan_destroy); on failure *out is
+ * NULL.  Errors: INVALID_ARG, UNSUPPORTED, PAGE_OOB, DUPLICATE_WRITE_PAGE,
+ * HOST_ALLOC. */
 rpa_status rpa_plan_create(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
                            int32_t num_cus, rpa_plan** out);
 
@@ -189,6 +203,13 @@ rpa_status rpa_plan_upload(rpa_plan* plan, void* d_workspace, size_t bytes, void
  * head h, copies k_new[i, h, :] into k_cache at page pages_r[(c_r+t)/P],
  * head h, slot (c_r+t)%P, and v_new likewise into v_cache.  A raw copy of the
  * stored elements: no rounding, no other byte of the pools changes.
+ * Source: "Disaggregated prefill and decode" (Perplexity), KV Messenger
+ * section: each layer appends its new KV entries to the paged cache, and an
+ * entry is valid once the append has run and before the attention that reads
+ * it; sharded-transfer section: pages hold heads before tokens (HND).
+ * Arguments: k_new / v_new token-major device rows as in the layout table;
+ * k_cache / v_cache device pools addressed by ks / vs (host structs).  The
+ * caller owns every buffer; the call only enqueues work on `stream`.
  * Shared latent (head dims 576/512): pass v_new = NULL and v_cache = NULL or
  * v_cache == k_cache; only k is written.  Pools are in the plan's dtype.
  * Errors: INVALID_ARG, NOT_UPLOADED, HIP. */
@@ -201,6 +222,16 @@ rpa_status rpa_kv_append(const rpa_plan* plan, const void* k_new, const void* v_
  *   s_j = sm_scale * <q[i,h,:], K(r, h/G, j)> for visible keys j,
  *   lse[i,h] = ln sum_j exp(s_j),  o[i,h,:] = sum_j exp(s_j - lse) V(r, h/G, j).
  * Split pieces are combined by the log-sum-exp merge inside this call.
+ * Source: "Disaggregated prefill and decode" (Perplexity), performance
+ * section: requests of one batch differ in qo_len (1 for decode, the chunk
+ * for prefill) and kv_len, and attention runs over both in one batch;
+ * "Accelerating Sonar through speculation", speculative-decoding section:
+ * verification attends n + 1 new tokens; "Chunked prefill" (k4i.top),
+ * section "correctness": a chunk's tokens see the whole cache and,
+ * causally, the chunk; partial results merge by log-sum-exp.
+ * Arguments: q, o token-major device tensors (layout table); pools as in
+ * rpa_kv_append; lse device float32 [total_q, num_qo_heads] or NULL.  The
+ * caller owns every buffer; the plan's workspace holds the split partials.
  * For the shared latent form pass v_cache == k_cache (or NULL) and vs == ks
  * (or NULL): values are the first head_dim_v elements of each key row.
  * `lse` may be NULL.  Errors: INVALID_ARG, UNSUPPORTED, NOT_UPLOADED, HIP. */
@@ -215,8 +246,9 @@ rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q, const void* 
  * o_a, o_b, o: [rows, heads, dim] in `dtype`; lse_a, lse_b, lse: [rows, heads]
  * float32 (lse may be NULL); dim is a multiple of 8 and the o buffers are
  * 16-byte aligned.  A state with lse = -inf contributes nothing;
- * two -inf states give (-inf, 0).  o may alias o_a or o_b.
- * Errors: INVALID_ARG, HIP. */
+ * two -inf states give (-inf, 0).  o may alias o_a or o_b; lse must not alias
+ * lse_a or lse_b (INVALID_ARG).  All pointers are device memory the caller
+ * owns.  Errors: INVALID_ARG, HIP. */
 rpa_status rpa_merge_state(const void* o_a, const float* lse_a, const void* o_b,
                            const float* lse_b, void* o, float* lse, int64_t rows,
                            int32_t heads, int32_t dim, int32_t dtype, void* stream);
@@ -233,21 +265,27 @@ rpa_status rpa_merge_state(const void* o_a, const float* lse_a, const void* o_b,
  * of page src_pages[i] of `src` into heads [dst_head0, dst_head0 + num_heads)
  * of page dst_pages[i] of `dst`: all page_size slots, `dim` elements per row.
  * A raw copy of the stored bits.
+ *   src_pool_pages / dst_pool_pages: pages each side holds; a pair whose
+ *     source or destination id lies outside [0, that count) is skipped on
+ *     the device (nothing read or written for it); with a NULL page list,
+ *     num_pages must not exceed the pool's count (else PAGE_OOB).
+ *   src_pool_heads / dst_pool_heads: heads each side holds; the head ranges
+ *     must lie inside them (else INVALID_ARG).
  *   src_pages / dst_pages: DEVICE int32 arrays of num_pages page ids, or NULL
  *     for the identity (page i); the caller owns them.
  *   strides (elements, as rpa_cache_strides): any layout, e.g. an HND pool,
  *     an NHD buffer (head_stride = dim, token_stride = heads * dim) or a
  *     packed shard buffer of num_heads heads.
  *   dtype: RPA_DTYPE_F32 or RPA_DTYPE_BF16; dim fills whole 16-byte chunks.
- * Regions written must not overlap regions read; ids and head ranges must lie
- * inside the pools (not checked: the call knows only strides).  num_pages = 0
- * is a no-op.  Errors: INVALID_ARG, HIP. */
+ * The pool counts and strides must describe memory the caller owns; regions
+ * written must not overlap regions read.  num_pages = 0 is a no-op.
+ * Errors: INVALID_ARG, PAGE_OOB, HIP. */
 rpa_status rpa_page_copy(const void* src, const rpa_cache_strides* src_strides,
-                         const int32_t* src_pages, void* dst,
-                         const rpa_cache_strides* dst_strides, const int32_t* dst_pages,
-                         int32_t num_pages, int32_t src_head0, int32_t dst_head0,
-                         int32_t num_heads, int32_t page_size, int32_t dim, int32_t dtype,
-                         void* stream);
+                         int32_t src_pool_pages, int32_t src_pool_heads, const int32_t* src_pages,
+                         void* dst, const rpa_cache_strides* dst_strides, int32_t dst_pool_pages,
+                         int32_t dst_pool_heads, const int32_t* dst_pages, int32_t num_pages,
+                         int32_t src_head0, int32_t dst_head0, int32_t num_heads,
+                         int32_t page_size, int32_t dim, int32_t dtype, void* stream);
 
 /* Free a plan.  Waits for the plan's last upload copy to finish reading the
  * staging buffer.  NULL is ignored. */

@@ -29,6 +29,8 @@ RPA_ERR_PAGE_OOB = -4
 RPA_ERR_DUPLICATE_WRITE_PAGE = -5
 RPA_ERR_HIP = -6
 RPA_ERR_NOT_UPLOADED = -7
+RPA_ERR_HOST_ALLOC = -8
+RPA_ERR_INTERNAL = -9
 
 RPA_DTYPE_F32 = 0
 RPA_DTYPE_BF16 = 1
@@ -96,8 +98,9 @@ def lib() -> ctypes.CDLL:
     L.rpa_batch_attention.argtypes = [vp, vp, vp, vp, P(rpa_cache_strides),
                                       P(rpa_cache_strides), vp, vp, vp]
     L.rpa_merge_state.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
-    L.rpa_page_copy.argtypes = [vp, P(rpa_cache_strides), vp, vp, P(rpa_cache_strides), vp, i32,
-                                i32, i32, i32, i32, i32, i32, vp]
+    L.rpa_page_copy.argtypes = [vp, P(rpa_cache_strides), i32, i32, vp, vp,
+                                P(rpa_cache_strides), i32, i32, vp, i32, i32, i32, i32, i32, i32,
+                                i32, vp]
     L.rpa_plan_destroy.argtypes = [vp]
     L.rpa_plan_destroy.restype = None
     L.rpa_status_string.argtypes = [i32]
@@ -111,10 +114,10 @@ def lib() -> ctypes.CDLL:
     L.rpa_profile_read.argtypes = [ctypes.c_char_p, P(ctypes.c_double), P(i64)]
     L.rpa_profile_reset.argtypes = []
     L.rpa_profile_select.argtypes = [ctypes.c_char_p]
-    for name in ("rpa_plan_create", "rpa_plan_workspace_size", "rpa_plan_upload", "rpa_kv_append",
-                 "rpa_batch_attention", "rpa_merge_state", "rpa_plan_debug_dump",
-                 "rpa_profile_enable", "rpa_profile_read", "rpa_profile_reset",
-                 "rpa_profile_select"):
+    for name in ("rpa_plan_create", "rpa_plan_create_tree", "rpa_plan_workspace_size",
+                 "rpa_plan_upload", "rpa_kv_append", "rpa_batch_attention", "rpa_merge_state",
+                 "rpa_page_copy", "rpa_plan_debug_dump", "rpa_profile_enable",
+                 "rpa_profile_read", "rpa_profile_reset", "rpa_profile_select"):
         getattr(L, name).restype = i32
     _lib_handle = L
     return L
@@ -277,13 +280,15 @@ def rpa_merge_state(o_a, lse_a, o_b, lse_b, o, lse, rows: int, heads: int, dim: 
                                  _stream(stream)))
 
 
-def rpa_page_copy(src, src_strides: rpa_cache_strides, src_pages, dst,
-                  dst_strides: rpa_cache_strides, dst_pages, num_pages: int, src_head0: int,
-                  dst_head0: int, num_heads: int, page_size: int, dim: int, dtype: int,
-                  stream=None):
+def rpa_page_copy(src, src_strides: rpa_cache_strides, src_pool_pages: int, src_pool_heads: int,
+                  src_pages, dst, dst_strides: rpa_cache_strides, dst_pool_pages: int,
+                  dst_pool_heads: int, dst_pages, num_pages: int, src_head0: int, dst_head0: int,
+                  num_heads: int, page_size: int, dim: int, dtype: int, stream=None):
     """Raw copy of head ranges of pages (page id arrays are device tensors or None)."""
-    _check(lib().rpa_page_copy(_ptr(src), ctypes.byref(src_strides), _ptr(src_pages), _ptr(dst),
-                               ctypes.byref(dst_strides), _ptr(dst_pages), int(num_pages),
+    _check(lib().rpa_page_copy(_ptr(src), ctypes.byref(src_strides), int(src_pool_pages),
+                               int(src_pool_heads), _ptr(src_pages), _ptr(dst),
+                               ctypes.byref(dst_strides), int(dst_pool_pages),
+                               int(dst_pool_heads), _ptr(dst_pages), int(num_pages),
                                int(src_head0), int(dst_head0), int(num_heads), int(page_size),
                                int(dim), int(dtype), _stream(stream)))
 
@@ -292,13 +297,29 @@ def copy_pages(src, dst, src_pages=None, dst_pages=None, src_head0=0, dst_head0=
                num_heads=None, stream=None):
     """Copy head ranges of pages between two 4-D views [pages, heads, slots, dim]
     (any strides, e.g. an HND pool, or an NHD buffer permuted to that order).
-    Page id lists are device int32 tensors (or None for 0, 1, ...)."""
+    Page id lists are device int32 tensors (or None for 0, 1, ...); pairs with
+    an id outside either view's page count are skipped by the kernel."""
     import torch
+    _require(src.dim() == 4 and dst.dim() == 4, "src and dst must be 4-D [pages, heads, slots, dim]")
+    _require(src.dtype == dst.dtype and src.dtype in (torch.bfloat16, torch.float32),
+             "src and dst must share a dtype (bfloat16 or float32)")
+    _require(src.shape[2] == dst.shape[2] and src.shape[3] == dst.shape[3],
+             "src and dst must have the same page size and row length")
+    _require(src.is_cuda and dst.is_cuda and src.device == dst.device,
+             "src and dst must be on the same GPU")
+    for ids, name in ((src_pages, "src_pages"), (dst_pages, "dst_pages")):
+        if ids is not None:
+            _require(ids.dtype == torch.int32 and ids.dim() == 1 and ids.is_contiguous()
+                     and ids.device == src.device, f"{name} must be a contiguous int32 vector "
+                     "on the pools' GPU")
     n = int(src_pages.numel()) if src_pages is not None else (
         int(dst_pages.numel()) if dst_pages is not None else int(src.shape[0]))
+    if src_pages is not None and dst_pages is not None:
+        _require(src_pages.numel() == dst_pages.numel(), "page lists differ in length")
     heads = int(num_heads if num_heads is not None else src.shape[1] - src_head0)
     dtype = RPA_DTYPE_BF16 if src.dtype == torch.bfloat16 else RPA_DTYPE_F32
-    rpa_page_copy(src, strides_of(src), src_pages, dst, strides_of(dst), dst_pages, n, src_head0,
+    rpa_page_copy(src, strides_of(src), int(src.shape[0]), int(src.shape[1]), src_pages, dst,
+                  strides_of(dst), int(dst.shape[0]), int(dst.shape[1]), dst_pages, n, src_head0,
                   dst_head0, heads, int(src.shape[2]), int(src.shape[3]), dtype, stream)
 
 
@@ -352,6 +373,96 @@ def rpa_profile_select(kernels=None):
 
 
 # ----------------------------------------------------------------------------
+# Host-side tensor checks (the C ABI sees raw addresses only, so a tensor of
+# the wrong dtype, shape or size would become an out-of-bounds device access)
+# ----------------------------------------------------------------------------
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise RpaError(RPA_ERR_INVALID_ARG, f"RPA_ERR_INVALID_ARG: {msg}")
+
+
+def _torch_dtype(cfg: rpa_attn_config):
+    import torch
+    return torch.bfloat16 if cfg.dtype == RPA_DTYPE_BF16 else torch.float32
+
+
+def _check_rows(name, t, shape, dtype, device=None):
+    """A contiguous tensor of exactly `shape` and `dtype` (on `device` if given)."""
+    _require(t is not None, f"{name} is required")
+    _require(t.dtype == dtype, f"{name} has dtype {t.dtype}, the plan needs {dtype}")
+    _require(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, "
+             f"the plan needs {tuple(shape)}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+    if device is not None:
+        _require(t.device == device, f"{name} is on {t.device}, not {device}")
+
+
+def _check_pool(name, pool, cfg: rpa_attn_config, num_pages: int, row_len: int, device=None):
+    """A 4-D pool view [pages >= num_pages, H_kv, page_size, >= row_len] of the
+    plan's dtype with a contiguous last dimension."""
+    _require(pool is not None, f"{name} is required")
+    _require(pool.dtype == _torch_dtype(cfg), f"{name} has dtype {pool.dtype}, "
+             f"the plan needs {_torch_dtype(cfg)}")
+    _require(pool.dim() == 4, f"{name} must be 4-D [pages, heads, page_size, dim]")
+    _require(pool.shape[0] >= num_pages, f"{name} holds {pool.shape[0]} pages, the plan's page "
+             f"ids reach {num_pages}")
+    _require(pool.shape[1] == cfg.num_kv_heads and pool.shape[2] == cfg.page_size,
+             f"{name} has {pool.shape[1]} heads of {pool.shape[2]} slots, the plan needs "
+             f"{cfg.num_kv_heads} of {cfg.page_size}")
+    _require(pool.shape[3] >= row_len, f"{name} rows hold {pool.shape[3]} elements, "
+             f"the plan needs {row_len}")
+    _require(pool.stride(3) == 1, f"{name}'s last dimension must be contiguous")
+    if device is not None:
+        _require(pool.device == device, f"{name} is on {pool.device}, not {device}")
+
+
+def check_append_args(cfg: rpa_attn_config, total_q: int, num_pages: int, k_new, v_new, k_cache,
+                      v_cache):
+    """Raises RpaError(INVALID_ARG) unless the tensors fit the plan's append."""
+    latent = cfg.head_dim_qk == 576
+    dt = _torch_dtype(cfg)
+    _check_rows("k_new", k_new, (total_q, cfg.num_kv_heads, cfg.head_dim_qk), dt)
+    _check_pool("k_cache", k_cache, cfg, num_pages, cfg.head_dim_qk)
+    if latent:
+        _require(v_new is None, "the shared latent cache takes no v_new")
+        _require(v_cache is None or v_cache is k_cache, "the shared latent cache takes no "
+                 "v_cache (or v_cache = k_cache)")
+    else:
+        _check_rows("v_new", v_new, (total_q, cfg.num_kv_heads, cfg.head_dim_v), dt)
+        _check_pool("v_cache", v_cache, cfg, num_pages, cfg.head_dim_v)
+    dev = k_new.device
+    _require(dev.type == "cuda", f"k_new is on {dev}, not a GPU")
+    for name, t in (("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t is not None:
+            _require(t.device == dev, f"{name} is on {t.device}, not {dev}")
+
+
+def check_attention_args(cfg: rpa_attn_config, total_q: int, num_pages: int, q, k_cache,
+                         v_cache, o, lse):
+    """Raises RpaError(INVALID_ARG) unless the tensors fit the plan's attention."""
+    import torch
+    latent = cfg.head_dim_qk == 576
+    dt = _torch_dtype(cfg)
+    _check_rows("q", q, (total_q, cfg.num_qo_heads, cfg.head_dim_qk), dt)
+    _check_rows("o", o, (total_q, cfg.num_qo_heads, cfg.head_dim_v), dt)
+    if lse is not None:
+        _check_rows("lse", lse, (total_q, cfg.num_qo_heads), torch.float32)
+    _check_pool("k_cache", k_cache, cfg, num_pages, cfg.head_dim_qk)
+    if latent:
+        _require(v_cache is None or v_cache is k_cache, "the shared latent cache takes no "
+                 "v_cache (or v_cache = k_cache)")
+    else:
+        _check_pool("v_cache", v_cache, cfg, num_pages, cfg.head_dim_v)
+    dev = q.device
+    _require(dev.type == "cuda", f"q is on {dev}, not a GPU")
+    for name, t in (("o", o), ("lse", lse), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t is not None:
+            _require(t.device == dev, f"{name} is on {t.device}, not {dev}")
+
+
+# ----------------------------------------------------------------------------
 # Convenience wrapper
 # ----------------------------------------------------------------------------
 
@@ -373,6 +484,7 @@ class Plan:
             self.handle = rpa_plan_create_tree(cfg, qo_indptr, kv_len, kv_page_indptr,
                                                kv_page_indices, num_pages, ti, tw, num_cus)
         self.total_q = int(np.asarray(qo_indptr)[-1]) if len(qo_indptr) else 0
+        self.num_pages = int(num_pages)
         self.ws_bytes = rpa_plan_workspace_size(self.handle)
         self.workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)
         base = self.workspace.data_ptr()
@@ -384,6 +496,7 @@ class Plan:
         return self.cfg.head_dim_qk == 576
 
     def append(self, k_new, v_new, k_cache, v_cache=None, stream=None):
+        check_append_args(self.cfg, self.total_q, self.num_pages, k_new, v_new, k_cache, v_cache)
         ks = strides_of(k_cache)
         vs = None if v_cache is None else strides_of(v_cache)
         rpa_kv_append(self.handle, k_new, v_new, k_cache, v_cache, ks, vs, stream)
@@ -396,6 +509,7 @@ class Plan:
         if lse is None and with_lse:
             lse = torch.empty((self.total_q, self.cfg.num_qo_heads), dtype=torch.float32,
                               device=q.device)
+        check_attention_args(self.cfg, self.total_q, self.num_pages, q, k_cache, v_cache, o, lse)
         ks = strides_of(k_cache)
         vs = None if v_cache is None else strides_of(v_cache)
         rpa_batch_attention(self.handle, q, k_cache, v_cache, ks, vs, o, lse, stream)
@@ -408,7 +522,14 @@ class Plan:
 def merge_state(o_a, lse_a, o_b, lse_b, stream=None):
     """Merge two attention states [rows, heads, dim] (torch tensors on the GPU)."""
     import torch
+    _require(o_a.dim() == 3, "o_a must be [rows, heads, dim]")
     rows, heads, dim = o_a.shape
+    _require(o_a.dtype in (torch.bfloat16, torch.float32), "o dtype must be bfloat16 or float32")
+    _check_rows("o_a", o_a, (rows, heads, dim), o_a.dtype, o_a.device)
+    _check_rows("o_b", o_b, (rows, heads, dim), o_a.dtype, o_a.device)
+    _check_rows("lse_a", lse_a, (rows, heads), torch.float32, o_a.device)
+    _check_rows("lse_b", lse_b, (rows, heads), torch.float32, o_a.device)
+    _require(o_a.is_cuda, "merge_state runs on the GPU")
     o = torch.empty_like(o_a)
     lse = torch.empty_like(lse_a)
     dtype = RPA_DTYPE_BF16 if o_a.dtype == torch.bfloat16 else RPA_DTYPE_F32

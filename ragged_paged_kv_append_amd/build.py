@@ -26,8 +26,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(PKG, "..", "include")]
 # Packed fp32 instructions are kept out of the device code on purpose.
-DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 # Per-file device flags.  The prefill kernel runs with the IEEE mode bit off:

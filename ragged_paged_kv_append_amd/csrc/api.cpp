@@ -3,8 +3,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
 #include <cstring>
+#include <exception>
 #include <map>
+#include <memory>
 #include <set>
 #include <mutex>
 #include <new>
@@ -18,16 +21,41 @@
 
 namespace {
 
-thread_local std::string g_last_error;
+// Message of the last failure on this thread.  A fixed buffer, so that
+// recording a failure never allocates (the handlers below run after an
+// allocation has failed).
+thread_local char g_last_error[512];
+
+void set_error(const char* msg) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+}
+void clear_error() { g_last_error[0] = '\0'; }
 
 rpa_status fail(rpa_status s, const std::string& msg) {
-  g_last_error = msg;
+  set_error(msg.c_str());
   return s;
 }
 
 rpa_status hip_fail(hipError_t e, const char* what) {
-  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
   return RPA_ERR_HIP;
+}
+
+// Runs an entry point's body; no C++ exception leaves the library.
+template <class F>
+rpa_status guarded(F&& body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    set_error("out of host memory");
+    return RPA_ERR_HOST_ALLOC;
+  } catch (const std::exception& e) {
+    set_error(e.what());
+    return RPA_ERR_INTERNAL;
+  } catch (...) {
+    set_error("unexpected internal error");
+    return RPA_ERR_INTERNAL;
+  }
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -181,11 +209,13 @@ RPA_EXPORT const char* rpa_status_string(rpa_status s) {
     case RPA_ERR_DUPLICATE_WRITE_PAGE: return "RPA_ERR_DUPLICATE_WRITE_PAGE";
     case RPA_ERR_HIP: return "RPA_ERR_HIP";
     case RPA_ERR_NOT_UPLOADED: return "RPA_ERR_NOT_UPLOADED";
+    case RPA_ERR_HOST_ALLOC: return "RPA_ERR_HOST_ALLOC";
+    case RPA_ERR_INTERNAL: return "RPA_ERR_INTERNAL";
   }
   return "RPA_ERR_UNKNOWN";
 }
 
-RPA_EXPORT const char* rpa_last_error_message(void) { return g_last_error.c_str(); }
+RPA_EXPORT const char* rpa_last_error_message(void) { return g_last_error; }
 
 namespace {
 
@@ -194,22 +224,13 @@ rpa_status create_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
                        rpa_plan** out) {
   if (!out) return fail(RPA_ERR_INVALID_ARG, "null output pointer");
   *out = nullptr;
-  rpa_plan* plan = new (std::nothrow) rpa_plan();
-  if (!plan) return fail(RPA_ERR_INVALID_ARG, "out of host memory");
+  std::unique_ptr<rpa_plan> plan(new rpa_plan());
   std::string err;
-  rpa_status s;
-  try {
-    s = rpa::build_plan(cfg, batch, tree_indptr, tree_words, num_cus, plan, &err);
-  } catch (const std::bad_alloc&) {
-    s = RPA_ERR_INVALID_ARG;
-    err = "out of host memory while planning";
-  }
-  if (s != RPA_OK) {
-    delete plan;
-    return fail(s, err);
-  }
-  *out = plan;
-  g_last_error.clear();
+  const rpa_status s = rpa::build_plan(cfg, batch, tree_indptr, tree_words, num_cus, plan.get(),
+                                       &err);
+  if (s != RPA_OK) return fail(s, err);
+  *out = plan.release();
+  clear_error();
   return RPA_OK;
 }
 
@@ -217,7 +238,7 @@ rpa_status create_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
 
 RPA_EXPORT rpa_status rpa_plan_create(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
                                       int32_t num_cus, rpa_plan** out) {
-  return create_plan(cfg, batch, nullptr, nullptr, num_cus, out);
+  return guarded([&] { return create_plan(cfg, batch, nullptr, nullptr, num_cus, out); });
 }
 
 RPA_EXPORT rpa_status rpa_plan_create_tree(const rpa_attn_config* cfg,
@@ -225,92 +246,105 @@ RPA_EXPORT rpa_status rpa_plan_create_tree(const rpa_attn_config* cfg,
                                            const int32_t* tree_indptr,
                                            const uint32_t* tree_words, int32_t num_cus,
                                            rpa_plan** out) {
-  if (!tree_indptr) return fail(RPA_ERR_INVALID_ARG, "null tree_indptr");
-  return create_plan(cfg, batch, tree_indptr, tree_words, num_cus, out);
+  return guarded([&] {
+    if (out) *out = nullptr;
+    if (!tree_indptr) return fail(RPA_ERR_INVALID_ARG, "null tree_indptr");
+    return create_plan(cfg, batch, tree_indptr, tree_words, num_cus, out);
+  });
 }
 
 RPA_EXPORT rpa_status rpa_plan_workspace_size(const rpa_plan* plan, size_t* bytes) {
-  if (!plan || !bytes) return fail(RPA_ERR_INVALID_ARG, "null plan or bytes pointer");
+  if (!plan || !bytes) {
+    set_error("null plan or bytes pointer");
+    return RPA_ERR_INVALID_ARG;
+  }
   *bytes = plan->ws_bytes;
   return RPA_OK;
 }
 
 RPA_EXPORT rpa_status rpa_plan_upload(rpa_plan* plan, void* d_workspace, size_t bytes,
                                       void* stream) {
-  if (!plan || !d_workspace) return fail(RPA_ERR_INVALID_ARG, "null plan or workspace");
-  if (!aligned(d_workspace, 256)) return fail(RPA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-  if (bytes < plan->ws_bytes)
-    return fail(RPA_ERR_WORKSPACE_TOO_SMALL,
-                "workspace has " + std::to_string(bytes) + " bytes, plan needs " +
-                    std::to_string(plan->ws_bytes));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (!plan->event) {
-    hipEvent_t ev;
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-    plan->event = ev;
-  } else {
-    // The previous upload may still be reading the staging buffer.
-    e = hipEventSynchronize(static_cast<hipEvent_t>(plan->event));
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-  }
-  if (!plan->staging) {
-    e = hipHostMalloc(&plan->staging, plan->meta_bytes, hipHostMallocDefault);
-    if (e != hipSuccess) {
-      plan->staging = nullptr;
-      return hip_fail(e, "hipHostMalloc");
+  return guarded([&] {
+    if (!plan || !d_workspace) return fail(RPA_ERR_INVALID_ARG, "null plan or workspace");
+    if (!aligned(d_workspace, 256))
+      return fail(RPA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    if (bytes < plan->ws_bytes)
+      return fail(RPA_ERR_WORKSPACE_TOO_SMALL,
+                  "workspace has " + std::to_string(bytes) + " bytes, plan needs " +
+                      std::to_string(plan->ws_bytes));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (!plan->event) {
+      hipEvent_t ev;
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+      plan->event = ev;
+    } else {
+      // The previous upload may still be reading the staging buffer.
+      e = hipEventSynchronize(static_cast<hipEvent_t>(plan->event));
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     }
-  }
-  std::memset(plan->staging, 0, plan->meta_bytes);
-  std::memcpy(plan->staging, plan->blob.data(), plan->blob.size() * sizeof(int32_t));
-  e = hipMemcpyAsync(d_workspace, plan->staging, plan->meta_bytes, hipMemcpyHostToDevice, st);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
-  e = hipEventRecord(static_cast<hipEvent_t>(plan->event), st);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  plan->d_ws = d_workspace;
-  plan->uploaded = true;
-  g_last_error.clear();
-  return RPA_OK;
+    if (!plan->staging) {
+      e = hipHostMalloc(&plan->staging, plan->meta_bytes, hipHostMallocDefault);
+      if (e != hipSuccess) {
+        plan->staging = nullptr;
+        return hip_fail(e, "hipHostMalloc");
+      }
+    }
+    std::memset(plan->staging, 0, plan->meta_bytes);
+    std::memcpy(plan->staging, plan->blob.data(), plan->blob.size() * sizeof(int32_t));
+    e = hipMemcpyAsync(d_workspace, plan->staging, plan->meta_bytes, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    e = hipEventRecord(static_cast<hipEvent_t>(plan->event), st);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    plan->d_ws = d_workspace;
+    plan->uploaded = true;
+    clear_error();
+    return RPA_OK;
+  });
 }
 
 RPA_EXPORT rpa_status rpa_kv_append(const rpa_plan* plan, const void* k_new, const void* v_new,
                                     void* k_cache, void* v_cache, const rpa_cache_strides* ks,
                                     const rpa_cache_strides* vs, void* stream) {
-  rpa_status s = check_uploaded(plan);
-  if (s != RPA_OK) return s;
-  const rpa_attn_config& c = plan->cfg;
-  const bool latent = shared_latent(c);
-  std::string why;
-  if (plan->total_q == 0) return RPA_OK;  // no new tokens: nothing to read or write
-  if (!plan->can_append)
-    return fail(RPA_ERR_INVALID_ARG,
-                "the plan has a request with kv_len < qo_len (cross attention): no append slots");
-  if (!k_new || !k_cache) return fail(RPA_ERR_INVALID_ARG, "null k_new or k_cache");
-  if (!aligned(k_new, 16) || !aligned(k_cache, 16))
-    return fail(RPA_ERR_INVALID_ARG, "k_new and k_cache must be 16-byte aligned");
-  if (!strides_ok(ks, c.head_dim_qk, c.dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "k: " + why);
-  if (latent) {
-    if (v_new) return fail(RPA_ERR_INVALID_ARG, "shared latent cache: v_new must be NULL");
-    if (v_cache && v_cache != k_cache)
-      return fail(RPA_ERR_INVALID_ARG, "shared latent cache: v_cache must be NULL or k_cache");
-  } else {
-    if (!v_new || !v_cache) return fail(RPA_ERR_INVALID_ARG, "null v_new or v_cache");
-    if (!aligned(v_new, 16) || !aligned(v_cache, 16))
-      return fail(RPA_ERR_INVALID_ARG, "v_new and v_cache must be 16-byte aligned");
-    if (!strides_ok(vs, c.head_dim_v, c.dtype, &why))
-      return fail(RPA_ERR_INVALID_ARG, "v: " + why);
-  }
-  rpa::DevPlan p = dev_plan(plan);
-  rpa::Strides k_st{ks->page_stride, ks->head_stride, ks->token_stride};
-  rpa::Strides v_st = latent ? k_st : rpa::Strides{vs->page_stride, vs->head_stride, vs->token_stride};
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = timed("append", st, [&] {
-    return rpa::launch_append(p, k_new, latent ? nullptr : v_new, k_cache,
-                              latent ? nullptr : v_cache, k_st, v_st, st);
+  return guarded([&] {
+    rpa_status s = check_uploaded(plan);
+    if (s != RPA_OK) return s;
+    const rpa_attn_config& c = plan->cfg;
+    const bool latent = shared_latent(c);
+    std::string why;
+    if (plan->total_q == 0) return RPA_OK;  // no new tokens: nothing to read or write
+    if (!plan->can_append)
+      return fail(RPA_ERR_INVALID_ARG,
+                  "the plan has a request with kv_len < qo_len (cross attention): no append slots");
+    if (!k_new || !k_cache) return fail(RPA_ERR_INVALID_ARG, "null k_new or k_cache");
+    if (!aligned(k_new, 16) || !aligned(k_cache, 16))
+      return fail(RPA_ERR_INVALID_ARG, "k_new and k_cache must be 16-byte aligned");
+    if (!strides_ok(ks, c.head_dim_qk, c.dtype, &why))
+      return fail(RPA_ERR_INVALID_ARG, "k: " + why);
+    if (latent) {
+      if (v_new) return fail(RPA_ERR_INVALID_ARG, "shared latent cache: v_new must be NULL");
+      if (v_cache && v_cache != k_cache)
+        return fail(RPA_ERR_INVALID_ARG, "shared latent cache: v_cache must be NULL or k_cache");
+    } else {
+      if (!v_new || !v_cache) return fail(RPA_ERR_INVALID_ARG, "null v_new or v_cache");
+      if (!aligned(v_new, 16) || !aligned(v_cache, 16))
+        return fail(RPA_ERR_INVALID_ARG, "v_new and v_cache must be 16-byte aligned");
+      if (!strides_ok(vs, c.head_dim_v, c.dtype, &why))
+        return fail(RPA_ERR_INVALID_ARG, "v: " + why);
+    }
+    rpa::DevPlan p = dev_plan(plan);
+    rpa::Strides k_st{ks->page_stride, ks->head_stride, ks->token_stride};
+    rpa::Strides v_st =
+        latent ? k_st : rpa::Strides{vs->page_stride, vs->head_stride, vs->token_stride};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("append", st, [&] {
+      return rpa::launch_append(p, k_new, latent ? nullptr : v_new, k_cache,
+                                latent ? nullptr : v_cache, k_st, v_st, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+    return RPA_OK;
   });
-  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
-  return RPA_OK;
 }
 
 RPA_EXPORT rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q,
@@ -318,157 +352,195 @@ RPA_EXPORT rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q,
                                           const rpa_cache_strides* ks,
                                           const rpa_cache_strides* vs, void* o, float* lse,
                                           void* stream) {
-  rpa_status s = check_uploaded(plan);
-  if (s != RPA_OK) return s;
-  const rpa_attn_config& c = plan->cfg;
-  const bool latent = shared_latent(c);
-  std::string why;
-  if (plan->total_q == 0) return RPA_OK;  // no query rows: nothing to compute
-  if (!q || !k_cache || !o) return fail(RPA_ERR_INVALID_ARG, "null q, k_cache or o");
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(o, 16))
-    return fail(RPA_ERR_INVALID_ARG, "q, k_cache and o must be 16-byte aligned");
-  if (lse && !aligned(lse, 4)) return fail(RPA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  if (!strides_ok(ks, c.head_dim_qk, c.dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "k: " + why);
-  rpa::Strides k_st{ks->page_stride, ks->head_stride, ks->token_stride};
-  rpa::Strides v_st = k_st;
-  const void* vc = v_cache;
-  if (latent) {
-    if (v_cache && v_cache != k_cache)
-      return fail(RPA_ERR_UNSUPPORTED, "576/512 needs the shared latent cache (v_cache == k_cache)");
-    if (vs && (vs->page_stride != ks->page_stride || vs->head_stride != ks->head_stride ||
-               vs->token_stride != ks->token_stride))
-      return fail(RPA_ERR_UNSUPPORTED, "576/512 needs vs == ks (shared latent cache)");
-    vc = k_cache;
-  } else {
-    if (!v_cache) return fail(RPA_ERR_INVALID_ARG, "null v_cache");
-    if (!aligned(v_cache, 16)) return fail(RPA_ERR_INVALID_ARG, "v_cache must be 16-byte aligned");
-    if (!strides_ok(vs, c.head_dim_v, c.dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "v: " + why);
-    v_st = rpa::Strides{vs->page_stride, vs->head_stride, vs->token_stride};
-  }
-  rpa::DevPlan p = dev_plan(plan);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (p.n_items[rpa::KC_GENERIC] > 0) {
-    e = timed("generic", st, [&] { return rpa::launch_generic(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
-    if (e != hipSuccess) return hip_fail(e, "generic attention launch");
-  }
-  if (p.n_items[rpa::KC_DECODE] > 0) {
-    e = timed("decode", st, [&] { return rpa::launch_decode(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
-    if (e != hipSuccess) return hip_fail(e, "decode attention launch");
-  }
-  if (p.n_items[rpa::KC_PREFILL] > 0) {
-    e = timed("prefill", st, [&] { return rpa::launch_prefill(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
-    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
-  }
-  if (p.n_items[rpa::KC_MLA] > 0) {
-    e = timed("mla", st, [&] { return rpa::launch_mla(p, q, k_cache, k_st, o, lse, st); });
-    if (e != hipSuccess) return hip_fail(e, "latent attention launch");
-  }
-  if (p.n_merge_rows > 0) {
-    e = timed("merge", st, [&] { return rpa::launch_merge_rows(p, o, lse, st); });
-    if (e != hipSuccess) return hip_fail(e, "merge launch");
-  }
-  return RPA_OK;
+  return guarded([&] {
+    rpa_status s = check_uploaded(plan);
+    if (s != RPA_OK) return s;
+    const rpa_attn_config& c = plan->cfg;
+    const bool latent = shared_latent(c);
+    std::string why;
+    if (plan->total_q == 0) return RPA_OK;  // no query rows: nothing to compute
+    if (!q || !k_cache || !o) return fail(RPA_ERR_INVALID_ARG, "null q, k_cache or o");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(o, 16))
+      return fail(RPA_ERR_INVALID_ARG, "q, k_cache and o must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(RPA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (!strides_ok(ks, c.head_dim_qk, c.dtype, &why))
+      return fail(RPA_ERR_INVALID_ARG, "k: " + why);
+    rpa::Strides k_st{ks->page_stride, ks->head_stride, ks->token_stride};
+    rpa::Strides v_st = k_st;
+    const void* vc = v_cache;
+    if (latent) {
+      if (v_cache && v_cache != k_cache)
+        return fail(RPA_ERR_UNSUPPORTED,
+                    "576/512 needs the shared latent cache (v_cache == k_cache)");
+      if (vs && (vs->page_stride != ks->page_stride || vs->head_stride != ks->head_stride ||
+                 vs->token_stride != ks->token_stride))
+        return fail(RPA_ERR_UNSUPPORTED, "576/512 needs vs == ks (shared latent cache)");
+      vc = k_cache;
+    } else {
+      if (!v_cache) return fail(RPA_ERR_INVALID_ARG, "null v_cache");
+      if (!aligned(v_cache, 16))
+        return fail(RPA_ERR_INVALID_ARG, "v_cache must be 16-byte aligned");
+      if (!strides_ok(vs, c.head_dim_v, c.dtype, &why))
+        return fail(RPA_ERR_INVALID_ARG, "v: " + why);
+      v_st = rpa::Strides{vs->page_stride, vs->head_stride, vs->token_stride};
+    }
+    rpa::DevPlan p = dev_plan(plan);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (p.n_items[rpa::KC_GENERIC] > 0) {
+      e = timed("generic", st,
+                [&] { return rpa::launch_generic(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
+      if (e != hipSuccess) return hip_fail(e, "generic attention launch");
+    }
+    if (p.n_items[rpa::KC_DECODE] > 0) {
+      e = timed("decode", st,
+                [&] { return rpa::launch_decode(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
+      if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+    }
+    if (p.n_items[rpa::KC_PREFILL] > 0) {
+      e = timed("prefill", st,
+                [&] { return rpa::launch_prefill(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
+      if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+    }
+    if (p.n_items[rpa::KC_MLA] > 0) {
+      e = timed("mla", st, [&] { return rpa::launch_mla(p, q, k_cache, k_st, o, lse, st); });
+      if (e != hipSuccess) return hip_fail(e, "latent attention launch");
+    }
+    if (p.n_merge_rows > 0) {
+      e = timed("merge", st, [&] { return rpa::launch_merge_rows(p, o, lse, st); });
+      if (e != hipSuccess) return hip_fail(e, "merge launch");
+    }
+    return RPA_OK;
+  });
 }
 
 RPA_EXPORT rpa_status rpa_merge_state(const void* o_a, const float* lse_a, const void* o_b,
                                       const float* lse_b, void* o, float* lse, int64_t rows,
                                       int32_t heads, int32_t dim, int32_t dtype, void* stream) {
-  if (dtype != RPA_DTYPE_F32 && dtype != RPA_DTYPE_BF16)
-    return fail(RPA_ERR_INVALID_ARG, "dtype must be RPA_DTYPE_F32 or RPA_DTYPE_BF16");
-  if (rows < 0 || heads <= 0 || dim <= 0) return fail(RPA_ERR_INVALID_ARG, "bad rows/heads/dim");
-  if (dim % 8 != 0) return fail(RPA_ERR_INVALID_ARG, "dim must be a multiple of 8");
-  if (rows == 0) return RPA_OK;
-  if (!o_a || !lse_a || !o_b || !lse_b || !o)
-    return fail(RPA_ERR_INVALID_ARG, "null o_a, lse_a, o_b, lse_b or o");
-  if (!aligned(o_a, 16) || !aligned(o_b, 16) || !aligned(o, 16))
-    return fail(RPA_ERR_INVALID_ARG, "o_a, o_b and o must be 16-byte aligned");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = timed("merge_state", st, [&] {
-    return rpa::launch_merge_state(o_a, lse_a, o_b, lse_b, o, lse, rows, heads, dim, dtype, st);
+  return guarded([&] {
+    if (dtype != RPA_DTYPE_F32 && dtype != RPA_DTYPE_BF16)
+      return fail(RPA_ERR_INVALID_ARG, "dtype must be RPA_DTYPE_F32 or RPA_DTYPE_BF16");
+    if (rows < 0 || heads <= 0 || dim <= 0)
+      return fail(RPA_ERR_INVALID_ARG, "bad rows/heads/dim");
+    if (dim % 8 != 0) return fail(RPA_ERR_INVALID_ARG, "dim must be a multiple of 8");
+    if (rows == 0) return RPA_OK;
+    if (!o_a || !lse_a || !o_b || !lse_b || !o)
+      return fail(RPA_ERR_INVALID_ARG, "null o_a, lse_a, o_b, lse_b or o");
+    if (!aligned(o_a, 16) || !aligned(o_b, 16) || !aligned(o, 16))
+      return fail(RPA_ERR_INVALID_ARG, "o_a, o_b and o must be 16-byte aligned");
+    // Several threads read each input lse value; one of them writes the
+    // output lse.  An output lse over an input would race.
+    if (lse && (lse == lse_a || lse == lse_b))
+      return fail(RPA_ERR_INVALID_ARG, "lse must not alias lse_a or lse_b");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("merge_state", st, [&] {
+      return rpa::launch_merge_state(o_a, lse_a, o_b, lse_b, o, lse, rows, heads, dim, dtype, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "merge_state launch");
+    return RPA_OK;
   });
-  if (e != hipSuccess) return hip_fail(e, "merge_state launch");
-  return RPA_OK;
 }
 
 RPA_EXPORT rpa_status rpa_page_copy(const void* src, const rpa_cache_strides* src_strides,
+                                    int32_t src_pool_pages, int32_t src_pool_heads,
                                     const int32_t* src_pages, void* dst,
-                                    const rpa_cache_strides* dst_strides,
-                                    const int32_t* dst_pages, int32_t num_pages,
-                                    int32_t src_head0, int32_t dst_head0, int32_t num_heads,
-                                    int32_t page_size, int32_t dim, int32_t dtype, void* stream) {
-  if (dtype != RPA_DTYPE_F32 && dtype != RPA_DTYPE_BF16)
-    return fail(RPA_ERR_INVALID_ARG, "dtype must be RPA_DTYPE_F32 or RPA_DTYPE_BF16");
-  if (num_pages < 0 || num_heads <= 0 || page_size <= 0 || dim <= 0 || src_head0 < 0 ||
-      dst_head0 < 0)
-    return fail(RPA_ERR_INVALID_ARG, "bad num_pages, heads, page_size or dim");
-  const int32_t vec = dtype == RPA_DTYPE_BF16 ? 8 : 4;
-  if (dim % vec) return fail(RPA_ERR_INVALID_ARG, "dim must fill whole 16-byte chunks");
-  if (num_pages == 0) return RPA_OK;
-  if (!src || !dst) return fail(RPA_ERR_INVALID_ARG, "null src or dst");
-  if (!aligned(src, 16) || !aligned(dst, 16))
-    return fail(RPA_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
-  if ((src_pages && !aligned(src_pages, 4)) || (dst_pages && !aligned(dst_pages, 4)))
-    return fail(RPA_ERR_INVALID_ARG, "page id arrays must be 4-byte aligned");
-  std::string why;
-  if (!strides_ok(src_strides, dim, dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "src: " + why);
-  if (!strides_ok(dst_strides, dim, dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "dst: " + why);
-  const int64_t es = dtype == RPA_DTYPE_BF16 ? 2 : 4;
-  if ((int64_t)num_heads * page_size * (dim * es / 16) > INT32_MAX)
-    return fail(RPA_ERR_INVALID_ARG, "page too large");
-  const rpa::Strides sb{src_strides->page_stride * es, src_strides->head_stride * es,
-                        src_strides->token_stride * es};
-  const rpa::Strides db{dst_strides->page_stride * es, dst_strides->head_stride * es,
-                        dst_strides->token_stride * es};
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = timed("page_copy", st, [&] {
-    return rpa::launch_page_copy(src, sb, src_pages, dst, db, dst_pages, num_pages, src_head0,
-                                 dst_head0, num_heads, page_size, (int32_t)(dim * es), st);
+                                    const rpa_cache_strides* dst_strides, int32_t dst_pool_pages,
+                                    int32_t dst_pool_heads, const int32_t* dst_pages,
+                                    int32_t num_pages, int32_t src_head0, int32_t dst_head0,
+                                    int32_t num_heads, int32_t page_size, int32_t dim,
+                                    int32_t dtype, void* stream) {
+  return guarded([&] {
+    if (dtype != RPA_DTYPE_F32 && dtype != RPA_DTYPE_BF16)
+      return fail(RPA_ERR_INVALID_ARG, "dtype must be RPA_DTYPE_F32 or RPA_DTYPE_BF16");
+    if (num_pages < 0 || num_heads <= 0 || page_size <= 0 || dim <= 0 || src_head0 < 0 ||
+        dst_head0 < 0)
+      return fail(RPA_ERR_INVALID_ARG, "bad num_pages, heads, page_size or dim");
+    if (src_pool_pages < 0 || dst_pool_pages < 0 || src_pool_heads <= 0 || dst_pool_heads <= 0)
+      return fail(RPA_ERR_INVALID_ARG, "bad pool page or head counts");
+    if ((int64_t)src_head0 + num_heads > src_pool_heads ||
+        (int64_t)dst_head0 + num_heads > dst_pool_heads)
+      return fail(RPA_ERR_INVALID_ARG, "head range outside the pool's heads");
+    if ((!src_pages && num_pages > src_pool_pages) || (!dst_pages && num_pages > dst_pool_pages))
+      return fail(RPA_ERR_PAGE_OOB, "identity page list longer than the pool");
+    const int32_t vec = dtype == RPA_DTYPE_BF16 ? 8 : 4;
+    if (dim % vec) return fail(RPA_ERR_INVALID_ARG, "dim must fill whole 16-byte chunks");
+    if (num_pages == 0) return RPA_OK;
+    if (!src || !dst) return fail(RPA_ERR_INVALID_ARG, "null src or dst");
+    if (!aligned(src, 16) || !aligned(dst, 16))
+      return fail(RPA_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+    if ((src_pages && !aligned(src_pages, 4)) || (dst_pages && !aligned(dst_pages, 4)))
+      return fail(RPA_ERR_INVALID_ARG, "page id arrays must be 4-byte aligned");
+    std::string why;
+    if (!strides_ok(src_strides, dim, dtype, &why))
+      return fail(RPA_ERR_INVALID_ARG, "src: " + why);
+    if (!strides_ok(dst_strides, dim, dtype, &why))
+      return fail(RPA_ERR_INVALID_ARG, "dst: " + why);
+    const int64_t es = dtype == RPA_DTYPE_BF16 ? 2 : 4;
+    if ((int64_t)num_heads * page_size * (dim * es / 16) > INT32_MAX)
+      return fail(RPA_ERR_INVALID_ARG, "page too large");
+    const rpa::Strides sb{src_strides->page_stride * es, src_strides->head_stride * es,
+                          src_strides->token_stride * es};
+    const rpa::Strides db{dst_strides->page_stride * es, dst_strides->head_stride * es,
+                          dst_strides->token_stride * es};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("page_copy", st, [&] {
+      return rpa::launch_page_copy(src, sb, src_pages, src_pool_pages, dst, db, dst_pages,
+                                   dst_pool_pages, num_pages, src_head0, dst_head0, num_heads,
+                                   page_size, (int32_t)(dim * es), st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "page_copy launch");
+    return RPA_OK;
   });
-  if (e != hipSuccess) return hip_fail(e, "page_copy launch");
-  return RPA_OK;
 }
 
 RPA_EXPORT rpa_status rpa_profile_enable(int32_t on) {
-  std::lock_guard<std::mutex> lock(g_prof_mu);
-  g_prof_on = on != 0;
-  return RPA_OK;
+  return guarded([&] {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof_on = on != 0;
+    return RPA_OK;
+  });
 }
 
 RPA_EXPORT rpa_status rpa_profile_select(const char* kernels) {
-  std::lock_guard<std::mutex> lock(g_prof_mu);
-  g_prof_only.clear();
-  if (kernels == nullptr) return RPA_OK;
-  std::string cur;
-  for (const char* c = kernels;; ++c) {
-    if (*c == ',' || *c == '\0') {
-      if (!cur.empty()) g_prof_only.insert(cur);
-      cur.clear();
-      if (*c == '\0') break;
-    } else {
-      cur.push_back(*c);
+  return guarded([&] {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof_only.clear();
+    if (kernels == nullptr) return RPA_OK;
+    std::string cur;
+    for (const char* c = kernels;; ++c) {
+      if (*c == ',' || *c == '\0') {
+        if (!cur.empty()) g_prof_only.insert(cur);
+        cur.clear();
+        if (*c == '\0') break;
+      } else {
+        cur.push_back(*c);
+      }
     }
-  }
-  return RPA_OK;
+    return RPA_OK;
+  });
 }
 
 RPA_EXPORT rpa_status rpa_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
-  if (!kernel || !total_ms || !launches) return fail(RPA_ERR_INVALID_ARG, "null argument");
-  std::lock_guard<std::mutex> lock(g_prof_mu);
-  hipError_t e = prof_drain();
-  if (e != hipSuccess) return hip_fail(e, "profile events");
-  auto it = g_prof_totals.find(kernel);
-  *total_ms = it == g_prof_totals.end() ? 0.0 : it->second.first;
-  *launches = it == g_prof_totals.end() ? 0 : it->second.second;
-  return RPA_OK;
+  return guarded([&] {
+    if (!kernel || !total_ms || !launches) return fail(RPA_ERR_INVALID_ARG, "null argument");
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    hipError_t e = prof_drain();
+    if (e != hipSuccess) return hip_fail(e, "profile events");
+    auto it = g_prof_totals.find(kernel);
+    *total_ms = it == g_prof_totals.end() ? 0.0 : it->second.first;
+    *launches = it == g_prof_totals.end() ? 0 : it->second.second;
+    return RPA_OK;
+  });
 }
 
 RPA_EXPORT rpa_status rpa_profile_reset(void) {
-  std::lock_guard<std::mutex> lock(g_prof_mu);
-  hipError_t e = prof_drain();
-  g_prof_totals.clear();
-  if (e != hipSuccess) return hip_fail(e, "profile events");
-  return RPA_OK;
+  return guarded([&] {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    hipError_t e = prof_drain();
+    g_prof_totals.clear();
+    if (e != hipSuccess) return hip_fail(e, "profile events");
+    return RPA_OK;
+  });
 }
 
 RPA_EXPORT void rpa_plan_destroy(rpa_plan* plan) {
@@ -478,51 +550,54 @@ RPA_EXPORT void rpa_plan_destroy(rpa_plan* plan) {
     (void)hipEventDestroy(static_cast<hipEvent_t>(plan->event));
   }
   if (plan->staging) (void)hipHostFree(plan->staging);
-  delete plan;
+  delete plan;  // vectors only: their destructors do not throw
 }
 
 RPA_EXPORT rpa_status rpa_plan_debug_dump(const rpa_plan* plan, const char* name, int32_t* dst,
                                           int64_t cap, int64_t* len) {
-  if (!plan || !name || !len) return fail(RPA_ERR_INVALID_ARG, "null plan, name or len");
-  const int32_t* src = nullptr;
-  int64_t n = 0;
-  std::vector<int32_t> tmp;
-  const std::string nm(name);
-  const int32_t* blob = plan->blob.data();
-  if (nm == "items") {
-    for (int k = 0; k < rpa::KC_COUNT; ++k)
-      tmp.insert(tmp.end(), blob + plan->off_items[k],
-                 blob + plan->off_items[k] + (int64_t)plan->n_items[k] * rpa::IT_WORDS);
-    src = tmp.data();
-    n = (int64_t)tmp.size();
-  } else if (nm == "splits") {
-    src = blob + plan->off_split;
-    n = (int64_t)plan->batch_size * rpa::SP_WORDS;
-  } else if (nm == "append") {
-    src = blob + plan->off_append;
-    n = (int64_t)plan->total_q * 2;
-  } else if (nm == "wg_prefill" || nm == "wg_mla" || nm == "wg_decode") {
-    const int k = nm == "wg_prefill" ? rpa::KC_PREFILL
-                                     : (nm == "wg_mla" ? rpa::KC_MLA : rpa::KC_DECODE);
-    src = blob + plan->off_wg[k];
-    n = plan->n_items[k] > 0 ? (int64_t)plan->n_wgs[k] + 1 : 0;
-  } else if (nm == "merge_rows") {
-    src = blob + plan->off_merge;
-    n = plan->n_merge_rows;
-  } else if (nm == "merge_info") {
-    src = blob + plan->off_merge_info;
-    n = (int64_t)plan->n_merge_rows * 4;
-  } else if (nm == "summary") {
-    int32_t total = 0;
-    for (int k = 0; k < rpa::KC_COUNT; ++k) total += plan->n_items[k];
-    tmp = {plan->batch_size, plan->total_q, total, (int32_t)plan->partial_rows,
-           plan->n_items[0], plan->n_items[1], plan->n_items[2], plan->n_items[3]};
-    src = tmp.data();
-    n = (int64_t)tmp.size();
-  } else {
-    return fail(RPA_ERR_INVALID_ARG, "unknown table name: " + nm);
-  }
-  *len = n;
-  if (dst && cap > 0) std::memcpy(dst, src, (size_t)std::min<int64_t>(cap, n) * sizeof(int32_t));
-  return RPA_OK;
+  return guarded([&] {
+    if (!plan || !name || !len) return fail(RPA_ERR_INVALID_ARG, "null plan, name or len");
+    const int32_t* src = nullptr;
+    int64_t n = 0;
+    std::vector<int32_t> tmp;
+    const std::string nm(name);
+    const int32_t* blob = plan->blob.data();
+    if (nm == "items") {
+      for (int k = 0; k < rpa::KC_COUNT; ++k)
+        tmp.insert(tmp.end(), blob + plan->off_items[k],
+                   blob + plan->off_items[k] + (int64_t)plan->n_items[k] * rpa::IT_WORDS);
+      src = tmp.data();
+      n = (int64_t)tmp.size();
+    } else if (nm == "splits") {
+      src = blob + plan->off_split;
+      n = (int64_t)plan->batch_size * rpa::SP_WORDS;
+    } else if (nm == "append") {
+      src = blob + plan->off_append;
+      n = (int64_t)plan->total_q * 2;
+    } else if (nm == "wg_prefill" || nm == "wg_mla" || nm == "wg_decode") {
+      const int k = nm == "wg_prefill" ? rpa::KC_PREFILL
+                                       : (nm == "wg_mla" ? rpa::KC_MLA : rpa::KC_DECODE);
+      src = blob + plan->off_wg[k];
+      n = plan->n_items[k] > 0 ? (int64_t)plan->n_wgs[k] + 1 : 0;
+    } else if (nm == "merge_rows") {
+      src = blob + plan->off_merge;
+      n = plan->n_merge_rows;
+    } else if (nm == "merge_info") {
+      src = blob + plan->off_merge_info;
+      n = (int64_t)plan->n_merge_rows * 4;
+    } else if (nm == "summary") {
+      int32_t total = 0;
+      for (int k = 0; k < rpa::KC_COUNT; ++k) total += plan->n_items[k];
+      tmp = {plan->batch_size, plan->total_q, total, (int32_t)plan->partial_rows,
+             plan->n_items[0], plan->n_items[1], plan->n_items[2], plan->n_items[3]};
+      src = tmp.data();
+      n = (int64_t)tmp.size();
+    } else {
+      return fail(RPA_ERR_INVALID_ARG, "unknown table name: " + nm);
+    }
+    *len = n;
+    if (dst && cap > 0)
+      std::memcpy(dst, src, (size_t)std::min<int64_t>(cap, n) * sizeof(int32_t));
+    return RPA_OK;
+  });
 }

@@ -30,7 +30,6 @@
 // Keys past the item's end are fetched from its last key (a written slot of
 // the same page), so the masked tail multiplies finite values by zero.
 
-#include <stdlib.h>
 
 #include "common.h"
 #include "../launch.h"
@@ -391,27 +390,16 @@ hipError_t launch_decode(const DevPlan& p, const void* q, const void* k_cache, c
                          Strides ks, Strides vs, void* o, float* lse, hipStream_t stream) {
   // Ring depth: the planner's choice (3 tiles, 24 KiB of LDS per wave, six
   // waves per CU, for one item per workgroup; 2 tiles, 16 KiB, for the cut
-  // lists it sizes for eight resident waves per CU).  RPA_DECODE_STAGES in
-  // {2, 3, 4, 6} overrides it (a tuning knob, read once).
-  static const int forced = [] {
-    const char* e = getenv("RPA_DECODE_STAGES");
-    const int v = e ? atoi(e) : 0;
-    return (v == 2 || v == 3 || v == 4 || v == 6) ? v : 0;
-  }();
-  const int stages = forced ? forced : (p.dec_stages == 2 ? 2 : 3);
+  // lists it sizes for eight resident waves per CU).
   const dim3 grid(p.n_wgs[KC_DECODE]), block(64);
   const bf16_t* qq = static_cast<const bf16_t*>(q);
   const bf16_t* kk = static_cast<const bf16_t*>(k_cache);
   const bf16_t* vv = static_cast<const bf16_t*>(v_cache);
   bf16_t* oo = static_cast<bf16_t*>(o);
-  if (stages == 3)
-    hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
-  else if (stages == 2)
+  if (p.dec_stages == 2)
     hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
-  else if (stages == 6)
-    hipLaunchKernelGGL(decode_kernel<6>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
   else
-    hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
+    hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, stream, p, qq, kk, vv, ks, vs, oo, lse);
   return hipGetLastError();
 }
 

@@ -24,15 +24,16 @@ namespace rpa {
 
 namespace {
 
-__global__ __launch_bounds__(256) void page_copy_kernel(const char* __restrict__ src,
-                                                        Strides src_b, const int32_t* src_pages,
-                                                        char* __restrict__ dst, Strides dst_b,
-                                                        const int32_t* dst_pages, int32_t src_h0,
-                                                        int32_t dst_h0, int32_t num_heads,
-                                                        int32_t page_size, int32_t row_chunks) {
+__global__ __launch_bounds__(256) void page_copy_kernel(
+    const char* __restrict__ src, Strides src_b, const int32_t* src_pages, int32_t src_pool_pages,
+    char* __restrict__ dst, Strides dst_b, const int32_t* dst_pages, int32_t dst_pool_pages,
+    int32_t src_h0, int32_t dst_h0, int32_t num_heads, int32_t page_size, int32_t row_chunks) {
   const int32_t i = blockIdx.x;
   const int64_t sp = src_pages ? src_pages[i] : i;
   const int64_t dp = dst_pages ? dst_pages[i] : i;
+  // Device-side page ids are not seen by the host: a pair with an id outside
+  // its pool is skipped rather than read or written out of bounds.
+  if (sp < 0 || sp >= src_pool_pages || dp < 0 || dp >= dst_pool_pages) return;
   const int32_t per_head = page_size * row_chunks;
   const int32_t total = num_heads * per_head;
   const char* s0 = src + sp * src_b.page + (int64_t)src_h0 * src_b.head;
@@ -51,8 +52,9 @@ __global__ __launch_bounds__(256) void page_copy_kernel(const char* __restrict__
 
 }  // namespace
 
-hipError_t launch_page_copy(const void* src, Strides src_b, const int32_t* src_pages, void* dst,
-                            Strides dst_b, const int32_t* dst_pages, int32_t num_pages,
+hipError_t launch_page_copy(const void* src, Strides src_b, const int32_t* src_pages,
+                            int32_t src_pool_pages, void* dst, Strides dst_b,
+                            const int32_t* dst_pages, int32_t dst_pool_pages, int32_t num_pages,
                             int32_t src_h0, int32_t dst_h0, int32_t num_heads, int32_t page_size,
                             int32_t row_bytes, hipStream_t stream) {
   if (num_pages == 0) return hipSuccess;
@@ -60,9 +62,9 @@ hipError_t launch_page_copy(const void* src, Strides src_b, const int32_t* src_p
   const int64_t per_page = (int64_t)num_heads * page_size * row_chunks;
   const int64_t ys = std::min<int64_t>((per_page + 255) / 256, 64);
   hipLaunchKernelGGL(page_copy_kernel, dim3((unsigned)num_pages, (unsigned)ys), dim3(256), 0,
-                     stream, static_cast<const char*>(src), src_b, src_pages,
-                     static_cast<char*>(dst), dst_b, dst_pages, src_h0, dst_h0, num_heads,
-                     page_size, row_chunks);
+                     stream, static_cast<const char*>(src), src_b, src_pages, src_pool_pages,
+                     static_cast<char*>(dst), dst_b, dst_pages, dst_pool_pages, src_h0, dst_h0,
+                     num_heads, page_size, row_chunks);
   return hipGetLastError();
 }
 

@@ -29,8 +29,10 @@ hipError_t launch_mla(const DevPlan& p, const void* q, const void* kv_cache, Str
 hipError_t launch_merge_rows(const DevPlan& p, void* o, float* lse, hipStream_t stream);
 
 // Copy of head ranges of pages between pools or buffers (strides in bytes).
-hipError_t launch_page_copy(const void* src, Strides src_b, const int32_t* src_pages, void* dst,
-                            Strides dst_b, const int32_t* dst_pages, int32_t num_pages,
+// Page pairs with an id outside [0, pool pages) are skipped.
+hipError_t launch_page_copy(const void* src, Strides src_b, const int32_t* src_pages,
+                            int32_t src_pool_pages, void* dst, Strides dst_b,
+                            const int32_t* dst_pages, int32_t dst_pool_pages, int32_t num_pages,
                             int32_t src_h0, int32_t dst_h0, int32_t num_heads, int32_t page_size,
                             int32_t row_bytes, hipStream_t stream);
 

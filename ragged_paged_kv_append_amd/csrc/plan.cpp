@@ -26,12 +26,6 @@ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-int32_t log2i(int32_t x) {
-  int32_t s = 0;
-  while ((1 << s) < x) ++s;
-  return s;
-}
-
 // Resident decode waves per CU that a cut decode batch is planned for: the
 // two-slot ring (16 KiB of LDS per wave) and ~150 VGPRs admit eight.
 constexpr int64_t kDecodeWavesPerCu = 8;
@@ -322,7 +316,6 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
         k = KC_MLA;
       }
     }
-    if (!class_available(k, c)) k = KC_GENERIC;
     if (k == KC_MLA && has_tree && tree_req[(size_t)r]) k = KC_GENERIC;
     cls[r] = k;
   }
@@ -740,7 +733,6 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
   plan->part_lse_off =
       plan->part_o_off + (size_t)round_up(partial_rows * c.num_qo_heads * c.head_dim_v * 4, 256);
   plan->ws_bytes = plan->part_lse_off + (size_t)round_up(partial_rows * c.num_qo_heads * 4, 256);
-  (void)log2i;
   return RPA_OK;
 }
 

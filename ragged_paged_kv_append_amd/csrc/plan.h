@@ -50,8 +50,4 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
                       const int32_t* tree_indptr, const uint32_t* tree_words, int32_t num_cus,
                       rpa_plan* plan, std::string* err);
 
-// Whether a specialised kernel class is compiled into the library; the planner
-// routes items of unavailable classes to the generic kernel.
-bool class_available(int32_t kernel_class, const rpa_attn_config& cfg);
-
 }  // namespace rpa

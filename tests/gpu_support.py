@@ -111,3 +111,56 @@ def max_err(got: torch.Tensor, want: np.ndarray) -> float:
         return 0.0
     assert np.all(np.isfinite(g)), "non-finite output"
     return float(np.max(np.abs(g - want)))
+
+
+def full_parity(spec, meta, tensors, label, tree_masks=None, num_cus=0, group_bytes=1 << 29,
+                log=print):
+    """Runs the batch through the library once (the launch configuration the
+    benchmark times), then checks the pools bit-exactly over the whole pool
+    and O / LSE of every request against the oracle.  The oracle runs over
+    groups of requests of at most `group_bytes` of float64 keys, so host
+    memory stays bounded at any batch size.  Returns (max|dO|, max|dLSE|)."""
+    q_raw, kn_raw = raw(tensors["q"]), raw(tensors["k_new"])
+    vn_raw = None if tensors["v_new"] is None else raw(tensors["v_new"])
+    kp_raw = raw(tensors["k_pool"])
+    vp_raw = None if tensors["v_pool"] is None else raw(tensors["v_pool"])
+    b = batch_of(meta)
+    kp2, vp2 = oracle.append(kp_raw, vp_raw, kn_raw, vn_raw, b)
+    cfg = config_of(spec)
+    plan = rpa.Plan(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices,
+                    meta.num_pages, num_cus=num_cus, tree_masks=tree_masks)
+    plan.append(tensors["k_new"], tensors["v_new"], tensors["k_pool"], tensors["v_pool"])
+    o, lse = plan.attention(tensors["q"], tensors["k_pool"], tensors["v_pool"])
+    torch.cuda.synchronize()
+    log(f"[{label}] summary={plan.debug('summary').tolist()}")
+    assert np.array_equal(raw(tensors["k_pool"]), kp2), "K pool differs from the oracle"
+    if vp2 is not None:
+        assert np.array_equal(raw(tensors["v_pool"]), vp2), "V pool differs from the oracle"
+    o_g = o.float().cpu().numpy().astype(np.float64)
+    lse_g = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(lse_g)), "non-finite output"
+    per_token = spec.num_kv_heads * (spec.head_dim_qk + (0 if vp2 is None else spec.head_dim_v)) * 8
+    eo = el = 0.0
+    r0 = 0
+    B = meta.batch_size
+    while r0 < B:
+        r1, acc = r0, 0
+        while r1 < B and (r1 == r0 or acc + int(meta.kv_len[r1]) * per_token <= group_bytes):
+            acc += int(meta.kv_len[r1]) * per_token
+            r1 += 1
+        reqs = list(range(r0, r1))
+        sub_meta, sub_pools, sub_rows, sel = compact(meta, reqs, {"k": kp2, "v": vp2},
+                                                     {"q": q_raw})
+        o_ref, lse_ref = oracle.attend(
+            f64(sub_rows["q"]), f64(sub_pools["k"]),
+            None if sub_pools["v"] is None else f64(sub_pools["v"]), batch_of(sub_meta),
+            spec.num_qo_heads, spec.num_kv_heads, spec.sm_scale, head_dim_v=spec.head_dim_v,
+            causal=spec.causal,
+            tree=None if tree_masks is None else [tree_masks[r] for r in reqs])
+        if len(sel):
+            eo = max(eo, float(np.max(np.abs(o_g[sel] - o_ref))))
+            el = max(el, float(np.max(np.abs(lse_g[sel] - lse_ref))))
+        r0 = r1
+    log(f"[{label}] all {B} requests: max|dO|={eo:.3g} max|dLSE|={el:.3g}")
+    assert eo <= TOL[spec.dtype] and el <= TOL[spec.dtype]
+    return eo, el

@@ -43,11 +43,12 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert rpa.rpa_abi_version() == 1
+    assert rpa.rpa_abi_version() == 2
     for code, name in [(0, "RPA_OK"), (-1, "RPA_ERR_INVALID_ARG"), (-2, "RPA_ERR_UNSUPPORTED"),
                        (-3, "RPA_ERR_WORKSPACE_TOO_SMALL"), (-4, "RPA_ERR_PAGE_OOB"),
                        (-5, "RPA_ERR_DUPLICATE_WRITE_PAGE"), (-6, "RPA_ERR_HIP"),
-                       (-7, "RPA_ERR_NOT_UPLOADED")]:
+                       (-7, "RPA_ERR_NOT_UPLOADED"), (-8, "RPA_ERR_HOST_ALLOC"),
+                       (-9, "RPA_ERR_INTERNAL")]:
         assert rpa.rpa_status_string(code) == name
 
 
@@ -378,8 +379,88 @@ def test_device_calls_validate_before_touching_the_device(L):
            4, 2, 8, rpa.RPA_DTYPE_F32, 0)
     expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_merge_state, fake, fake, fake, fake, fake, fake, 4, 2,
            8, 9, 0)
+    # an output lse over an input lse would race between the threads of a row
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_merge_state, fake, fake + 4096, fake + 8192,
+           fake + 12288, fake, fake + 4096, 4, 2, 8, rpa.RPA_DTYPE_F32, 0)
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_merge_state, fake, fake + 4096, fake + 8192,
+           fake + 12288, fake, fake + 12288, 4, 2, 8, rpa.RPA_DTYPE_F32, 0)
     with pytest.raises(rpa.RpaError):
         rpa.rpa_plan_debug_dump(plan, "no_such_table")
+
+
+def test_page_copy_validates_pools_before_touching_the_device(L):
+    st = rpa.rpa_cache_strides(2 * 16 * 128, 16 * 128, 128)
+    fake = 1 << 40  # never dereferenced: validation fails first
+    bf16 = rpa.RPA_DTYPE_BF16
+    # (src_pool_pages, src_pool_heads, src_pages, dst_pool_pages, dst_pool_heads, dst_pages,
+    #  num_pages, src_head0, dst_head0, num_heads) -> status
+    cases = [
+        ((10, 2, None, 9, 2, None, 10, 0, 0, 2), rpa.RPA_ERR_PAGE_OOB),   # identity past dst
+        ((9, 2, None, 10, 2, None, 10, 0, 0, 2), rpa.RPA_ERR_PAGE_OOB),   # identity past src
+        ((10, 2, None, 10, 2, None, 4, 1, 0, 2), rpa.RPA_ERR_INVALID_ARG),  # src heads 1..2 of 2
+        ((10, 2, None, 10, 1, None, 4, 0, 0, 2), rpa.RPA_ERR_INVALID_ARG),  # dst has one head
+        ((10, 0, None, 10, 2, None, 4, 0, 0, 1), rpa.RPA_ERR_INVALID_ARG),  # no heads
+        ((-1, 2, None, 10, 2, None, 0, 0, 0, 1), rpa.RPA_ERR_INVALID_ARG),  # negative pool
+    ]
+    for (sp, sh, sids, dp, dh, dids, n, h0s, h0d, nh), want in cases:
+        got = L.rpa_page_copy(fake, ctypes.byref(st), sp, sh, sids, fake, ctypes.byref(st), dp,
+                              dh, dids, n, h0s, h0d, nh, 16, 128, bf16, None)
+        assert got == want, ((sp, sh, dp, dh, n, h0s, h0d, nh), got, want)
+    # device page lists are checked in the kernel, so the host accepts any count
+    # of them; a zero-length copy returns before any device work
+    assert L.rpa_page_copy(fake, ctypes.byref(st), 1, 2, fake, fake, ctypes.byref(st), 1, 2,
+                           fake, 0, 0, 0, 2, 16, 128, bf16, None) == rpa.RPA_OK
+
+
+def test_binding_checks_tensors_before_any_launch():
+    """The binding's checks of dtype, shape, contiguity, pool size and device
+    raise INVALID_ARG before the C ABI is called (CPU tensors here: each case
+    has exactly one thing wrong, and the all-correct case fails on the device)."""
+    import torch
+    cfg = rpa.make_config(8, 2, 128, 128, 16, "bf16")
+    T, P, npg = 5, 16, 7
+    bf = torch.bfloat16
+
+    def good():
+        return {"k_new": torch.zeros((T, 2, 128), dtype=bf), "v_new": torch.zeros((T, 2, 128), dtype=bf),
+                "k_cache": torch.zeros((npg, 2, P, 128), dtype=bf),
+                "v_cache": torch.zeros((npg, 2, P, 128), dtype=bf),
+                "q": torch.zeros((T, 8, 128), dtype=bf), "o": torch.zeros((T, 8, 128), dtype=bf),
+                "lse": torch.zeros((T, 8), dtype=torch.float32)}
+
+    def append(t):
+        rpa.check_append_args(cfg, T, npg, t["k_new"], t["v_new"], t["k_cache"], t["v_cache"])
+
+    def attend(t):
+        rpa.check_attention_args(cfg, T, npg, t["q"], t["k_cache"], t["v_cache"], t["o"], t["lse"])
+
+    bad = {
+        "k_new dtype": ("k_new", lambda t: t.float()),
+        "k_new shape": ("k_new", lambda t: t[:T - 1]),
+        "v_new heads": ("v_new", lambda t: torch.zeros((T, 1, 128), dtype=bf)),
+        "q non-contiguous": ("q", lambda t: torch.zeros((T, 128, 8), dtype=bf).transpose(1, 2)),
+        "o dtype": ("o", lambda t: t.float()),
+        "lse dtype": ("lse", lambda t: t.double()),
+        "k_cache too few pages": ("k_cache", lambda t: t[:npg - 1]),
+        "v_cache page size": ("v_cache", lambda t: torch.zeros((npg, 2, 8, 128), dtype=bf)),
+        "k_cache row": ("k_cache", lambda t: torch.zeros((npg, 2, P, 64), dtype=bf)),
+        "v_cache last dim strided": ("v_cache",
+                                     lambda t: torch.zeros((npg, 2, P, 256), dtype=bf)[..., ::2]),
+    }
+    for label, (key, mutate) in bad.items():
+        t = good()
+        t[key] = mutate(t[key])
+        fns = [append] if key in ("k_new", "v_new") else [attend] if key in ("q", "o", "lse") \
+            else [append, attend]
+        for fn in fns:
+            with pytest.raises(rpa.RpaError) as ei:
+                fn(t)
+            assert ei.value.status == rpa.RPA_ERR_INVALID_ARG, label
+            assert "GPU" not in str(ei.value), (label, str(ei.value))
+    for fn in (append, attend):
+        with pytest.raises(rpa.RpaError) as ei:
+            fn(good())
+        assert "not a GPU" in str(ei.value)
 
 
 def test_plan_debug_dump_append_matches_oracle(L):

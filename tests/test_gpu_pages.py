@@ -134,8 +134,35 @@ def test_page_copy_argument_checks_launch_nothing():
     pool = torch.zeros((4, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
     st = rpa.strides_of(pool)
     with pytest.raises(rpa.RpaError):   # dim not a whole number of 16-byte chunks
-        rpa.rpa_page_copy(pool, st, None, pool, st, None, 4, 0, 0, 2, 16, 100, rpa.RPA_DTYPE_BF16)
-    with pytest.raises(rpa.RpaError):   # misaligned destination
-        rpa.rpa_page_copy(pool, st, None, pool.data_ptr() + 2, st, None, 4, 0, 0, 2, 16, 128,
+        rpa.rpa_page_copy(pool, st, 4, 2, None, pool, st, 4, 2, None, 4, 0, 0, 2, 16, 100,
                           rpa.RPA_DTYPE_BF16)
-    rpa.rpa_page_copy(None, st, None, None, st, None, 0, 0, 0, 2, 16, 128, rpa.RPA_DTYPE_BF16)
+    with pytest.raises(rpa.RpaError):   # misaligned destination
+        rpa.rpa_page_copy(pool, st, 4, 2, None, pool.data_ptr() + 2, st, 4, 2, None, 4, 0, 0, 2,
+                          16, 128, rpa.RPA_DTYPE_BF16)
+    with pytest.raises(rpa.RpaError) as ei:   # identity list longer than the destination pool
+        rpa.rpa_page_copy(pool, st, 4, 2, None, pool, st, 3, 2, None, 4, 0, 0, 2, 16, 128,
+                          rpa.RPA_DTYPE_BF16)
+    assert ei.value.status == rpa.RPA_ERR_PAGE_OOB
+    with pytest.raises(rpa.RpaError):   # head range past the source's heads
+        rpa.rpa_page_copy(pool, st, 4, 2, None, pool, st, 4, 2, None, 4, 1, 0, 2, 16, 128,
+                          rpa.RPA_DTYPE_BF16)
+    rpa.rpa_page_copy(None, st, 4, 2, None, None, st, 4, 2, None, 0, 0, 0, 2, 16, 128,
+                      rpa.RPA_DTYPE_BF16)
+
+
+def test_page_copy_skips_out_of_range_device_ids():
+    """Device page ids outside a pool are skipped in the kernel: those pairs
+    write nothing, the others are copied as usual."""
+    g = torch.Generator(device="cuda").manual_seed(11)
+    src = torch.randn((20, 2, 16, 128), generator=g, device="cuda").to(torch.bfloat16)
+    dst = torch.zeros((12, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    sp = [3, 25, 7, -1, 19, 4]
+    dp = [0, 1, 12, 3, 11, -5]
+    rpa.copy_pages(src, dst, src_pages=ids(sp), dst_pages=ids(dp))
+    torch.cuda.synchronize()
+    want = np.zeros_like(raw(dst))
+    host = raw(src)
+    for s_, d_ in zip(sp, dp):
+        if 0 <= s_ < 20 and 0 <= d_ < 12:
+            want[d_] = host[s_]
+    assert raw(dst).tobytes() == want.tobytes()

@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 import ragged_paged_kv_append_amd as rpa
-from tests.gpu_support import (TOL, batch_of, compact, config_of, expected, f64, max_err,
+from tests.gpu_support import (TOL, config_of, expected, f64, full_parity, max_err,
                                poison_tail_slots, raw, run_library)
 
 pytestmark = pytest.mark.gpu
@@ -294,52 +294,23 @@ def test_invalid_calls_launch_nothing():
 # ----------------------------------------------------------------------------
 
 
-def sampled_parity(spec, meta, tensors, requests, label):
-    """Pools bit-exact over the whole pool; O/LSE checked on sampled requests."""
-    q_raw, kn_raw = raw(tensors["q"]), raw(tensors["k_new"])
-    vn_raw = None if tensors["v_new"] is None else raw(tensors["v_new"])
-    kp_raw = raw(tensors["k_pool"])
-    vp_raw = None if tensors["v_pool"] is None else raw(tensors["v_pool"])
-    b = batch_of(meta)
-    kp2, vp2 = oracle.append(kp_raw, vp_raw, kn_raw, vn_raw, b)
-    o, lse, plan = run_library(spec, meta, tensors)
-    log(f"[{label}] summary={plan.debug('summary').tolist()}")
-    assert raw(tensors["k_pool"]).tobytes() == kp2.tobytes(), "K pool differs from the oracle"
-    if vp2 is not None:
-        assert raw(tensors["v_pool"]).tobytes() == vp2.tobytes(), "V pool differs from the oracle"
-    sub_meta, sub_pools, sub_rows, sel = compact(meta, requests, {"k": kp2, "v": vp2},
-                                                 {"q": q_raw})
-    sb = batch_of(sub_meta)
-    o_ref, lse_ref = oracle.attend(f64(sub_rows["q"]), f64(sub_pools["k"]),
-                                   None if sub_pools["v"] is None else f64(sub_pools["v"]), sb,
-                                   spec.num_qo_heads, spec.num_kv_heads, spec.sm_scale,
-                                   head_dim_v=spec.head_dim_v, causal=spec.causal)
-    sel_t = torch.from_numpy(sel).cuda()
-    eo = max_err(o.index_select(0, sel_t), o_ref)
-    el = max_err(lse.index_select(0, sel_t), lse_ref)
-    log(f"[{label}] sampled {len(requests)} requests: max|dO|={eo:.3g} max|dLSE|={el:.3g}")
-    assert eo <= TOL[spec.dtype] and el <= TOL[spec.dtype]
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-
-
 def test_workload_mixed_7b_full():
     spec, meta, tensors = workloads.workload("mixed_7b", device="cuda")
-    sampled_parity(spec, meta, tensors, range(meta.batch_size), "mixed_7b")
+    full_parity(spec, meta, tensors, "mixed_7b", log=log)
 
 
-def test_workload_decode_verify_gqa_sampled():
+def test_workload_decode_verify_gqa_full():
+    """All 256 requests (128 decodes, 128 four-token verifications) element by
+    element, in the launch configuration the benchmark times."""
     spec, meta, tensors = workloads.workload("decode_verify_gqa", device="cuda")
-    kv = meta.kv_len
-    picks = sorted(set([int(np.argmax(kv)), int(np.argmin(kv))] +
-                       list(np.random.default_rng(4).choice(meta.batch_size, 22, replace=False))))
-    sampled_parity(spec, meta, tensors, picks, "decode_verify_gqa")
+    full_parity(spec, meta, tensors, "decode_verify_gqa", log=log)
 
 
-def test_workload_mla_absorbed_sampled():
+def test_workload_mla_absorbed_full():
+    """All 64 latent requests (two query tokens over 128 heads each) element by
+    element, in the launch configuration the benchmark times."""
     spec, meta, tensors = workloads.workload("mla_absorbed", device="cuda")
-    kv = meta.kv_len
-    picks = sorted(set([int(np.argmax(kv)), int(np.argmin(kv)), 1, 17, 33, 50]))
-    sampled_parity(spec, meta, tensors, picks, "mla_absorbed")
+    full_parity(spec, meta, tensors, "mla_absorbed", log=log)
 
 
 def _chunked_run(spec, pages, num_pages, q, k, v, C, stop_after=None, pools=None):

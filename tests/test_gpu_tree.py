@@ -15,7 +15,8 @@ import torch
 import oracle
 import workloads
 import ragged_paged_kv_append_amd as rpa
-from tests.gpu_support import TOL, batch_of, config_of, f64, max_err, poison_tail_slots, raw
+from tests.gpu_support import (TOL, batch_of, config_of, f64, full_parity, max_err,
+                               poison_tail_slots, raw)
 
 pytestmark = pytest.mark.gpu
 
@@ -107,3 +108,21 @@ def test_chain_mask_reproduces_causal_verify():
     dl = (outs[0][1] - outs[1][1]).abs().max().item()
     log(f"chain vs causal: max|dO|={d:.3g} max|dLSE|={dl:.3g}")
     assert d <= 2e-2 and dl <= 2e-2
+
+
+def test_tree_verify_full_size_workload():
+    """The verify workload at full size (256 requests, 32/8 heads) with every
+    4-token verification as the draft tree the benchmark times (parents
+    -1, 0, 0, 1: a root, its two children, one grandchild), every request
+    compared with the oracle's tree-masked attention."""
+    spec, meta, tensors = workloads.workload("decode_verify_gqa", device="cuda")
+    parents = [-1, 0, 0, 1]
+    tree = np.zeros((4, 4), dtype=bool)
+    for t_ in range(4):
+        u = t_
+        while u >= 0:
+            tree[t_, u] = True
+            u = parents[u]
+    qo = np.diff(meta.qo_indptr)
+    masks = [tree if int(qo[r]) == 4 else None for r in range(meta.batch_size)]
+    full_parity(spec, meta, tensors, "decode_verify_gqa tree", tree_masks=masks, log=log)
