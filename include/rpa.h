@@ -240,6 +240,26 @@ rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q, const void* 
                                const rpa_cache_strides* vs, void* o, float* lse,
                                void* stream);
 
+/* rpa_batch_attention without a workspace, for callers that cannot allocate
+ * device memory at the point of the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * same kernels and the same results as rpa_batch_attention; the plan need not
+ * be uploaded.  The plan's metadata is copied from its host memory into a
+ * static device array of the library (RPA_STATIC_SCRATCH_BYTES, one per GPU,
+ * held until the process ends) with one asynchronous copy on `stream`, and
+ * the split partials live there too.  The call allocates nothing.
+ * Every call on a GPU uses that GPU's one array, so calls whose work may
+ * overlap on one GPU (two streams, or two threads) race: order them on one
+ * stream.  The plan must stay alive until the call's work has run.
+ * Errors: as rpa_batch_attention, and WORKSPACE_TOO_SMALL when the plan's
+ * workspace (rpa_plan_workspace_size) exceeds RPA_STATIC_SCRATCH_BYTES. */
+#define RPA_STATIC_SCRATCH_BYTES (128u << 20)
+rpa_status rpa_batch_attention_noalloc(const rpa_plan* plan, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const rpa_cache_strides* ks,
+                                       const rpa_cache_strides* vs, void* o, float* lse,
+                                       void* stream);
+
 /* Standalone softmax merge of two attention states over disjoint key sets
  * ("Chunked prefill", section "correctness"):
  *   lse = ln(e^lse_a + e^lse_b),  o = e^(lse_a-lse) o_a + e^(lse_b-lse) o_b.

@@ -40,7 +40,8 @@ KC_GENERIC, KC_DECODE, KC_PREFILL, KC_MLA = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
     "rpa_plan_create", "rpa_plan_create_tree", "rpa_plan_workspace_size", "rpa_plan_upload",
-    "rpa_kv_append", "rpa_batch_attention", "rpa_merge_state", "rpa_page_copy",
+    "rpa_kv_append", "rpa_batch_attention", "rpa_batch_attention_noalloc", "rpa_merge_state",
+    "rpa_page_copy",
     "rpa_plan_destroy",
     "rpa_status_string",
     "rpa_last_error_message", "rpa_abi_version", "rpa_plan_debug_dump", "rpa_profile_enable",
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.rpa_kv_append.argtypes = [vp, vp, vp, vp, vp, P(rpa_cache_strides), P(rpa_cache_strides), vp]
     L.rpa_batch_attention.argtypes = [vp, vp, vp, vp, P(rpa_cache_strides),
                                       P(rpa_cache_strides), vp, vp, vp]
+    L.rpa_batch_attention_noalloc.argtypes = [vp, vp, vp, vp, P(rpa_cache_strides),
+                                              P(rpa_cache_strides), vp, vp, vp]
     L.rpa_merge_state.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
     L.rpa_page_copy.argtypes = [vp, P(rpa_cache_strides), i32, i32, vp, vp,
                                 P(rpa_cache_strides), i32, i32, vp, i32, i32, i32, i32, i32, i32,
@@ -115,7 +118,8 @@ def lib() -> ctypes.CDLL:
     L.rpa_profile_reset.argtypes = []
     L.rpa_profile_select.argtypes = [ctypes.c_char_p]
     for name in ("rpa_plan_create", "rpa_plan_create_tree", "rpa_plan_workspace_size",
-                 "rpa_plan_upload", "rpa_kv_append", "rpa_batch_attention", "rpa_merge_state",
+                 "rpa_plan_upload", "rpa_kv_append", "rpa_batch_attention",
+                 "rpa_batch_attention_noalloc", "rpa_merge_state",
                  "rpa_page_copy", "rpa_plan_debug_dump", "rpa_profile_enable",
                  "rpa_profile_read", "rpa_profile_reset", "rpa_profile_select"):
         getattr(L, name).restype = i32
@@ -271,6 +275,16 @@ def rpa_batch_attention(plan: _PlanHandle, q, k_cache, v_cache, ks: rpa_cache_st
     _check(lib().rpa_batch_attention(plan.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                      ctypes.byref(ks), None if vs is None else ctypes.byref(vs),
                                      _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def rpa_batch_attention_noalloc(plan: _PlanHandle, q, k_cache, v_cache, ks: rpa_cache_strides,
+                                vs: Optional[rpa_cache_strides], o, lse=None, stream=None):
+    """rpa_batch_attention with the plan's metadata and partials in the
+    library's static device scratch (no workspace, no allocation)."""
+    _check(lib().rpa_batch_attention_noalloc(plan.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                             ctypes.byref(ks),
+                                             None if vs is None else ctypes.byref(vs), _ptr(o),
+                                             _ptr(lse), _stream(stream)))
 
 
 def rpa_merge_state(o_a, lse_a, o_b, lse_b, o, lse, rows: int, heads: int, dim: int, dtype: int,

@@ -60,9 +60,10 @@ rpa_status guarded(F&& body) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-rpa::DevPlan dev_plan(const rpa_plan* plan) {
+// Device view of a plan whose workspace (metadata, then partials) starts at ws.
+rpa::DevPlan dev_plan(const rpa_plan* plan, void* ws_base) {
   rpa::DevPlan p{};
-  const int32_t* base = static_cast<const int32_t*>(plan->d_ws);
+  const int32_t* base = static_cast<const int32_t*>(ws_base);
   p.qo_indptr = base + plan->off_qo_indptr;
   p.kv_len = base + plan->off_kv_len;
   p.page_indptr = base + plan->off_page_indptr;
@@ -82,7 +83,7 @@ rpa::DevPlan dev_plan(const rpa_plan* plan) {
                     ? reinterpret_cast<const uint32_t*>(base + plan->off_tree_mask) : nullptr;
   p.n_merge_rows = plan->n_merge_rows;
   p.dec_stages = plan->dec_stages;
-  char* ws = static_cast<char*>(plan->d_ws);
+  char* ws = static_cast<char*>(ws_base);
   p.part_o = reinterpret_cast<float*>(ws + plan->part_o_off);
   p.part_lse = reinterpret_cast<float*>(ws + plan->part_lse_off);
   p.batch_size = plan->batch_size;
@@ -333,7 +334,7 @@ RPA_EXPORT rpa_status rpa_kv_append(const rpa_plan* plan, const void* k_new, con
       if (!strides_ok(vs, c.head_dim_v, c.dtype, &why))
         return fail(RPA_ERR_INVALID_ARG, "v: " + why);
     }
-    rpa::DevPlan p = dev_plan(plan);
+    rpa::DevPlan p = dev_plan(plan, plan->d_ws);
     rpa::Strides k_st{ks->page_stride, ks->head_stride, ks->token_stride};
     rpa::Strides v_st =
         latent ? k_st : rpa::Strides{vs->page_stride, vs->head_stride, vs->token_stride};
@@ -347,6 +348,82 @@ RPA_EXPORT rpa_status rpa_kv_append(const rpa_plan* plan, const void* k_new, con
   });
 }
 
+namespace {
+
+// Pool views of an attention call, after validation.
+struct AttnPools {
+  rpa::Strides k_st, v_st;
+  const void* vc;
+};
+
+// Validates the tensor arguments of an attention call against the plan.
+rpa_status attention_args(const rpa_plan* plan, const void* q, const void* k_cache,
+                          const void* v_cache, const rpa_cache_strides* ks,
+                          const rpa_cache_strides* vs, const void* o, const float* lse,
+                          AttnPools* out) {
+  const rpa_attn_config& c = plan->cfg;
+  const bool latent = shared_latent(c);
+  std::string why;
+  if (!q || !k_cache || !o) return fail(RPA_ERR_INVALID_ARG, "null q, k_cache or o");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(o, 16))
+    return fail(RPA_ERR_INVALID_ARG, "q, k_cache and o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(RPA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (!strides_ok(ks, c.head_dim_qk, c.dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "k: " + why);
+  out->k_st = rpa::Strides{ks->page_stride, ks->head_stride, ks->token_stride};
+  out->v_st = out->k_st;
+  out->vc = v_cache;
+  if (latent) {
+    if (v_cache && v_cache != k_cache)
+      return fail(RPA_ERR_UNSUPPORTED, "576/512 needs the shared latent cache (v_cache == k_cache)");
+    if (vs && (vs->page_stride != ks->page_stride || vs->head_stride != ks->head_stride ||
+               vs->token_stride != ks->token_stride))
+      return fail(RPA_ERR_UNSUPPORTED, "576/512 needs vs == ks (shared latent cache)");
+    out->vc = k_cache;
+  } else {
+    if (!v_cache) return fail(RPA_ERR_INVALID_ARG, "null v_cache");
+    if (!aligned(v_cache, 16)) return fail(RPA_ERR_INVALID_ARG, "v_cache must be 16-byte aligned");
+    if (!strides_ok(vs, c.head_dim_v, c.dtype, &why)) return fail(RPA_ERR_INVALID_ARG, "v: " + why);
+    out->v_st = rpa::Strides{vs->page_stride, vs->head_stride, vs->token_stride};
+  }
+  return RPA_OK;
+}
+
+// Launches the attention kernels of every class the plan uses, then the merge
+// of split pieces, on one stream.
+rpa_status run_attention(const rpa::DevPlan& p, const void* q, const void* k_cache,
+                         const AttnPools& a, void* o, float* lse, hipStream_t st) {
+  hipError_t e;
+  if (p.n_items[rpa::KC_GENERIC] > 0) {
+    e = timed("generic", st, [&] {
+      return rpa::launch_generic(p, q, k_cache, a.vc, a.k_st, a.v_st, o, lse, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "generic attention launch");
+  }
+  if (p.n_items[rpa::KC_DECODE] > 0) {
+    e = timed("decode", st, [&] {
+      return rpa::launch_decode(p, q, k_cache, a.vc, a.k_st, a.v_st, o, lse, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+  }
+  if (p.n_items[rpa::KC_PREFILL] > 0) {
+    e = timed("prefill", st, [&] {
+      return rpa::launch_prefill(p, q, k_cache, a.vc, a.k_st, a.v_st, o, lse, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  }
+  if (p.n_items[rpa::KC_MLA] > 0) {
+    e = timed("mla", st, [&] { return rpa::launch_mla(p, q, k_cache, a.k_st, o, lse, st); });
+    if (e != hipSuccess) return hip_fail(e, "latent attention launch");
+  }
+  if (p.n_merge_rows > 0) {
+    e = timed("merge", st, [&] { return rpa::launch_merge_rows(p, o, lse, st); });
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return RPA_OK;
+}
+
+}  // namespace
+
 RPA_EXPORT rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q,
                                           const void* k_cache, const void* v_cache,
                                           const rpa_cache_strides* ks,
@@ -355,62 +432,44 @@ RPA_EXPORT rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q,
   return guarded([&] {
     rpa_status s = check_uploaded(plan);
     if (s != RPA_OK) return s;
-    const rpa_attn_config& c = plan->cfg;
-    const bool latent = shared_latent(c);
-    std::string why;
     if (plan->total_q == 0) return RPA_OK;  // no query rows: nothing to compute
-    if (!q || !k_cache || !o) return fail(RPA_ERR_INVALID_ARG, "null q, k_cache or o");
-    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(o, 16))
-      return fail(RPA_ERR_INVALID_ARG, "q, k_cache and o must be 16-byte aligned");
-    if (lse && !aligned(lse, 4)) return fail(RPA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    if (!strides_ok(ks, c.head_dim_qk, c.dtype, &why))
-      return fail(RPA_ERR_INVALID_ARG, "k: " + why);
-    rpa::Strides k_st{ks->page_stride, ks->head_stride, ks->token_stride};
-    rpa::Strides v_st = k_st;
-    const void* vc = v_cache;
-    if (latent) {
-      if (v_cache && v_cache != k_cache)
-        return fail(RPA_ERR_UNSUPPORTED,
-                    "576/512 needs the shared latent cache (v_cache == k_cache)");
-      if (vs && (vs->page_stride != ks->page_stride || vs->head_stride != ks->head_stride ||
-                 vs->token_stride != ks->token_stride))
-        return fail(RPA_ERR_UNSUPPORTED, "576/512 needs vs == ks (shared latent cache)");
-      vc = k_cache;
-    } else {
-      if (!v_cache) return fail(RPA_ERR_INVALID_ARG, "null v_cache");
-      if (!aligned(v_cache, 16))
-        return fail(RPA_ERR_INVALID_ARG, "v_cache must be 16-byte aligned");
-      if (!strides_ok(vs, c.head_dim_v, c.dtype, &why))
-        return fail(RPA_ERR_INVALID_ARG, "v: " + why);
-      v_st = rpa::Strides{vs->page_stride, vs->head_stride, vs->token_stride};
-    }
-    rpa::DevPlan p = dev_plan(plan);
+    AttnPools a;
+    s = attention_args(plan, q, k_cache, v_cache, ks, vs, o, lse, &a);
+    if (s != RPA_OK) return s;
+    return run_attention(dev_plan(plan, plan->d_ws), q, k_cache, a, o, lse,
+                         static_cast<hipStream_t>(stream));
+  });
+}
+
+RPA_EXPORT rpa_status rpa_batch_attention_noalloc(const rpa_plan* plan, const void* q,
+                                                  const void* k_cache, const void* v_cache,
+                                                  const rpa_cache_strides* ks,
+                                                  const rpa_cache_strides* vs, void* o,
+                                                  float* lse, void* stream) {
+  return guarded([&] {
+    if (!plan) return fail(RPA_ERR_INVALID_ARG, "null plan");
+    if (plan->total_q == 0) return RPA_OK;  // no query rows: nothing to compute
+    AttnPools a;
+    rpa_status s = attention_args(plan, q, k_cache, v_cache, ks, vs, o, lse, &a);
+    if (s != RPA_OK) return s;
+    if (plan->ws_bytes > rpa::kStaticScratchBytes)
+      return fail(RPA_ERR_WORKSPACE_TOO_SMALL,
+                  "the plan needs " + std::to_string(plan->ws_bytes) +
+                      " bytes of workspace; the static scratch holds " +
+                      std::to_string(rpa::kStaticScratchBytes) +
+                      " (use rpa_batch_attention with a workspace)");
+    void* ws = nullptr;
+    hipError_t e = rpa::static_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the static scratch");
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (p.n_items[rpa::KC_GENERIC] > 0) {
-      e = timed("generic", st,
-                [&] { return rpa::launch_generic(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
-      if (e != hipSuccess) return hip_fail(e, "generic attention launch");
-    }
-    if (p.n_items[rpa::KC_DECODE] > 0) {
-      e = timed("decode", st,
-                [&] { return rpa::launch_decode(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
-      if (e != hipSuccess) return hip_fail(e, "decode attention launch");
-    }
-    if (p.n_items[rpa::KC_PREFILL] > 0) {
-      e = timed("prefill", st,
-                [&] { return rpa::launch_prefill(p, q, k_cache, vc, k_st, v_st, o, lse, st); });
-      if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
-    }
-    if (p.n_items[rpa::KC_MLA] > 0) {
-      e = timed("mla", st, [&] { return rpa::launch_mla(p, q, k_cache, k_st, o, lse, st); });
-      if (e != hipSuccess) return hip_fail(e, "latent attention launch");
-    }
-    if (p.n_merge_rows > 0) {
-      e = timed("merge", st, [&] { return rpa::launch_merge_rows(p, o, lse, st); });
-      if (e != hipSuccess) return hip_fail(e, "merge launch");
-    }
-    return RPA_OK;
+    // The metadata goes from the plan's host copy into the scratch, ordered
+    // on the stream before the kernels that read it.  Nothing in the scratch
+    // needs to start at zero: every partial the merge reads is written by
+    // this call's attention kernels first.
+    e = hipMemcpyAsync(ws, plan->blob.data(), plan->blob.size() * sizeof(int32_t),
+                       hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync of the plan metadata");
+    return run_attention(dev_plan(plan, ws), q, k_cache, a, o, lse, st);
   });
 }
 

@@ -8,6 +8,13 @@
 
 namespace rpa {
 
+// Size of the static device scratch used by rpa_batch_attention_noalloc.
+constexpr size_t kStaticScratchBytes = RPA_STATIC_SCRATCH_BYTES;
+
+// Device address of this device's static scratch (looked up once per device,
+// with that device current).
+hipError_t static_scratch(void** out);
+
 hipError_t launch_append(const DevPlan& p, const void* k_new, const void* v_new, void* k_cache,
                          void* v_cache, Strides ks, Strides vs, hipStream_t stream);
 

@@ -519,3 +519,20 @@ def test_tree_mask_plan_validation(L):
     expect(rpa.RPA_ERR_UNSUPPORTED,
            lambda: rpa.rpa_plan_create_tree(cfg, [0, 65], [70], [0, 5], [0, 1, 2, 3, 4], 5,
                                             ti2, tw2))
+
+
+def test_noalloc_attention_rejects_plans_beyond_the_static_scratch(L):
+    """The allocation-free entry point checks the plan's workspace against the
+    static scratch (128 MiB) before any device work."""
+    cfg = rpa.make_config(8, 1, 128, 128, 16, "bf16")
+    n = 32768
+    plan = rpa.rpa_plan_create(cfg, [0, n], [n], [0, n // 16], np.arange(n // 16), n // 16)
+    assert rpa.rpa_plan_workspace_size(plan) > (128 << 20)
+    st = rpa.rpa_cache_strides(16 * 128, 16 * 128, 128)
+    fake = 1 << 40  # never dereferenced: the size check fails first
+    expect(rpa.RPA_ERR_WORKSPACE_TOO_SMALL, rpa.rpa_batch_attention_noalloc, plan, fake, fake,
+           fake, st, st, fake, None, 0)
+    assert "static scratch" in rpa.rpa_last_error_message()
+    # argument checks come first, as in rpa_batch_attention
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_batch_attention_noalloc, plan, None, fake, fake, st,
+           st, fake, None, 0)
