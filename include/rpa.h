@@ -102,7 +102,7 @@ typedef enum rpa_dtype {
  *           kv_len = 0 gets the empty state o = 0, lse = -inf, and a plan
  *           with any kv_len < qo_len cannot append (rpa_kv_append returns
  *           RPA_ERR_INVALID_ARG).
- *   sm_scale: multiplier of q.k (e.g. 1/sqrt(head_dim_qk)). */
+ *   sm_scale: multiplier of q.k (e.g. 1/sqrt(head_dim_qk)); finite and > 0. */
 typedef struct rpa_attn_config {
   int32_t num_qo_heads;
   int32_t num_kv_heads;

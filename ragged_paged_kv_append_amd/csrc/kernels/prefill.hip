@@ -6,38 +6,48 @@
 // rectangle) and causally to itself (a triangle), as in the chunked-prefill
 // post (sections "core-idea" and "correctness").
 //
-// One workgroup of eight wavefronts takes a work item: request r, KV head g,
-// up to 256 query rows (row = token * G + head-in-group, so the G query heads
-// sharing a KV head sit in one tile and share its K/V loads), keys [k0, k1).
-// Each wavefront owns 32 rows.  The planner packs the items onto one resident
-// workgroup per compute unit, longest first; a workgroup runs its list.
+// One workgroup of four wavefronts, one per SIMD, takes a work item: request
+// r, KV head g, up to 256 query rows (row = token * G + head-in-group, so the
+// G query heads sharing a KV head sit in one tile and share its K/V loads),
+// keys [k0, k1).  Each wavefront owns 64 rows, as two 32-row blocks, and the
+// whole register file of its SIMD: Q of its rows and the S^T accumulators in
+// VGPRs, the O^T accumulators in AGPRs.  The planner packs the items onto one
+// resident workgroup per compute unit, longest first; a workgroup runs its
+// list.
 //
 // K/V tiles of 64 keys (16 KiB each) move from HBM/L2 into a four-slot LDS
-// ring with the gfx950 global-to-LDS DMA, issued four tiles ahead of the step
-// that uses them.  The V tile is transposed once per workgroup into a V^T
-// buffer (rows = head dims, keys in the order the PV product consumes them),
-// so that the per-wave PV operands are plain 16-byte LDS reads: the
-// transposing LDS read is four times slower than a 16-byte read, and each
-// wave would otherwise transpose the whole tile for itself.  K rows keep
-// chunk c at c ^ (k % 16), V rows at c ^ 4 (k % 4), V^T rows at
-// c ^ ((d / 2) % 8): every LDS read pattern below is bank-conflict free.
+// ring with the gfx950 global-to-LDS DMA, two tiles ahead; each wave moves 16
+// key rows of every tile.  K rows keep 16-byte chunk c at c ^ (k % 16), V rows
+// at c ^ 4 (k % 4), so the K-operand reads and the transposing V reads are
+// bank-conflict free.
 //
-// Per wavefront, tile j goes through a matrix phase and a softmax phase:
-//   M(j): S^T_j[key][row] = K_j[key][:] . Q[row][:] and
-//         O^T[d][row] += V^T_{j-1}[d][key] . P^T_{j-1}[key][row]
-//         (mfma 32x32x16 bf16; K and V^T from LDS, Q resident in registers,
-//         the S^T accumulators laid out as the P^T operand);
-//   V(j): mask (only tiles that straddle a row's last visible key), row max,
-//         P_j = exp2(S_j * scale * log2 e - m) rounded to bf16, row sum of the
-//         rounded P.  The running max is raised only when a tile's max
-//         exceeds it by more than 8 (a factor of 256, log2 units), so the O
-//         rescale is almost never run.
-// The two wavefronts that share a SIMD (w and w + 4) belong to two groups
-// that run these phases half a step apart, one group's M beside the other
-// group's V, with a workgroup barrier between slots; each phase's inputs and
-// outputs are pinned to its slot so that the compiler cannot move work
-// across the barriers.  The page ids of a work item's tiles are loaded once
-// per item, one tile per lane.
+// The products run in steps of 32 keys.  Step h of a wavefront issues
+//   - the S^T products of step h + 1: S^T[key][row] = K[key][:] . Q[row][:]
+//     (mfma 32x32x16 bf16, 16 products, K from LDS, Q resident);
+//   - the PV products of step h - 1: O^T[d][row] += V^T[d][key] P^T[key][row]
+//     (16 products; V^T comes straight from the V rows through the
+//     transposing LDS read, P^T from registers: the S^T accumulator layout is
+//     the P^T operand layout);
+// and, between those products, the vector work of step h: P = exp2(S') rounded
+// to bf16, the row sums of P and a running max of S'.  The products of one
+// step do not depend on its vector work, so one wavefront keeps its SIMD's
+// matrix core busy while it runs the softmax in the gaps.
+//
+// The mask comes out of the matrix core with S: the first product of each
+// S^T chain accumulates onto a block that holds 0, or -1e30 for a masked
+// (key, row) pair (the causal diagonal, a tree mask, keys past the item).
+// The vector pipe, which sets the pace next to the matrix core, then spends
+// one fma (S' = S * scale * log2 e - m), one exp, half a conversion, one add
+// and half a max per score.  (Q is not scaled instead: rounding Q * scale to
+// bf16 moves large scores by whole units.)
+//
+// O is never rescaled.  P is taken against a fixed per-row reference m (0 on
+// the first pass): the scores only have to stay within 2^64 of it, above and
+// below, for P, the sums and O to stay well inside the float range without
+// losing precision.  A row whose largest S' leaves that window makes the
+// workgroup finish the item and do it over once, with the row's largest
+// scaled score as its reference.  This keeps O touched by the matrix cores
+// alone, so it stays in AGPRs.
 
 #include "common.h"
 #include "../launch.h"
@@ -47,18 +57,15 @@ namespace rpa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kKT = 64;                     // keys per tile
-constexpr int kTileBytes = kKT * kD * 2;    // 16 KiB
-constexpr int kSlotBytes = 2 * kTileBytes;  // K tile + V tile
-constexpr int kSlots = 4;                   // ring depth
-// Tiles in flight ahead of the one being computed.  Two cover the memory
-// latency; more outstanding DMA only makes each issue stall longer.
-constexpr int kLookahead = 2;
-constexpr int kWaves = 8;
-constexpr int kDmaRows = kKT / (kWaves / 2);  // key rows each DMA wave moves per tile (16)
-constexpr int kDmaInst = 2 * kDmaRows / 4;    // its DMA instructions per tile, K and V (8)
+constexpr int kWaves = 4;
+constexpr int kKT = 64;                     // keys per ring tile
+constexpr int kStep = 32;                   // keys per softmax step
+constexpr int kTileBytes = kKT * kD * 2;    // 16 KiB: the K (or V) rows of a tile
+constexpr int kSlotBytes = 2 * kTileBytes;  // K tile, then V tile
+constexpr int kSlots = 4;
+constexpr int kDmaInst = 2 * (kKT / kWaves) / 4;  // per wave and tile: 4 K + 4 V (8)
 constexpr float kMinusBig = -1.0e30f;
-constexpr float kRescaleSlack = 8.f;        // log2 units
+constexpr float kWindow = 64.f;             // log2 units around the reference
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
@@ -70,20 +77,22 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   return x;
 }
 
-// 16-byte LDS read at byte address a.
 __device__ __forceinline__ u32x4_t lds_ld16(uint32_t a) {
   return *reinterpret_cast<const lds_u32x4*>((uintptr_t)a);
 }
 
-// Workgroup barrier.  Cross-wave data are the DMA'd ring tiles (each wave
-// waits for its own part with vmcnt before the barrier) and the V^T writes
-// (covered here by the LDS count); no memory fence, which would make the
-// compiler drain the DMA in flight.
-// The scheduling barriers keep the compiler from moving register-only work
-// (exponentials, products) across it, which would undo the phase split below.
+// Transposing read of four 16-bit elements (see common.h).
+__device__ __forceinline__ u32x2_t lds_tr8(uint32_t a) {
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a));
+}
+
+// Workgroup barrier.  The data shared between waves are the DMA'd ring tiles
+// (each wave waits for its own part with vmcnt before the barrier).  The
+// scheduling barriers keep the compiler from moving work across it.
 __device__ __forceinline__ void barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -96,102 +105,182 @@ __device__ __forceinline__ void wait_vmem() {
 // lane copies 16 bytes from `src` to LDS byte address lds + 16 * lane.  It is
 // issued from inline assembly so that the compiler does not track it: left to
 // itself the compiler makes later LDS reads wait for all DMA in flight, while
-// the kernel waits for exactly the tile it needs (explicit vmcnt counts,
-// which operations the compiler adds can only make stricter).  M0, which
-// carries the LDS address, is saved and restored around the instruction; the
-// DMA reads M0 one wait state after the write that sets it.
+// the kernel waits for exactly the tiles it needs (explicit vmcnt counts).
+// M0, which carries the LDS address, is saved and restored around the
+// instruction; the DMA reads M0 one wait state after the write that sets it.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(lds)
       : "memory");
 }
 
-// Positions of 16-byte chunk c inside a K row (key k), a V row (key k) and a
-// V^T row (head dim d).
-__device__ __forceinline__ int k_pos(int c, int k) { return c ^ (k & 15); }
-__device__ __forceinline__ int v_pos(int c, int k) { return c ^ (4 * (k & 3)); }
-__device__ __forceinline__ int vt_pos(int c, int d) { return c ^ ((d >> 1) & 7); }
+// The same DMA with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// offset (the saddr form: no per-lane address arithmetic).  The base comes
+// from v_readfirstlane / v_readlane, and a memory instruction reads an SGPR
+// that a VALU instruction wrote only five wait states later: s_nop 4 first.
+__device__ __forceinline__ void dma16_base(const void* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+
+// A 64-bit pointer that is uniform across the wave, moved into SGPRs.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// The S^T products are issued from inline assembly so that their
+// accumulators stay in VGPRs, where the softmax reads them (the compiler
+// puts every matrix-core result of a kernel that uses AGPRs into AGPRs, and
+// the O^T accumulators fill them).  A chain of products on one accumulator
+// needs no wait states between its links.  The results are read by vector
+// instructions only one step later, after the 16 PV products of the step
+// that produced them.
+// Q, the B operand, stays in AGPRs (the matrix cores read either file).  The
+// first product of a chain starts from the block c (0, or -1e30 where
+// masked).
+__device__ __forceinline__ void mfma_s_first(f32x16_t& d, const u32x4_t& a, const u32x4_t& b,
+                                             const f32x16_t& c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+}
+__device__ __forceinline__ void mfma_s(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+
+// Operand reads from LDS, from inline assembly: the compiler neither waits
+// for them nor reuses their registers early; the kernel waits explicitly.
+// A K operand: one 16-byte read.
+__device__ __forceinline__ void ds_k(u32x4_t& d, uint32_t a) {
+  asm volatile("ds_read_b128 %0, %1" : "=v"(d) : "v"(a) : "memory");
+}
+// A V^T operand: two transposing reads, key rows r .. r + 3 and r + 8 .. r + 11.
+__device__ __forceinline__ void ds_vt(u32x4_t& d, uint32_t a) {
+  u32x2_t lo, hi;
+  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:2048"
+               : "=&v"(lo), "=&v"(hi)
+               : "v"(a)
+               : "memory");
+  d = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+template <int N>
+__device__ __forceinline__ void wait_lds() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait_lds with a count known after unrolling (n in 0..15).
+__device__ __forceinline__ void wait_lds_n(int n) {
+  switch (n) {
+    case 0: wait_lds<0>(); break;
+    case 1: wait_lds<1>(); break;
+    case 2: wait_lds<2>(); break;
+    case 3: wait_lds<3>(); break;
+    case 4: wait_lds<4>(); break;
+    case 5: wait_lds<5>(); break;
+    case 6: wait_lds<6>(); break;
+    case 7: wait_lds<7>(); break;
+    case 8: wait_lds<8>(); break;
+    case 9: wait_lds<9>(); break;
+    case 10: wait_lds<10>(); break;
+    case 11: wait_lds<11>(); break;
+    case 12: wait_lds<12>(); break;
+    case 13: wait_lds<13>(); break;
+    case 14: wait_lds<14>(); break;
+    default: wait_lds<15>(); break;
+  }
+}
+
+// LDS reads issued in slot s of a step (see the operand schedule below).
+constexpr int reads_in_slot(int s) {
+  return s == 0 ? 2 : (s % 2 != 0 ? 0 : (s <= 16 ? 1 : 2));
+}
+// Reads issued in the five slots before slot u (of this or the previous step).
+constexpr int reads_before(int u) {
+  int n = 0;
+  for (int d = 1; d <= 5; ++d) n += reads_in_slot(((u - d) % 32 + 32) % 32);
+  return n < 15 ? n : 15;
+}
+
+// The PV products, also from inline assembly (accumulators in AGPRs), so that
+// their order against the S^T products and the softmax is the program order.
+__device__ __forceinline__ void mfma_pv(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
 
 }  // namespace
 
-__global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q,
-                                                      const bf16_t* __restrict__ kc,
-                                                      const bf16_t* __restrict__ vc, Strides ks,
-                                                      Strides vs, bf16_t* __restrict__ o,
-                                                      float* __restrict__ lse) {
-  // ring[slot]: K tile, then V tile (rows of 128 bf16).  vt[b]: V^T of a tile,
-  // 128 rows (head dims) of 64 keys; in a row, 16-byte chunk 2 c + hh holds
-  // the keys 16 c + 4 hh + (0..3) and 16 c + 8 + 4 hh + (0..3).
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
+                    const bf16_t* __restrict__ vc, Strides ks, Strides vs,
+                    bf16_t* __restrict__ o, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots][kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char vt[2][kTileBytes];
+  __shared__ int32_t restart;  // set when a step moved a row's reference max
   const int tid = threadIdx.x;
   // The wave index is uniform within a wave; readfirstlane tells the compiler,
   // so everything derived from it stays in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int col = lane & 31;   // query row of this lane within the wave (S^T / O^T column)
+  const int col = lane & 31;   // row of this lane within a 32-row block
   const int half = lane >> 5;  // k-slot group of the 32x32x16 operands
   const uint32_t ring_lds =
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)ring;
-  const uint32_t vt_lds =
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)vt;
 
-  // ---- per-lane constants, shared by every item of this workgroup ----------
-  // Buffer bases are multiples of 1024, so the XORs below, which touch bits
-  // 4..7 only, commute with adding them.
-  // K operand of mfma i of a 32-key block: chunk 2 i + half of key row col,
-  // at k_rd ^ 32 i (+ 32 rows = + 8192 bytes for the second block).
-  const uint32_t k_rd = col * 256 + 16 * k_pos(half, col);
-  // V^T operand of 16-key chunk kc16 and 32-dim block nb: chunk 2 kc16 + half
-  // of V^T row 32 nb + col, at vt_rd ^ 32 kc16 (+ 4096 bytes per nb).
-  const uint32_t vt_rd = col * 128 + 16 * vt_pos(half, col);
-  // Transpose role: instruction i = 2 ih + il of wave w handles unit
-  // u = 16 w + 4 i + lane / 16, i.e. keys 4 (u / 8) .. + 3 and head dims
-  // 16 (u % 8) .. + 15.  Lane c + 4 e of a 16-lane group reads key row
-  // 4 (u / 8) + e, dims 16 (u % 8) + 4 c .. + 3; the transposing read hands
-  // lane l of the group V^T[16 (u % 8) + l][4 keys], written as 8 bytes of
-  // V^T row 16 (u % 8) + l.  The source of instruction i is
-  // (tr_src ^ 128 il) + 1024 ih, its destination (tr_dst ^ 16 ih) + 8192 il.
-  uint32_t tr_src, tr_dst;
-  {
-    const int u = 16 * wave + (lane >> 4);
-    const int kq = u >> 3, cb = u & 7;
-    const int l16 = lane & 15, c = l16 & 3, e = l16 >> 2;
-    const int R = 4 * kq + e;                       // key row read by this lane
-    tr_src = kTileBytes + R * 256 + 16 * v_pos(2 * cb + (c >> 1), R) + 8 * (c & 1);
-    const int dd = 16 * cb + l16;                   // V^T row written by this lane
-    const int kc16 = kq >> 2, q4 = kq & 3;          // 16-key chunk and 4-key group in it
-    tr_dst = dd * 128 + 16 * vt_pos(2 * kc16 + (q4 & 1), dd) + 8 * (q4 >> 1);
-  }
-  // DMA role (waves of the first group only, so that the DMA issue, which
-  // stalls the issuing wave while many transfers are outstanding, sits among
-  // that wave's matrix products): wave w < 4 moves key rows 16 w .. 16 w + 15
-  // of every tile (a run of keys inside one page for any page size >= 16);
-  // instruction i carries rows 16 w + 4 i + lane / 16 and lane % 16 is the
-  // 16-byte position in the row, which holds chunk (lane % 16) ^ perm.  Byte
-  // offsets from the first key of the wave's rows.
-  // The offsets are recomputed at each instruction (a few vector operations
-  // beside the matrix products) rather than held in registers.
-  const bool dma_wave = wave < kWaves / 2;
+  // ---- per-lane LDS offsets, shared by every item ------------------------------
+  // The ring base is a multiple of 1024, so the XORs below, which touch bits
+  // 5..7 only, commute with adding it.
+  // K operand of step i of a 32-key half: chunk 2 i + half of key row col, at
+  // k_rd ^ 32 i (+ 8192 for the second half of the tile).
+  const uint32_t k_rd = col * 256 + 16 * (half ^ (col & 15));
+  // V^T operand (d block nb, 16-key chunk kc) by two transposing reads: lane
+  // reads key row 4 half + (lane % 16) / 4 (+ 8 for the second read) and four
+  // dims 32 nb + 16 (col / 16) + 4 (lane % 4) .. + 3, which gives it
+  // V^T[d = 32 nb + col][keys 4 half + 0..3 (, 8 + 4 half + 0..3)].  With the
+  // V swizzle the dims sit at byte v_rd ^ 64 nb of the row (+ 4096 kc).
+  const int q4 = (lane & 15) >> 2;
+  const uint32_t v_rd = 256u * (4 * half + q4) + 64u * q4 + 32u * (col >> 4) + 8u * (lane & 3);
 
-  // Both V^T buffers start as zeros, so that the first PV product of an item
-  // (P = 0) never meets a non-finite value.
-#pragma unroll
-  for (int i = 0; i < 2 * kTileBytes / (16 * 64 * kWaves); ++i)
-    *reinterpret_cast<lds_u32x4*>((uintptr_t)(vt_lds + 16 * (tid + 64 * kWaves * i))) =
-        u32x4_t{0u, 0u, 0u, 0u};
+  // DMA lane offsets of a full tile (the fast path, for token strides that
+  // are multiples of 256 bytes): instruction i of this wave carries key rows
+  // 4 i + lane / 16 of its 16, lane % 16 being the swizzled 16-byte position.
+  // K row rr keeps chunk c at c ^ (rr % 16), so for instruction i the offset
+  // is dk_off ^ 64 i plus 4 i rows (a scalar add); V rows keep chunk c at
+  // c ^ 4 (rr % 4), the same for every instruction: dv_off plus 4 i rows.
+  const int l4 = lane >> 4, p16 = lane & 15;
+  const uint32_t ktok = 2u * (uint32_t)ks.token, vtok = 2u * (uint32_t)vs.token;
+  const bool dma_fast_ok = (ktok % 256u) == 0 && (vtok % 256u) == 0 &&
+                           (int64_t)ktok * 16 < (int64_t)1 << 31 &&
+                           (int64_t)vtok * 16 < (int64_t)1 << 31;
+  const uint32_t dk_off = (uint32_t)l4 * ktok + 16u * (uint32_t)(p16 ^ l4);
+  const uint32_t dv_off = (uint32_t)l4 * vtok + 16u * (uint32_t)(p16 ^ (4 * l4));
+
+  // Zero the ring once: the PV products of an item's first step multiply a
+  // zero P by whatever the slot of the tile before it holds, which must be
+  // finite.
+  for (int i = tid; i < kSlots * kSlotBytes / 16; i += 64 * kWaves)
+    *reinterpret_cast<lds_u32x4*>((uintptr_t)(ring_lds + 16 * i)) = u32x4_t{0u, 0u, 0u, 0u};
+  if (tid == 0) restart = 0;
 
   const int32_t wb0 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][blockIdx.x]);
   const int32_t wb1 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][blockIdx.x + 1]);
-  for (int32_t idx = wb0; idx < wb1; ++idx) {
-    // Item fields and request lengths are wave-uniform: readfirstlane keeps
-    // them, and the loop control derived from them, in scalar registers.
+  float m_keep[2] = {0.f, 0.f};  // references for an item done over
+  bool again = false;
+  for (int32_t idx = wb0; idx < wb1;) {
     auto uni = [](int32_t x) __attribute__((always_inline)) {
       return __builtin_amdgcn_readfirstlane(x);
     };
@@ -214,56 +303,64 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
       return min(k1, (causal ? cached + row / G : L - 1) + 1);
     };
 
-    const int32_t row = row0 + wave * 32 + col;
-    const bool row_ok = row < row1;
-    const int32_t t = row_ok ? row / G : 0;
-    const int32_t h = g * G + (row_ok ? row % G : 0);
-    const int32_t kend_row = row_ok ? key_end(row) : k0;
+    // This lane's rows: 64 wave + 32 rb + col of the item's tile.
+    bool row_ok[2];
+    int32_t t_of[2], h_of[2], kend_row[2];
+    uint32_t tm_lo[2], tm_hi[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int32_t row = row0 + 64 * wave + 32 * rb + col;
+      row_ok[rb] = row < row1;
+      t_of[rb] = row_ok[rb] ? row / G : 0;
+      h_of[rb] = g * G + (row_ok[rb] ? row % G : 0);
+      kend_row[rb] = row_ok[rb] ? key_end(row) : k0;
+      tm_lo[rb] = tm_hi[rb] = 0u;
+      if (tree && row_ok[rb]) {
+        tm_lo[rb] = p.tree_mask[2 * (int64_t)(q0 + t_of[rb])];
+        tm_hi[rb] = p.tree_mask[2 * (int64_t)(q0 + t_of[rb]) + 1];
+      }
+    }
     const int32_t kend = uni(key_end(row1 - 1));
-    const int32_t wrow0 = row0 + wave * 32;
-    const bool wave_has_rows = wrow0 < row1;
-    const int32_t kend_wmin = uni(wave_has_rows ? key_end(wrow0) : k0);
-    // Tiles from mask_from on need the element mask.
+    const int32_t wrow0 = row0 + 64 * wave;
+    const int32_t kend_wmin = uni(wrow0 < row1 ? key_end(wrow0) : k0);
+    // Steps that start at or past mask_from need the element mask.
     const int32_t mask_from = tree ? min(kend_wmin, max(cached, k0)) : kend_wmin;
-    const uint64_t tmask = (tree && row_ok)
-                               ? ((uint64_t)p.tree_mask[2 * (int64_t)(q0 + t) + 1] << 32) |
-                                     p.tree_mask[2 * (int64_t)(q0 + t)]
-                               : 0ull;
-    const int32_t ntiles = (kend - k0 + kKT - 1) / kKT;
+    const int32_t nsteps = (kend - k0 + kStep - 1) / kStep;
+    const int32_t ntiles = (nsteps + 1) / 2;
 
-    u32x4_t qf[8];  // Q operand, loaded once the first tiles are in flight
     const int32_t* pages = p.page_indices + p.page_indptr[r];
     const char* kbase = reinterpret_cast<const char*>(kc + (int64_t)g * ks.head);
     const char* vbase = reinterpret_cast<const char*>(vc + (int64_t)g * vs.head);
-    if (idx > wb0) wait_vmem<0>();  // the previous item's output stores
     // Page id of the first key row this wave moves for tile T, in lane T % 64
     // of pid[T / 64] (the planner keeps an item within 128 tiles).  Rows past
     // k1 are clamped onto the item's last key.
     int32_t pid[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int32_t gkey = min(k0 + (lane + 64 * c) * kKT + kDmaRows * wave, k1 - 1);
-      pid[c] = dma_wave && (c == 0 || ntiles > 64) ? pages[gkey >> p.page_shift] : 0;
+      const int32_t gkey = min(k0 + (lane + 64 * c) * kKT + 16 * wave, k1 - 1);
+      pid[c] = (c == 0 || ntiles > 64) ? pages[gkey >> p.page_shift] : 0;
     }
-    // DMA of tile T into ring slot `slot` by a wave of the first group: 4 K
-    // and 4 V instructions, x = 0..7.  Keys past k1 are fetched from the
-    // item's last key (a written slot of the same page), so masked keys hold
-    // finite values.
+    // DMA of tile T into ring slot T % 4: this wave's key rows 16 wave ..
+    // + 15, instruction x = 0..3 for K, 4..7 for V, each 4 rows of 256 bytes
+    // (lane / 16 is the row, lane % 16 the swizzled 16-byte position).  Keys
+    // past k1 are fetched from the item's last key (a written slot of the
+    // same page), so masked keys hold finite values.
     struct DmaTile {
       const char* kg;
       const char* vg;
-      uint32_t kl;
+      uint32_t lds;
       int32_t rmax;  // rows past the first that exist
     };
-    auto dma_setup = [&](int32_t T, int slot) __attribute__((always_inline)) {
-      const int32_t gkey = min(k0 + T * kKT + kDmaRows * wave, k1 - 1);  // first key of this wave's rows
+    auto dma_setup = [&](int32_t T) __attribute__((always_inline)) {
+      const int32_t gkey = min(k0 + T * kKT + 16 * wave, k1 - 1);
       const int64_t page = T < 64 ? __builtin_amdgcn_readlane(pid[0], T)
                                   : __builtin_amdgcn_readlane(pid[1], T - 64);
       const int64_t in_page = gkey & (p.page_size - 1);
       DmaTile d;
       d.kg = kbase + 2 * (page * ks.page + in_page * ks.token);
       d.vg = vbase + 2 * (page * vs.page + in_page * vs.token);
-      d.kl = __builtin_amdgcn_readfirstlane(ring_lds + slot * kSlotBytes + kDmaRows * wave * 256);
+      d.lds = __builtin_amdgcn_readfirstlane(ring_lds + (T & (kSlots - 1)) * kSlotBytes +
+                                             16 * wave * 256);
       d.rmax = k1 - 1 - gkey;
       return d;
     };
@@ -271,313 +368,394 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(DevPlan p, const bf16_t
       const int i = x & 3;
       const bool v = x >= 4;
       const int ln = (int)opaque((uint32_t)lane);
-      const int rr = 4 * i + (ln >> 4);  // row within the wave's 16 rows (= its index mod 16)
+      const int rr = 4 * i + (ln >> 4);  // row within the wave's 16 (= its key mod 16)
       const int row = min(rr, d.rmax);   // rows past the last key repeat it
-      const uint32_t off =
-          v ? 2u * (uint32_t)(row * vs.token + 8 * v_pos(ln & 15, rr))
-            : 2u * (uint32_t)(row * ks.token + 8 * k_pos(ln & 15, rr));
-      dma16((v ? d.vg : d.kg) + off, d.kl + (v ? kTileBytes : 0) + 1024 * i);
-    };
-    auto issue = [&](int32_t T, int slot) __attribute__((always_inline)) {
-      const DmaTile d = dma_setup(T, slot);
-#pragma unroll
-      for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
-    };
-
-    // Transpose of the V tile in ring slot `slot` into vt[buf]: this wave's
-    // four transposing reads, then its four writes.
-    auto transpose_read = [&](int slot, s16x4_t (&v)[4]) __attribute__((always_inline)) {
-      const uint32_t src = opaque(ring_lds + slot * kSlotBytes + tr_src);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        v[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(uintptr_t)((src ^ (128u * (i & 1))) + 1024u * (i >> 1)));
-    };
-    auto transpose_write = [&](int buf, const s16x4_t (&v)[4]) __attribute__((always_inline)) {
-      const uint32_t dst = opaque(vt_lds + buf * kTileBytes + tr_dst);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(
-            (uintptr_t)((dst ^ (16u * (i >> 1))) + 8192u * (i & 1))) = v[i];
-    };
-    auto transpose = [&](int slot, int buf) __attribute__((always_inline)) {
-      s16x4_t v[4];
-      transpose_read(slot, v);
-      transpose_write(buf, v);
-    };
-
-    // Waits until this wave's part of tile `tile` has landed, when tiles up
-    // to `last` have been issued: each wave issues kDmaInst instructions per
-    // tile, in tile order.
-    auto wait_tile = [&](int32_t tile, int32_t last) __attribute__((always_inline)) {
-      const int32_t later = last - tile;  // tiles issued after it
-      if (later >= 3) wait_vmem<3 * kDmaInst>();
-      else if (later == 2) wait_vmem<2 * kDmaInst>();
-      else if (later == 1) wait_vmem<kDmaInst>();
-      else wait_vmem<0>();
+      const int chunk = v ? ((ln & 15) ^ (4 * (rr & 3))) : ((ln & 15) ^ (rr & 15));
+      const uint32_t off = v ? 2u * (uint32_t)(row * vs.token + 8 * chunk)
+                             : 2u * (uint32_t)(row * ks.token + 8 * chunk);
+      dma16((v ? d.vg : d.kg) + off, d.lds + (v ? kTileBytes : 0) + 1024 * i);
     };
 
     const float sc = p.sm_scale * kLog2e;
-    float m = kMinusBig;  // running reference max of this row, log2 units
-    float lsum = 0.f;     // this lane's share of the running row sum
-    f32x16_t oacc[4];     // O^T: element 4 b + j of block nb is head dim 32 nb + 8 b + 4 half + j
+    // The reference of each row (first pass 0).
+    float m[2] = {again ? m_keep[0] : 0.f, again ? m_keep[1] : 0.f};
+    float lsum[2] = {0.f, 0.f};           // this lane's share of each row's sum
+    float rmax[2] = {kMinusBig, kMinusBig};  // this lane's largest S' of each row
+    f32x16_t oacc[4][2];  // [nb][rb]: element i is O^T[32 nb + 8 (i/4) + 4 half + i%4][row]
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[nb][i] = 0.f;
-    f32x16_t sacc[2];  // S^T of the current tile, two 32-key blocks
-    u32x4_t pb[4];     // P^T of the previous tile, bf16 pairs, one 16-key chunk each
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) pb[c] = u32x4_t{0u, 0u, 0u, 0u};
-
-    // K operand i of block b2 of the tile in ring slot `slot`.
-    auto kld = [&](uint32_t kt, int i, int b2) __attribute__((always_inline)) {
-      return lds_ld16((kt ^ (32u * i)) + 8192u * b2);
-    };
-    // V^T operand of 16-key chunk kc16 and 32-dim block nb.
-    auto vld = [&](uint32_t vtb, int kc16, int nb) __attribute__((always_inline)) {
-      return lds_ld16((vtb ^ (32u * kc16)) + 4096u * nb);
-    };
-
-    // Matrix phase M(j): S^T_j = K_j Q^T into sacc, and
-    // O^T += V^T_{j-1} P^T_{j-1}.  The products of the two contractions
-    // alternate, with their LDS operands read one step ahead.  At j = 0, P is
-    // zero (and V^T finite); at j = ntiles, the S product reads a stale ring
-    // slot and its result is not used.
-    // With refill, this (first-group) wave's DMA of tile j + kLookahead into
-    // its ring slot goes between the products, one instruction per step.
-    auto mphase = [&](int32_t j, bool refill) __attribute__((always_inline)) {
-      DmaTile rd{};
-      if (refill) rd = dma_setup(j + kLookahead, (j + kLookahead) & (kSlots - 1));
-      const uint32_t kt = opaque(ring_lds + (j & (kSlots - 1)) * kSlotBytes + k_rd);
-      const uint32_t vtb = opaque(vt_lds + ((j - 1) & 1) * kTileBytes + vt_rd);
+        for (int i = 0; i < 16; ++i) oacc[nb][rb][i] = 0.f;
+    // S^T of two steps (by parity), -1e30 where masked: element i of [par][rb] is key
+    // kb + 8 (i/4) + 4 half + i%4 of row 32 rb + col.
+    f32x16_t sacc[2][2];
+    // P^T of two steps (by parity), bf16 pairs: [par][rb][kc] holds the keys
+    // 16 kc + 8 (e/4) + 4 half + e%4, e = 0..7, of the step.
+    u32x4_t pb[2][2][2];
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[b2][i] = 0.f;
-      // step i: S products i of both blocks, PV products (kc16 = i / 2,
-      // nb = 2 (i % 2) + 0, 1).  The operands of step i are read two steps
-      // ahead; the scheduling barrier at the end of each step keeps the
-      // compiler from sinking the reads next to their products.
-      constexpr int kAhead = 2;
-      u32x4_t ka[kAhead + 1][2], va[kAhead + 1][2];
-      auto fetch = [&](int i) __attribute__((always_inline)) {
-        const int b = i % (kAhead + 1);
-        ka[b][0] = kld(kt, i, 0);
-        ka[b][1] = kld(kt, i, 1);
-        va[b][0] = vld(vtb, i >> 1, 2 * (i & 1));
-        va[b][1] = vld(vtb, i >> 1, 2 * (i & 1) + 1);
-      };
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int i = 0; i < kAhead; ++i) fetch(i);
+        for (int c = 0; c < 2; ++c) pb[a][b][c] = u32x4_t{0u, 0u, 0u, 0u};
+    // Start blocks of the S^T chains: 0, or -1e30 where the key is masked
+    // for the row (set before the products of a step that needs the mask,
+    // put back to 0 after it).
+    f32x16_t cinit[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int b = i % (kAhead + 1), c = i & 1;
-        if (i + kAhead < 8) fetch(i + kAhead);
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[b][0]), as_bf16x8(qf[i]),
-                                                          sacc[0], 0, 0, 0);
-        oacc[2 * c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(va[b][0]), as_bf16x8(pb[i >> 1]), oacc[2 * c], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[b][1]), as_bf16x8(qf[i]),
-                                                          sacc[1], 0, 0, 0);
-        oacc[2 * c + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(va[b][1]), as_bf16x8(pb[i >> 1]), oacc[2 * c + 1], 0, 0, 0);
-        if (refill) dma_x(rd, i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-
-    // Softmax phase V(j): mask (tiles that straddle a row's last visible key),
-    // row max, lazy rescale, P^T_j = exp2(S^T_j * scale * log2 e - m) as bf16
-    // pairs, and the row sum of the rounded P.
-    // Element i of S^T block b2 of the tile at kb is key
-    // kb + 32 b2 + 8 (i / 4) + 4 half + i % 4 of row `col`.
-    auto vphase = [&](int32_t j) __attribute__((always_inline)) {
-      // S enters here and P leaves at the end through empty asm statements:
-      // the phase's arithmetic stays between the barriers that delimit it.
-      asm volatile("" : "+v"(sacc[0]), "+v"(sacc[1]));
-      const int32_t kb = k0 + j * kKT;
-      if (kb + kKT > mask_from) {
-        // Two uniform branches, each one compare and one select per element
-        // (plus the bit test for trees), with no per-element control flow.
-        const int32_t lim = kend_row - kb - 4 * half;
-        if (!tree) {
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-          for (int b2 = 0; b2 < 2; ++b2)
+      for (int i = 0; i < 16; ++i) cinit[rb][i] = 0.f;
+    // Mask of the step whose keys start at kb, into cinit.
+    auto set_mask = [&](int32_t kb) __attribute__((always_inline)) {
+      if (!tree) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int idx = 32 * b2 + 8 * (i >> 2) + (i & 3);
-              sacc[b2][i] = idx < lim ? sacc[b2][i] : kMinusBig;
-            }
-        } else {
-          const int32_t rel = kb + 4 * half - cached;  // new-token index of element offset 0
-          const uint32_t tlo = (uint32_t)tmask, thi = (uint32_t)(tmask >> 32);
+        for (int rb = 0; rb < 2; ++rb) {
+          const int32_t lim = kend_row[rb] - kb - 4 * half;
 #pragma unroll
-          for (int b2 = 0; b2 < 2; ++b2)
+          for (int i = 0; i < 16; ++i) {
+            const int e = 8 * (i >> 2) + (i & 3);
+            cinit[rb][i] = e < lim ? 0.f : kMinusBig;
+          }
+        }
+      } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int idx = 32 * b2 + 8 * (i >> 2) + (i & 3);
-              const int32_t bi = rel + idx;  // < 0: a cached key, always visible
-              const uint32_t word = bi >= 32 ? thi : tlo;
-              const bool in_tree = bi < 0 || ((word >> (bi & 31)) & 1u) != 0;
-              sacc[b2][i] = (idx < lim) & in_tree ? sacc[b2][i] : kMinusBig;
-            }
+        for (int rb = 0; rb < 2; ++rb) {
+          const int32_t lim = kend_row[rb] - kb - 4 * half;
+          const int32_t rel = kb + 4 * half - cached;  // new-token index of offset 0
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int e = 8 * (i >> 2) + (i & 3);
+            const int32_t bi = rel + e;  // < 0: a cached key, always visible
+            const uint32_t word = bi >= 32 ? tm_hi[rb] : tm_lo[rb];
+            // bitwise, not short-circuit: no per-element branch
+            const bool vis = (e < lim) & ((bi < 0) | (((word >> (bi & 31)) & 1u) != 0));
+            cinit[rb][i] = vis ? 0.f : kMinusBig;
+          }
         }
       }
-      // Row max as a tree (independent operations for the scheduler).
-      float mx8[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        mx8[k] = fmaxf(fmaxf(sacc[k >> 2][4 * (k & 3)], sacc[k >> 2][4 * (k & 3) + 1]),
-                       fmaxf(sacc[k >> 2][4 * (k & 3) + 2], sacc[k >> 2][4 * (k & 3) + 3]));
-      float mx = fmaxf(fmaxf(fmaxf(mx8[0], mx8[1]), fmaxf(mx8[2], mx8[3])),
-                       fmaxf(fmaxf(mx8[4], mx8[5]), fmaxf(mx8[6], mx8[7])));
-      mx = max_halves(mx);
-      // The reference max is raised only when this tile's max exceeds it by
-      // more than kRescaleSlack; O and the row sum are rescaled then.
-      const float mt = mx > 0.5f * kMinusBig ? mx * sc : kMinusBig;
-      const bool raise = mt > m + kRescaleSlack;
-      if (__ballot(raise)) {
-        const float m_new = raise ? mt : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        lsum *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) oacc[nb] *= alpha;
-        m = m_new;
-      }
-      // A row with no visible key so far has m = kMinusBig; its masked
-      // entries (kMinusBig) then still map to exp2 = 0.
-      const float neg_m = m > 0.5f * kMinusBig ? -m : 0.f;
-      // P in place of S, each stage over all 32 entries so that the
-      // exponentials do not wait on one another's inputs.
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[b2][i] = __builtin_fmaf(sacc[b2][i], sc, neg_m);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[b2][i] = __builtin_amdgcn_exp2f(sacc[b2][i]);
-      __builtin_amdgcn_sched_barrier(0);
-      // word w = k-slot pair e = w % 4 of 16-key chunk kc16 = w / 4; the row
-      // sum is taken over the fp32 P, in four partial sums, with plain adds:
-      // v_dot2 would serialise against the other wave's matrix products on
-      // this SIMD, the adds overlap them.
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        const int kc16 = w >> 2, e = w & 3, b2 = kc16 >> 1, hb = kc16 & 1;
-        const float x0 = sacc[b2][8 * hb + 2 * e], x1 = sacc[b2][8 * hb + 2 * e + 1];
-        pb[kc16][e] = pack_bf16x2(x0, x1);
-        ps[e] += x0 + x1;
-      }
-      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(lsum));
     };
-
-    // This wave's eighth of the V transpose of tile j (ring slot j % kSlots
-    // into vt[j % 2]).
-    auto transpose_part = [&](int32_t j) __attribute__((always_inline)) {
-      transpose(j & (kSlots - 1), j & 1);
-    };
-
-    // The page ids are complete before the first DMA is issued (the DMA
-    // addresses need them); the empty asm statement marks them as such.
-    asm volatile("" : "+v"(pid[0]), "+v"(pid[1]));
-    barrier();  // the previous item's waves are done with the ring and vt
-    if (dma_wave) {
+    auto clear_mask = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < kLookahead; ++j)
-        if (j < ntiles) issue(j, j);
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cinit[rb][i] = 0.f;
+    };
+    // Steps whose keys start at or past this need the mask.
+    const int32_t mask_kb = mask_from - kStep + 1;
+
+    asm volatile("" : "+v"(pid[0]), "+v"(pid[1]));  // page ids complete before the DMA
+    barrier();  // the previous item's waves are done with the ring
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      if (T < ntiles) {
+        const DmaTile d = dma_setup(T);
+#pragma unroll
+        for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
+      }
     }
-
-    // Q operand of the S^T products: qf[i] = Q[row][16 i + 8 half .. + 8),
-    // loaded while the first tiles are in flight.  The empty asm statement
-    // makes the compiler complete these loads here (its wait also covers the
-    // first tiles, whose latency the Q loads now share); a load still pending
-    // in its view would make it wait for every untracked DMA in flight at
-    // the first use inside the loop.
-    {
-      const bf16_t* qrow = q + ((int64_t)(q0 + t) * p.num_qo_heads + h) * kD + 8 * half;
+    // Q operand of the S^T products: qf[rb][i] = Q[row 32 rb + col][16 i + 8 half .. + 8).
+    u32x4_t qf[2][8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const bf16_t* qrow =
+          q + ((int64_t)(q0 + t_of[rb]) * p.num_qo_heads + h_of[rb]) * kD + 8 * half;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        qf[i] = row_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * i) : u32x4_t{0u, 0u, 0u, 0u};
-      asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]),
-                   "+v"(qf[5]), "+v"(qf[6]), "+v"(qf[7]));
+        qf[rb][i] = row_ok[rb] ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * i)
+                               : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    // Q, the tree-mask rows, the first two tiles and the previous item's
+    // output stores complete.  The empty asm statements mark the loads as
+    // complete, so that the compiler adds no wait of its own inside the loop
+    // (its count would not know about the DMA and would drain it).
+    wait_vmem<0>();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+a"(qf[rb][i]));
+      asm volatile("" : "+v"(tm_lo[rb]), "+v"(tm_hi[rb]));
+    }
+    if (k0 >= mask_kb) set_mask(k0);
+    // Vector writes of cinit, then a product reads it: wait states.
+    asm volatile("s_nop 4" : "+v"(cinit[0]), "+v"(cinit[1]));
+    barrier();  // tiles 0 and 1 are in the ring
+
+    // K operands of step h (ring slot of tile h / 2, its half h % 2), three
+    // steps ahead of the products that use them.
+    auto kaddr = [&](int32_t h) __attribute__((always_inline)) {
+      return opaque(ring_lds + ((h >> 1) & (kSlots - 1)) * kSlotBytes + 8192u * (h & 1) + k_rd);
+    };
+    auto vaddr = [&](int32_t h) __attribute__((always_inline)) {
+      return opaque(ring_lds + ((h >> 1) & (kSlots - 1)) * kSlotBytes + kTileBytes +
+                    8192u * (h & 1) + v_rd);
+    };
+    // ---- operand rings -----------------------------------------------------------
+    // Step u uses K operand i (of step u + 1) in slots 2 i, 2 i + 1, from
+    // kr[i % 4], and V^T operand j = 4 kc + nb (of step u - 1) in slots
+    // 16 + 2 j, 17 + 2 j, from vr[j % 4].  Reads, each issued after its slot's
+    // product: slot 0 V^T (u - 1, 3); slots 2..8 K (u + 1, 4..7); slots 10..16
+    // K (u + 2, 0..3); slots 18..24 V^T (u - 1, 4..7); slots 26..30 V^T
+    // (u, 0..2).  Every operand is read at least six slots before its first
+    // product; no ring register is overwritten before a product after its
+    // last reader has issued (a product reads its sources during its
+    // passes).  LDS reads complete in order, so before a product the wave
+    // waits until no more are outstanding than were issued in the five slots
+    // before it.
+    u32x4_t kr[4], vr[4];
+    // Step -1: the S^T products of step 0 alone (K of tile 0, first half).
+    {
+      const uint32_t ka = kaddr(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ds_k(kr[i], ka ^ (32u * i));
+      wait_lds<0>();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i == 4 || i == 5) wait_lds<2>();
+        if (i == 6) wait_lds<1>();
+        if (i == 7) wait_lds<0>();
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          if (i == 0) mfma_s_first(sacc[0][rb], kr[0], qf[rb][0], cinit[rb]);
+          else mfma_s(sacc[0][rb], kr[i % 4], qf[rb][i]);
+        }
+        // operand i + 3 into the register of operand i - 1 (one pair ago)
+        if (i >= 1 && i + 3 < 8) ds_k(kr[(i + 3) % 4], ka ^ (32u * (i + 3)));
+      }
+      // The softmax of step 0 reads these accumulators next: wait states for
+      // the products' latency (the compiler adds none after inline assembly);
+      // they also let the last product read its operand before kr is reused.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc[0][0]), "+v"(sacc[0][1]));
+      // K operands 0..3 of step 1 (tile 0, second half) for the first step;
+      // the V^T operands of step -1 only meet P = 0, so zeros do.
+      const uint32_t kn = kaddr(1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ds_k(kr[i], kn ^ (32u * i));
+        vr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      wait_lds<0>();
     }
 
-    // Two groups of four wavefronts (one of each per SIMD) run the phases
-    // M(0) V(0) M(1) V(1) ... M(ntiles) half a step apart, so that one
-    // group's products overlap the other group's softmax.  Slot 2 j: group 0
-    // runs M(j), group 1 runs V(j - 1); slot 2 j + 1: group 0 runs V(j),
-    // group 1 runs M(j).  Each slot begins with a workgroup barrier.
-    //   K_j and V^T_{j-1} are read in slots 2 j and 2 j + 1;
-    //   V_j is transposed into vt[j % 2] in slots 2 j (group 1) and 2 j + 1
-    //   (group 0), each wave its eighth, in the slot of its softmax phase;
-    //   tile j + kLookahead is loaded into ring slot (j + kLookahead) % kSlots
-    //   in slot 2 j (the tile that slot held was last read in slot 2 j - 3).
-    // Waits for tile j before slot 2 j: tiles up to j + kLookahead - 1 have
-    // been issued by then.  Only the first group issues DMA; the second sees
-    // each tile through the barrier that follows the first group's wait.
-    auto wait_for = [&](int32_t j) __attribute__((always_inline)) {
-      if (j < ntiles) wait_tile(j, min(j + kLookahead - 1, ntiles - 1));
-    };
-    // In slot 2 j the first group loads tile j + kLookahead (inside its
-    // matrix phase).
-    auto refill_due = [&](int32_t j) __attribute__((always_inline)) {
-      return j + kLookahead < ntiles;
-    };
-    if (wave < kWaves / 2) {
-      for (int32_t j = 0; j <= ntiles; ++j) {
-        wait_for(j);
-        barrier();  // slot 2 j
-        mphase(j, refill_due(j));
-        barrier();  // slot 2 j + 1
-        if (j < ntiles) {
-          vphase(j);
-          transpose_part(j);
+    // Main loop: tile T holds steps 2 T (parity 0) and 2 T + 1 (parity 1).
+    // Step h issues the S^T products of step h + 1 in its slots 0..15 and the
+    // PV products of step h - 1 in slots 16..31, with the softmax of step h
+    // spread over the slots.  In the parity-0 step of tile T, after slot 9,
+    // the wave waits for its DMA of tile T + 1 and all waves meet at a
+    // barrier: tile T + 1 is then in the ring (its K rows are read from slot
+    // 10 on), and every wave is past step 2 T - 1, so the slot of tile T - 2
+    // (whose last V^T reads were in step 2 T - 2) is free for tile T + 2,
+    // which is loaded after the barrier, half in each step.  A step past the
+    // last one only computes unused products from finite ring contents.
+    bool masked = k0 >= mask_kb;  // cinit holds the mask of the step being computed
+    for (int32_t T = 0; T < ntiles; ++T) {
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int32_t h = 2 * T + par;
+        const uint32_t ka_next = kaddr(h + 1);   // K of step h + 1
+        const uint32_t ka_next2 = kaddr(h + 2);  // K of step h + 2
+        const uint32_t va_prev = vaddr(h - 1);   // V of step h - 1
+        const uint32_t va_cur = vaddr(h);        // V of step h
+        f32x16_t(&sc_in)[2] = sacc[par];        // S^T of step h
+        f32x16_t(&sc_out)[2] = sacc[par ^ 1];   // S^T of step h + 1
+        u32x4_t(&p_out)[2][2] = pb[par];        // P^T of step h
+        u32x4_t(&p_in)[2][2] = pb[par ^ 1];     // P^T of step h - 1
+        const bool dma_due = T + 2 < ntiles;
+        DmaTile dd{};
+        // The start blocks of step h + 1: uniform branches, taken only near
+        // the diagonal and past the item's keys.
+        {
+          const int32_t kb1 = k0 + kStep * (h + 1);
+          if (kb1 >= mask_kb) {
+            set_mask(kb1);
+            masked = true;
+          } else if (masked) {
+            clear_mask();
+            masked = false;
+          }
+          // Vector writes of cinit, then a product reads it: wait states.
+          asm volatile("s_nop 4" : "+v"(cinit[0]), "+v"(cinit[1]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        float ps[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // Each slot: one matrix product, then a share of the softmax, the
+        // operand reads and the DMA.  The empty asm statements at the end of a
+        // slot pin what the slot computed: without them the compiler sinks the
+        // pure arithmetic to its first use, all of it behind the products.
+#pragma unroll
+        for (int sl = 0; sl < 32; ++sl) {
+          // ---- matrix product of this slot -------------------------------------
+          wait_lds_n(reads_before(sl));
+          if (sl < 16) {
+            const int i = sl >> 1, rb = sl & 1;
+            if (i == 0) mfma_s_first(sc_out[rb], kr[0], qf[rb][0], cinit[rb]);
+            else mfma_s(sc_out[rb], kr[i % 4], qf[rb][i]);
+          } else {
+            const int j = (sl - 16) >> 1, rb = (sl - 16) & 1;  // operand j = 4 kc + nb
+            mfma_pv(oacc[j & 3][rb], vr[j % 4], p_in[rb][j >> 2]);
+          }
+          // ---- operand reads of this slot --------------------------------------
+          if (sl == 0) {
+            ds_vt(vr[3], va_prev ^ (64u * 3));  // V^T (h - 1, 3): kc 0, nb 3
+          } else if (sl >= 2 && sl <= 8 && (sl & 1) == 0) {
+            const int i = sl / 2 + 3;  // K (h + 1, 4..7)
+            ds_k(kr[i % 4], ka_next ^ (32u * i));
+          } else if (sl >= 10 && sl <= 16 && (sl & 1) == 0) {
+            const int i = (sl - 10) / 2;  // K (h + 2, 0..3)
+            ds_k(kr[i], ka_next2 ^ (32u * i));
+          } else if (sl >= 18 && sl <= 24 && (sl & 1) == 0) {
+            const int j = (sl - 18) / 2 + 4;  // V^T (h - 1, 4..7): kc 1
+            ds_vt(vr[j % 4], (va_prev ^ (64u * (j & 3))) + 4096u);
+          } else if (sl >= 26 && (sl & 1) == 0) {
+            const int j = (sl - 26) / 2;  // V^T (h, 0..2): kc 0
+            ds_vt(vr[j], va_cur ^ (64u * j));
+          }
+          // ---- softmax of step h -----------------------------------------------
+          if (sl < 16) {
+            // S' = S * scale * log2 e - m, its running max and P = exp2(S'),
+            // two scores per slot (what the vector pipe can do in the 32
+            // cycles of one product)
+            const int e0 = 2 * sl, rb = e0 >> 4, i0 = e0 & 15;
+            const float x0 = __builtin_fmaf(sc_in[rb][i0], sc, -m[rb]);
+            const float x1 = __builtin_fmaf(sc_in[rb][i0 + 1], sc, -m[rb]);
+            rmax[rb] = fmaxf(rmax[rb], fmaxf(x0, x1));
+            sc_in[rb][i0] = __builtin_amdgcn_exp2f(x0);
+            sc_in[rb][i0 + 1] = __builtin_amdgcn_exp2f(x1);
+            asm volatile("" : "+v"(sc_in[0]), "+v"(sc_in[1]), "+v"(rmax[0]), "+v"(rmax[1]));
+          } else if (sl < 24) {
+            // bf16 pairs of P and the row sums (of the fp32 P, with plain adds:
+            // v_dot2 would hold up the matrix core)
+            const int w0 = 2 * (sl - 16);  // word index 0..15 over [rb][kc][e]
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int w = w0 + u, rb = w >> 3, kcc = (w >> 2) & 1, e = w & 3;
+              const float x0 = sc_in[rb][8 * kcc + 2 * e], x1 = sc_in[rb][8 * kcc + 2 * e + 1];
+              p_out[rb][kcc][e] = pack_bf16x2(x0, x1);
+              ps[rb][e] += x0 + x1;
+            }
+            asm volatile("" : "+v"(p_out[0][0]), "+v"(p_out[0][1]), "+v"(p_out[1][0]),
+                         "+v"(p_out[1][1]));
+            asm volatile("" : "+v"(ps[0][0]), "+v"(ps[0][1]), "+v"(ps[0][2]), "+v"(ps[0][3]),
+                         "+v"(ps[1][0]), "+v"(ps[1][1]), "+v"(ps[1][2]), "+v"(ps[1][3]));
+          } else if (sl == 24) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              lsum[rb] += (ps[rb][0] + ps[rb][1]) + (ps[rb][2] + ps[rb][3]);
+            asm volatile("" : "+v"(lsum[0]), "+v"(lsum[1]));
+          }
+          // ---- DMA of tile T + 2: slots 22, 25, 28, 31 of both steps -------------
+          if (sl >= 22 && (sl - 22) % 3 == 0 && dma_due) {
+            const int x = 4 * par + (sl - 22) / 3;
+            if (x == 0 || x == 4) dd = dma_setup(T + 2);
+            const bool fast = dma_fast_ok && k0 + (T + 3) * kKT <= k1;  // a full tile
+            if (fast) {
+              const int i = x & 3;
+              const char* b = x >= 4 ? dd.vg + 4 * i * vtok : dd.kg + 4 * i * ktok;
+              const uint32_t off = x >= 4 ? dv_off : (dk_off ^ (64u * i));
+              dma16_base(uniform_ptr(b), opaque(off),
+                         dd.lds + (x >= 4 ? kTileBytes : 0) + 1024 * i);
+            } else {
+              dma_x(dd, x);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (sl == 9 && par == 0) {
+            // Tile T + 1 (this wave's DMA, then everyone's) is in the ring, and
+            // every wave is past step 2 T - 1: the slot of tile T - 2 is free.
+            wait_vmem<0>();
+            barrier();
+          }
+        }
+        asm volatile("" : "+v"(p_out[0][0]), "+v"(p_out[0][1]), "+v"(p_out[1][0]),
+                     "+v"(p_out[1][1]), "+v"(lsum[0]), "+v"(lsum[1]));
+        if (par == 0 && h + 1 >= nsteps) break;
+      }
+    }
+    // The PV products of the last step: V^T operands 0..2 were read by it,
+    // the others are read here.
+    {
+      const int32_t hl = nsteps - 1;
+      const uint32_t va_last = vaddr(hl);
+      u32x4_t ve[5];
+#pragma unroll
+      for (int j = 3; j < 8; ++j) ds_vt(ve[j - 3], (va_last ^ (64u * (j & 3))) + 4096u * (j >> 2));
+      wait_lds<0>();
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        if ((hl & 1) != par) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x4_t va = j < 3 ? vr[j] : ve[j - 3];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) mfma_pv(oacc[j & 3][rb], va, pb[par][rb][j >> 2]);
         }
       }
-    } else {
-      for (int32_t j = 0; j <= ntiles; ++j) {
-        barrier();  // slot 2 j
-        if (j >= 1) vphase(j - 1);
-        if (j < ntiles) transpose_part(j);
-        barrier();  // slot 2 j + 1
-        mphase(j, false);
-      }
+      // Vector reads of O^T follow: wait states for the products' latency.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+a"(oacc[0][0]), "+a"(oacc[0][1]), "+a"(oacc[1][0]), "+a"(oacc[1][1]),
+                     "+a"(oacc[2][0]), "+a"(oacc[2][1]), "+a"(oacc[3][0]), "+a"(oacc[3][1]));
     }
 
-    // Finish: the row sum is split over the two halves of the wave.
-    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
-    if (row_ok) {
+    // A row whose scores left the window around its reference: do the item
+    // over (once) with the row's largest scaled score as reference.
+    bool moved = false;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float x = max_halves(rmax[rb]);  // largest S' of the row (kMinusBig: no key)
+      const bool out = row_ok[rb] && x > 0.5f * kMinusBig && (x > kWindow || x < -kWindow);
+      moved |= out;
+      m_keep[rb] = out ? m[rb] + x : m[rb];
+    }
+    if (moved && !again) restart = 1;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier();
+    const bool redo = __builtin_amdgcn_readfirstlane(restart) != 0;
+    barrier();  // every wave has read the flag
+    if (redo) {
+      if (tid == 0) restart = 0;  // ordered before any new write by the item's barriers
+      again = true;
+      continue;
+    }
+    again = false;
+    ++idx;
+
+    // Finish: the row sums are split over the two halves of the wave.
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      if (!row_ok[rb]) continue;
+      const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32, 64);
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-      const float lse_nat = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
-      const int32_t i_tok = q0 + t;
+      const float lse_nat = ltot > 0.f ? (m[rb] + log2f(ltot)) * kLn2 : -INFINITY;
+      const int32_t i_tok = q0 + t_of[rb];
+      const int32_t hh = h_of[rb];
       // Lane holds O^T[d][row] for d = 32 nb + 8 b + 4 half + j (element 4 b + j of block nb).
       if (S == 1) {
-        bf16_t* orow = o + ((int64_t)i_tok * p.num_qo_heads + h) * kD + 4 * half;
+        bf16_t* orow = o + ((int64_t)i_tok * p.num_qo_heads + hh) * kD + 4 * half;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const uint32_t lo = pack_bf16x2(oacc[nb][4 * b] * inv, oacc[nb][4 * b + 1] * inv);
-            const uint32_t hi = pack_bf16x2(oacc[nb][4 * b + 2] * inv, oacc[nb][4 * b + 3] * inv);
+            const uint32_t lo =
+                pack_bf16x2(oacc[nb][rb][4 * b] * inv, oacc[nb][rb][4 * b + 1] * inv);
+            const uint32_t hi =
+                pack_bf16x2(oacc[nb][rb][4 * b + 2] * inv, oacc[nb][rb][4 * b + 3] * inv);
             *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * b) = make_uint2(lo, hi);
           }
-        if (half == 0 && lse) lse[(int64_t)i_tok * p.num_qo_heads + h] = lse_nat;
+        if (half == 0 && lse) lse[(int64_t)i_tok * p.num_qo_heads + hh] = lse_nat;
       } else {
-        const int64_t prow = (int64_t)part0 + (int64_t)s * n + t;
-        float* orow = p.part_o + (prow * p.num_qo_heads + h) * kD + 4 * half;
+        const int64_t prow = (int64_t)part0 + (int64_t)s * n + t_of[rb];
+        float* orow = p.part_o + (prow * p.num_qo_heads + hh) * kD + 4 * half;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
           for (int b = 0; b < 4; ++b)
             *reinterpret_cast<float4*>(orow + 32 * nb + 8 * b) =
-                make_float4(oacc[nb][4 * b] * inv, oacc[nb][4 * b + 1] * inv,
-                            oacc[nb][4 * b + 2] * inv, oacc[nb][4 * b + 3] * inv);
-        if (half == 0) p.part_lse[prow * p.num_qo_heads + h] = lse_nat;
+                make_float4(oacc[nb][rb][4 * b] * inv, oacc[nb][rb][4 * b + 1] * inv,
+                            oacc[nb][rb][4 * b + 2] * inv, oacc[nb][rb][4 * b + 3] * inv);
+        if (half == 0) p.part_lse[prow * p.num_qo_heads + hh] = lse_nat;
       }
     }
   }

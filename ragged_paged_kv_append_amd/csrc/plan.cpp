@@ -152,8 +152,10 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
     *err = "causal must be 0 or 1";
     return RPA_ERR_INVALID_ARG;
   }
-  if (!std::isfinite(c.sm_scale)) {
-    *err = "sm_scale must be finite";
+  // The kernels take a row's maximum score before scaling, which is the
+  // maximum scaled score only for a positive scale.
+  if (!std::isfinite(c.sm_scale) || !(c.sm_scale > 0.f)) {
+    *err = "sm_scale must be finite and positive";
     return RPA_ERR_INVALID_ARG;
   }
   const bool dims_ok = (c.head_dim_qk == 64 && c.head_dim_v == 64) ||

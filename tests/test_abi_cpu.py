@@ -343,6 +343,8 @@ def test_plan_create_error_paths(L):
         (rpa.RPA_ERR_INVALID_ARG, rpa.rpa_attn_config(4, 2, 64, 64, 16, 7, 1, 0.1)),
         (rpa.RPA_ERR_INVALID_ARG, rpa.rpa_attn_config(4, 2, 64, 64, 16, 0, 2, 0.1)),
         (rpa.RPA_ERR_INVALID_ARG, rpa.rpa_attn_config(4, 2, 64, 64, 16, 0, 1, float("nan"))),
+        (rpa.RPA_ERR_INVALID_ARG, rpa.rpa_attn_config(4, 2, 64, 64, 16, 0, 1, 0.0)),
+        (rpa.RPA_ERR_INVALID_ARG, rpa.rpa_attn_config(4, 2, 64, 64, 16, 0, 1, -0.125)),
     ]
     for status, c in bad:
         expect(status, lambda c=c: call(cfg=c))
