@@ -34,7 +34,10 @@ DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-p
 # masked keys carry a large negative finite value and unused key slots are
 # filled from a valid key).
 FILE_FLAGS = {
-    "prefill.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+    # the prefill step loop is unrolled over its 64 slots (two steps): a body
+    # above the default pragma threshold would stay rolled, its register
+    # arrays in scratch memory
+    "prefill.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-pragma-unroll-threshold=200000"],
     "mla.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
 }
 

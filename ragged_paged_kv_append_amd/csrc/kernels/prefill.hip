@@ -101,51 +101,45 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// One global-to-LDS DMA instruction (gfx950 global_load_lds_dwordx4): every
-// lane copies 16 bytes from `src` to LDS byte address lds + 16 * lane.  It is
-// issued from inline assembly so that the compiler does not track it: left to
-// itself the compiler makes later LDS reads wait for all DMA in flight, while
-// the kernel waits for exactly the tiles it needs (explicit vmcnt counts).
-// M0, which carries the LDS address, is saved and restored around the
-// instruction; the DMA reads M0 one wait state after the write that sets it.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds)
-      : "memory");
+// One global-to-LDS DMA instruction (gfx950 global_load_lds_dwordx4, saddr
+// form) for the lanes in `lanes`: each copies 16 bytes from base + off to LDS
+// byte address lds + 16 * lane; the other lanes move nothing, and what their
+// LDS bytes held stays.  It is issued from inline assembly so that the
+// compiler does not track it: left to itself the compiler makes later LDS
+// reads wait for all DMA in flight, while the kernel waits for exactly the
+// tiles it needs (explicit vmcnt counts).  EXEC and M0 (the LDS address) are
+// saved and restored around the instruction; the DMA reads M0 one wait state
+// after the write that sets it, and a memory instruction reads an SGPR that a
+// vector instruction (v_readlane, v_readfirstlane) wrote only five wait
+// states later: the first instruction of a tile waits (NOP), the others use
+// scalar values formed by scalar instructions.
+#define RPA_DMA16_BODY                \
+  "s_mov_b64 %1, exec\n\t"             \
+  "s_mov_b64 exec, %5\n\t"             \
+  "s_mov_b32 %0, m0\n\t"               \
+  "s_mov_b32 m0, %4\n\t"               \
+  "s_nop 0\n\t"                        \
+  "global_load_lds_dwordx4 %2, %3\n\t" \
+  "s_mov_b32 m0, %0\n\t"               \
+  "s_mov_b64 exec, %1"
+template <bool NOP>
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds,
+                                      uint64_t lanes) {
+  uint32_t saved_m0;
+  uint64_t saved_exec;
+  if (NOP) {
+    asm volatile("s_nop 4\n\t" RPA_DMA16_BODY
+                 : "=&s"(saved_m0), "=&s"(saved_exec)
+                 : "v"(off), "s"(base), "s"(lds), "s"(lanes)
+                 : "memory");
+  } else {
+    asm volatile(RPA_DMA16_BODY
+                 : "=&s"(saved_m0), "=&s"(saved_exec)
+                 : "v"(off), "s"(base), "s"(lds), "s"(lanes)
+                 : "memory");
+  }
 }
-
-// The same DMA with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
-// offset (the saddr form: no per-lane address arithmetic).  The base comes
-// from v_readfirstlane / v_readlane, and a memory instruction reads an SGPR
-// that a VALU instruction wrote only five wait states later: s_nop 4 first.
-__device__ __forceinline__ void dma16_base(const void* base, uint32_t off, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds)
-      : "memory");
-}
-
-// A 64-bit pointer that is uniform across the wave, moved into SGPRs.
-__device__ __forceinline__ const char* uniform_ptr(const char* p) {
-  const uint64_t b = reinterpret_cast<uint64_t>(p);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | (uint64_t)lo);
-}
+#undef RPA_DMA16_BODY
 
 // The S^T products are issued from inline assembly so that their
 // accumulators stay in VGPRs, where the softmax reads them (the compiler
@@ -218,6 +212,15 @@ constexpr int reads_before(int u) {
   return n < 15 ? n : 15;
 }
 
+// Softmax schedule of a step (see the main loop): exps of elements 0, 1 in
+// slot 0, 2, 3 in slot 1 and e >= 4 in slot e - 2; the bf16 pack of pair p
+// in slot 2 (p = 0), 3 (p = 1) or 2 p + 1 (p >= 2).
+constexpr int exp_count(int s) { return s < 2 ? 2 : (s <= 29 ? 1 : 0); }
+constexpr int exp_first(int s) { return (s < 2 ? 2 * s : s + 2) & 31; }
+constexpr int pack_pair(int s) {
+  return s == 2 ? 0 : (s == 3 ? 1 : ((s >= 5 && (s & 1)) ? (s - 1) / 2 : -1));
+}
+
 // The PV products, also from inline assembly (accumulators in AGPRs), so that
 // their order against the S^T products and the softmax is the program order.
 __device__ __forceinline__ void mfma_pv(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
@@ -255,18 +258,15 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
   const int q4 = (lane & 15) >> 2;
   const uint32_t v_rd = 256u * (4 * half + q4) + 64u * q4 + 32u * (col >> 4) + 8u * (lane & 3);
 
-  // DMA lane offsets of a full tile (the fast path, for token strides that
-  // are multiples of 256 bytes): instruction i of this wave carries key rows
-  // 4 i + lane / 16 of its 16, lane % 16 being the swizzled 16-byte position.
-  // K row rr keeps chunk c at c ^ (rr % 16), so for instruction i the offset
-  // is dk_off ^ 64 i plus 4 i rows (a scalar add); V rows keep chunk c at
-  // c ^ 4 (rr % 4), the same for every instruction: dv_off plus 4 i rows.
+  // DMA lanes: instruction i of a wave's share of a tile carries its key rows
+  // 4 i + lane / 16 (of 16), lane % 16 being the swizzled 16-byte position:
+  // K row rr keeps chunk c at c ^ (rr % 16), V rows keep it at c ^ 4 (rr % 4).
+  // The instruction's first row is in its scalar base; a lane adds its row
+  // within the four (lane / 16) and its chunk.
   const int l4 = lane >> 4, p16 = lane & 15;
   const uint32_t ktok = 2u * (uint32_t)ks.token, vtok = 2u * (uint32_t)vs.token;
-  const bool dma_fast_ok = (ktok % 256u) == 0 && (vtok % 256u) == 0 &&
-                           (int64_t)ktok * 16 < (int64_t)1 << 31 &&
-                           (int64_t)vtok * 16 < (int64_t)1 << 31;
-  const uint32_t dk_off = (uint32_t)l4 * ktok + 16u * (uint32_t)(p16 ^ l4);
+  const uint32_t k_lrow = (uint32_t)l4 * ktok;
+  const uint32_t xk = 16u * (uint32_t)(p16 ^ l4);  // K chunk of instruction 0 (^ 64 i)
   const uint32_t dv_off = (uint32_t)l4 * vtok + 16u * (uint32_t)(p16 ^ (4 * l4));
 
   // Zero the ring once: the PV products of an item's first step multiply a
@@ -331,31 +331,24 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
     const int32_t* pages = p.page_indices + p.page_indptr[r];
     const char* kbase = reinterpret_cast<const char*>(kc + (int64_t)g * ks.head);
     const char* vbase = reinterpret_cast<const char*>(vc + (int64_t)g * vs.head);
-    // Page id of the first key row this wave moves for tile T, in lane T % 64
-    // of pid[T / 64] (the planner keeps an item within 128 tiles).  Rows past
-    // k1 are clamped onto the item's last key.
-    int32_t pid[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int32_t gkey = min(k0 + (lane + 64 * c) * kKT + 16 * wave, k1 - 1);
-      pid[c] = (c == 0 || ntiles > 64) ? pages[gkey >> p.page_shift] : 0;
-    }
+    // Page id of the first key row this wave moves for tile T, in lane T (the
+    // planner keeps an item within 64 tiles), clamped to the item's last key.
+    int32_t pid = pages[min(k0 + lane * kKT + 16 * wave, k1 - 1) >> p.page_shift];
     // DMA of tile T into ring slot T % 4: this wave's key rows 16 wave ..
-    // + 15, instruction x = 0..3 for K, 4..7 for V, each 4 rows of 256 bytes
-    // (lane / 16 is the row, lane % 16 the swizzled 16-byte position).  Keys
-    // past k1 are fetched from the item's last key (a written slot of the
-    // same page), so masked keys hold finite values.
+    // + 15 (one page: pages hold a multiple of 16 keys), instruction x = 0..3
+    // for K, 4..7 for V, each 4 rows of 256 bytes.  Rows at or past k1 are not
+    // moved: their ring bytes keep an older tile's finite values, which the
+    // mask hides.  A tile past the item moves nothing.  No branches.
     struct DmaTile {
       const char* kg;
       const char* vg;
       uint32_t lds;
-      int32_t rmax;  // rows past the first that exist
+      int32_t rmax;  // rows past the first that exist (< 0: none)
     };
     auto dma_setup = [&](int32_t T) __attribute__((always_inline)) {
-      const int32_t gkey = min(k0 + T * kKT + 16 * wave, k1 - 1);
-      const int64_t page = T < 64 ? __builtin_amdgcn_readlane(pid[0], T)
-                                  : __builtin_amdgcn_readlane(pid[1], T - 64);
-      const int64_t in_page = gkey & (p.page_size - 1);
+      const int32_t gkey = k0 + T * kKT + 16 * wave;
+      const int64_t page = __builtin_amdgcn_readlane(pid, T);
+      const int64_t in_page = min(gkey, k1 - 1) & (p.page_size - 1);
       DmaTile d;
       d.kg = kbase + 2 * (page * ks.page + in_page * ks.token);
       d.vg = vbase + 2 * (page * vs.page + in_page * vs.token);
@@ -367,13 +360,13 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
     auto dma_x = [&](const DmaTile& d, int x) __attribute__((always_inline)) {
       const int i = x & 3;
       const bool v = x >= 4;
-      const int ln = (int)opaque((uint32_t)lane);
-      const int rr = 4 * i + (ln >> 4);  // row within the wave's 16 (= its key mod 16)
-      const int row = min(rr, d.rmax);   // rows past the last key repeat it
-      const int chunk = v ? ((ln & 15) ^ (4 * (rr & 3))) : ((ln & 15) ^ (rr & 15));
-      const uint32_t off = v ? 2u * (uint32_t)(row * vs.token + 8 * chunk)
-                             : 2u * (uint32_t)(row * ks.token + 8 * chunk);
-      dma16((v ? d.vg : d.kg) + off, d.lds + (v ? kTileBytes : 0) + 1024 * i);
+      // lanes of rows 4 i .. 4 i + 3 that exist: 16 per row
+      const int32_t nr = min(max(d.rmax - 4 * i + 1, 0), 4);
+      const uint64_t lanes = nr >= 4 ? ~0ull : ((1ull << (16 * nr)) - 1ull);
+      const char* b = v ? d.vg + (int64_t)(4 * i) * vtok : d.kg + (int64_t)(4 * i) * ktok;
+      const uint32_t off = v ? dv_off : k_lrow + (xk ^ (64u * i));
+      if (i == 0) dma16<true>(b, opaque(off), d.lds + (v ? kTileBytes : 0), lanes);
+      else dma16<false>(b, opaque(off), d.lds + (v ? kTileBytes : 0) + 1024 * i, lanes);
     };
 
     const float sc = p.sm_scale * kLog2e;
@@ -446,15 +439,13 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
     // Steps whose keys start at or past this need the mask.
     const int32_t mask_kb = mask_from - kStep + 1;
 
-    asm volatile("" : "+v"(pid[0]), "+v"(pid[1]));  // page ids complete before the DMA
+    asm volatile("" : "+v"(pid));  // page ids complete before the DMA
     barrier();  // the previous item's waves are done with the ring
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      if (T < ntiles) {
-        const DmaTile d = dma_setup(T);
+      const DmaTile d = dma_setup(T);
 #pragma unroll
-        for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
-      }
+      for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
     }
     // Q operand of the S^T products: qf[rb][i] = Q[row 32 rb + col][16 i + 8 half .. + 8).
     u32x4_t qf[2][8];
@@ -562,7 +553,6 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
         f32x16_t(&sc_out)[2] = sacc[par ^ 1];   // S^T of step h + 1
         u32x4_t(&p_out)[2][2] = pb[par];        // P^T of step h
         u32x4_t(&p_in)[2][2] = pb[par ^ 1];     // P^T of step h - 1
-        const bool dma_due = T + 2 < ntiles;
         DmaTile dd{};
         // The start blocks of step h + 1: uniform branches, taken only near
         // the diagonal and past the item's keys.
@@ -581,6 +571,7 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
         __builtin_amdgcn_sched_barrier(0);
 
         float ps[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        float xprev = 0.f;  // S' of the first element of the pair in flight
         // Each slot: one matrix product, then a share of the softmax, the
         // operand reads and the DMA.  The empty asm statements at the end of a
         // slot pin what the slot computed: without them the compiler sinks the
@@ -588,7 +579,8 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
 #pragma unroll
         for (int sl = 0; sl < 32; ++sl) {
           // ---- matrix product of this slot -------------------------------------
-          wait_lds_n(reads_before(sl));
+          // (an odd slot's product reuses the operand of the slot before it)
+          if ((sl & 1) == 0) wait_lds_n(reads_before(sl));
           if (sl < 16) {
             const int i = sl >> 1, rb = sl & 1;
             if (i == 0) mfma_s_first(sc_out[rb], kr[0], qf[rb][0], cinit[rb]);
@@ -614,52 +606,52 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
             ds_vt(vr[j], va_cur ^ (64u * j));
           }
           // ---- softmax of step h -----------------------------------------------
-          if (sl < 16) {
-            // S' = S * scale * log2 e - m, its running max and P = exp2(S'),
-            // two scores per slot (what the vector pipe can do in the 32
-            // cycles of one product)
-            const int e0 = 2 * sl, rb = e0 >> 4, i0 = e0 & 15;
-            const float x0 = __builtin_fmaf(sc_in[rb][i0], sc, -m[rb]);
-            const float x1 = __builtin_fmaf(sc_in[rb][i0 + 1], sc, -m[rb]);
-            rmax[rb] = fmaxf(rmax[rb], fmaxf(x0, x1));
-            sc_in[rb][i0] = __builtin_amdgcn_exp2f(x0);
-            sc_in[rb][i0 + 1] = __builtin_amdgcn_exp2f(x1);
-            asm volatile("" : "+v"(sc_in[0]), "+v"(sc_in[1]), "+v"(rmax[0]), "+v"(rmax[1]));
-          } else if (sl < 24) {
-            // bf16 pairs of P and the row sums (of the fp32 P, with plain adds:
-            // v_dot2 would hold up the matrix core)
-            const int w0 = 2 * (sl - 16);  // word index 0..15 over [rb][kc][e]
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int w = w0 + u, rb = w >> 3, kcc = (w >> 2) & 1, e = w & 3;
+          // Spread over the 32 slots so that each holds about one exp and three
+          // other vector instructions (what the vector pipe can do next to one
+          // 32-cycle product): S' = S * scale * log2 e - m and P = exp2(S') for
+          // elements 0..3 in slots 0 and 1 and for element e >= 4 in slot e - 2;
+          // the running max of each pair of S' with its second element; the
+          // bf16 pair of P and its sum two slots after its exps.
+          {
+            const int ne = exp_count(sl), e0 = exp_first(sl);
+            auto soft_one = [&](int e) __attribute__((always_inline)) {
+              const int rb = (e >> 4) & 1, i = e & 15;
+              const float x = __builtin_fmaf(sc_in[rb][i], sc, -m[rb]);
+              if (e & 1) {
+                rmax[rb] = fmaxf(rmax[rb], fmaxf(xprev, x));
+              } else {
+                xprev = x;
+              }
+              sc_in[rb][i] = __builtin_amdgcn_exp2f(x);
+            };
+            if (ne >= 1) soft_one(e0);
+            if (ne >= 2) soft_one(e0 + 1);
+            const int pp = pack_pair(sl);
+            if (pp >= 0) {
+              // bf16 pairs of P and the row sums (of the fp32 P, with plain adds:
+              // v_dot2 would hold up the matrix core)
+              const int rb = (pp >> 3) & 1, kcc = (pp >> 2) & 1, e = pp & 3;
               const float x0 = sc_in[rb][8 * kcc + 2 * e], x1 = sc_in[rb][8 * kcc + 2 * e + 1];
               p_out[rb][kcc][e] = pack_bf16x2(x0, x1);
               ps[rb][e] += x0 + x1;
             }
+            if (sl == 31) {
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb)
+                lsum[rb] += (ps[rb][0] + ps[rb][1]) + (ps[rb][2] + ps[rb][3]);
+            }
+            asm volatile("" : "+v"(sc_in[0]), "+v"(sc_in[1]), "+v"(rmax[0]), "+v"(rmax[1]),
+                         "+v"(xprev));
             asm volatile("" : "+v"(p_out[0][0]), "+v"(p_out[0][1]), "+v"(p_out[1][0]),
-                         "+v"(p_out[1][1]));
+                         "+v"(p_out[1][1]), "+v"(lsum[0]), "+v"(lsum[1]));
             asm volatile("" : "+v"(ps[0][0]), "+v"(ps[0][1]), "+v"(ps[0][2]), "+v"(ps[0][3]),
                          "+v"(ps[1][0]), "+v"(ps[1][1]), "+v"(ps[1][2]), "+v"(ps[1][3]));
-          } else if (sl == 24) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-              lsum[rb] += (ps[rb][0] + ps[rb][1]) + (ps[rb][2] + ps[rb][3]);
-            asm volatile("" : "+v"(lsum[0]), "+v"(lsum[1]));
           }
           // ---- DMA of tile T + 2: slots 22, 25, 28, 31 of both steps -------------
-          if (sl >= 22 && (sl - 22) % 3 == 0 && dma_due) {
+          if (sl >= 22 && (sl - 22) % 3 == 0) {
             const int x = 4 * par + (sl - 22) / 3;
             if (x == 0 || x == 4) dd = dma_setup(T + 2);
-            const bool fast = dma_fast_ok && k0 + (T + 3) * kKT <= k1;  // a full tile
-            if (fast) {
-              const int i = x & 3;
-              const char* b = x >= 4 ? dd.vg + 4 * i * vtok : dd.kg + 4 * i * ktok;
-              const uint32_t off = x >= 4 ? dv_off : (dk_off ^ (64u * i));
-              dma16_base(uniform_ptr(b), opaque(off),
-                         dd.lds + (x >= 4 ? kTileBytes : 0) + 1024 * i);
-            } else {
-              dma_x(dd, x);
-            }
+            dma_x(dd, x);
           }
           __builtin_amdgcn_sched_barrier(0);
           if (sl == 9 && par == 0) {

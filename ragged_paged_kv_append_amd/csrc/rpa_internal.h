@@ -36,7 +36,7 @@ enum SplitField : int32_t { SP_COUNT = 0, SP_CHUNK, SP_BASE, SP_WORDS };
 constexpr int GEN_ROWS = 4;        // rows per generic item (one wave each)
 constexpr int DEC_MAX_ROWS = 16;   // rows per decode item (one MFMA column block)
 constexpr int PRE_ROWS = 256;      // rows per prefill item
-constexpr int PRE_MAX_KEYS = 8192; // keys per prefill item (128 tiles: two page-id registers)
+constexpr int PRE_MAX_KEYS = 4096; // keys per prefill item (64 tiles: one page-id register)
 constexpr int MLA_MAX_KEYS = 32768; // keys per latent item (its page ids fit an LDS table)
 constexpr int TREE_MAX_NEW = 64;   // new tokens of a request with a tree mask (one 64-bit row)
 constexpr int MLA_ROWS = 128;      // rows per latent-attention item
