@@ -188,8 +188,9 @@ rpa_status rpa_plan_create_tree(const rpa_attn_config* cfg, const rpa_batch_desc
                                 const int32_t* tree_indptr, const uint32_t* tree_words,
                                 int32_t num_cus, rpa_plan** out);
 
-/* Device bytes the plan needs in its workspace: metadata plus float32 partial
- * outputs of split pieces.  Host only. */
+/* Device bytes the plan needs in its workspace: metadata plus the partial
+ * outputs of split pieces (in the attention dtype, with float32 log-sum-exp
+ * values).  Host only. */
 rpa_status rpa_plan_workspace_size(const rpa_plan* plan, size_t* bytes);
 
 /* Copy the plan's metadata into a caller-owned device workspace (256-byte

@@ -269,15 +269,15 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
   const uint32_t xk = 16u * (uint32_t)(p16 ^ l4);  // K chunk of instruction 0 (^ 64 i)
   const uint32_t dv_off = (uint32_t)l4 * vtok + 16u * (uint32_t)(p16 ^ (4 * l4));
 
-  // Zero the ring once: the PV products of an item's first step multiply a
-  // zero P by whatever the slot of the tile before it holds, which must be
-  // finite.
+  const int32_t wb0 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][blockIdx.x]);
+  const int32_t wb1 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][blockIdx.x + 1]);
+  // Zero the ring once (while the item list loads): the PV products of an
+  // item's first step multiply a zero P by whatever the slot of the tile
+  // before it holds, and key rows past an item keep an older tile's values;
+  // both must be finite.
   for (int i = tid; i < kSlots * kSlotBytes / 16; i += 64 * kWaves)
     *reinterpret_cast<lds_u32x4*>((uintptr_t)(ring_lds + 16 * i)) = u32x4_t{0u, 0u, 0u, 0u};
   if (tid == 0) restart = 0;
-
-  const int32_t wb0 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][blockIdx.x]);
-  const int32_t wb1 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][blockIdx.x + 1]);
   float m_keep[2] = {0.f, 0.f};  // references for an item done over
   bool again = false;
   for (int32_t idx = wb0; idx < wb1;) {
@@ -724,30 +724,27 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
       const int32_t i_tok = q0 + t_of[rb];
       const int32_t hh = h_of[rb];
       // Lane holds O^T[d][row] for d = 32 nb + 8 b + 4 half + j (element 4 b + j of block nb).
-      if (S == 1) {
-        bf16_t* orow = o + ((int64_t)i_tok * p.num_qo_heads + hh) * kD + 4 * half;
+      // The output row, or the row of piece s's partial (the same bf16 layout).
+      const int64_t prow = (int64_t)part0 + (int64_t)s * n + t_of[rb];
+      bf16_t* orow = (S == 1 ? o + (int64_t)i_tok * p.num_qo_heads * kD
+                             : static_cast<bf16_t*>(p.part_o) + prow * p.num_qo_heads * kD) +
+                     (int64_t)hh * kD + 4 * half;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t lo =
-                pack_bf16x2(oacc[nb][rb][4 * b] * inv, oacc[nb][rb][4 * b + 1] * inv);
-            const uint32_t hi =
-                pack_bf16x2(oacc[nb][rb][4 * b + 2] * inv, oacc[nb][rb][4 * b + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * b) = make_uint2(lo, hi);
-          }
-        if (half == 0 && lse) lse[(int64_t)i_tok * p.num_qo_heads + hh] = lse_nat;
-      } else {
-        const int64_t prow = (int64_t)part0 + (int64_t)s * n + t_of[rb];
-        float* orow = p.part_o + (prow * p.num_qo_heads + hh) * kD + 4 * half;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            *reinterpret_cast<float4*>(orow + 32 * nb + 8 * b) =
-                make_float4(oacc[nb][rb][4 * b] * inv, oacc[nb][rb][4 * b + 1] * inv,
-                            oacc[nb][rb][4 * b + 2] * inv, oacc[nb][rb][4 * b + 3] * inv);
-        if (half == 0) p.part_lse[prow * p.num_qo_heads + hh] = lse_nat;
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t lo =
+              pack_bf16x2(oacc[nb][rb][4 * b] * inv, oacc[nb][rb][4 * b + 1] * inv);
+          const uint32_t hi =
+              pack_bf16x2(oacc[nb][rb][4 * b + 2] * inv, oacc[nb][rb][4 * b + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * b) = make_uint2(lo, hi);
+        }
+      if (half == 0) {
+        if (S == 1) {
+          if (lse) lse[(int64_t)i_tok * p.num_qo_heads + hh] = lse_nat;
+        } else {
+          p.part_lse[prow * p.num_qo_heads + hh] = lse_nat;
+        }
       }
     }
   }
