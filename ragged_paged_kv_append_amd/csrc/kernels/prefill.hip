@@ -439,15 +439,21 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
     // Steps whose keys start at or past this need the mask.
     const int32_t mask_kb = mask_from - kStep + 1;
 
-    asm volatile("" : "+v"(pid));  // page ids complete before the DMA
+    // Page ids and tree-mask rows complete before the DMA (the compiler's own
+    // wait for them must not drain the DMA stream later).
+    asm volatile("" : "+v"(pid), "+v"(tm_lo[0]), "+v"(tm_hi[0]), "+v"(tm_lo[1]), "+v"(tm_hi[1]));
     barrier();  // the previous item's waves are done with the ring
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const DmaTile d = dma_setup(T);
+    // Tile 0, then Q, then tile 1: the products start once tile 0 and Q are
+    // in (vector-memory loads complete in order), while tile 1 lands.
+    {
+      const DmaTile d = dma_setup(0);
 #pragma unroll
       for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
     }
-    // Q operand of the S^T products: qf[rb][i] = Q[row 32 rb + col][16 i + 8 half .. + 8).
+    // Q operand of the S^T products: qf[rb][i] = Q[row 32 rb + col][16 i + 8 half .. + 8),
+    // loaded into AGPRs from inline assembly (counted with the DMA).  Rows
+    // past the item read a valid row of the request (t_of = 0): their
+    // results are never stored.
     u32x4_t qf[2][8];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -455,24 +461,22 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
           q + ((int64_t)(q0 + t_of[rb]) * p.num_qo_heads + h_of[rb]) * kD + 8 * half;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        qf[rb][i] = row_ok[rb] ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * i)
-                               : u32x4_t{0u, 0u, 0u, 0u};
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(qf[rb][i]) : "v"(qrow + 16 * i) : "memory");
     }
-    // Q, the tree-mask rows, the first two tiles and the previous item's
-    // output stores complete.  The empty asm statements mark the loads as
-    // complete, so that the compiler adds no wait of its own inside the loop
-    // (its count would not know about the DMA and would drain it).
-    wait_vmem<0>();
+    {
+      const DmaTile d = dma_setup(1);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+      for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
+    }
+    wait_vmem<kDmaInst>();  // tile 0 and Q are in; tile 1 may still be in flight
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) asm volatile("" : "+a"(qf[rb][i]));
-      asm volatile("" : "+v"(tm_lo[rb]), "+v"(tm_hi[rb]));
-    }
     if (k0 >= mask_kb) set_mask(k0);
     // Vector writes of cinit, then a product reads it: wait states.
     asm volatile("s_nop 4" : "+v"(cinit[0]), "+v"(cinit[1]));
-    barrier();  // tiles 0 and 1 are in the ring
+    barrier();  // tile 0 is in the ring (tile 1 is waited for in step 0)
 
     // K operands of step h (ring slot of tile h / 2, its half h % 2), three
     // steps ahead of the products that use them.
