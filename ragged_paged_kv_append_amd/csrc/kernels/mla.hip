@@ -433,48 +433,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (moved) restart = 1;
     };
 
-    // PV phase of the tile in `slot`.
-    // PV products of the tile in `slot`.
-    auto pv_phase = [&](int slot) __attribute__((always_inline)) {
-      const int ln = opaque_lane(lane);
-      const int pc = ln & 31, ph = ln >> 5;
-      // Transposing read: lane ln reads row 4 ph + (ln % 16) / 4 (+ 8 for the
-      // high half) of a 16-key block, 4 value dims at element column
-      // 32 nb + 16 (pc / 16) + 4 (ln % 4) of the wave's 128.
-      const int tr_row = 4 * ph + ((ln & 15) >> 2);
-      const uint32_t vt = ring_lds + slot * kTileBytes + (uint32_t)tr_row * kRowBytes +
-                          2u * (128 * wave + 16 * (pc >> 4) + 4 * (ln & 3));
+    // PV products of the tile in `slot`, operands read from inline assembly
+    // with explicit waits (the compiler's own waits stop the products after
+    // every few reads): the V^T operands of the first 16-key half are read
+    // before the barrier that publishes P (pv_first), then P of that half and
+    // both operands of the second half, and the first half's products run
+    // while the second half's reads land (pv_rest).
+    const int pv_ln = opaque_lane(lane);
+    const int pv_pc = pv_ln & 31, pv_ph = pv_ln >> 5;
+    // Transposing read: lane ln reads row 4 ph + (ln % 16) / 4 (+ 8 for the
+    // high half) of a 16-key block, 4 value dims at element column
+    // 32 nb + 16 (pc / 16) + 4 (ln % 4) of the wave's 128.
+    const int pv_tr_row = 4 * pv_ph + ((pv_ln & 15) >> 2);
+    const uint32_t pv_vt0 = ring_lds + (uint32_t)pv_tr_row * kRowBytes +
+                            2u * (128 * wave + 16 * (pv_pc >> 4) + 4 * (pv_ln & 3));
+    // P^T operand of row block rb: row 32 rb + pc, keys
+    // 16 kc + 8 (e / 4) + 4 ph + e % 4 (two 8-byte reads, 16 bytes apart).
+    const uint32_t pv_pt = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16_t*)
+                               &plds[pv_pc * kPRow + 4 * pv_ph];
+    auto read_vt = [&](u32x4_t& d, uint32_t vt, int kc, int nb) __attribute__((always_inline)) {
+      u32x2_t lo, hi;
+      asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
+                   : "=&v"(lo), "=&v"(hi)
+                   : "v"(vt), "i"(16 * kc * kRowBytes + 64 * nb),
+                     "i"(16 * kc * kRowBytes + 64 * nb + 8 * kRowBytes)
+                   : "memory");
+      d = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    };
+    auto read_pt = [&](u32x4_t& d, int kc, int rb) __attribute__((always_inline)) {
+      u32x2_t lo, hi;
+      asm volatile("ds_read_b64 %0, %2 offset:%3\n\tds_read_b64 %1, %2 offset:%4"
+                   : "=&v"(lo), "=&v"(hi)
+                   : "v"(pv_pt), "i"(2 * (32 * rb * kPRow + 16 * kc)),
+                     "i"(2 * (32 * rb * kPRow + 16 * kc + 8))
+                   : "memory");
+      d = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4_t pv_va[2][4], pv_pb[2][4];
+    auto pv_first = [&](int slot) __attribute__((always_inline)) {
+      const uint32_t vt = (uint32_t)opaque_lane((int)(pv_vt0 + slot * kTileBytes));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) read_vt(pv_va[0][nb], vt, 0, nb);
+    };
+    auto pv_rest = [&](int slot) __attribute__((always_inline)) {
+      const uint32_t vt = (uint32_t)opaque_lane((int)(pv_vt0 + slot * kTileBytes));
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) read_pt(pv_pb[0][rb], 0, rb);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) read_vt(pv_va[1][nb], vt, 1, nb);
+      // the first half's operands are in (LDS operations complete in order)
+      asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) read_pt(pv_pb[1][rb], 1, rb);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        u32x4_t va[4];
+        if (kc == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const uint32_t a = vt + 16 * kc * kRowBytes + 64 * nb;
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a);
-          const s16x4_t hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(a + 8 * kRowBytes));
-          const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
-          const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
-          va[nb] = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
-        }
-        // P^T operand of row block rb: row 32 rb + pc, keys
-        // 16 kc + 8 (e / 4) + 4 ph + e % 4.
-        u32x4_t pbv[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const bf16_t* prow = &plds[(32 * rb + pc) * kPRow + 16 * kc + 4 * ph];
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(prow);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(prow + 8);
-          pbv[rb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-        }
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb)
-            oacc[nb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[nb]),
-                                                                   as_bf16x8(pbv[rb]), oacc[nb][rb],
-                                                                   0, 0, 0);
-        }
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+a"(oacc[nb][rb])
+                         : "v"(pv_va[kc][nb]), "v"(pv_pb[kc][rb]));
       }
     };
 
@@ -493,13 +513,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       barrier();
       dma_begin(tile + 1 < ntiles, k0 + (tile + 1) * kKT, slot ^ 1);
       s_phase(k0 + tile * kKT, slot);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's P is in LDS
+      pv_first(slot);
+      // this wave's P is in LDS (its stores precede the eight V^T reads)
+      asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
       barrier();
-      restarted |= __builtin_amdgcn_readfirstlane(restart) != 0;
-      pv_phase(slot);
+      pv_rest(slot);
       ++tile;
       slot ^= 1;
     }
+    // Every wave set the flag, if at all, before a barrier of the loop.
+    restarted = __builtin_amdgcn_readfirstlane(restart) != 0;
 
     if (restarted) {
       // The item start's barrier orders this behind every wave's DMA and
