@@ -23,7 +23,9 @@
  *
  * Shape of a step: rpa_plan_create (host) -> rpa_plan_upload (async H2D) ->
  * per layer { rpa_kv_append ; rpa_batch_attention }.  The plan is reused by
- * every layer of the step.
+ * every layer of the step.  Split form: rpa_plan_create_split ->
+ * rpa_plan_upload -> per layer { rpa_split_attention, with rpa_kv_append
+ * before, after or beside it }.
  *
  * Notation: request r has n_r = qo_len new tokens, L_r = kv_len keys counting
  * the new ones, c_r = L_r - n_r cached keys, and page size P.  New token t of
@@ -68,7 +70,7 @@
 extern "C" {
 #endif
 
-#define RPA_ABI_VERSION 2
+#define RPA_ABI_VERSION 3
 
 typedef enum rpa_status {
   RPA_OK = 0,
@@ -188,6 +190,28 @@ rpa_status rpa_plan_create_tree(const rpa_attn_config* cfg, const rpa_batch_desc
                                 const int32_t* tree_indptr, const uint32_t* tree_words,
                                 int32_t num_cus, rpa_plan** out);
 
+/* rpa_plan_create for the split execution of a causal step ("Chunked
+ * prefill" (k4i.top), section "correctness": the chunk's attention is the
+ * softmax merge of its attention over the cached history and its causal
+ * attention over the chunk itself).  The plan has two parts:
+ *   cache part: new token t of request r sees all c_r cached keys of its
+ *     pages (no mask);
+ *   own part:   it sees new tokens 0 .. t of its request, read from the
+ *     step's k_new / v_new rows (token-major, the layout table) instead of
+ *     the pages;
+ * both parts' states are merged per row.  The result equals
+ * rpa_batch_attention after rpa_kv_append, and the pages' slots for the new
+ * tokens are never read, so the append may run before, after or beside the
+ * attention (rpa_kv_append accepts this plan).  Each part is balanced over
+ * num_cus compute units on its own; one call runs a constant number of
+ * launches whatever the batch: the cache part's kernel classes, the own
+ * part's, and one merge.
+ * Arguments and ownership as rpa_plan_create; cfg->causal must be 1 and the
+ * head dims 64/64 or 128/128.  Errors: as rpa_plan_create; INVALID_ARG for
+ * causal = 0, UNSUPPORTED for the 576/512 latent form. */
+rpa_status rpa_plan_create_split(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                                 int32_t num_cus, rpa_plan** out);
+
 /* Device bytes the plan needs in its workspace: metadata plus the partial
  * outputs of split pieces (in the attention dtype, with float32 log-sum-exp
  * values).  Host only. */
@@ -240,6 +264,28 @@ rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q, const void* 
                                const void* v_cache, const rpa_cache_strides* ks,
                                const rpa_cache_strides* vs, void* o, float* lse,
                                void* stream);
+
+/* Attention of a split plan (rpa_plan_create_split): the same o and lse as
+ * rpa_batch_attention over the pages after the append, computed from the
+ * cached keys in the pools and the step's own keys in k_new / v_new.
+ * Source: "Chunked prefill" (k4i.top), section "correctness": history part
+ * and chunk part merge by log-sum-exp into the one-shot result.
+ * Arguments: q, o, lse as rpa_batch_attention; k_new / v_new the step's new
+ * rows, token-major contiguous [total_q, num_kv_heads, d] (16-byte
+ * aligned), the buffers rpa_kv_append copies from; k_cache / v_cache and
+ * ks / vs the pools, of which only the first c_r keys of each request are
+ * read.  The two parts write their partial states (attention dtype, float32
+ * log-sum-exp) to the plan's workspace; the merge writes o and lse.  The
+ * prefill-sized requests of both parts run in one launch, side by side on
+ * shares of the compute units in proportion to their work.  The caller owns
+ * every buffer; the call only enqueues work on `stream`.
+ * Errors: INVALID_ARG (also for a plan not made by rpa_plan_create_split),
+ * NOT_UPLOADED, HIP.  rpa_batch_attention and rpa_batch_attention_noalloc
+ * reject a split plan with INVALID_ARG. */
+rpa_status rpa_split_attention(const rpa_plan* plan, const void* q, const void* k_new,
+                               const void* v_new, const void* k_cache, const void* v_cache,
+                               const rpa_cache_strides* ks, const rpa_cache_strides* vs,
+                               void* o, float* lse, void* stream);
 
 /* rpa_batch_attention without a workspace, for callers that cannot allocate
  * device memory at the point of the call: code under HIP graph capture,
@@ -349,6 +395,8 @@ rpa_status rpa_profile_reset(void);
  * per merge row: first partial row, partial-row stride between pieces,
  * pieces holding a key the row sees, 0), "summary" (batch_size,
  * total_q, num items, partial rows, number of items per kernel class 0..3).
+ * For a split plan the names give the cache part's tables (it holds the
+ * merge and the append map) and "own:<name>" the own part's.
  * Errors: INVALID_ARG for an unknown name. */
 rpa_status rpa_plan_debug_dump(const rpa_plan* plan, const char* name, int32_t* dst,
                                int64_t cap, int64_t* len);

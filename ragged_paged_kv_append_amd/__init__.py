@@ -39,8 +39,9 @@ RPA_DTYPE_BF16 = 1
 KC_GENERIC, KC_DECODE, KC_PREFILL, KC_MLA = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
-    "rpa_plan_create", "rpa_plan_create_tree", "rpa_plan_workspace_size", "rpa_plan_upload",
-    "rpa_kv_append", "rpa_batch_attention", "rpa_batch_attention_noalloc", "rpa_merge_state",
+    "rpa_plan_create", "rpa_plan_create_tree", "rpa_plan_create_split", "rpa_plan_workspace_size",
+    "rpa_plan_upload", "rpa_kv_append", "rpa_batch_attention", "rpa_batch_attention_noalloc",
+    "rpa_split_attention", "rpa_merge_state",
     "rpa_page_copy",
     "rpa_plan_destroy",
     "rpa_status_string",
@@ -93,6 +94,7 @@ def lib() -> ctypes.CDLL:
     L.rpa_plan_create.argtypes = [P(rpa_attn_config), P(rpa_batch_desc), i32, P(vp)]
     L.rpa_plan_create_tree.argtypes = [P(rpa_attn_config), P(rpa_batch_desc),
                                        P(ctypes.c_int32), P(ctypes.c_uint32), i32, P(vp)]
+    L.rpa_plan_create_split.argtypes = [P(rpa_attn_config), P(rpa_batch_desc), i32, P(vp)]
     L.rpa_plan_workspace_size.argtypes = [vp, P(sz)]
     L.rpa_plan_upload.argtypes = [vp, vp, sz, vp]
     L.rpa_kv_append.argtypes = [vp, vp, vp, vp, vp, P(rpa_cache_strides), P(rpa_cache_strides), vp]
@@ -100,6 +102,8 @@ def lib() -> ctypes.CDLL:
                                       P(rpa_cache_strides), vp, vp, vp]
     L.rpa_batch_attention_noalloc.argtypes = [vp, vp, vp, vp, P(rpa_cache_strides),
                                               P(rpa_cache_strides), vp, vp, vp]
+    L.rpa_split_attention.argtypes = [vp, vp, vp, vp, vp, vp, P(rpa_cache_strides),
+                                      P(rpa_cache_strides), vp, vp, vp]
     L.rpa_merge_state.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
     L.rpa_page_copy.argtypes = [vp, P(rpa_cache_strides), i32, i32, vp, vp,
                                 P(rpa_cache_strides), i32, i32, vp, i32, i32, i32, i32, i32, i32,
@@ -117,9 +121,10 @@ def lib() -> ctypes.CDLL:
     L.rpa_profile_read.argtypes = [ctypes.c_char_p, P(ctypes.c_double), P(i64)]
     L.rpa_profile_reset.argtypes = []
     L.rpa_profile_select.argtypes = [ctypes.c_char_p]
-    for name in ("rpa_plan_create", "rpa_plan_create_tree", "rpa_plan_workspace_size",
-                 "rpa_plan_upload", "rpa_kv_append", "rpa_batch_attention",
-                 "rpa_batch_attention_noalloc", "rpa_merge_state",
+    for name in ("rpa_plan_create", "rpa_plan_create_tree", "rpa_plan_create_split",
+                 "rpa_plan_workspace_size", "rpa_plan_upload", "rpa_kv_append",
+                 "rpa_batch_attention", "rpa_batch_attention_noalloc", "rpa_split_attention",
+                 "rpa_merge_state",
                  "rpa_page_copy", "rpa_plan_debug_dump", "rpa_profile_enable",
                  "rpa_profile_read", "rpa_profile_reset", "rpa_profile_select"):
         getattr(L, name).restype = i32
@@ -231,6 +236,19 @@ def rpa_plan_create_tree(cfg: rpa_attn_config, qo_indptr, kv_len, kv_page_indptr
     return _PlanHandle(out.value, arrays + [ti, tw])
 
 
+def rpa_plan_create_split(cfg: rpa_attn_config, qo_indptr, kv_len, kv_page_indptr,
+                          kv_page_indices, num_pages: int, num_cus: int = 0) -> _PlanHandle:
+    """Host-only planning of a causal step's split execution."""
+    L = lib()
+    arrays = [_i32(qo_indptr), _i32(kv_len), _i32(kv_page_indptr), _i32(kv_page_indices)]
+    batch = rpa_batch_desc(len(arrays[1]), _i32p(arrays[0]), _i32p(arrays[1]), _i32p(arrays[2]),
+                           _i32p(arrays[3]), int(num_pages))
+    out = ctypes.c_void_p()
+    _check(L.rpa_plan_create_split(ctypes.byref(cfg), ctypes.byref(batch), int(num_cus),
+                                   ctypes.byref(out)))
+    return _PlanHandle(out.value, arrays)
+
+
 def tree_mask_words(masks) -> tuple[np.ndarray, np.ndarray]:
     """Pack per-request boolean masks ([n_r, n_r] arrays, or None for no mask)
     into (tree_indptr, tree_words) for rpa_plan_create_tree: row t of a
@@ -275,6 +293,13 @@ def rpa_batch_attention(plan: _PlanHandle, q, k_cache, v_cache, ks: rpa_cache_st
     _check(lib().rpa_batch_attention(plan.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                      ctypes.byref(ks), None if vs is None else ctypes.byref(vs),
                                      _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def rpa_split_attention(plan: _PlanHandle, q, k_new, v_new, k_cache, v_cache,
+                        ks: rpa_cache_strides, vs: rpa_cache_strides, o, lse=None, stream=None):
+    _check(lib().rpa_split_attention(plan.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                     _ptr(k_cache), _ptr(v_cache), ctypes.byref(ks),
+                                     ctypes.byref(vs), _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def rpa_batch_attention_noalloc(plan: _PlanHandle, q, k_cache, v_cache, ks: rpa_cache_strides,
@@ -552,81 +577,57 @@ def merge_state(o_a, lse_a, o_b, lse_b, stream=None):
 
 
 class SplitChunkAttention:
-    """Split execution of a step's attention ("Chunked prefill", section
-    "correctness"): the new tokens of each request attend
+    """Split execution of a causal step's attention ("Chunked prefill",
+    section "correctness"): the new tokens of each request attend
 
-      (a) to the request's cached keys (c_r = kv_len - qo_len of them), every
-          new token seeing all of them: one cross-attention plan over the page
-          pool (causal masking off, kv_len = c_r);
-      (b) causally to the step's own keys and values, read straight from the
-          k_new / v_new buffers (token-major [total_q, num_kv_heads, d]) as a
-          pool of page_size-token pages: one causal plan per request with
-          kv_len = qo_len;
+      (a) to the request's c_r = kv_len - qo_len cached keys in the pages,
+          every new token seeing all of them, and
+      (b) causally to the step's own keys and values, read from the k_new /
+          v_new buffers (token-major [total_q, num_kv_heads, d]),
 
-    and the two states are combined by rpa_merge_state.  The result equals the
-    attention over the pages after rpa_kv_append, and the append may run
-    before, after or beside it.  Bottom-right causal attention only; not for
-    the shared-latent form (its values are a view of the keys).  Every step
-    runs in the library's kernels; this class only builds the plans and
-    chains the calls.
+    and the two states are merged, all inside rpa_split_attention (one
+    launch per kernel class and part, then one merge, whatever the batch
+    size).  The result equals the attention over the pages after
+    rpa_kv_append, and the append may run before, after or beside it.  Not
+    for the shared-latent form.  This class only holds the plan and its
+    workspace and marshals the call.
     """
 
     def __init__(self, cfg: rpa_attn_config, qo_indptr, kv_len, kv_page_indptr, kv_page_indices,
-                 num_pages: int, device="cuda", num_cus: int = 0):
-        if not cfg.causal:
-            raise RpaError(RPA_ERR_INVALID_ARG, "split execution is defined for causal attention")
-        if cfg.head_dim_qk == 576:
-            raise RpaError(RPA_ERR_UNSUPPORTED, "split execution of the shared latent form")
-        qo = np.asarray(qo_indptr, dtype=np.int64)
-        kv = np.asarray(kv_len, dtype=np.int64)
-        n = qo[1:] - qo[:-1]
-        cached = kv - n
-        if np.any(cached < 0):
-            raise RpaError(RPA_ERR_INVALID_ARG, "kv_len < qo_len")
+                 num_pages: int, device="cuda", num_cus: int = 0, stream=None):
+        import torch
         self.cfg = cfg
-        self.qo = qo
-        self.total_q = int(qo[-1]) if len(qo) else 0
-        cross = rpa_attn_config(cfg.num_qo_heads, cfg.num_kv_heads, cfg.head_dim_qk,
-                                cfg.head_dim_v, cfg.page_size, cfg.dtype, 0, cfg.sm_scale)
-        self.cache_plan = Plan(cross, qo, cached, kv_page_indptr, kv_page_indices, num_pages,
-                               device=device, num_cus=num_cus)
-        P = cfg.page_size
-        self.chunk_plans = []
-        for r in range(len(n)):
-            if n[r] == 0:
-                continue
-            pages = -(-int(n[r]) // P)
-            plan = Plan(cfg, [0, int(n[r])], [int(n[r])], [0, pages], np.arange(pages), pages,
-                        device=device, num_cus=num_cus)
-            self.chunk_plans.append((int(qo[r]), int(n[r]), plan))
+        self.handle = rpa_plan_create_split(cfg, qo_indptr, kv_len, kv_page_indptr,
+                                            kv_page_indices, num_pages, num_cus)
+        self.total_q = int(np.asarray(qo_indptr)[-1]) if len(qo_indptr) else 0
+        self.num_pages = int(num_pages)
+        self.ws_bytes = rpa_plan_workspace_size(self.handle)
+        self.workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)
+        self.ws_ptr = (self.workspace.data_ptr() + 255) // 256 * 256
+        rpa_plan_upload(self.handle, self.ws_ptr, self.ws_bytes, stream)
+
+    def append(self, k_new, v_new, k_cache, v_cache, stream=None):
+        check_append_args(self.cfg, self.total_q, self.num_pages, k_new, v_new, k_cache, v_cache)
+        rpa_kv_append(self.handle, k_new, v_new, k_cache, v_cache, strides_of(k_cache),
+                      strides_of(v_cache), stream)
 
     def run(self, q, k_new, v_new, k_cache, v_cache, o=None, lse=None, stream=None):
         """o, lse of the step (o in q's dtype, lse float32, natural log)."""
         import torch
-        H, d_v, P = self.cfg.num_qo_heads, self.cfg.head_dim_v, self.cfg.page_size
-        key = (q.dtype, q.device)
-        if getattr(self, "_tmp_key", None) != key:
-            # the two partial states, kept for later calls with this plan
-            mk = lambda: (torch.empty((self.total_q, H, d_v), dtype=q.dtype, device=q.device),
-                          torch.empty((self.total_q, H), dtype=torch.float32, device=q.device))
-            self._tmp = mk() + mk()
-            self._tmp_key = key
-        o_a, lse_a, o_b, lse_b = self._tmp
-        self.cache_plan.attention(q, k_cache, v_cache, o=o_a, lse=lse_a, stream=stream)
-        es = q.element_size()
-        # token-major rows as pages of P tokens: page, head and token strides
-        ks = rpa_cache_strides(P * k_new.stride(0), k_new.stride(1), k_new.stride(0))
-        vs = rpa_cache_strides(P * v_new.stride(0), v_new.stride(1), v_new.stride(0))
-        for i0, n, plan in self.chunk_plans:
-            rpa_batch_attention(plan.handle, q.data_ptr() + i0 * q.stride(0) * es,
-                                k_new.data_ptr() + i0 * k_new.stride(0) * es,
-                                v_new.data_ptr() + i0 * v_new.stride(0) * es, ks, vs,
-                                o_b.data_ptr() + i0 * o_b.stride(0) * es,
-                                lse_b.data_ptr() + i0 * lse_b.stride(0) * 4, stream)
+        H, d_v = self.cfg.num_qo_heads, self.cfg.head_dim_v
         if o is None:
-            o = torch.empty_like(o_a)
+            o = torch.empty((self.total_q, H, d_v), dtype=q.dtype, device=q.device)
         if lse is None:
-            lse = torch.empty_like(lse_a)
-        dtype = RPA_DTYPE_BF16 if q.dtype == torch.bfloat16 else RPA_DTYPE_F32
-        rpa_merge_state(o_a, lse_a, o_b, lse_b, o, lse, self.total_q, H, d_v, dtype, stream)
+            lse = torch.empty((self.total_q, H), dtype=torch.float32, device=q.device)
+        check_attention_args(self.cfg, self.total_q, self.num_pages, q, k_cache, v_cache, o, lse)
+        cfg = self.cfg
+        _check_rows("k_new", k_new, (self.total_q, cfg.num_kv_heads, cfg.head_dim_qk), q.dtype,
+                    q.device)
+        _check_rows("v_new", v_new, (self.total_q, cfg.num_kv_heads, cfg.head_dim_v), q.dtype,
+                    q.device)
+        rpa_split_attention(self.handle, q, k_new, v_new, k_cache, v_cache, strides_of(k_cache),
+                            strides_of(v_cache), o, lse, stream)
         return o, lse
+
+    def debug(self, name: str) -> np.ndarray:
+        return rpa_plan_debug_dump(self.handle, name)

@@ -130,6 +130,9 @@ rpa_status check_uploaded(const rpa_plan* plan) {
 
 bool shared_latent(const rpa_attn_config& c) { return c.head_dim_qk == 576; }
 
+constexpr const char* kSplitPlanMsg =
+    "a split plan runs through rpa_split_attention (it reads the step's own K/V rows)";
+
 // ---- optional per-kernel event timing -------------------------------------------
 
 struct ProfRecord {
@@ -251,6 +254,22 @@ RPA_EXPORT rpa_status rpa_plan_create_tree(const rpa_attn_config* cfg,
     if (out) *out = nullptr;
     if (!tree_indptr) return fail(RPA_ERR_INVALID_ARG, "null tree_indptr");
     return create_plan(cfg, batch, tree_indptr, tree_words, num_cus, out);
+  });
+}
+
+RPA_EXPORT rpa_status rpa_plan_create_split(const rpa_attn_config* cfg,
+                                            const rpa_batch_desc* batch, int32_t num_cus,
+                                            rpa_plan** out) {
+  return guarded([&] {
+    if (!out) return fail(RPA_ERR_INVALID_ARG, "null output pointer");
+    *out = nullptr;
+    std::unique_ptr<rpa_plan> plan(new rpa_plan());
+    std::string err;
+    const rpa_status s = rpa::build_split_plan(cfg, batch, num_cus, plan.get(), &err);
+    if (s != RPA_OK) return fail(s, err);
+    *out = plan.release();
+    clear_error();
+    return RPA_OK;
   });
 }
 
@@ -388,10 +407,11 @@ rpa_status attention_args(const rpa_plan* plan, const void* q, const void* k_cac
   return RPA_OK;
 }
 
-// Launches the attention kernels of every class the plan uses, then the merge
-// of split pieces, on one stream.
+// Launches the attention kernels of every class the plan uses, then (with
+// `merge`) the merge of split pieces, on one stream.
 rpa_status run_attention(const rpa::DevPlan& p, const void* q, const void* k_cache,
-                         const AttnPools& a, void* o, float* lse, hipStream_t st) {
+                         const AttnPools& a, void* o, float* lse, hipStream_t st,
+                         bool merge = true) {
   hipError_t e;
   if (p.n_items[rpa::KC_GENERIC] > 0) {
     e = timed("generic", st, [&] {
@@ -415,8 +435,52 @@ rpa_status run_attention(const rpa::DevPlan& p, const void* q, const void* k_cac
     e = timed("mla", st, [&] { return rpa::launch_mla(p, q, k_cache, a.k_st, o, lse, st); });
     if (e != hipSuccess) return hip_fail(e, "latent attention launch");
   }
-  if (p.n_merge_rows > 0) {
+  if (merge && p.n_merge_rows > 0) {
     e = timed("merge", st, [&] { return rpa::launch_merge_rows(p, o, lse, st); });
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return RPA_OK;
+}
+
+// Split execution: the cache part's and the own part's kernels, then the
+// merge of both.  Streaming classes run part after part; the prefill items of
+// both parts share one launch, each part's workgroups planned for its share
+// of the compute units.
+rpa_status run_split(const rpa::DevPlan& cp, const AttnPools& ca, const rpa::DevPlan& op,
+                     const AttnPools& oa, const void* q, const void* k_cache, const void* k_new,
+                     void* o, float* lse, hipStream_t st) {
+  hipError_t e;
+  for (const bool own : {false, true}) {
+    const rpa::DevPlan& p = own ? op : cp;
+    const AttnPools& a = own ? oa : ca;
+    const void* kc = own ? k_new : k_cache;
+    if (p.n_items[rpa::KC_GENERIC] > 0) {
+      e = timed("generic", st, [&] {
+        return rpa::launch_generic(p, q, kc, a.vc, a.k_st, a.v_st, o, lse, st);
+      });
+      if (e != hipSuccess) return hip_fail(e, "generic attention launch");
+    }
+    if (p.n_items[rpa::KC_DECODE] > 0) {
+      e = timed("decode", st, [&] {
+        return rpa::launch_decode(p, q, kc, a.vc, a.k_st, a.v_st, o, lse, st);
+      });
+      if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+    }
+  }
+  const bool pc = cp.n_items[rpa::KC_PREFILL] > 0, po = op.n_items[rpa::KC_PREFILL] > 0;
+  if (pc || po) {
+    e = timed("prefill", st, [&] {
+      if (pc && po)
+        return rpa::launch_prefill2(cp, k_cache, ca.vc, ca.k_st, ca.v_st, op, k_new, oa.vc,
+                                    oa.k_st, oa.v_st, q, o, lse, st);
+      const rpa::DevPlan& p = pc ? cp : op;
+      const AttnPools& a = pc ? ca : oa;
+      return rpa::launch_prefill(p, q, pc ? k_cache : k_new, a.vc, a.k_st, a.v_st, o, lse, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  }
+  if (cp.n_merge_rows > 0) {
+    e = timed("merge", st, [&] { return rpa::launch_merge_rows(cp, o, lse, st); });
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return RPA_OK;
@@ -430,6 +494,7 @@ RPA_EXPORT rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q,
                                           const rpa_cache_strides* vs, void* o, float* lse,
                                           void* stream) {
   return guarded([&] {
+    if (plan && plan->own_part) return fail(RPA_ERR_INVALID_ARG, kSplitPlanMsg);
     rpa_status s = check_uploaded(plan);
     if (s != RPA_OK) return s;
     if (plan->total_q == 0) return RPA_OK;  // no query rows: nothing to compute
@@ -441,6 +506,41 @@ RPA_EXPORT rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q,
   });
 }
 
+RPA_EXPORT rpa_status rpa_split_attention(const rpa_plan* plan, const void* q,
+                                          const void* k_new, const void* v_new,
+                                          const void* k_cache, const void* v_cache,
+                                          const rpa_cache_strides* ks,
+                                          const rpa_cache_strides* vs, void* o, float* lse,
+                                          void* stream) {
+  return guarded([&] {
+    if (plan && !plan->own_part)
+      return fail(RPA_ERR_INVALID_ARG, "not a split plan (create it with rpa_plan_create_split)");
+    rpa_status s = check_uploaded(plan);
+    if (s != RPA_OK) return s;
+    if (plan->total_q == 0) return RPA_OK;  // no query rows: nothing to compute
+    AttnPools a;
+    s = attention_args(plan, q, k_cache, v_cache, ks, vs, o, lse, &a);
+    if (s != RPA_OK) return s;
+    if (!k_new || !v_new) return fail(RPA_ERR_INVALID_ARG, "null k_new or v_new");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16))
+      return fail(RPA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+    const rpa_attn_config& c = plan->cfg;
+    // The step's own rows, token-major [total_q, num_kv_heads, d]: request
+    // r's page (id qo_indptr[r]) starts at its first row, so the page stride
+    // is one row.
+    const int64_t krow = (int64_t)c.num_kv_heads * c.head_dim_qk;
+    const int64_t vrow = (int64_t)c.num_kv_heads * c.head_dim_v;
+    AttnPools own;
+    own.k_st = rpa::Strides{krow, c.head_dim_qk, krow};
+    own.v_st = rpa::Strides{vrow, c.head_dim_v, vrow};
+    own.vc = v_new;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(plan->d_ws);
+    return run_split(dev_plan(plan, ws), a, dev_plan(plan->own_part.get(), ws + plan->own_off),
+                     own, q, k_cache, k_new, o, lse, st);
+  });
+}
+
 RPA_EXPORT rpa_status rpa_batch_attention_noalloc(const rpa_plan* plan, const void* q,
                                                   const void* k_cache, const void* v_cache,
                                                   const rpa_cache_strides* ks,
@@ -448,6 +548,7 @@ RPA_EXPORT rpa_status rpa_batch_attention_noalloc(const rpa_plan* plan, const vo
                                                   float* lse, void* stream) {
   return guarded([&] {
     if (!plan) return fail(RPA_ERR_INVALID_ARG, "null plan");
+    if (plan->own_part) return fail(RPA_ERR_INVALID_ARG, kSplitPlanMsg);
     if (plan->total_q == 0) return RPA_OK;  // no query rows: nothing to compute
     AttnPools a;
     rpa_status s = attention_args(plan, q, k_cache, v_cache, ks, vs, o, lse, &a);
@@ -619,7 +720,13 @@ RPA_EXPORT rpa_status rpa_plan_debug_dump(const rpa_plan* plan, const char* name
     const int32_t* src = nullptr;
     int64_t n = 0;
     std::vector<int32_t> tmp;
-    const std::string nm(name);
+    std::string nm(name);
+    // "own:<table>" reads the own part of a split plan
+    if (nm.compare(0, 4, "own:") == 0) {
+      if (!plan->own_part) return fail(RPA_ERR_INVALID_ARG, "not a split plan: " + nm);
+      plan = plan->own_part.get();
+      nm = nm.substr(4);
+    }
     const int32_t* blob = plan->blob.data();
     if (nm == "items") {
       for (int k = 0; k < rpa::KC_COUNT; ++k)

@@ -227,12 +227,30 @@ __device__ __forceinline__ void mfma_pv(f32x16_t& d, const u32x4_t& a, const u32
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 
+// A plan and the pools its items read.
+struct PrefillPart {
+  DevPlan p;
+  const bf16_t* kc;
+  const bf16_t* vc;
+  Strides ks, vs;
+};
+
 }  // namespace
 
+// Workgroups 0 .. wgs0 - 1 run part0's workgroup lists, the rest part1's
+// (wgs0 = the grid for a single plan).
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
-                    const bf16_t* __restrict__ vc, Strides ks, Strides vs,
-                    bf16_t* __restrict__ o, float* __restrict__ lse) {
+void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
+                    const bf16_t* __restrict__ q, bf16_t* __restrict__ o,
+                    float* __restrict__ lse) {
+  const int32_t bid = (int32_t)__builtin_amdgcn_workgroup_id_x();
+  const bool second = bid >= wgs0;
+  const PrefillPart& pt = second ? part1 : part0;
+  const DevPlan& p = pt.p;
+  const bf16_t* __restrict__ kc = pt.kc;
+  const bf16_t* __restrict__ vc = pt.vc;
+  const Strides ks = pt.ks, vs = pt.vs;
+  const int32_t wg = bid - (second ? wgs0 : 0);
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots][kSlotBytes];
   __shared__ int32_t restart;  // set when a step moved a row's reference max
   const int tid = threadIdx.x;
@@ -269,8 +287,8 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
   const uint32_t xk = 16u * (uint32_t)(p16 ^ l4);  // K chunk of instruction 0 (^ 64 i)
   const uint32_t dv_off = (uint32_t)l4 * vtok + 16u * (uint32_t)(p16 ^ (4 * l4));
 
-  const int32_t wb0 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][blockIdx.x]);
-  const int32_t wb1 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][blockIdx.x + 1]);
+  const int32_t wb0 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][wg]);
+  const int32_t wb1 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][wg + 1]);
   // Zero the ring once (while the item list loads): the PV products of an
   // item's first step multiply a zero P by whatever the slot of the tile
   // before it holds, and key rows past an item keep an older tile's values;
@@ -771,9 +789,25 @@ void prefill_kernel(DevPlan p, const bf16_t* __restrict__ q, const bf16_t* __res
 hipError_t launch_prefill(const DevPlan& p, const void* q, const void* k_cache,
                           const void* v_cache, Strides ks, Strides vs, void* o, float* lse,
                           hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_kernel, dim3(p.n_wgs[KC_PREFILL]), dim3(64 * kWaves), 0, stream, p,
-                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_cache),
-                     static_cast<const bf16_t*>(v_cache), ks, vs, static_cast<bf16_t*>(o), lse);
+  const PrefillPart part{p, static_cast<const bf16_t*>(k_cache),
+                         static_cast<const bf16_t*>(v_cache), ks, vs};
+  hipLaunchKernelGGL(prefill_kernel, dim3(p.n_wgs[KC_PREFILL]), dim3(64 * kWaves), 0, stream,
+                     part, part, p.n_wgs[KC_PREFILL], static_cast<const bf16_t*>(q),
+                     static_cast<bf16_t*>(o), lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill2(const DevPlan& p0, const void* k0, const void* v0, Strides ks0,
+                           Strides vs0, const DevPlan& p1, const void* k1, const void* v1,
+                           Strides ks1, Strides vs1, const void* q, void* o, float* lse,
+                           hipStream_t stream) {
+  const PrefillPart a{p0, static_cast<const bf16_t*>(k0), static_cast<const bf16_t*>(v0), ks0,
+                      vs0};
+  const PrefillPart b{p1, static_cast<const bf16_t*>(k1), static_cast<const bf16_t*>(v1), ks1,
+                      vs1};
+  const int32_t w0 = p0.n_wgs[KC_PREFILL], w1 = p1.n_wgs[KC_PREFILL];
+  hipLaunchKernelGGL(prefill_kernel, dim3(w0 + w1), dim3(64 * kWaves), 0, stream, a, b, w0,
+                     static_cast<const bf16_t*>(q), static_cast<bf16_t*>(o), lse);
   return hipGetLastError();
 }
 

@@ -29,6 +29,14 @@ hipError_t launch_prefill(const DevPlan& p, const void* q, const void* k_cache,
                           const void* v_cache, Strides ks, Strides vs, void* o, float* lse,
                           hipStream_t stream);
 
+// One prefill launch over the items of two plans (the two parts of a split
+// execution), each with its own pools: workgroups 0 .. p0.n_wgs - 1 run p0's
+// lists, the next p1.n_wgs run p1's.
+hipError_t launch_prefill2(const DevPlan& p0, const void* k0, const void* v0, Strides ks0,
+                           Strides vs0, const DevPlan& p1, const void* k1, const void* v1,
+                           Strides ks1, Strides vs1, const void* q, void* o, float* lse,
+                           hipStream_t stream);
+
 hipError_t launch_mla(const DevPlan& p, const void* q, const void* kv_cache, Strides ks, void* o,
                       float* lse, hipStream_t stream);
 

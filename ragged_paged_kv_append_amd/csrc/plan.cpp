@@ -130,11 +130,17 @@ bool pack_latent_pairs(std::vector<int32_t>& items, const std::vector<int64_t>& 
   return true;
 }
 
-}  // namespace
-
-rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
-                      const int32_t* tree_indptr, const uint32_t* tree_words, int32_t num_cus,
-                      rpa_plan* plan, std::string* err) {
+// Plans one batch.  A part plan (one half of the split execution) skips two
+// checks that belong to the whole step: the page-size bound (the step's own
+// rows form one page per request, of 2^30 tokens) and the check of the pages
+// the append writes (the whole step has been checked for those).
+// prefill_cus (> 0) replaces num_cus for the prefill class only: the
+// compute units that class's workgroups get in a launch shared with another
+// plan's.
+rpa_status build_plan_impl(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                           const int32_t* tree_indptr, const uint32_t* tree_words,
+                           int32_t num_cus, bool part, int32_t prefill_cus, rpa_plan* plan,
+                           std::string* err) {
   if (!cfg || !batch || !plan) {
     *err = "null cfg, batch or plan pointer";
     return RPA_ERR_INVALID_ARG;
@@ -169,7 +175,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
     *err = "the 576/512 latent form has exactly one KV head";
     return RPA_ERR_UNSUPPORTED;
   }
-  if (!is_pow2(c.page_size) || c.page_size > 256) {
+  if (!is_pow2(c.page_size) || (c.page_size > 256 && !part)) {
     *err = "page_size must be a power of two in [1, 256]";
     return RPA_ERR_UNSUPPORTED;
   }
@@ -279,7 +285,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
   }
 
   // A page the append writes must be referenced exactly once in the batch.
-  if (B > 0) {
+  if (B > 0 && !part) {
     std::vector<uint8_t> refs((size_t)batch->num_pages, 0);
     for (int32_t r = 0; r < B; ++r) {
       const int64_t need = ceil_div(kvl[r], P);
@@ -324,6 +330,9 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
 
   // ---- split of kv ranges into pieces ----------------------------------------
   const int64_t cus = num_cus > 0 ? num_cus : 256;
+  auto cus_of = [&](int k) -> int64_t {
+    return (k == KC_PREFILL && prefill_cus > 0) ? prefill_cus : cus;
+  };
   // Streaming classes (generic, decode): pieces sized so the whole batch makes
   // about 8 items per compute unit.  Tile classes (prefill, latent): pieces
   // sized so that one piece of a full row tile carries about the average load
@@ -352,7 +361,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
                                             KEY_ALIGN));
   int64_t tile_piece[KC_COUNT] = {0, 0, 0, 0};
   for (int k : {(int)KC_PREFILL, (int)KC_MLA}) {
-    const int64_t slots = wgs_per_cu(k) * cus;
+    const int64_t slots = wgs_per_cu(k) * cus_of(k);
     tile_piece[k] = std::max<int64_t>(
         4 * KEY_ALIGN, round_up(ceil_div(std::max<int64_t>(tile_work[k], 1),
                                          slots * rows_per_item(k, 0)), KEY_ALIGN));
@@ -558,7 +567,7 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
     }
     if (k == KC_MLA && pack_latent_pairs(items[k], cost[k], wgs_per_cu(k) * cus, &wg_indptr[k]))
       continue;
-    const int64_t slots = std::min<int64_t>(m, wgs_per_cu(k) * cus);
+    const int64_t slots = std::min<int64_t>(m, wgs_per_cu(k) * cus_of(k));
     std::vector<int64_t> load(slots, 0);
     std::vector<std::vector<int64_t>> lists(slots);
     // costs are already sorted in decreasing order
@@ -736,6 +745,221 @@ rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
       plan->part_o_off + (size_t)round_up(partial_rows * c.num_qo_heads * c.head_dim_v *
                                               (c.dtype == RPA_DTYPE_BF16 ? 2 : 4), 256);
   plan->ws_bytes = plan->part_lse_off + (size_t)round_up(partial_rows * c.num_qo_heads * 4, 256);
+  return RPA_OK;
+}
+
+// Appends a table to a plan blob, 16-byte aligned; returns its word offset.
+int64_t push_table(std::vector<int32_t>& blob, const std::vector<int32_t>& t) {
+  const int64_t off = (int64_t)blob.size();
+  blob.insert(blob.end(), t.begin(), t.end());
+  while (blob.size() % 4) blob.push_back(0);
+  return off;
+}
+
+// Work of the busiest prefill workgroup of a plan: per item its (row,
+// visible key) pairs, rows rounded up to the 32-row blocks the kernel
+// computes, plus a fixed cost of 256 keys per item.
+int64_t prefill_busiest(const rpa_plan& pl, bool causal) {
+  if (pl.n_items[KC_PREFILL] == 0) return 0;
+  const int32_t* blob = pl.blob.data();
+  const int32_t* items = blob + pl.off_items[KC_PREFILL];
+  const int32_t* wg = blob + pl.off_wg[KC_PREFILL];
+  const int32_t* qo = blob + pl.off_qo_indptr;
+  const int32_t* kvl = blob + pl.off_kv_len;
+  int64_t worst = 0;
+  for (int32_t b = 0; b < pl.n_wgs[KC_PREFILL]; ++b) {
+    int64_t load = 0;
+    for (int32_t j = wg[b]; j < wg[b + 1]; ++j) {
+      const int32_t* it = items + (int64_t)j * IT_WORDS;
+      const int32_t r = it[IT_REQ];
+      const int64_t cached = (int64_t)kvl[r] - (qo[r + 1] - qo[r]);
+      const int64_t kend = causal ? std::min<int64_t>(it[IT_K1], cached + (it[IT_ROW1] - 1) / pl.group + 1)
+                                  : it[IT_K1];
+      load += (std::max<int64_t>(kend - it[IT_K0], 0) + 256) * round_up(it[IT_ROW1] - it[IT_ROW0], 32);
+    }
+    worst = std::max(worst, load);
+  }
+  return worst;
+}
+
+}  // namespace
+
+rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                      const int32_t* tree_indptr, const uint32_t* tree_words, int32_t num_cus,
+                      rpa_plan* plan, std::string* err) {
+  return build_plan_impl(cfg, batch, tree_indptr, tree_words, num_cus, false, 0, plan, err);
+}
+
+rpa_status build_split_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                            int32_t num_cus, rpa_plan* plan, std::string* err) {
+  // The whole step, planned as one batch: every check of lengths and pages,
+  // and the append map, which the split plan keeps.
+  rpa_plan whole;
+  rpa_status s = build_plan(cfg, batch, nullptr, nullptr, num_cus, &whole, err);
+  if (s != RPA_OK) return s;
+  const rpa_attn_config c = *cfg;
+  if (!c.causal) {
+    *err = "split execution is defined for causal attention (causal must be 1)";
+    return RPA_ERR_INVALID_ARG;
+  }
+  if (c.head_dim_qk == 576) {
+    *err = "split execution of the shared latent form is not supported";
+    return RPA_ERR_UNSUPPORTED;
+  }
+  const int32_t B = batch->batch_size;
+  const int32_t* qo = batch->qo_indptr;
+  const int64_t total_q = B > 0 ? qo[B] : 0;
+
+  // Cache part: every new token sees all c_r cached keys of its request.
+  std::vector<int32_t> cached((size_t)B), own_len((size_t)B), own_indptr((size_t)B + 1, 0),
+      own_pages;
+  for (int32_t r = 0; r < B; ++r) {
+    const int32_t n = qo[r + 1] - qo[r];
+    cached[(size_t)r] = batch->kv_len[r] - n;
+    own_len[(size_t)r] = n;
+    // Own part: the request's n_r new rows, token-major from row qo[r] of
+    // the step's K/V buffers, as one page whose id is that row.
+    if (n > 0) own_pages.push_back(qo[r]);
+    own_indptr[(size_t)r + 1] = (int32_t)own_pages.size();
+  }
+  if (own_pages.empty()) own_pages.push_back(0);
+  // The prefill-class items of both parts run in one launch, so the compute
+  // units are shared between them, each part's prefill items balanced over
+  // its share.  The other classes run part after part, each over every
+  // compute unit.  The share starts from the parts' (row, visible key) pairs;
+  // a few larger own shares are planned too and the one whose busiest
+  // workgroup has the least work is kept: an item's fixed cost (its Q load,
+  // first tiles and output stores take about as long as four 64-key steps)
+  // weighs most on the own part, whose items are short.
+  double w_cache = 0.0, w_own = 0.0;
+  const int32_t G = c.num_qo_heads / c.num_kv_heads;
+  for (int32_t r = 0; r < B; ++r) {
+    const double n = (double)own_len[(size_t)r];
+    if (n * G <= DEC_MAX_ROWS) continue;
+    w_cache += n * (double)cached[(size_t)r];
+    w_own += n * (n + 1.0) / 2.0;
+  }
+  const int32_t cus = num_cus > 0 ? num_cus : 256;
+  rpa_attn_config cc = c;
+  cc.causal = 0;
+  const rpa_batch_desc cb{B, qo, cached.data(), batch->kv_page_indptr, batch->kv_page_indices,
+                          batch->num_pages};
+  rpa_attn_config oc = c;
+  oc.page_size = 1 << 30;
+  const rpa_batch_desc ob{B, qo, own_len.data(), own_indptr.data(), own_pages.data(),
+                          (int32_t)std::max<int64_t>(total_q, 1)};
+  std::unique_ptr<rpa_plan> own(new rpa_plan());
+  if (w_cache > 0.0 && w_own > 0.0 && cus > 1) {
+    const int32_t c0 = std::min(cus - 1, std::max<int32_t>(
+        1, (int32_t)std::lround((double)cus * w_own / (w_own + w_cache))));
+    int64_t best = -1;
+    int32_t best_own = c0;
+    for (const double f : {1.0, 1.5, 2.0, 3.0}) {
+      const int32_t co = std::min(cus - 1, std::max<int32_t>(1, (int32_t)std::lround(c0 * f)));
+      if (f > 1.0 && co == best_own) continue;
+      rpa_plan pc, po;
+      s = build_plan_impl(&cc, &cb, nullptr, nullptr, cus, true, cus - co, &pc, err);
+      if (s != RPA_OK) return s;
+      s = build_plan_impl(&oc, &ob, nullptr, nullptr, cus, true, co, &po, err);
+      if (s != RPA_OK) return s;
+      const int64_t span = std::max(prefill_busiest(pc, false), prefill_busiest(po, true));
+      if (best < 0 || span < best) {
+        best = span;
+        best_own = co;
+      }
+    }
+    s = build_plan_impl(&cc, &cb, nullptr, nullptr, cus, true, cus - best_own, plan, err);
+    if (s != RPA_OK) return s;
+    s = build_plan_impl(&oc, &ob, nullptr, nullptr, cus, true, best_own, own.get(), err);
+  } else {
+    s = build_plan_impl(&cc, &cb, nullptr, nullptr, cus, true, cus, plan, err);
+    if (s != RPA_OK) return s;
+    s = build_plan_impl(&oc, &ob, nullptr, nullptr, cus, true, cus, own.get(), err);
+  }
+  if (s != RPA_OK) return s;
+
+  // Pieces of request r: the cache part's S_c pieces (keys 0 .. c_r - 1),
+  // then the own part's S_o pieces (the new keys), numbered after them, all
+  // in one block of partial rows.  A row sees every cache piece and a prefix
+  // of the own pieces, so its live pieces are again a prefix.
+  int32_t* csplit = plan->blob.data() + plan->off_split;
+  int32_t* osplit = own->blob.data() + own->off_split;
+  std::vector<int32_t> own_live((size_t)total_q, 1);
+  for (int32_t x = 0; x < own->n_merge_rows; ++x) {
+    const int32_t i = own->blob[(size_t)(own->off_merge + x)];
+    own_live[(size_t)i] = own->blob[(size_t)(own->off_merge_info + 4 * x + 2)];
+  }
+  std::vector<int32_t> shift((size_t)B, 0), merge_rows, merge_info;
+  int64_t partial_rows = 0;
+  for (int32_t r = 0; r < B; ++r) {
+    const int32_t n = qo[r + 1] - qo[r];
+    int32_t* cs = csplit + (size_t)r * SP_WORDS;
+    int32_t* os = osplit + (size_t)r * SP_WORDS;
+    const int32_t sc = (n > 0 && cached[(size_t)r] > 0) ? cs[SP_COUNT] : 0;
+    const int32_t so = n > 0 ? os[SP_COUNT] : 0;
+    if (sc + so <= 1) {
+      // nothing to merge: the own part (if any) writes the output
+      cs[SP_COUNT] = os[SP_COUNT] = 1;
+      cs[SP_BASE] = os[SP_BASE] = -1;
+      continue;
+    }
+    const int64_t base = partial_rows;
+    partial_rows += (int64_t)(sc + so) * n;
+    for (int32_t* x : {cs, os}) {
+      x[SP_COUNT] = sc + so;
+      x[SP_CHUNK] = 0;
+      x[SP_BASE] = (int32_t)base;
+    }
+    shift[(size_t)r] = sc;
+    for (int32_t t = 0; t < n; ++t) {
+      const int32_t i = qo[r] + t;
+      merge_rows.push_back(i);
+      merge_info.push_back((int32_t)base + t);
+      merge_info.push_back(n);
+      merge_info.push_back(sc + (so > 1 ? own_live[(size_t)i] : 1));
+      merge_info.push_back(0);
+    }
+  }
+  if (partial_rows > INT32_MAX / 2) {
+    *err = "batch too large: partial rows overflow";
+    return RPA_ERR_INVALID_ARG;
+  }
+  for (int k = 0; k < KC_COUNT; ++k) {
+    int32_t* it = own->blob.data() + own->off_items[k];
+    for (int32_t j = 0; j < own->n_items[k]; ++j, it += IT_WORDS) it[IT_SPLIT] += shift[(size_t)it[IT_REQ]];
+  }
+  // The cache part's plan carries the merge of both parts and the whole
+  // step's append map; the own part merges nothing.
+  std::copy(whole.blob.begin() + whole.off_append,
+            whole.blob.begin() + whole.off_append + total_q * 2,
+            plan->blob.begin() + plan->off_append);
+  plan->can_append = whole.can_append;
+  plan->blob.resize((size_t)plan->off_merge);
+  plan->off_merge = push_table(plan->blob, merge_rows);
+  plan->off_merge_info = push_table(plan->blob, merge_info);
+  plan->n_merge_rows = (int32_t)merge_rows.size();
+  own->blob.resize((size_t)own->off_merge);
+  own->off_merge = own->off_merge_info = (int64_t)own->blob.size();
+  own->n_merge_rows = 0;
+
+  // Workspace: the cache part's metadata, the own part's, then the shared
+  // partial rows.
+  const int64_t c_words = round_up((int64_t)plan->blob.size(), 64);
+  plan->blob.resize((size_t)c_words, 0);
+  plan->own_off = (size_t)c_words * 4;
+  plan->blob.insert(plan->blob.end(), own->blob.begin(), own->blob.end());
+  plan->meta_bytes = (size_t)round_up((int64_t)plan->blob.size() * 4, 256);
+  plan->partial_rows = own->partial_rows = partial_rows;
+  plan->part_o_off = plan->meta_bytes;
+  plan->part_lse_off =
+      plan->part_o_off + (size_t)round_up(partial_rows * c.num_qo_heads * c.head_dim_v *
+                                              (c.dtype == RPA_DTYPE_BF16 ? 2 : 4), 256);
+  plan->ws_bytes = plan->part_lse_off + (size_t)round_up(partial_rows * c.num_qo_heads * 4, 256);
+  own->part_o_off = plan->part_o_off - plan->own_off;
+  own->part_lse_off = plan->part_lse_off - plan->own_off;
+  own->meta_bytes = plan->meta_bytes - plan->own_off;
+  own->ws_bytes = plan->ws_bytes - plan->own_off;
+  plan->own_part = std::move(own);
   return RPA_OK;
 }
 

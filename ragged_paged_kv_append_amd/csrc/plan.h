@@ -1,6 +1,7 @@
 // Host-side plan object and planner entry point (pure C++, no HIP calls).
 #pragma once
 
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -33,6 +34,15 @@ struct rpa_plan {
   size_t part_lse_off = 0;
   size_t ws_bytes = 0;
 
+  // Split execution ("Chunked prefill", section "correctness"): this plan is
+  // the cache part (cross attention over the pages, kv_len = c_r, no causal
+  // mask) and carries the merge of both parts; own_part is the causal
+  // attention over the step's own rows, read token-major from its K/V
+  // buffers.  Its metadata follows this plan's in the workspace, at byte
+  // own_off; both parts write the same partial rows.  Null for other plans.
+  std::unique_ptr<rpa_plan> own_part;
+  size_t own_off = 0;
+
   // Upload state (set by rpa_plan_upload).
   void* d_ws = nullptr;
   void* staging = nullptr;   // pinned host buffer, meta_bytes long
@@ -49,5 +59,11 @@ namespace rpa {
 rpa_status build_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
                       const int32_t* tree_indptr, const uint32_t* tree_words, int32_t num_cus,
                       rpa_plan* plan, std::string* err);
+
+// Plans the split execution of one causal step (see own_part above).  The
+// whole step is checked as by build_plan; the result is the cache part with
+// its own_part set.
+rpa_status build_split_plan(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
+                            int32_t num_cus, rpa_plan* plan, std::string* err);
 
 }  // namespace rpa

@@ -114,12 +114,14 @@ def max_err(got: torch.Tensor, want: np.ndarray) -> float:
 
 
 def full_parity(spec, meta, tensors, label, tree_masks=None, num_cus=0, group_bytes=1 << 29,
-                log=print):
+                log=print, split=False):
     """Runs the batch through the library once (the launch configuration the
     benchmark times), then checks the pools bit-exactly over the whole pool
     and O / LSE of every request against the oracle.  The oracle runs over
     groups of requests of at most `group_bytes` of float64 keys, so host
-    memory stays bounded at any batch size.  Returns (max|dO|, max|dLSE|)."""
+    memory stays bounded at any batch size.  With `split`, the step runs in
+    split form (rpa_split_attention before the append, which then must not
+    matter).  Returns (max|dO|, max|dLSE|)."""
     q_raw, kn_raw = raw(tensors["q"]), raw(tensors["k_new"])
     vn_raw = None if tensors["v_new"] is None else raw(tensors["v_new"])
     kp_raw = raw(tensors["k_pool"])
@@ -127,10 +129,18 @@ def full_parity(spec, meta, tensors, label, tree_masks=None, num_cus=0, group_by
     b = batch_of(meta)
     kp2, vp2 = oracle.append(kp_raw, vp_raw, kn_raw, vn_raw, b)
     cfg = config_of(spec)
-    plan = rpa.Plan(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices,
-                    meta.num_pages, num_cus=num_cus, tree_masks=tree_masks)
-    plan.append(tensors["k_new"], tensors["v_new"], tensors["k_pool"], tensors["v_pool"])
-    o, lse = plan.attention(tensors["q"], tensors["k_pool"], tensors["v_pool"])
+    if split:
+        plan = rpa.SplitChunkAttention(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr,
+                                       meta.kv_page_indices, meta.num_pages, num_cus=num_cus)
+        o, lse = plan.run(tensors["q"], tensors["k_new"], tensors["v_new"], tensors["k_pool"],
+                          tensors["v_pool"])
+        plan.append(tensors["k_new"], tensors["v_new"], tensors["k_pool"], tensors["v_pool"])
+    else:
+        plan = rpa.Plan(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr,
+                        meta.kv_page_indices, meta.num_pages, num_cus=num_cus,
+                        tree_masks=tree_masks)
+        plan.append(tensors["k_new"], tensors["v_new"], tensors["k_pool"], tensors["v_pool"])
+        o, lse = plan.attention(tensors["q"], tensors["k_pool"], tensors["v_pool"])
     torch.cuda.synchronize()
     log(f"[{label}] summary={plan.debug('summary').tolist()}")
     assert np.array_equal(raw(tensors["k_pool"]), kp2), "K pool differs from the oracle"

@@ -6,6 +6,7 @@ their argument-validation paths, which return before any HIP call.
 """
 
 import ctypes
+import math
 import os
 import re
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert rpa.rpa_abi_version() == 2
+    assert rpa.rpa_abi_version() == 3
     for code, name in [(0, "RPA_OK"), (-1, "RPA_ERR_INVALID_ARG"), (-2, "RPA_ERR_UNSUPPORTED"),
                        (-3, "RPA_ERR_WORKSPACE_TOO_SMALL"), (-4, "RPA_ERR_PAGE_OOB"),
                        (-5, "RPA_ERR_DUPLICATE_WRITE_PAGE"), (-6, "RPA_ERR_HIP"),
@@ -538,3 +539,138 @@ def test_noalloc_attention_rejects_plans_beyond_the_static_scratch(L):
     # argument checks come first, as in rpa_batch_attention
     expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_batch_attention_noalloc, plan, None, fake, fake, st,
            st, fake, None, 0)
+
+
+def split_plan_for(meta, cfg, num_cus=0):
+    return rpa.rpa_plan_create_split(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr,
+                                     meta.kv_page_indices, meta.num_pages, num_cus)
+
+
+SPLIT_BATCHES = [
+    # hq, hkv, d, P, qo lens, kv lens
+    (32, 32, 128, 16, [1, 1, 512, 40], [3000, 17, 1536, 40]),
+    (8, 1, 128, 16, [512], [8192]),
+    (8, 1, 128, 16, [512, 4, 3], [2048, 700, 3]),
+    (16, 2, 128, 64, [129, 0, 33], [1000, 64, 97]),
+    (4, 2, 64, 16, [1, 16, 5], [37, 36, 5]),
+    (32, 8, 128, 16, [4, 1, 4096], [9000, 1, 4096 + 700]),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_BATCHES, ids=[f"b{i}" for i in range(len(SPLIT_BATCHES))])
+def test_split_plan_covers_cache_and_own_keys(L, case):
+    """Split execution ("Chunked prefill", section "correctness"): the cache
+    part covers each row's c_r cached keys once, the own part its new keys
+    0 .. t once, their pieces share one block of partial rows (cache pieces
+    first), and the merge reads exactly the pieces that hold a visible key."""
+    hq, hkv, d, P, qo, kv = case
+    dtype = "f32" if d == 64 else "bf16"
+    cfg = rpa.make_config(hq, hkv, d, d, P, dtype, True, 1.0 / math.sqrt(d))
+    meta = workloads.make_meta(qo, kv, P, 11 + sum(kv))
+    plan = split_plan_for(meta, cfg)
+    G = hq // hkv
+    B = meta.batch_size
+    batch = oracle.Batch(meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices, P)
+    parts = {"cache": rpa.rpa_plan_debug_dump(plan, "items").reshape(-1, 8),
+             "own": rpa.rpa_plan_debug_dump(plan, "own:items").reshape(-1, 8)}
+    sp_c = rpa.rpa_plan_debug_dump(plan, "splits").reshape(-1, 3)
+    sp_o = rpa.rpa_plan_debug_dump(plan, "own:splits").reshape(-1, 3)
+    assert len(rpa.rpa_plan_debug_dump(plan, "own:merge_rows")) == 0
+    cover = {"cache": {}, "own": {}}
+    pieces = {}  # (r, s) -> key range and part
+    for part, items in parts.items():
+        for r_, g, row0, row1, k0, k1, s, kc in items.tolist():
+            n = batch.qo_len(r_)
+            lim = int(meta.kv_len[r_]) - n if part == "cache" else n
+            assert 0 <= k0 < k1 <= lim and 0 <= row0 < row1 <= n * G
+            assert pieces.setdefault((r_, s), (part, k0, k1)) == (part, k0, k1)
+            for row in range(row0, row1):
+                cover[part].setdefault((r_, g, row), []).append((k0, k1))
+    mrows = rpa.rpa_plan_debug_dump(plan, "merge_rows").tolist()
+    minfo = rpa.rpa_plan_debug_dump(plan, "merge_info").reshape(-1, 4)
+    info_of = {i: tuple(minfo[x].tolist()) for x, i in enumerate(mrows)}
+    assert len(info_of) == len(mrows)
+    app = rpa.rpa_plan_debug_dump(plan, "append").reshape(-1, 2)
+    expected_rows = 0
+    for r_ in range(B):
+        n = batch.qo_len(r_)
+        c = int(meta.kv_len[r_]) - n
+        S = int(sp_c[r_][0])
+        if n > 0:
+            assert (sp_c[r_][0], sp_c[r_][2]) == (sp_o[r_][0], sp_o[r_][2])
+        n_cache = len({s for (rr, s), v in pieces.items() if rr == r_ and v[0] == "cache"})
+        n_own = len({s for (rr, s), v in pieces.items() if rr == r_ and v[0] == "own"})
+        if n == 0:
+            assert n_cache == n_own == 0
+            continue
+        assert n_cache == (0 if c == 0 else n_cache) and n_own >= 1
+        assert S == max(1, n_cache + n_own)
+        # cache pieces are 0 .. S_c - 1, own pieces follow
+        for (rr, s), v in pieces.items():
+            if rr == r_:
+                assert (s < n_cache) == (v[0] == "cache")
+        for g in range(hkv):
+            for row in range(n * G):
+                t = row // G
+                cr = sorted(cover["cache"].get((r_, g, row), []))
+                if c > 0:
+                    assert cr[0][0] == 0 and cr[-1][1] == c and len(cr) == n_cache
+                    assert all(a[1] == b[0] for a, b in zip(cr, cr[1:]))
+                else:
+                    assert not cr
+                orng = sorted(cover["own"].get((r_, g, row), []))
+                assert orng[0][0] == 0 and orng[-1][1] > t
+                assert all(a[1] == b[0] for a, b in zip(orng, orng[1:]))
+                live_own = sum(1 for (rr, s), v in pieces.items()
+                               if rr == r_ and v[0] == "own" and v[1] <= t)
+                assert len(orng) == live_own
+                i = int(meta.qo_indptr[r_]) + t
+                if S > 1:
+                    assert info_of[i] == (int(sp_c[r_][2]) + t, n, n_cache + live_own, 0)
+                else:
+                    assert i not in info_of
+        for t in range(n):
+            assert tuple(app[int(meta.qo_indptr[r_]) + t]) == oracle.slot_of(batch, r_, c + t)
+        if S > 1:
+            expected_rows += S * n
+    summary = rpa.rpa_plan_debug_dump(plan, "summary")
+    assert summary[3] == expected_rows
+
+
+def test_split_plan_validation(L):
+    cfg = rpa.make_config(8, 2, 128, 128, 16, "bf16", True, 0.1)
+    meta = workloads.make_meta([4, 1], [20, 9], 16, 3)
+    plan = split_plan_for(meta, cfg)
+    fused = plan_for(meta, cfg)
+    st = rpa.rpa_cache_strides(2 * 16 * 128, 16 * 128, 128)
+    fake = 1 << 40  # never dereferenced: validation fails first
+    # each plan kind runs only through its own entry point
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_batch_attention, plan, fake, fake, fake, st, st, fake,
+           None, 0)
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_batch_attention_noalloc, plan, fake, fake, fake, st,
+           st, fake, None, 0)
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_split_attention, fused, fake, fake, fake, fake, fake,
+           st, st, fake, None, 0)
+    expect(rpa.RPA_ERR_NOT_UPLOADED, rpa.rpa_split_attention, plan, fake, fake, fake, fake, fake,
+           st, st, fake, None, 0)
+    expect(rpa.RPA_ERR_NOT_UPLOADED, rpa.rpa_kv_append, plan, fake, fake, fake, fake, st, st, 0)
+    # the whole step is checked as by rpa_plan_create
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_plan_create_split,
+           rpa.make_config(8, 2, 128, 128, 16, "bf16", False, 0.1), meta.qo_indptr, meta.kv_len,
+           meta.kv_page_indptr, meta.kv_page_indices, meta.num_pages)
+    expect(rpa.RPA_ERR_UNSUPPORTED, rpa.rpa_plan_create_split,
+           rpa.make_config(16, 1, 576, 512, 16, "bf16", True, 0.1), meta.qo_indptr, meta.kv_len,
+           meta.kv_page_indptr, meta.kv_page_indices, meta.num_pages)
+    expect(rpa.RPA_ERR_PAGE_OOB, rpa.rpa_plan_create_split, cfg, meta.qo_indptr, meta.kv_len,
+           meta.kv_page_indptr, meta.kv_page_indices, 1)
+    expect(rpa.RPA_ERR_INVALID_ARG, rpa.rpa_plan_create_split, cfg, [0, 4, 5], [3, 9],
+           meta.kv_page_indptr, meta.kv_page_indices, meta.num_pages)
+    with pytest.raises(rpa.RpaError):
+        rpa.rpa_plan_debug_dump(fused, "own:items")
+    # two requests may share a cached prefix page: only pages the append
+    # writes must be unshared
+    shared = split_plan_for(workloads.Meta(np.array([0, 2, 4], np.int32),
+                                           np.array([18, 18], np.int32),
+                                           np.array([0, 2, 4], np.int32),
+                                           np.array([0, 1, 0, 2], np.int32), 3, 16), cfg)
+    assert rpa.rpa_plan_workspace_size(shared) > 0

@@ -16,7 +16,8 @@ import torch
 import oracle
 import workloads
 import ragged_paged_kv_append_amd as rpa
-from tests.gpu_support import TOL, batch_of, config_of, f64, max_err, poison_tail_slots, raw
+from tests.gpu_support import (TOL, batch_of, config_of, f64, full_parity, max_err,
+                               poison_tail_slots, raw)
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +159,41 @@ def test_split_execution_chunked_prompt_equals_one_shot():
     eo, el = max_err(o, o_ref), max_err(lse, lse_ref)
     log(f"[chunked_gqa split] max|dO|={eo:.3g} max|dLSE|={el:.3g}")
     assert eo <= 2e-2 and el <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["mixed_7b", "decode_verify_gqa"])
+def test_split_execution_full_workload(name):
+    """Every request of a full benchmark batch in split form (decodes, the
+    prefill chunk, verifications), element by element against the oracle's
+    attention after the append; the split attention runs before the append."""
+    spec, meta, tensors = workloads.workload(name, device="cuda")
+    new_slots_nan(meta, tensors)
+    log(f"split full {name}")
+    full_parity(spec, meta, tensors, f"split {name}", log=log, split=True)
+
+
+def test_split_execution_plan_reuse_and_append_order():
+    """One split plan, called twice with different inputs, the append run
+    before the first call and after the second: both match the oracle."""
+    spec = spec_of("bf16", 16, 4, 128, 16, 4242)
+    qo, kv = [300, 1, 4, 64], [2000, 513, 37, 64]
+    meta = workloads.make_meta(qo, kv, 16, 4242)
+    split = rpa.SplitChunkAttention(config_of(spec), meta.qo_indptr, meta.kv_len,
+                                    meta.kv_page_indptr, meta.kv_page_indices, meta.num_pages)
+    b = batch_of(meta)
+    for it, seed in enumerate((4242, 4243)):
+        t = workloads.make_tensors(spec, meta, seed, device="cuda")
+        host = {k: raw(v) for k, v in t.items()}
+        if it == 0:
+            split.append(t["k_new"], t["v_new"], t["k_pool"], t["v_pool"])
+        o, lse = split.run(t["q"], t["k_new"], t["v_new"], t["k_pool"], t["v_pool"])
+        if it == 1:
+            split.append(t["k_new"], t["v_new"], t["k_pool"], t["v_pool"])
+        torch.cuda.synchronize()
+        kp2, vp2 = oracle.append(host["k_pool"], host["v_pool"], host["k_new"], host["v_new"], b)
+        assert np.array_equal(raw(t["k_pool"]), kp2) and np.array_equal(raw(t["v_pool"]), vp2)
+        o_ref, lse_ref = oracle.attend(f64(host["q"]), f64(kp2), f64(vp2), b, 16, 4,
+                                       spec.sm_scale)
+        eo, el = max_err(o, o_ref), max_err(lse, lse_ref)
+        log(f"  call {it}: max|dO|={eo:.3g} max|dLSE|={el:.3g}")
+        assert eo <= TOL["bf16"] and el <= TOL["bf16"]
