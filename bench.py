@@ -2,6 +2,7 @@
 """Benchmark of ragged paged attention with KV append on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --workload chunked_gqa --one-shot   # the 8192-token prompt in one step
     python bench.py --copy-calibration      # 1 GiB device copy, for HBM counter scaling
 
 A step is one pass of the hot path over one batch: KV append of the batch's
@@ -512,6 +513,9 @@ def main():
     ap.add_argument("--no-parts", action="store_true",
                     help="time the workload's step only (no sub-batch or variant parts), "
                          "so that a profiler's per-kernel averages cover that step alone")
+    ap.add_argument("--one-shot", action="store_true",
+                    help="chunked_gqa only: time the whole 8192-token prompt as one step "
+                         "(append, then attention) and nothing else, for profiler runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                          "kernel that FETCH_SIZE / WRITE_SIZE counter readings are scaled by)")
@@ -533,7 +537,10 @@ def main():
     torch.cuda.set_device(0)
     name = args.workload
     if name == "chunked_gqa":
-        main_chunked(args)
+        if args.one_shot:
+            main_one_shot(args)
+        else:
+            main_chunked(args)
         return
     log(f"workload {name}: generating inputs")
     spec, meta, tensors = workloads.workload(name, device="cuda")
@@ -699,6 +706,42 @@ def main():
         "parts": parts,
     }
     print(json.dumps(line), flush=True)
+
+
+def main_one_shot(args):
+    """The 8192-token GQA prompt of chunked_gqa attended in one step (one plan
+    over the whole prompt): the prefill kernel at its largest single-request
+    size.  One JSON line with the step's attention TFLOP/s."""
+    import torch
+    import workloads
+    import ragged_paged_kv_append_amd as rpa
+    spec = workloads.SPECS["chunked_gqa"]
+    L = spec.extra["prompt_len"]
+    q, k, v = workloads.make_prompt(spec, spec.seed, device="cuda")
+    meta = workloads.make_meta([L], [L], spec.page_size, spec.seed)
+    shape = (meta.num_pages, spec.num_kv_heads, spec.page_size, spec.head_dim_qk)
+    k_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    v_pool = k_pool.clone()
+    o = torch.empty((L, spec.num_qo_heads, spec.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((L, spec.num_qo_heads), dtype=torch.float32, device="cuda")
+    cfg = rpa.make_config(spec.num_qo_heads, spec.num_kv_heads, spec.head_dim_qk, spec.head_dim_v,
+                          spec.page_size, spec.dtype, spec.causal, spec.sm_scale)
+    plan = rpa.Plan(cfg, [0, L], [L], meta.kv_page_indptr, meta.kv_page_indices, meta.num_pages)
+
+    def step():
+        plan.append(k, v, k_pool, v_pool)
+        plan.attention(q, k_pool, v_pool, o=o, lse=lse)
+    log(f"workload chunked_gqa one-shot: timing {args.steps} steps after {args.warmup} warmup")
+    tm = timed_steps(step, args.steps, args.warmup)
+    w = work(spec, [L], [L])
+    kernels = tm["kernels"]
+    attn = sum(t * c for name, (t, c) in kernels.items() if name != "append")
+    pre = kernels.get("prefill", (None, 0))[0]
+    print(json.dumps({"workload": "chunked_gqa one-shot", "prompt_len": L, "flops": w["flops"],
+                      "ms_per_step": tm["median_ms"], "attention_ms": attn,
+                      "tflops": w["flops"] / (attn * 1e-3) / 1e12,
+                      "prefill_kernel_tflops": None if not pre else w["flops"] / (pre * 1e-3) / 1e12,
+                      "kernels_us": {kk: t * 1e3 for kk, (t, c) in kernels.items()}}), flush=True)
 
 
 def main_chunked(args):
