@@ -21,56 +21,54 @@ namespace rpa {
 // KV append
 // ----------------------------------------------------------------------------
 
-// One thread per 16-byte chunk of one (token, KV head) row.  K rows first,
-// then V rows.  A plain copy: the stored bits move unchanged.
+// One workgroup per new token: its page and slot are one scalar load, and its
+// threads copy the token's K rows (all KV heads, contiguous in k_new) and then
+// its V rows, 16 bytes per thread and step.  A plain copy: the stored bits
+// move unchanged.  kc_div / vc_div: 16-byte chunks per K / V row.
 template <typename T>
 __global__ __launch_bounds__(256) void append_kernel(DevPlan p, const T* __restrict__ k_new,
                                                      const T* __restrict__ v_new,
                                                      T* __restrict__ k_cache,
                                                      T* __restrict__ v_cache, Strides ks,
-                                                     Strides vs) {
+                                                     Strides vs, int32_t kc_div, int32_t vc_div) {
   constexpr int kVec = 16 / sizeof(T);
-  const int64_t k_chunks = p.head_dim_qk / kVec;
-  const int64_t v_chunks = v_new ? p.head_dim_v / kVec : 0;
-  const int64_t per_row = k_chunks + v_chunks;
-  const int64_t total = (int64_t)p.total_q * p.num_kv_heads * per_row;
-  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < total;
-       x += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = x / per_row;          // token * H_kv + head
-    const int64_t ch = x - row * per_row;
-    const int64_t i = row / p.num_kv_heads;
-    const int64_t h = row - i * p.num_kv_heads;
-    const int64_t page = p.append[2 * i];
-    const int64_t slot = p.append[2 * i + 1];
-    if (ch < k_chunks) {
-      const uint4 val =
-          *reinterpret_cast<const uint4*>(k_new + (row * p.head_dim_qk) + ch * kVec);
-      *reinterpret_cast<uint4*>(k_cache + page * ks.page + h * ks.head + slot * ks.token +
-                                ch * kVec) = val;
-    } else {
-      const int64_t cv = ch - k_chunks;
-      const uint4 val = *reinterpret_cast<const uint4*>(v_new + (row * p.head_dim_v) + cv * kVec);
-      *reinterpret_cast<uint4*>(v_cache + page * vs.page + h * vs.head + slot * vs.token +
-                                cv * kVec) = val;
-    }
+  const int64_t i = blockIdx.x;  // new token (global row)
+  const int64_t page = p.append[2 * i];
+  const int64_t slot = p.append[2 * i + 1];
+  const int32_t H = p.num_kv_heads;
+  const int32_t kn = H * kc_div;             // K chunks of the token
+  const int32_t vn = v_new ? H * vc_div : 0;  // V chunks
+  const uint4* ksrc = reinterpret_cast<const uint4*>(k_new + i * H * p.head_dim_qk);
+  for (int32_t c = threadIdx.x; c < kn; c += blockDim.x) {
+    const int32_t h = c / kc_div, ch = c - h * kc_div;
+    *reinterpret_cast<uint4*>(k_cache + page * ks.page + h * ks.head + slot * ks.token +
+                              ch * kVec) = ksrc[c];
+  }
+  if (vn == 0) return;
+  const uint4* vsrc = reinterpret_cast<const uint4*>(v_new + i * H * p.head_dim_v);
+  for (int32_t c = threadIdx.x; c < vn; c += blockDim.x) {
+    const int32_t h = c / vc_div, ch = c - h * vc_div;
+    *reinterpret_cast<uint4*>(v_cache + page * vs.page + h * vs.head + slot * vs.token +
+                              ch * kVec) = vsrc[c];
   }
 }
 
 hipError_t launch_append(const DevPlan& p, const void* k_new, const void* v_new, void* k_cache,
                          void* v_cache, Strides ks, Strides vs, hipStream_t stream) {
   const int vec = p.dtype == RPA_DTYPE_BF16 ? 8 : 4;
-  const int64_t per_row = p.head_dim_qk / vec + (v_new ? p.head_dim_v / vec : 0);
-  const int64_t total = (int64_t)p.total_q * p.num_kv_heads * per_row;
-  if (total == 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
+  if (p.total_q == 0) return hipSuccess;
+  const int32_t kc = p.head_dim_qk / vec, vc = v_new ? p.head_dim_v / vec : 1;
+  const int32_t chunks = p.num_kv_heads * (kc + (v_new ? vc : 0));
+  const int bs = chunks >= 256 ? 256 : (chunks + 63) / 64 * 64;
   if (p.dtype == RPA_DTYPE_BF16) {
-    hipLaunchKernelGGL(append_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, stream, p,
+    hipLaunchKernelGGL(append_kernel<bf16_t>, dim3((unsigned)p.total_q), dim3(bs), 0, stream, p,
                        static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new),
-                       static_cast<bf16_t*>(k_cache), static_cast<bf16_t*>(v_cache), ks, vs);
+                       static_cast<bf16_t*>(k_cache), static_cast<bf16_t*>(v_cache), ks, vs, kc,
+                       vc);
   } else {
-    hipLaunchKernelGGL(append_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, p,
+    hipLaunchKernelGGL(append_kernel<float>, dim3((unsigned)p.total_q), dim3(bs), 0, stream, p,
                        static_cast<const float*>(k_new), static_cast<const float*>(v_new),
-                       static_cast<float*>(k_cache), static_cast<float*>(v_cache), ks, vs);
+                       static_cast<float*>(k_cache), static_cast<float*>(v_cache), ks, vs, kc, vc);
   }
   return hipGetLastError();
 }

@@ -457,20 +457,10 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     // Steps whose keys start at or past this need the mask.
     const int32_t mask_kb = mask_from - kStep + 1;
 
-    // Page ids and tree-mask rows complete before the DMA (the compiler's own
-    // wait for them must not drain the DMA stream later).
-    asm volatile("" : "+v"(pid), "+v"(tm_lo[0]), "+v"(tm_hi[0]), "+v"(tm_lo[1]), "+v"(tm_hi[1]));
-    barrier();  // the previous item's waves are done with the ring
-    // Tile 0, then Q, then tile 1: the products start once tile 0 and Q are
-    // in (vector-memory loads complete in order), while tile 1 lands.
-    {
-      const DmaTile d = dma_setup(0);
-#pragma unroll
-      for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
-    }
     // Q operand of the S^T products: qf[rb][i] = Q[row 32 rb + col][16 i + 8 half .. + 8),
-    // loaded into AGPRs from inline assembly (counted with the DMA).  Rows
-    // past the item read a valid row of the request (t_of = 0): their
+    // loaded into AGPRs from inline assembly while the page ids are on their
+    // way (the previous item's last products read qf long before its stores).
+    // Rows past the item read a valid row of the request (t_of = 0): their
     // results are never stored.
     u32x4_t qf[2][8];
 #pragma unroll
@@ -481,12 +471,25 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
       for (int i = 0; i < 8; ++i)
         asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(qf[rb][i]) : "v"(qrow + 16 * i) : "memory");
     }
+    // Page ids, Q and tree-mask rows complete before the DMA (the compiler's
+    // own wait for them, which drains every vector-memory load, must not
+    // drain the DMA stream later).
+    wait_vmem<0>();
+    asm volatile("" : "+v"(pid), "+v"(tm_lo[0]), "+v"(tm_hi[0]), "+v"(tm_lo[1]), "+v"(tm_hi[1]));
+    barrier();  // the previous item's waves are done with the ring
+    // Tiles 0 and 1: the products start once tile 0 is in (vector-memory
+    // loads complete in order), while tile 1 lands.
+    {
+      const DmaTile d = dma_setup(0);
+#pragma unroll
+      for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
+    }
     {
       const DmaTile d = dma_setup(1);
 #pragma unroll
       for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
     }
-    wait_vmem<kDmaInst>();  // tile 0 and Q are in; tile 1 may still be in flight
+    wait_vmem<kDmaInst>();  // tile 0 is in; tile 1 may still be in flight
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
