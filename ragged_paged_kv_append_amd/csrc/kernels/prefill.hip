@@ -718,11 +718,15 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
 
     // A row whose scores left the window around its reference: do the item
     // over (once) with the row's largest scaled score as reference.
+    // A masked score leaves the products near kMinusBig, so its S' is near
+    // kMinusBig * scale - m: a row with no key in the item stays below half
+    // of that and is not a row that left the window.
+    const float no_key = 0.5f * kMinusBig * sc;
     bool moved = false;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const float x = max_halves(rmax[rb]);  // largest S' of the row (kMinusBig: no key)
-      const bool out = row_ok[rb] && x > 0.5f * kMinusBig && (x > kWindow || x < -kWindow);
+      const float x = max_halves(rmax[rb]);  // largest S' of the row
+      const bool out = row_ok[rb] && x > no_key - m[rb] && (x > kWindow || x < -kWindow);
       moved |= out;
       m_keep[rb] = out ? m[rb] + x : m[rb];
     }
