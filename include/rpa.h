@@ -212,9 +212,8 @@ rpa_status rpa_plan_create_tree(const rpa_attn_config* cfg, const rpa_batch_desc
 rpa_status rpa_plan_create_split(const rpa_attn_config* cfg, const rpa_batch_desc* batch,
                                  int32_t num_cus, rpa_plan** out);
 
-/* Device bytes the plan needs in its workspace: metadata plus the partial
- * outputs of split pieces (in the attention dtype, with float32 log-sum-exp
- * values).  Host only. */
+/* Device bytes the plan needs in its workspace: metadata plus the float32
+ * partial outputs and log-sum-exp values of split pieces.  Host only. */
 rpa_status rpa_plan_workspace_size(const rpa_plan* plan, size_t* bytes);
 
 /* Copy the plan's metadata into a caller-owned device workspace (256-byte
@@ -274,8 +273,8 @@ rpa_status rpa_batch_attention(const rpa_plan* plan, const void* q, const void* 
  * rows, token-major contiguous [total_q, num_kv_heads, d] (16-byte
  * aligned), the buffers rpa_kv_append copies from; k_cache / v_cache and
  * ks / vs the pools, of which only the first c_r keys of each request are
- * read.  The two parts write their partial states (attention dtype, float32
- * log-sum-exp) to the plan's workspace; the merge writes o and lse.  The
+ * read.  The two parts write their partial states (float32) to the plan's
+ * workspace; the merge writes o and lse.  The
  * prefill-sized requests of both parts run in one launch, side by side on
  * shares of the compute units in proportion to their work.  The caller owns
  * every buffer; the call only enqueues work on `stream`.

@@ -84,7 +84,7 @@ rpa::DevPlan dev_plan(const rpa_plan* plan, void* ws_base) {
   p.n_merge_rows = plan->n_merge_rows;
   p.dec_stages = plan->dec_stages;
   char* ws = static_cast<char*>(ws_base);
-  p.part_o = ws + plan->part_o_off;
+  p.part_o = reinterpret_cast<float*>(ws + plan->part_o_off);
   p.part_lse = reinterpret_cast<float*>(ws + plan->part_lse_off);
   p.batch_size = plan->batch_size;
   p.total_q = plan->total_q;

@@ -78,7 +78,7 @@ hipError_t launch_append(const DevPlan& p, const void* k_new, const void* v_new,
 // ----------------------------------------------------------------------------
 
 // Writes one row's result: the final output when the request is not split,
-// else the partial of piece s (normalized like the output, in its dtype).
+// else the float32 partial of piece s (normalized like the output).
 template <typename T>
 __device__ __forceinline__ void write_row(const DevPlan& p, int32_t r, int32_t i, int32_t t,
                                           int32_t h, int32_t s, int32_t n, float lse_nat,
@@ -91,8 +91,8 @@ __device__ __forceinline__ void write_row(const DevPlan& p, int32_t r, int32_t i
     if (write_lse && lse) lse[(int64_t)i * p.num_qo_heads + h] = lse_nat;
   } else {
     const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + t;
-    T* orow = static_cast<T*>(p.part_o) + (prow * p.num_qo_heads + h) * p.head_dim_v;
-    for (int32_t c = 0; c < count; ++c) orow[d0 + c * stride] = from_f32<T>(vals[c]);
+    float* orow = p.part_o + (prow * p.num_qo_heads + h) * p.head_dim_v;
+    for (int32_t c = 0; c < count; ++c) orow[d0 + c * stride] = vals[c];
     if (write_lse) p.part_lse[prow * p.num_qo_heads + h] = lse_nat;
   }
 }
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DevPlan p, T* __restric
       if (s0 + u < S_eff) {
         const int64_t prow = prow0 + (int64_t)(s0 + u) * n;
         ls[u] = p.part_lse[prow * H + h];
-        load8(static_cast<const T*>(p.part_o) + (prow * H + h) * DV + d0, v[u]);
+        load8(p.part_o + (prow * H + h) * DV + d0, v[u]);
       } else {
         ls[u] = -INFINITY;
       }

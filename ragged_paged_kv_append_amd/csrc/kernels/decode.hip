@@ -362,18 +362,24 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
   const float lse_nat = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
   const int32_t i = q0 + t;
   const int32_t S = p.split[r * SP_WORDS + SP_COUNT];
-  // The output row, or the row of piece s's partial (the same bf16 layout).
+  // The output row (bf16), or the float32 row of piece s's partial.
   const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + t;
-  bf16_t* orow = (S == 1 ? o + (int64_t)i * p.num_qo_heads * kD
-                         : static_cast<bf16_t*>(p.part_o) + prow * p.num_qo_heads * kD) +
-                 (int64_t)h * kD + 4 * grp;
+  if (S == 1) {
+    bf16_t* orow = o + ((int64_t)i * p.num_qo_heads + h) * kD + 4 * grp;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const uint32_t lo = (uint32_t)f32_to_bf16(acc[nb][0] * inv) |
-                        ((uint32_t)f32_to_bf16(acc[nb][1] * inv) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(acc[nb][2] * inv) |
-                        ((uint32_t)f32_to_bf16(acc[nb][3] * inv) << 16);
-    *reinterpret_cast<uint2*>(orow + 16 * nb) = make_uint2(lo, hi);
+    for (int nb = 0; nb < 8; ++nb) {
+      const uint32_t lo = (uint32_t)f32_to_bf16(acc[nb][0] * inv) |
+                          ((uint32_t)f32_to_bf16(acc[nb][1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(acc[nb][2] * inv) |
+                          ((uint32_t)f32_to_bf16(acc[nb][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + 16 * nb) = make_uint2(lo, hi);
+    }
+  } else {
+    float* orow = p.part_o + (prow * p.num_qo_heads + h) * kD + 4 * grp;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      *reinterpret_cast<float4*>(orow + 16 * nb) =
+          make_float4(acc[nb][0] * inv, acc[nb][1] * inv, acc[nb][2] * inv, acc[nb][3] * inv);
   }
   if (grp == 0) {
     if (S == 1) {

@@ -567,16 +567,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const f32x16_t& acc = oacc[nb][rb];
-        // The output row, or the row of piece s's partial (the same bf16 layout).
-        const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + t;
-        bf16_t* orow = (S == 1 ? o + (int64_t)(q0 + t) * p.num_qo_heads * kDV
-                               : static_cast<bf16_t*>(p.part_o) + prow * p.num_qo_heads * kDV) +
-                       (int64_t)h * kDV + 128 * wave + 32 * nb + 4 * phalf;
+        // The output row (bf16), or the float32 row of piece s's partial.
+        const int64_t col = (int64_t)h * kDV + 128 * wave + 32 * nb + 4 * phalf;
+        if (S == 1) {
+          bf16_t* orow = o + (int64_t)(q0 + t) * p.num_qo_heads * kDV + col;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          *reinterpret_cast<uint2*>(orow + 8 * b) =
-              make_uint2(pack_bf16x2(acc[4 * b] * inv, acc[4 * b + 1] * inv),
-                         pack_bf16x2(acc[4 * b + 2] * inv, acc[4 * b + 3] * inv));
+          for (int b = 0; b < 4; ++b)
+            *reinterpret_cast<uint2*>(orow + 8 * b) =
+                make_uint2(pack_bf16x2(acc[4 * b] * inv, acc[4 * b + 1] * inv),
+                           pack_bf16x2(acc[4 * b + 2] * inv, acc[4 * b + 3] * inv));
+        } else {
+          const int64_t prow = (int64_t)p.split[r * SP_WORDS + SP_BASE] + (int64_t)s * n + t;
+          float* orow = p.part_o + prow * p.num_qo_heads * kDV + col;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            *reinterpret_cast<float4*>(orow + 8 * b) =
+                make_float4(acc[4 * b] * inv, acc[4 * b + 1] * inv, acc[4 * b + 2] * inv,
+                            acc[4 * b + 3] * inv);
+        }
       }
     }
   }

@@ -745,49 +745,56 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
 
     // Finish: the row sums are split over the two halves of the wave.  Lane
     // l holds O^T[d][row] for d = 32 nb + 8 b + 4 half + j (element 4 b + j
-    // of block nb); lanes l and l ^ 32 hold the same row.  One swap between
-    // the halves per pair of b gives each lane eight consecutive dims (half 0
-    // those of the even b, half 1 those of the odd b), stored as 16 bytes.
+    // of block nb); lanes l and l ^ 32 hold the same row.  Output rows
+    // (bf16): one swap between the halves per pair of b gives each lane eight
+    // consecutive dims (half 0 those of the even b, half 1 those of the odd
+    // b), stored as 16 bytes.  Partial rows of a split piece (float32): each
+    // lane's four consecutive dims are 16 bytes already.
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32, 64);
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
       const float lse_nat = ltot > 0.f ? (m[rb] + log2f(ltot)) * kLn2 : -INFINITY;
-      uint4 out[4][2];  // [nb][pair of b]
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          uint32_t w[2][2];  // [b of the pair][lo, hi]
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int b = 2 * pr + u;
-            w[u][0] = pack_bf16x2(oacc[nb][rb][4 * b] * inv, oacc[nb][rb][4 * b + 1] * inv);
-            w[u][1] = pack_bf16x2(oacc[nb][rb][4 * b + 2] * inv, oacc[nb][rb][4 * b + 3] * inv);
-          }
-          const auto lo = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
-          const auto hi = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
-          out[nb][pr] = make_uint4(lo[0], hi[0], lo[1], hi[1]);
-        }
-      if (!row_ok[rb]) continue;
       const int32_t i_tok = q0 + t_of[rb];
       const int32_t hh = h_of[rb];
-      // The output row, or the row of piece s's partial (the same bf16 layout).
-      const int64_t prow = (int64_t)part0 + (int64_t)s * n + t_of[rb];
-      bf16_t* orow = (S == 1 ? o + (int64_t)i_tok * p.num_qo_heads * kD
-                             : static_cast<bf16_t*>(p.part_o) + prow * p.num_qo_heads * kD) +
-                     (int64_t)hh * kD + 8 * half;
+      if (S == 1) {
+        uint4 out[4][2];  // [nb][pair of b]
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr)
-          *reinterpret_cast<uint4*>(orow + 32 * nb + 16 * pr) = out[nb][pr];
-      if (half == 0) {
-        if (S == 1) {
-          if (lse) lse[(int64_t)i_tok * p.num_qo_heads + hh] = lse_nat;
-        } else {
-          p.part_lse[prow * p.num_qo_heads + hh] = lse_nat;
-        }
+          for (int pr = 0; pr < 2; ++pr) {
+            uint32_t w[2][2];  // [b of the pair][lo, hi]
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int b = 2 * pr + u;
+              w[u][0] = pack_bf16x2(oacc[nb][rb][4 * b] * inv, oacc[nb][rb][4 * b + 1] * inv);
+              w[u][1] =
+                  pack_bf16x2(oacc[nb][rb][4 * b + 2] * inv, oacc[nb][rb][4 * b + 3] * inv);
+            }
+            const auto lo = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+            const auto hi = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+            out[nb][pr] = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+          }
+        if (!row_ok[rb]) continue;
+        bf16_t* orow = o + ((int64_t)i_tok * p.num_qo_heads + hh) * kD + 8 * half;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr)
+            *reinterpret_cast<uint4*>(orow + 32 * nb + 16 * pr) = out[nb][pr];
+        if (half == 0 && lse) lse[(int64_t)i_tok * p.num_qo_heads + hh] = lse_nat;
+      } else {
+        if (!row_ok[rb]) continue;
+        const int64_t prow = (int64_t)part0 + (int64_t)s * n + t_of[rb];
+        float* orow = p.part_o + (prow * p.num_qo_heads + hh) * kD + 4 * half;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            *reinterpret_cast<float4*>(orow + 32 * nb + 8 * b) =
+                make_float4(oacc[nb][rb][4 * b] * inv, oacc[nb][rb][4 * b + 1] * inv,
+                            oacc[nb][rb][4 * b + 2] * inv, oacc[nb][rb][4 * b + 3] * inv);
+        if (half == 0) p.part_lse[prow * p.num_qo_heads + hh] = lse_nat;
       }
     }
   }

@@ -1,5 +1,5 @@
 // Static device scratch of rpa_batch_attention_noalloc: the plan's metadata
-// and the partial outputs of split pieces, for callers that cannot
+// and the float32 partial outputs of split pieces, for callers that cannot
 // allocate device memory.  One copy of the array exists on every GPU the
 // library runs on, held until the process ends.
 

@@ -742,8 +742,7 @@ rpa_status build_plan_impl(const rpa_attn_config* cfg, const rpa_batch_desc* bat
   plan->meta_bytes = (size_t)round_up((int64_t)blob.size() * 4, 256);
   plan->part_o_off = plan->meta_bytes;
   plan->part_lse_off =
-      plan->part_o_off + (size_t)round_up(partial_rows * c.num_qo_heads * c.head_dim_v *
-                                              (c.dtype == RPA_DTYPE_BF16 ? 2 : 4), 256);
+      plan->part_o_off + (size_t)round_up(partial_rows * c.num_qo_heads * c.head_dim_v * 4, 256);
   plan->ws_bytes = plan->part_lse_off + (size_t)round_up(partial_rows * c.num_qo_heads * 4, 256);
   return RPA_OK;
 }
@@ -952,8 +951,7 @@ rpa_status build_split_plan(const rpa_attn_config* cfg, const rpa_batch_desc* ba
   plan->partial_rows = own->partial_rows = partial_rows;
   plan->part_o_off = plan->meta_bytes;
   plan->part_lse_off =
-      plan->part_o_off + (size_t)round_up(partial_rows * c.num_qo_heads * c.head_dim_v *
-                                              (c.dtype == RPA_DTYPE_BF16 ? 2 : 4), 256);
+      plan->part_o_off + (size_t)round_up(partial_rows * c.num_qo_heads * c.head_dim_v * 4, 256);
   plan->ws_bytes = plan->part_lse_off + (size_t)round_up(partial_rows * c.num_qo_heads * 4, 256);
   own->part_o_off = plan->part_o_off - plan->own_off;
   own->part_lse_off = plan->part_lse_off - plan->own_off;

@@ -66,7 +66,7 @@ struct DevPlan {
   // 32 bits of new token i's row: bit u = it sees new token u of its request.
   const int32_t* tree_req;
   const uint32_t* tree_mask;
-  void* part_o;                 // [partial rows][num_qo_heads][head_dim_v], output dtype
+  float* part_o;                // [partial rows][num_qo_heads][head_dim_v], float32
   float* part_lse;              // [partial rows][num_qo_heads]
   int32_t n_items[KC_COUNT];
   int32_t n_wgs[KC_COUNT];      // workgroups of each class's launch

@@ -108,6 +108,18 @@ def test_prefill_tiles_and_splits_bf16():
     check_full(spec, meta, tensors, num_cus=0, label="prefill-default")
 
 
+@pytest.mark.parametrize("scale", [0.01, 0.1, 0.3])
+def test_prefill_rows_without_keys_in_a_piece(scale):
+    """An MHA chunk whose key pieces start past the first rows of a row tile
+    (those rows see no key of the piece: the piece's items must still run once,
+    and the merge skips those rows' empty partial states), at softmax scales
+    where a masked score's scaled value lies above -5e29."""
+    spec = workloads.Spec("nokey", 16, 16, 128, 128, 16, "bf16", scale, 41)
+    meta = workloads.make_meta([512, 300], [1636, 1000], 16, 41)
+    tensors = workloads.make_tensors(spec, meta, 41, device="cuda")
+    check_full(spec, meta, tensors, num_cus=0, label=f"nokey{scale}")
+
+
 def test_interleaved_kv_pages():
     # K and V of a page interleaved in one allocation: [pages][2][H][P][d]
     spec = small_spec("bf16", 8, 2, 128, 128, 16, True, 11)
