@@ -6,17 +6,19 @@
 // rectangle) and causally to itself (a triangle), as in the chunked-prefill
 // post (sections "core-idea" and "correctness").
 //
-// One workgroup of four wavefronts, one per SIMD, takes a work item: request
+// One workgroup of eight wavefronts, two per SIMD, takes a work item: request
 // r, KV head g, up to 256 query rows (row = token * G + head-in-group, so the
 // G query heads sharing a KV head sit in one tile and share its K/V loads),
-// keys [k0, k1).  Each wavefront owns 64 rows, as two 32-row blocks, and the
-// whole register file of its SIMD: Q of its rows and the S^T accumulators in
-// VGPRs, the O^T accumulators in AGPRs.  The planner packs the items onto one
+// keys [k0, k1).  Each wavefront owns one 32-row block and half the register
+// file of its SIMD: Q of its rows and the S^T accumulators in VGPRs, the O^T
+// accumulators in AGPRs.  (The code also builds with four wavefronts of two
+// blocks each, one per SIMD; two per SIMD let one wave's products run while
+// the other waits on its DMA issue or its LDS reads.)  The planner packs the items onto one
 // resident workgroup per compute unit, longest first; a workgroup runs its
 // list.
 //
 // K/V tiles of 64 keys (16 KiB each) move from HBM/L2 into a four-slot LDS
-// ring with the gfx950 global-to-LDS DMA, two tiles ahead; each wave moves 16
+// ring with the gfx950 global-to-LDS DMA, two tiles ahead; each wave moves 8
 // key rows of every tile.  K rows keep 16-byte chunk c at c ^ (k % 16), V rows
 // at c ^ 4 (k % 4), so the K-operand reads and the transposing V reads are
 // bank-conflict free.
@@ -30,8 +32,9 @@
 //     the P^T operand layout);
 // and, between those products, the vector work of step h: P = exp2(S') rounded
 // to bf16, the row sums of P and a running max of S'.  The products of one
-// step do not depend on its vector work, so one wavefront keeps its SIMD's
-// matrix core busy while it runs the softmax in the gaps.
+// step do not depend on its vector work, so a wavefront keeps its SIMD's
+// matrix core busy while it runs the softmax in the gaps, and the SIMD's
+// second wavefront fills what the first leaves idle.
 //
 // The mask comes out of the matrix core with S: the first product of each
 // S^T chain accumulates onto a block that holds 0, or -1e30 for a masked
@@ -57,13 +60,17 @@ namespace rpa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kRB = 256 / kWaves / 32;      // 32-row blocks per wave
+constexpr int kWaveRows = 32 * kRB;         // query rows per wave
+constexpr int kDmaRows = 64 / kWaves;       // key rows each wave moves per tile
+constexpr int kDmaHalf = kDmaRows / 4;      // its DMA instructions per K (or V) share
 constexpr int kKT = 64;                     // keys per ring tile
 constexpr int kStep = 32;                   // keys per softmax step
 constexpr int kTileBytes = kKT * kD * 2;    // 16 KiB: the K (or V) rows of a tile
 constexpr int kSlotBytes = 2 * kTileBytes;  // K tile, then V tile
 constexpr int kSlots = 4;
-constexpr int kDmaInst = 2 * (kKT / kWaves) / 4;  // per wave and tile: 4 K + 4 V (8)
+constexpr int kDmaInst = 2 * kDmaHalf;       // per wave and tile
 constexpr float kMinusBig = -1.0e30f;
 constexpr float kWindow = 64.f;             // log2 units around the reference
 
@@ -215,10 +222,13 @@ constexpr int reads_before(int u) {
 // Softmax schedule of a step (see the main loop): exps of elements 0, 1 in
 // slot 0, 2, 3 in slot 1 and e >= 4 in slot e - 2; the bf16 pack of pair p
 // in slot 2 (p = 0), 3 (p = 1) or 2 p + 1 (p >= 2).
-constexpr int exp_count(int s) { return s < 2 ? 2 : (s <= 29 ? 1 : 0); }
-constexpr int exp_first(int s) { return (s < 2 ? 2 * s : s + 2) & 31; }
+constexpr int exp_count(int s) {
+  return kRB == 1 ? ((s & 1) == 0 ? 1 : 0) : (s < 2 ? 2 : (s <= 29 ? 1 : 0));
+}
+constexpr int exp_first(int s) { return kRB == 1 ? s / 2 : ((s < 2 ? 2 * s : s + 2) & 31); }
 constexpr int pack_pair(int s) {
-  return s == 2 ? 0 : (s == 3 ? 1 : ((s >= 5 && (s & 1)) ? (s - 1) / 2 : -1));
+  return kRB == 1 ? ((s & 3) == 3 ? s / 4 : -1)
+                  : (s == 2 ? 0 : (s == 3 ? 1 : ((s >= 5 && (s & 1)) ? (s - 1) / 2 : -1)));
 }
 
 // The PV products, also from inline assembly (accumulators in AGPRs), so that
@@ -239,7 +249,7 @@ struct PrefillPart {
 
 // Workgroups 0 .. wgs0 - 1 run part0's workgroup lists, the rest part1's
 // (wgs0 = the grid for a single plan).
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
                     const bf16_t* __restrict__ q, bf16_t* __restrict__ o,
                     float* __restrict__ lse) {
@@ -285,6 +295,8 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
   const uint32_t ktok = 2u * (uint32_t)ks.token, vtok = 2u * (uint32_t)vs.token;
   const uint32_t k_lrow = (uint32_t)l4 * ktok;
   const uint32_t xk = 16u * (uint32_t)(p16 ^ l4);  // K chunk of instruction 0 (^ 64 i)
+  // (^ 16 (r % 16) for this wave's first row r of a tile)
+  const uint32_t kx_wave = 16u * (uint32_t)((kDmaRows * wave) & 15);
   const uint32_t dv_off = (uint32_t)l4 * vtok + 16u * (uint32_t)(p16 ^ (4 * l4));
 
   const int32_t wb0 = __builtin_amdgcn_readfirstlane(p.wg_indptr[KC_PREFILL][wg]);
@@ -321,13 +333,13 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
       return min(k1, (causal ? cached + row / G : L - 1) + 1);
     };
 
-    // This lane's rows: 64 wave + 32 rb + col of the item's tile.
+    // This lane's rows: kWaveRows wave + 32 rb + col of the item's tile.
     bool row_ok[2];
     int32_t t_of[2], h_of[2], kend_row[2];
     uint32_t tm_lo[2], tm_hi[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int32_t row = row0 + 64 * wave + 32 * rb + col;
+    for (int rb = 0; rb < kRB; ++rb) {
+      const int32_t row = row0 + kWaveRows * wave + 32 * rb + col;
       row_ok[rb] = row < row1;
       t_of[rb] = row_ok[rb] ? row / G : 0;
       h_of[rb] = g * G + (row_ok[rb] ? row % G : 0);
@@ -339,7 +351,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
       }
     }
     const int32_t kend = uni(key_end(row1 - 1));
-    const int32_t wrow0 = row0 + 64 * wave;
+    const int32_t wrow0 = row0 + kWaveRows * wave;
     const int32_t kend_wmin = uni(wrow0 < row1 ? key_end(wrow0) : k0);
     // Steps that start at or past mask_from need the element mask.
     const int32_t mask_from = tree ? min(kend_wmin, max(cached, k0)) : kend_wmin;
@@ -351,10 +363,10 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     const char* vbase = reinterpret_cast<const char*>(vc + (int64_t)g * vs.head);
     // Page id of the first key row this wave moves for tile T, in lane T (the
     // planner keeps an item within 64 tiles), clamped to the item's last key.
-    int32_t pid = pages[min(k0 + lane * kKT + 16 * wave, k1 - 1) >> p.page_shift];
-    // DMA of tile T into ring slot T % 4: this wave's key rows 16 wave ..
-    // + 15 (one page: pages hold a multiple of 16 keys), instruction x = 0..3
-    // for K, 4..7 for V, each 4 rows of 256 bytes.  Rows at or past k1 are not
+    int32_t pid = pages[min(k0 + lane * kKT + kDmaRows * wave, k1 - 1) >> p.page_shift];
+    // DMA of tile T into ring slot T % 4: this wave's kDmaRows key rows from
+    // kDmaRows wave (one page: pages hold a multiple of 16 keys), instructions
+    // x < kDmaHalf for K, the next kDmaHalf for V, each 4 rows of 256 bytes.  Rows at or past k1 are not
     // moved: their ring bytes keep an older tile's finite values, which the
     // mask hides.  A tile past the item moves nothing.  No branches.
     struct DmaTile {
@@ -364,25 +376,25 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
       int32_t rmax;  // rows past the first that exist (< 0: none)
     };
     auto dma_setup = [&](int32_t T) __attribute__((always_inline)) {
-      const int32_t gkey = k0 + T * kKT + 16 * wave;
+      const int32_t gkey = k0 + T * kKT + kDmaRows * wave;
       const int64_t page = __builtin_amdgcn_readlane(pid, T);
       const int64_t in_page = min(gkey, k1 - 1) & (p.page_size - 1);
       DmaTile d;
       d.kg = kbase + 2 * (page * ks.page + in_page * ks.token);
       d.vg = vbase + 2 * (page * vs.page + in_page * vs.token);
       d.lds = __builtin_amdgcn_readfirstlane(ring_lds + (T & (kSlots - 1)) * kSlotBytes +
-                                             16 * wave * 256);
+                                             kDmaRows * wave * 256);
       d.rmax = k1 - 1 - gkey;
       return d;
     };
     auto dma_x = [&](const DmaTile& d, int x) __attribute__((always_inline)) {
-      const int i = x & 3;
-      const bool v = x >= 4;
+      const int i = x % kDmaHalf;
+      const bool v = x >= kDmaHalf;
       // lanes of rows 4 i .. 4 i + 3 that exist: 16 per row
       const int32_t nr = min(max(d.rmax - 4 * i + 1, 0), 4);
       const uint64_t lanes = nr >= 4 ? ~0ull : ((1ull << (16 * nr)) - 1ull);
       const char* b = v ? d.vg + (int64_t)(4 * i) * vtok : d.kg + (int64_t)(4 * i) * ktok;
-      const uint32_t off = v ? dv_off : k_lrow + (xk ^ (64u * i));
+      const uint32_t off = v ? dv_off : k_lrow + (xk ^ (64u * i) ^ kx_wave);
       if (i == 0) dma16<true>(b, opaque(off), d.lds + (v ? kTileBytes : 0), lanes);
       else dma16<false>(b, opaque(off), d.lds + (v ? kTileBytes : 0) + 1024 * i, lanes);
     };
@@ -396,7 +408,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[nb][rb][i] = 0.f;
     // S^T of two steps (by parity), -1e30 where masked: element i of [par][rb] is key
@@ -416,14 +428,14 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     // put back to 0 after it).
     f32x16_t cinit[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) cinit[rb][i] = 0.f;
     // Mask of the step whose keys start at kb, into cinit.
     auto set_mask = [&](int32_t kb) __attribute__((always_inline)) {
       if (!tree) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
           const int32_t lim = kend_row[rb] - kb - 4 * half;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -433,7 +445,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
         }
       } else {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
           const int32_t lim = kend_row[rb] - kb - 4 * half;
           const int32_t rel = kb + 4 * half - cached;  // new-token index of offset 0
 #pragma unroll
@@ -450,7 +462,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     };
     auto clear_mask = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) cinit[rb][i] = 0.f;
     };
@@ -464,7 +476,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     // results are never stored.
     u32x4_t qf[2][8];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       const bf16_t* qrow =
           q + ((int64_t)(q0 + t_of[rb]) * p.num_qo_heads + h_of[rb]) * kD + 8 * half;
 #pragma unroll
@@ -475,7 +487,9 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     // own wait for them, which drains every vector-memory load, must not
     // drain the DMA stream later).
     wait_vmem<0>();
-    asm volatile("" : "+v"(pid), "+v"(tm_lo[0]), "+v"(tm_hi[0]), "+v"(tm_lo[1]), "+v"(tm_hi[1]));
+    asm volatile("" : "+v"(pid));
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) asm volatile("" : "+v"(tm_lo[rb]), "+v"(tm_hi[rb]));
     barrier();  // the previous item's waves are done with the ring
     // Tiles 0 and 1: the products start once tile 0 is in (vector-memory
     // loads complete in order), while tile 1 lands.
@@ -491,12 +505,12 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     }
     wait_vmem<kDmaInst>();  // tile 0 is in; tile 1 may still be in flight
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) asm volatile("" : "+a"(qf[rb][i]));
     if (k0 >= mask_kb) set_mask(k0);
     // Vector writes of cinit, then a product reads it: wait states.
-    asm volatile("s_nop 4" : "+v"(cinit[0]), "+v"(cinit[1]));
+    if constexpr (kRB == 2) asm volatile("s_nop 4" : "+v"(cinit[0]), "+v"(cinit[1])); else asm volatile("s_nop 4" : "+v"(cinit[0]));
     barrier();  // tile 0 is in the ring (tile 1 is waited for in step 0)
 
     // K operands of step h (ring slot of tile h / 2, its half h % 2), three
@@ -533,7 +547,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
         if (i == 6) wait_lds<1>();
         if (i == 7) wait_lds<0>();
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
           if (i == 0) mfma_s_first(sacc[0][rb], kr[0], qf[rb][0], cinit[rb]);
           else mfma_s(sacc[0][rb], kr[i % 4], qf[rb][i]);
         }
@@ -543,7 +557,10 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
       // The softmax of step 0 reads these accumulators next: wait states for
       // the products' latency (the compiler adds none after inline assembly);
       // they also let the last product read its operand before kr is reused.
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc[0][0]), "+v"(sacc[0][1]));
+      if constexpr (kRB == 2)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc[0][0]), "+v"(sacc[0][1]));
+      else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc[0][0]));
       // K operands 0..3 of step 1 (tile 0, second half) for the first step;
       // the V^T operands of step -1 only meet P = 0, so zeros do.
       const uint32_t kn = kaddr(1);
@@ -591,7 +608,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
             masked = false;
           }
           // Vector writes of cinit, then a product reads it: wait states.
-          asm volatile("s_nop 4" : "+v"(cinit[0]), "+v"(cinit[1]));
+          if constexpr (kRB == 2) asm volatile("s_nop 4" : "+v"(cinit[0]), "+v"(cinit[1])); else asm volatile("s_nop 4" : "+v"(cinit[0]));
         }
         __builtin_amdgcn_sched_barrier(0);
 
@@ -608,11 +625,13 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
           if ((sl & 1) == 0) wait_lds_n(reads_before(sl));
           if (sl < 16) {
             const int i = sl >> 1, rb = sl & 1;
-            if (i == 0) mfma_s_first(sc_out[rb], kr[0], qf[rb][0], cinit[rb]);
-            else mfma_s(sc_out[rb], kr[i % 4], qf[rb][i]);
+            if (rb < kRB) {
+              if (i == 0) mfma_s_first(sc_out[rb], kr[0], qf[rb][0], cinit[rb]);
+              else mfma_s(sc_out[rb], kr[i % 4], qf[rb][i]);
+            }
           } else {
             const int j = (sl - 16) >> 1, rb = (sl - 16) & 1;  // operand j = 4 kc + nb
-            mfma_pv(oacc[j & 3][rb], vr[j % 4], p_in[rb][j >> 2]);
+            if (rb < kRB) mfma_pv(oacc[j & 3][rb], vr[j % 4], p_in[rb][j >> 2]);
           }
           // ---- operand reads of this slot --------------------------------------
           if (sl == 0) {
@@ -641,6 +660,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
             const int ne = exp_count(sl), e0 = exp_first(sl);
             auto soft_one = [&](int e) __attribute__((always_inline)) {
               const int rb = (e >> 4) & 1, i = e & 15;
+              if (rb >= kRB) return;
               const float x = __builtin_fmaf(sc_in[rb][i], sc, -m[rb]);
               if (e & 1) {
                 rmax[rb] = fmaxf(rmax[rb], fmaxf(xprev, x));
@@ -656,26 +676,30 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
               // bf16 pairs of P and the row sums (of the fp32 P, with plain adds:
               // v_dot2 would hold up the matrix core)
               const int rb = (pp >> 3) & 1, kcc = (pp >> 2) & 1, e = pp & 3;
-              const float x0 = sc_in[rb][8 * kcc + 2 * e], x1 = sc_in[rb][8 * kcc + 2 * e + 1];
-              p_out[rb][kcc][e] = pack_bf16x2(x0, x1);
-              ps[rb][e] += x0 + x1;
+              if (rb < kRB) {
+                const float x0 = sc_in[rb][8 * kcc + 2 * e], x1 = sc_in[rb][8 * kcc + 2 * e + 1];
+                p_out[rb][kcc][e] = pack_bf16x2(x0, x1);
+                ps[rb][e] += x0 + x1;
+              }
             }
             if (sl == 31) {
 #pragma unroll
-              for (int rb = 0; rb < 2; ++rb)
+              for (int rb = 0; rb < kRB; ++rb)
                 lsum[rb] += (ps[rb][0] + ps[rb][1]) + (ps[rb][2] + ps[rb][3]);
             }
-            asm volatile("" : "+v"(sc_in[0]), "+v"(sc_in[1]), "+v"(rmax[0]), "+v"(rmax[1]),
-                         "+v"(xprev));
-            asm volatile("" : "+v"(p_out[0][0]), "+v"(p_out[0][1]), "+v"(p_out[1][0]),
-                         "+v"(p_out[1][1]), "+v"(lsum[0]), "+v"(lsum[1]));
-            asm volatile("" : "+v"(ps[0][0]), "+v"(ps[0][1]), "+v"(ps[0][2]), "+v"(ps[0][3]),
-                         "+v"(ps[1][0]), "+v"(ps[1][1]), "+v"(ps[1][2]), "+v"(ps[1][3]));
+            asm volatile("" : "+v"(xprev));
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb) {
+              asm volatile("" : "+v"(sc_in[rb]), "+v"(rmax[rb]), "+v"(lsum[rb]));
+              asm volatile("" : "+v"(p_out[rb][0]), "+v"(p_out[rb][1]));
+              asm volatile("" : "+v"(ps[rb][0]), "+v"(ps[rb][1]), "+v"(ps[rb][2]), "+v"(ps[rb][3]));
+            }
           }
           // ---- DMA of tile T + 2: slots 22, 25, 28, 31 of both steps -------------
-          if (sl >= 22 && (sl - 22) % 3 == 0) {
-            const int x = 4 * par + (sl - 22) / 3;
-            if (x == 0 || x == 4) dd = dma_setup(T + 2);
+          if (sl >= 22 && (sl - 22) % 3 == 0 && (sl - 22) / 3 < kDmaInst / 2) {
+            const int idx = (sl - 22) / 3;
+            const int x = (kDmaInst / 2) * par + idx;
+            if (idx == 0) dd = dma_setup(T + 2);
             dma_x(dd, x);
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -686,8 +710,9 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
             barrier();
           }
         }
-        asm volatile("" : "+v"(p_out[0][0]), "+v"(p_out[0][1]), "+v"(p_out[1][0]),
-                     "+v"(p_out[1][1]), "+v"(lsum[0]), "+v"(lsum[1]));
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          asm volatile("" : "+v"(p_out[rb][0]), "+v"(p_out[rb][1]), "+v"(lsum[rb]));
         if (par == 0 && h + 1 >= nsteps) break;
       }
     }
@@ -707,13 +732,17 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
         for (int j = 0; j < 8; ++j) {
           const u32x4_t va = j < 3 ? vr[j] : ve[j - 3];
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) mfma_pv(oacc[j & 3][rb], va, pb[par][rb][j >> 2]);
+          for (int rb = 0; rb < kRB; ++rb) mfma_pv(oacc[j & 3][rb], va, pb[par][rb][j >> 2]);
         }
       }
       // Vector reads of O^T follow: wait states for the products' latency.
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                   : "+a"(oacc[0][0]), "+a"(oacc[0][1]), "+a"(oacc[1][0]), "+a"(oacc[1][1]),
-                     "+a"(oacc[2][0]), "+a"(oacc[2][1]), "+a"(oacc[3][0]), "+a"(oacc[3][1]));
+      if constexpr (kRB == 2)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(oacc[0][0]), "+a"(oacc[0][1]), "+a"(oacc[1][0]), "+a"(oacc[1][1]),
+                       "+a"(oacc[2][0]), "+a"(oacc[2][1]), "+a"(oacc[3][0]), "+a"(oacc[3][1]));
+      else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(oacc[0][0]), "+a"(oacc[1][0]), "+a"(oacc[2][0]), "+a"(oacc[3][0]));
     }
 
     // A row whose scores left the window around its reference: do the item
@@ -724,7 +753,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     const float no_key = 0.5f * kMinusBig * sc;
     bool moved = false;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       const float x = max_halves(rmax[rb]);  // largest S' of the row
       const bool out = row_ok[rb] && x > no_key - m[rb] && (x > kWindow || x < -kWindow);
       moved |= out;
@@ -751,7 +780,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     // b), stored as 16 bytes.  Partial rows of a split piece (float32): each
     // lane's four consecutive dims are 16 bytes already.
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32, 64);
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
       const float lse_nat = ltot > 0.f ? (m[rb] + log2f(ltot)) * kLn2 : -INFINITY;
