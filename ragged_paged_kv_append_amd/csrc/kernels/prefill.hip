@@ -31,26 +31,32 @@
 //     transposing LDS read, P^T from registers: the S^T accumulator layout is
 //     the P^T operand layout);
 // and, between those products, the vector work of step h: P = exp2(S') rounded
-// to bf16, the row sums of P and a running max of S'.  The products of one
-// step do not depend on its vector work, so a wavefront keeps its SIMD's
-// matrix core busy while it runs the softmax in the gaps, and the SIMD's
+// to bf16.  The row sums of P come from the matrix core too: two small
+// products per step multiply the P^T operands by a 0/1 selector (mfma_sum).
+// The products of one step do not depend on its vector work, so a wavefront
+// keeps its SIMD's matrix core busy while it runs the softmax in the gaps, and the SIMD's
 // second wavefront fills what the first leaves idle.
 //
 // The mask comes out of the matrix core with S: the first product of each
 // S^T chain accumulates onto a block that holds 0, or -1e30 for a masked
 // (key, row) pair (the causal diagonal, a tree mask, keys past the item).
 // The vector pipe, which sets the pace next to the matrix core, then spends
-// one fma (S' = S * scale * log2 e - m), one exp, half a conversion, one add
-// and half a max per score.  (Q is not scaled instead: rounding Q * scale to
-// bf16 moves large scores by whole units.)
+// one fma (S' = S * scale * log2 e - m), one exp and half a conversion per
+// score.  (Q is not scaled instead: rounding Q * scale to bf16 moves large
+// scores by whole units.)
 //
 // O is never rescaled.  P is taken against a fixed per-row reference m (0 on
-// the first pass): the scores only have to stay within 2^64 of it, above and
-// below, for P, the sums and O to stay well inside the float range without
-// losing precision.  A row whose largest S' leaves that window makes the
-// workgroup finish the item and do it over once, with the row's largest
-// scaled score as its reference.  This keeps O touched by the matrix cores
-// alone, so it stays in AGPRs.
+// the first pass): the scores only have to stay within about 2^64 of it,
+// above and below, for P, the sums and O to stay well inside the float range
+// without losing precision.  The row sum s checks this without a running
+// max: s is at least the row's largest P and at most the number of keys
+// times it.  A row with s outside [2^-64, 2^64] makes the workgroup finish
+// the item and do it over once with reference m + log2 s (its sum is then
+// 1).  Only a row whose s is 0 or not finite (every P under- or overflowed,
+// or a tree row that may see no key of the item) needs its largest score:
+// the item is then done over keeping each row's largest score, and once more
+// with it as the reference of the rows that left the window.  This keeps O
+// touched by the matrix cores alone, so it stays in AGPRs.
 
 #include "common.h"
 #include "../launch.h"
@@ -73,6 +79,10 @@ constexpr int kSlots = 4;
 constexpr int kDmaInst = 2 * kDmaHalf;       // per wave and tile
 constexpr float kMinusBig = -1.0e30f;
 constexpr float kWindow = 64.f;             // log2 units around the reference
+// Passes over an item: the first (reference 0, checked by the row sums), a
+// final one (references set by a check, not checked again) and one that
+// keeps each row's largest scaled score (reference 0, checked by it).
+constexpr int kFirst = 0, kFinal = 1, kTrack = 2;
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
@@ -237,6 +247,18 @@ __device__ __forceinline__ void mfma_pv(f32x16_t& d, const u32x4_t& a, const u32
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 
+// Row sums of P on the matrix core: a 16x16x32 product D[m][n] += A[m][k]
+// B[k][n] whose B operand is a P^T operand of the PV products.  In the
+// 16x16x32 layout lane l holds B[8 (l / 16) + 0..7][l % 16] and
+// D[4 (l / 16) + 0..3][l % 16]; its eight P values are those of row l % 32.
+// With A[m][k] = 1 where ((k / 8) & 1) == ((m / 4) & 1), else 0 (the
+// selector), output block m / 4 = q sums the lanes 16 g + n with g = q
+// (mod 2), which hold row n + 16 (q & 1): each lane's four results are the
+// sum over the operand's 16 keys of its own row l % 32.
+__device__ __forceinline__ void mfma_sum(f32x4_t& d, const u32x4_t& sel, const u32x4_t& p) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "a"(sel), "v"(p));
+}
+
 // A plan and the pools its items read.
 struct PrefillPart {
   DevPlan p;
@@ -249,7 +271,8 @@ struct PrefillPart {
 
 // Workgroups 0 .. wgs0 - 1 run part0's workgroup lists, the rest part1's
 // (wgs0 = the grid for a single plan).
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+__global__ __launch_bounds__(64 * kWaves)
+__attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
                     const bf16_t* __restrict__ q, bf16_t* __restrict__ o,
                     float* __restrict__ lse) {
@@ -262,7 +285,8 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
   const Strides ks = pt.ks, vs = pt.vs;
   const int32_t wg = bid - (second ? wgs0 : 0);
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots][kSlotBytes];
-  __shared__ int32_t restart;  // set when a step moved a row's reference max
+  __shared__ int32_t restart;  // set when a row needs a final pass with a new reference
+  __shared__ int32_t retrack;  // set when a row needs the pass that keeps its max
   const int tid = threadIdx.x;
   // The wave index is uniform within a wave; readfirstlane tells the compiler,
   // so everything derived from it stays in scalar registers.
@@ -307,9 +331,20 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
   // both must be finite.
   for (int i = tid; i < kSlots * kSlotBytes / 16; i += 64 * kWaves)
     *reinterpret_cast<lds_u32x4*>((uintptr_t)(ring_lds + 16 * i)) = u32x4_t{0u, 0u, 0u, 0u};
-  if (tid == 0) restart = 0;
-  float m_keep[2] = {0.f, 0.f};  // references for an item done over
-  bool again = false;
+  if (tid == 0) {
+    restart = 0;
+    retrack = 0;
+  }
+  // The selector of mfma_sum: lane l holds A[l % 16][8 (l / 16) + 0..7],
+  // bf16 ones where ((l / 16) & 1) == ((l / 4) & 1), else zeros.
+  u32x4_t sel_ones;
+  {
+    const uint32_t v = (((lane >> 4) ^ (lane >> 2)) & 1) ? 0u : 0x3F803F80u;
+    sel_ones = u32x4_t{v, v, v, v};
+  }
+  asm volatile("" : "+a"(sel_ones));
+  float m_keep[2] = {0.f, 0.f};  // references for the final pass of an item
+  int pass = kFirst;
   for (int32_t idx = wb0; idx < wb1;) {
     auto uni = [](int32_t x) __attribute__((always_inline)) {
       return __builtin_amdgcn_readfirstlane(x);
@@ -366,9 +401,9 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     int32_t pid = pages[min(k0 + lane * kKT + kDmaRows * wave, k1 - 1) >> p.page_shift];
     // DMA of tile T into ring slot T % 4: this wave's kDmaRows key rows from
     // kDmaRows wave (one page: pages hold a multiple of 16 keys), instructions
-    // x < kDmaHalf for K, the next kDmaHalf for V, each 4 rows of 256 bytes.  Rows at or past k1 are not
-    // moved: their ring bytes keep an older tile's finite values, which the
-    // mask hides.  A tile past the item moves nothing.  No branches.
+    // x < kDmaHalf for K, the next kDmaHalf for V, each 4 rows of 256 bytes.
+    // Rows at or past k1 are not moved: their ring bytes keep an older tile's
+    // finite values, which the mask hides.  A tile past the item moves nothing.  No branches.
     struct DmaTile {
       const char* kg;
       const char* vg;
@@ -401,9 +436,14 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
 
     const float sc = p.sm_scale * kLog2e;
     // The reference of each row (first pass 0).
-    float m[2] = {again ? m_keep[0] : 0.f, again ? m_keep[1] : 0.f};
-    float lsum[2] = {0.f, 0.f};           // this lane's share of each row's sum
-    float rmax[2] = {kMinusBig, kMinusBig};  // this lane's largest S' of each row
+    float m[2];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+      m[rb] = !row_ok[rb] ? -kMinusBig : (pass == kFinal ? m_keep[rb] : 0.f);
+    f32x4_t ssum[2];  // the row's sum of P (all four elements), from mfma_sum
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) ssum[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float rmax[2] = {kMinusBig, kMinusBig};  // this lane's largest raw score of each row (kTrack)
     f32x16_t oacc[4][2];  // [nb][rb]: element i is O^T[32 nb + 8 (i/4) + 4 half + i%4][row]
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -431,6 +471,13 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) cinit[rb][i] = 0.f;
+    // Vector writes of cinit, then a product reads it: wait states.
+    auto cinit_ready = [&]() __attribute__((always_inline)) {
+      if constexpr (kRB == 2)
+        asm volatile("s_nop 4" : "+v"(cinit[0]), "+v"(cinit[1]));
+      else
+        asm volatile("s_nop 4" : "+v"(cinit[0]));
+    };
     // Mask of the step whose keys start at kb, into cinit.
     auto set_mask = [&](int32_t kb) __attribute__((always_inline)) {
       if (!tree) {
@@ -481,7 +528,10 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
           q + ((int64_t)(q0 + t_of[rb]) * p.num_qo_heads + h_of[rb]) * kD + 8 * half;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(qf[rb][i]) : "v"(qrow + 16 * i) : "memory");
+        asm volatile("global_load_dwordx4 %0, %1, off"
+                     : "=a"(qf[rb][i])
+                     : "v"(qrow + 16 * i)
+                     : "memory");
     }
     // Page ids, Q and tree-mask rows complete before the DMA (the compiler's
     // own wait for them, which drains every vector-memory load, must not
@@ -509,8 +559,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
 #pragma unroll
       for (int i = 0; i < 8; ++i) asm volatile("" : "+a"(qf[rb][i]));
     if (k0 >= mask_kb) set_mask(k0);
-    // Vector writes of cinit, then a product reads it: wait states.
-    if constexpr (kRB == 2) asm volatile("s_nop 4" : "+v"(cinit[0]), "+v"(cinit[1])); else asm volatile("s_nop 4" : "+v"(cinit[0]));
+    cinit_ready();
     barrier();  // tile 0 is in the ring (tile 1 is waited for in step 0)
 
     // K operands of step h (ring slot of tile h / 2, its half h % 2), three
@@ -583,6 +632,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     // which is loaded after the barrier, half in each step.  A step past the
     // last one only computes unused products from finite ring contents.
     bool masked = k0 >= mask_kb;  // cinit holds the mask of the step being computed
+    const bool track_pass = __builtin_amdgcn_readfirstlane(pass) == kTrack;  // (scalar)
     for (int32_t T = 0; T < ntiles; ++T) {
 #pragma unroll
       for (int par = 0; par < 2; ++par) {
@@ -607,13 +657,10 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
             clear_mask();
             masked = false;
           }
-          // Vector writes of cinit, then a product reads it: wait states.
-          if constexpr (kRB == 2) asm volatile("s_nop 4" : "+v"(cinit[0]), "+v"(cinit[1])); else asm volatile("s_nop 4" : "+v"(cinit[0]));
+          cinit_ready();
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        float ps[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        float xprev = 0.f;  // S' of the first element of the pair in flight
         // Each slot: one matrix product, then a share of the softmax, the
         // operand reads and the DMA.  The empty asm statements at the end of a
         // slot pin what the slot computed: without them the compiler sinks the
@@ -632,6 +679,25 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
           } else {
             const int j = (sl - 16) >> 1, rb = (sl - 16) & 1;  // operand j = 4 kc + nb
             if (rb < kRB) mfma_pv(oacc[j & 3][rb], vr[j % 4], p_in[rb][j >> 2]);
+            // the row sums of step h - 1: kc 0 in slot 17, kc 1 in slot 25
+            if (sl == 17 || sl == 25) {
+#pragma unroll
+              for (int rs = 0; rs < kRB; ++rs)
+                mfma_sum(ssum[rs], sel_ones, p_in[rs][(sl - 17) / 8]);
+            }
+          }
+          // ---- kTrack passes: each row's largest raw score of step h -----------
+          // (the scale is positive, so it gives the largest S'; masked scores
+          // stay near kMinusBig).  A uniform branch, before the first exp of
+          // the step overwrites its score.
+          if (sl == 0 && track_pass) {
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb) {
+              float a = rmax[rb];
+#pragma unroll
+              for (int i = 0; i < 16; i += 2) a = fmaxf(a, fmaxf(sc_in[rb][i], sc_in[rb][i + 1]));
+              rmax[rb] = a;
+            }
           }
           // ---- operand reads of this slot --------------------------------------
           if (sl == 0) {
@@ -650,49 +716,33 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
             ds_vt(vr[j], va_cur ^ (64u * j));
           }
           // ---- softmax of step h -----------------------------------------------
-          // Spread over the 32 slots so that each holds about one exp and three
-          // other vector instructions (what the vector pipe can do next to one
-          // 32-cycle product): S' = S * scale * log2 e - m and P = exp2(S') for
-          // elements 0..3 in slots 0 and 1 and for element e >= 4 in slot e - 2;
-          // the running max of each pair of S' with its second element; the
-          // bf16 pair of P and its sum two slots after its exps.
+          // Spread over the 32 slots: S' = S * scale * log2 e - m and
+          // P = exp2(S') for one element per even slot (with two 32-row
+          // blocks: elements 0..3 in slots 0 and 1 and element e >= 4 in slot
+          // e - 2); the bf16 pair of P two slots after its exps.
           {
             const int ne = exp_count(sl), e0 = exp_first(sl);
             auto soft_one = [&](int e) __attribute__((always_inline)) {
               const int rb = (e >> 4) & 1, i = e & 15;
               if (rb >= kRB) return;
               const float x = __builtin_fmaf(sc_in[rb][i], sc, -m[rb]);
-              if (e & 1) {
-                rmax[rb] = fmaxf(rmax[rb], fmaxf(xprev, x));
-              } else {
-                xprev = x;
-              }
               sc_in[rb][i] = __builtin_amdgcn_exp2f(x);
             };
             if (ne >= 1) soft_one(e0);
             if (ne >= 2) soft_one(e0 + 1);
             const int pp = pack_pair(sl);
             if (pp >= 0) {
-              // bf16 pairs of P and the row sums (of the fp32 P, with plain adds:
-              // v_dot2 would hold up the matrix core)
+              // bf16 pairs of P (their row sums come from mfma_sum)
               const int rb = (pp >> 3) & 1, kcc = (pp >> 2) & 1, e = pp & 3;
               if (rb < kRB) {
                 const float x0 = sc_in[rb][8 * kcc + 2 * e], x1 = sc_in[rb][8 * kcc + 2 * e + 1];
                 p_out[rb][kcc][e] = pack_bf16x2(x0, x1);
-                ps[rb][e] += x0 + x1;
               }
             }
-            if (sl == 31) {
-#pragma unroll
-              for (int rb = 0; rb < kRB; ++rb)
-                lsum[rb] += (ps[rb][0] + ps[rb][1]) + (ps[rb][2] + ps[rb][3]);
-            }
-            asm volatile("" : "+v"(xprev));
 #pragma unroll
             for (int rb = 0; rb < kRB; ++rb) {
-              asm volatile("" : "+v"(sc_in[rb]), "+v"(rmax[rb]), "+v"(lsum[rb]));
+              asm volatile("" : "+v"(sc_in[rb]));
               asm volatile("" : "+v"(p_out[rb][0]), "+v"(p_out[rb][1]));
-              asm volatile("" : "+v"(ps[rb][0]), "+v"(ps[rb][1]), "+v"(ps[rb][2]), "+v"(ps[rb][3]));
             }
           }
           // ---- DMA of tile T + 2: slots 22, 25, 28, 31 of both steps -------------
@@ -712,7 +762,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
         }
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
-          asm volatile("" : "+v"(p_out[rb][0]), "+v"(p_out[rb][1]), "+v"(lsum[rb]));
+          asm volatile("" : "+v"(p_out[rb][0]), "+v"(p_out[rb][1]));
         if (par == 0 && h + 1 >= nsteps) break;
       }
     }
@@ -734,45 +784,78 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
 #pragma unroll
           for (int rb = 0; rb < kRB; ++rb) mfma_pv(oacc[j & 3][rb], va, pb[par][rb][j >> 2]);
         }
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          mfma_sum(ssum[rb], sel_ones, pb[par][rb][0]);
+          mfma_sum(ssum[rb], sel_ones, pb[par][rb][1]);
+        }
       }
-      // Vector reads of O^T follow: wait states for the products' latency.
+      // Vector reads of O^T and the sums follow: wait states for the
+      // products' latency.
       if constexpr (kRB == 2)
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                      : "+a"(oacc[0][0]), "+a"(oacc[0][1]), "+a"(oacc[1][0]), "+a"(oacc[1][1]),
-                       "+a"(oacc[2][0]), "+a"(oacc[2][1]), "+a"(oacc[3][0]), "+a"(oacc[3][1]));
+                       "+a"(oacc[2][0]), "+a"(oacc[2][1]), "+a"(oacc[3][0]), "+a"(oacc[3][1]),
+                       "+a"(ssum[0]), "+a"(ssum[1]));
       else
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                     : "+a"(oacc[0][0]), "+a"(oacc[1][0]), "+a"(oacc[2][0]), "+a"(oacc[3][0]));
+                     : "+a"(oacc[0][0]), "+a"(oacc[1][0]), "+a"(oacc[2][0]), "+a"(oacc[3][0]),
+                       "+a"(ssum[0]));
     }
 
-    // A row whose scores left the window around its reference: do the item
-    // over (once) with the row's largest scaled score as reference.
-    // A masked score leaves the products near kMinusBig, so its S' is near
-    // kMinusBig * scale - m: a row with no key in the item stays below half
-    // of that and is not a row that left the window.
-    const float no_key = 0.5f * kMinusBig * sc;
-    bool moved = false;
+    // Did the item's rows stay in the window around their references?
+    //   kFirst: by the row sums.  A row with s in [2^-64, 2^64] did; one with
+    //   s finite and positive outside it gets reference m + log2 s for a final
+    //   pass; one with s = 0 that has keys (every P underflowed; a tree row
+    //   may have none), or with s not finite, needs the kTrack pass.  Rows
+    //   past the causal limit of the item's keys have none.
+    //   kTrack: by the largest S'.  A masked score leaves the products near
+    //   kMinusBig, so its S' is near kMinusBig * scale - m: a row with no key
+    //   in the item stays below half of that and did not leave the window;
+    //   a row that did gets its largest scaled score as reference.
+    //   kFinal: not checked.
+    bool shift = false, track = false;
+    if (pass == kTrack) {
+      const float no_key = 0.5f * kMinusBig * sc;
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      const float x = max_halves(rmax[rb]);  // largest S' of the row
-      const bool out = row_ok[rb] && x > no_key - m[rb] && (x > kWindow || x < -kWindow);
-      moved |= out;
-      m_keep[rb] = out ? m[rb] + x : m[rb];
+      for (int rb = 0; rb < kRB; ++rb) {
+        const float x = max_halves(rmax[rb]) * sc - m[rb];  // largest S' of the row
+        const bool out = row_ok[rb] && x > no_key - m[rb] && (x > kWindow || x < -kWindow);
+        shift |= out;
+        m_keep[rb] = out ? m[rb] + x : m[rb];
+      }
+    } else if (pass == kFirst) {
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const float sum = ssum[rb][0];
+        const bool inside = sum >= 0x1p-64f && sum <= 0x1p64f;  // (false for NaN)
+        const bool no_key = !tree && kend_row[rb] <= k0;
+        const bool finite_pos = sum > 0.f && sum < INFINITY;
+        const bool bad = row_ok[rb] && !inside && !(sum == 0.f && no_key);
+        shift |= bad && finite_pos;
+        track |= bad && !finite_pos;
+        m_keep[rb] = bad && finite_pos ? m[rb] + log2f(sum) : m[rb];
+      }
     }
-    if (moved && !again) restart = 1;
+    if (track) retrack = 1;
+    if (shift) restart = 1;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier();
-    const bool redo = __builtin_amdgcn_readfirstlane(restart) != 0;
-    barrier();  // every wave has read the flag
-    if (redo) {
-      if (tid == 0) restart = 0;  // ordered before any new write by the item's barriers
-      again = true;
+    const bool do_track = __builtin_amdgcn_readfirstlane(retrack) != 0;
+    const bool do_final = __builtin_amdgcn_readfirstlane(restart) != 0;
+    barrier();  // every wave has read the flags
+    if (do_track || do_final) {
+      if (tid == 0) {  // ordered before any new write by the item's barriers
+        restart = 0;
+        retrack = 0;
+      }
+      pass = do_track ? kTrack : kFinal;
       continue;
     }
-    again = false;
+    pass = kFirst;
     ++idx;
 
-    // Finish: the row sums are split over the two halves of the wave.  Lane
+    // Finish: every lane holds its row's sum (ssum).  Lane
     // l holds O^T[d][row] for d = 32 nb + 8 b + 4 half + j (element 4 b + j
     // of block nb); lanes l and l ^ 32 hold the same row.  Output rows
     // (bf16): one swap between the halves per pair of b gives each lane eight
@@ -781,7 +864,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     // lane's four consecutive dims are 16 bytes already.
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-      const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32, 64);
+      const float ltot = ssum[rb][0];
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
       const float lse_nat = ltot > 0.f ? (m[rb] + log2f(ltot)) * kLn2 : -INFINITY;
       const int32_t i_tok = q0 + t_of[rb];
