@@ -230,6 +230,42 @@ def test_scores_jump_far_above_the_first_tiles(case):
     check_full(spec, meta, tensors, num_cus=num_cus, label=f"growing {dtype} d{dqk}")
 
 
+
+DEEP = [
+    # (dtype, hq, hkv, dqk, dv, P, qo, kv, log2 score of every key against 0)
+    ("bf16", 16, 2, 128, 128, 16, [1, 5, 40], [700, 300, 500], -300.0),  # every P underflows
+    ("bf16", 16, 2, 128, 128, 16, [1, 5, 40], [700, 300, 500], -80.0),   # sums below 2^-64
+    ("bf16", 128, 1, 576, 512, 64, [2, 1], [900, 400], -300.0),          # latent
+    ("f32", 8, 2, 64, 64, 16, [1, 3], [300, 200], -300.0),               # generic
+]
+
+
+@pytest.mark.parametrize("case", DEEP, ids=[f"d{i}" for i in range(len(DEEP))])
+def test_scores_far_below_zero(case):
+    # Every key close to one vector u and every query -beta u: all scores of a
+    # row sit near one large negative value, so that against a reference of 0
+    # every P underflows (or every row sum falls below 2^-64).  The softmax is
+    # well defined (weights near uniform): each kernel must move its reference
+    # down to the scores.
+    dtype, hq, hkv, dqk, dv, P, qo, kv, target = case
+    spec = small_spec(dtype, hq, hkv, dqk, dv, P, True, 53)
+    meta = workloads.make_meta(qo, kv, P, 53)
+    tensors = workloads.make_tensors(spec, meta, 53, device="cuda")
+    gen = torch.Generator().manual_seed(53)
+    u = torch.randn(dqk, generator=gen)
+    u *= math.sqrt(dqk) / float(u.norm())  # |u|^2 = dqk
+    beta = -target / (dqk * spec.sm_scale * math.log2(math.e))
+    used = torch.from_numpy(workloads.referenced_pages(meta))
+    kp = tensors["k_pool"]
+    keys = (u + 0.02 * torch.randn(tuple(kp.shape), generator=gen)).to(kp.dtype)
+    kp[used.cuda()] = keys[used].cuda()
+    kn = tensors["k_new"]
+    kn.copy_((u + 0.02 * torch.randn(tuple(kn.shape), generator=gen)).to(kn.dtype).cuda())
+    tensors["q"].copy_((-beta * u).expand(tuple(tensors["q"].shape)).to(tensors["q"].dtype).cuda())
+    log(f"case {case}")
+    check_full(spec, meta, tensors, label=f"deep {dtype} d{dqk} {target}")
+
+
 LONG = [
     # (dtype, hq, hkv, dqk, dv, P, qo, kv, num_cus): few compute units, so pieces stay long
     ("bf16", 32, 8, 128, 128, 16, [1, 4], [40000, 9000], 1),    # decode pieces past 256 pages
