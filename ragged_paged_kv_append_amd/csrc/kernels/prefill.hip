@@ -435,7 +435,10 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     };
 
     const float sc = p.sm_scale * kLog2e;
-    // The reference of each row (first pass 0).
+    // The reference of each row: 0 in the first and kTrack passes.  Rows past
+    // the item take one far above any score, so that their P are 0: one
+    // overflowing P of any row would turn the sums of the rows that share its
+    // mfma_sum product into NaN (inf times a zero of the selector).
     float m[2];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
@@ -855,9 +858,9 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     pass = kFirst;
     ++idx;
 
-    // Finish: every lane holds its row's sum (ssum).  Lane
-    // l holds O^T[d][row] for d = 32 nb + 8 b + 4 half + j (element 4 b + j
-    // of block nb); lanes l and l ^ 32 hold the same row.  Output rows
+    // Finish: every lane holds its row's sum (ssum).  Lane l holds O^T[d][row]
+    // for d = 32 nb + 8 b + 4 half + j (element 4 b + j of block nb); lanes l
+    // and l ^ 32 hold the same row.  Output rows
     // (bf16): one swap between the halves per pair of b gives each lane eight
     // consecutive dims (half 0 those of the even b, half 1 those of the odd
     // b), stored as 16 bytes.  Partial rows of a split piece (float32): each
