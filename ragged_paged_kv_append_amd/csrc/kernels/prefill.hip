@@ -519,11 +519,17 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     // Steps whose keys start at or past this need the mask.
     const int32_t mask_kb = mask_from - kStep + 1;
 
+    // Page ids and tree-mask rows complete first: the compiler's own wait for
+    // them drains every vector-memory operation, so it must come before the
+    // untracked loads (Q, the DMA) are issued.
+    asm volatile("" : "+v"(pid));
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) asm volatile("" : "+v"(tm_lo[rb]), "+v"(tm_hi[rb]));
     // Q operand of the S^T products: qf[rb][i] = Q[row 32 rb + col][16 i + 8 half .. + 8),
-    // loaded into AGPRs from inline assembly while the page ids are on their
-    // way (the previous item's last products read qf long before its stores).
-    // Rows past the item read a valid row of the request (t_of = 0): their
-    // results are never stored.
+    // loaded into AGPRs from inline assembly, so that its latency overlaps
+    // that of the first tiles (the previous item's last products read qf long
+    // before its stores).  Rows past the item read a valid row of the request
+    // (t_of = 0): their results are never stored.
     u32x4_t qf[2][8];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
@@ -536,15 +542,8 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
                      : "v"(qrow + 16 * i)
                      : "memory");
     }
-    // Page ids, Q and tree-mask rows complete before the DMA (the compiler's
-    // own wait for them, which drains every vector-memory load, must not
-    // drain the DMA stream later).
-    wait_vmem<0>();
-    asm volatile("" : "+v"(pid));
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) asm volatile("" : "+v"(tm_lo[rb]), "+v"(tm_hi[rb]));
     barrier();  // the previous item's waves are done with the ring
-    // Tiles 0 and 1: the products start once tile 0 is in (vector-memory
+    // Tiles 0 and 1: the products start once Q and tile 0 are in (vector-memory
     // loads complete in order), while tile 1 lands.
     {
       const DmaTile d = dma_setup(0);
@@ -556,7 +555,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
 #pragma unroll
       for (int x = 0; x < kDmaInst; ++x) dma_x(d, x);
     }
-    wait_vmem<kDmaInst>();  // tile 0 is in; tile 1 may still be in flight
+    wait_vmem<kDmaInst>();  // Q and tile 0 are in; tile 1 may still be in flight
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
@@ -842,29 +841,15 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     }
     if (track) retrack = 1;
     if (shift) restart = 1;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    barrier();
-    const bool do_track = __builtin_amdgcn_readfirstlane(retrack) != 0;
-    const bool do_final = __builtin_amdgcn_readfirstlane(restart) != 0;
-    barrier();  // every wave has read the flags
-    if (do_track || do_final) {
-      if (tid == 0) {  // ordered before any new write by the item's barriers
-        restart = 0;
-        retrack = 0;
-      }
-      pass = do_track ? kTrack : kFinal;
-      continue;
-    }
-    pass = kFirst;
-    ++idx;
-
-    // Finish: every lane holds its row's sum (ssum).  Lane l holds O^T[d][row]
-    // for d = 32 nb + 8 b + 4 half + j (element 4 b + j of block nb); lanes l
-    // and l ^ 32 hold the same row.  Output rows
-    // (bf16): one swap between the halves per pair of b gives each lane eight
-    // consecutive dims (half 0 those of the even b, half 1 those of the odd
-    // b), stored as 16 bytes.  Partial rows of a split piece (float32): each
-    // lane's four consecutive dims are 16 bytes already.
+    // Finish, before the workgroup learns whether the item is done over (a
+    // pass that is done over stores its rows again, later in program order),
+    // so that the stores overlap the wait for the other waves.  Every lane
+    // holds its row's sum (ssum).  Lane l holds O^T[d][row] for d = 32 nb +
+    // 8 b + 4 half + j (element 4 b + j of block nb); lanes l and l ^ 32 hold
+    // the same row.  Output rows (bf16): one swap between the halves per pair
+    // of b gives each lane eight consecutive dims (half 0 those of the even b,
+    // half 1 those of the odd b), stored as 16 bytes.  Partial rows of a split
+    // piece (float32): each lane's four consecutive dims are 16 bytes already.
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       const float ltot = ssum[rb][0];
@@ -912,6 +897,21 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
         if (half == 0) p.part_lse[prow * p.num_qo_heads + hh] = lse_nat;
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier();
+    const bool do_track = __builtin_amdgcn_readfirstlane(retrack) != 0;
+    const bool do_final = __builtin_amdgcn_readfirstlane(restart) != 0;
+    barrier();  // every wave has read the flags
+    if (do_track || do_final) {
+      if (tid == 0) {  // ordered before any new write by the item's barriers
+        restart = 0;
+        retrack = 0;
+      }
+      pass = do_track ? kTrack : kFinal;
+      continue;
+    }
+    pass = kFirst;
+    ++idx;
   }
 }
 
