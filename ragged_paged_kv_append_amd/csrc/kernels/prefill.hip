@@ -359,6 +359,9 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     const int32_t L = uni(p.kv_len[r]);
     const int32_t S = uni(p.split[r * SP_WORDS + SP_COUNT]);     // pieces of this request
     const int32_t part0 = uni(p.split[r * SP_WORDS + SP_BASE]);  // its first partial row
+    // (read with the other per-request values: where it is used, the load
+    // would add a level of memory latency before the first tile)
+    const int32_t pg_base = uni(p.page_indptr[r]);
     const int32_t cached = L - n;
     // A request with a tree mask sees every key up to L - 1, filtered among
     // the new tokens by its 64-bit mask row.
@@ -393,7 +396,7 @@ void prefill_kernel(PrefillPart part0, PrefillPart part1, int32_t wgs0,
     const int32_t nsteps = (kend - k0 + kStep - 1) / kStep;
     const int32_t ntiles = (nsteps + 1) / 2;
 
-    const int32_t* pages = p.page_indices + p.page_indptr[r];
+    const int32_t* pages = p.page_indices + pg_base;
     const char* kbase = reinterpret_cast<const char*>(kc + (int64_t)g * ks.head);
     const char* vbase = reinterpret_cast<const char*>(vc + (int64_t)g * vs.head);
     // Page id of the first key row this wave moves for tile T, in lane T (the
