@@ -386,6 +386,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 sacc[b][rb][i] =
                     (kb + 16 * b + 4 * kg + i < kend_row[rb]) ? sacc[b][rb][i] : kMinusBig;
         }
+        // This lane's largest score of each row.  The row's largest (a
+        // reduction over the four lane groups kg) is needed only when some
+        // lane's own would move its row's reference, which after a row's
+        // first tile is rare: a wave-uniform branch skips the reduction.
+        float mxl[2];
+        bool up = false;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           float mx = kMinusBig;
@@ -393,14 +399,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[b][rb][i]);
-          mx = max_halves(max_rows16(mx));  // over the four lane groups kg
-          const float mt = mx > 0.5f * kMinusBig ? mx * sc : kMinusBig;
-          if (mt > m[rb] + kRestartSlack) {
-            // While the row has seen no key its O and sum are still zero:
-            // the first reference costs nothing.
-            if (m[rb] > 0.5f * kMinusBig) moved = true;
-            m[rb] = mt;
+          mxl[rb] = mx;
+          up |= (mx > 0.5f * kMinusBig ? mx * sc : kMinusBig) > m[rb] + kRestartSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const float mx = max_halves(max_rows16(mxl[rb]));
+            const float mt = mx > 0.5f * kMinusBig ? mx * sc : kMinusBig;
+            if (mt > m[rb] + kRestartSlack) {
+              // While the row has seen no key its O and sum are still zero:
+              // the first reference costs nothing.
+              if (m[rb] > 0.5f * kMinusBig) moved = true;
+              m[rb] = mt;
+            }
           }
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
           // Masked scores sit at kMinusBig: against a finite reference their
           // exponent is hugely negative (P = 0); a row with no key yet takes
           // reference 0 here, which gives the same.
