@@ -323,14 +323,19 @@ __global__ __launch_bounds__(64) void decode_kernel(DevPlan p, const bf16_t* __r
         }
       }
     }
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = max_halves(max_rows16(mx));
     // The reference max moves only when the tile beats it by more than the
-    // slack (P then stays below 2^8), so O is rescaled on few tiles.
+    // slack (P then stays below 2^8), so O is rescaled on few tiles.  The
+    // row's largest score (a reduction over the four lanes of the row) is
+    // needed only when some lane's own beats its reference: a wave-uniform
+    // vote skips the reduction on the other tiles.
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     float alpha = 1.f;
-    if (mx > m + kRescaleSlack) {
-      if (m > 0.5f * kMinusBig) alpha = __builtin_amdgcn_exp2f(m - mx);
-      m = mx;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      mx = max_halves(max_rows16(mx));
+      if (mx > m + kRescaleSlack) {
+        if (m > 0.5f * kMinusBig) alpha = __builtin_amdgcn_exp2f(m - mx);
+        m = mx;
+      }
     }
     // Masked keys sit at kMinusBig; a row with no key yet takes reference 0,
     // so they still come out as 0.
