@@ -6,9 +6,9 @@
 // range.  A one-wave workgroup runs its list of work items, in turn; an item
 // is request r, KV head g, all of its n_r * G query rows (at most 16: decode
 // rows and verify rows of n + 1 draft tokens, "Accelerating Sonar through
-// speculation"), keys [k0, k1).  The item streams its keys in tiles of 16 tokens (one page head slice for P = 16, a
-// quarter page for P = 64), so every tile is one contiguous 4 KiB run of K and
-// one of V in the HND layout.
+// speculation"), keys [k0, k1).  The item streams its keys in tiles of 16
+// tokens (one page head slice for P = 16, a quarter page for P = 64), so every
+// tile is one contiguous 4 KiB run of K and one of V in the HND layout.
 //
 // Streaming: tiles move from HBM into a ring of kStages LDS slots with the
 // gfx950 global-to-LDS DMA (global_load_lds_dwordx4, 1 KiB per instruction),

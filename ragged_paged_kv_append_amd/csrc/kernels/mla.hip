@@ -148,7 +148,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ uint32_t doff[10][64 * kWaves];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const uint32_t ring_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)ring;
+  const uint32_t ring_lds =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)ring;
 
   // ---- S-phase role: rows 32 wave + 16 rb + kq, keys 16 kb + 4 kg + i -------------
   const int kq = lane & 15, kg = lane >> 4;

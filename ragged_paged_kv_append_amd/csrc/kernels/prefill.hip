@@ -10,12 +10,12 @@
 // r, KV head g, up to 256 query rows (row = token * G + head-in-group, so the
 // G query heads sharing a KV head sit in one tile and share its K/V loads),
 // keys [k0, k1).  Each wavefront owns one 32-row block and half the register
-// file of its SIMD: Q of its rows and the S^T accumulators in VGPRs, the O^T
-// accumulators in AGPRs.  (The code also builds with four wavefronts of two
+// file of its SIMD: Q of its rows and the O^T accumulators in AGPRs, the S^T
+// accumulators in VGPRs.  (The code also builds with four wavefronts of two
 // blocks each, one per SIMD; two per SIMD let one wave's products run while
-// the other waits on its DMA issue or its LDS reads.)  The planner packs the items onto one
-// resident workgroup per compute unit, longest first; a workgroup runs its
-// list.
+// the other waits on its DMA issue or its LDS reads.)  The planner packs the
+// items onto one resident workgroup per compute unit, longest first; a
+// workgroup runs its list.
 //
 // K/V tiles of 64 keys (16 KiB each) move from HBM/L2 into a four-slot LDS
 // ring with the gfx950 global-to-LDS DMA, two tiles ahead; each wave moves 8
@@ -34,8 +34,8 @@
 // to bf16.  The row sums of P come from the matrix core too: two small
 // products per step multiply the P^T operands by a 0/1 selector (mfma_sum).
 // The products of one step do not depend on its vector work, so a wavefront
-// keeps its SIMD's matrix core busy while it runs the softmax in the gaps, and the SIMD's
-// second wavefront fills what the first leaves idle.
+// keeps its SIMD's matrix core busy while it runs the softmax in the gaps,
+// and the SIMD's second wavefront fills what the first leaves idle.
 //
 // The mask comes out of the matrix core with S: the first product of each
 // S^T chain accumulates onto a block that holds 0, or -1e30 for a masked
