@@ -511,7 +511,12 @@ rpa_status build_plan_impl(const rpa_attn_config* cfg, const rpa_batch_desc* bat
           items[k].insert(items[k].end(), it, it + IT_WORDS);
           const int64_t rows_cost = (k == KC_PREFILL || k == KC_MLA) ? round_up(row1 - row0, 32)
                                                                       : row1 - row0;
-          cost[k].push_back((std::min(k1, p_last + 1) - k0) * rows_cost);
+          // A prefill item also costs a fixed start and finish (its Q and
+          // first tiles, its stores), about what 256 keys take: without it
+          // the packing put short items on workgroups that were already
+          // among the busiest (one-shot prompt: 154 -> 150 us).
+          const int64_t fixed = k == KC_PREFILL ? 256 : 0;
+          cost[k].push_back((std::min(k1, p_last + 1) - k0 + fixed) * rows_cost);
         }
       }
     }
