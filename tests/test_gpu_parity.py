@@ -132,6 +132,29 @@ def test_interleaved_kv_pages():
     o, lse, _ = check_full(spec, meta, tensors, label="interleaved")
 
 
+def test_step_without_new_tokens_changes_nothing():
+    """Requests with cached keys but no new token: the append writes no slot,
+    attention has no query row, and the pools keep every byte (fused and split
+    execution alike)."""
+    spec = small_spec("bf16", 8, 2, 128, 128, 16, True, 13)
+    meta = workloads.make_meta([0, 0, 0], [70, 0, 33], 16, 13)
+    tensors = workloads.make_tensors(spec, meta, 13, device="cuda")
+    kp0, vp0 = raw(tensors["k_pool"]).tobytes(), raw(tensors["v_pool"]).tobytes()
+    cfg = config_of(spec)
+    plan = rpa.Plan(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr, meta.kv_page_indices,
+                    meta.num_pages)
+    plan.append(tensors["k_new"], tensors["v_new"], tensors["k_pool"], tensors["v_pool"])
+    o, lse = plan.attention(tensors["q"], tensors["k_pool"], tensors["v_pool"])
+    split = rpa.SplitChunkAttention(cfg, meta.qo_indptr, meta.kv_len, meta.kv_page_indptr,
+                                    meta.kv_page_indices, meta.num_pages)
+    o2, lse2 = split.run(tensors["q"], tensors["k_new"], tensors["v_new"], tensors["k_pool"],
+                         tensors["v_pool"])
+    torch.cuda.synchronize()
+    assert o.shape == (0, 8, 128) and lse.shape == (0, 8)
+    assert o2.shape == (0, 8, 128) and lse2.shape == (0, 8)
+    assert raw(tensors["k_pool"]).tobytes() == kp0 and raw(tensors["v_pool"]).tobytes() == vp0
+
+
 def test_deterministic_outputs():
     spec = small_spec("bf16", 16, 4, 128, 128, 16, True, 3)
     meta = workloads.make_meta([1, 4, 40], [3000, 2000, 800], 16, 3)
